@@ -1,0 +1,204 @@
+/*
+ * gva.h - C ABI of a Grouped Value Attention (GVA) decode library for AMD MI355X (gfx950).
+ *
+ * Sources (web pages about arXiv:2609.13285, "Grouped Value Attention: Efficient KV Caching
+ * via On-Demand Key Reconstruction"):
+ *   [review]   shibing624.github.io review, "GVA：KV 缓存里的 Key 其实可以不存"
+ *   [summary]  agihunt.info summary of the paper
+ *   [kvcache]  liumengxuan04.github.io, "KV Cache 优化（一）：从 MHA 到 MQA 与 GQA"
+ *
+ * Notation follows the pages: T cached tokens, H query heads, G value groups, d_h value
+ * width, d_n content-query width, d_r positional width, g(h) the group of head h.
+ *
+ * One layer's cache holds, per token, the G grouped values v_g (d_h wide) and ONE positional
+ * key kr (d_r wide) shared by all heads and stored already rotated ([review] section 缓存账本;
+ * section 关键技巧二). No content key is ever stored: head h's content key would be
+ * K_h = V_g(h) M_h with M_h of shape d_h x d_n ([review] section 第二次尝试), and because M_h is
+ * fixed it is folded into the query, q~_h = q_nope_h M_h^T ([review] section 关键技巧一). The
+ * score of cached position j is q~_h . v_{j,g(h)} + rot(q_rope_h) . kr_j ([review] section
+ * 关键技巧二, the two-term score), followed by a softmax and a weighted sum over the same
+ * cached values ([summary]; [kvcache] section 1).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory on the current HIP device; "host" is host
+ *     memory. All device buffers are owned by the caller; the library allocates nothing.
+ *   - Every call is asynchronous on `stream` and does no host/device synchronisation.
+ *   - Inputs are read-only; outputs are fully overwritten and must not alias inputs.
+ *   - Argument errors are detected on the host and returned before any launch; the detail
+ *     is available from gva_last_error() on the calling thread.
+ *   - Errors that only the device can see (a bad block-table entry, a position beyond the
+ *     cache or the RoPE table, a length above the stated bound) set bits in *err_flag when
+ *     err_flag is not NULL; the affected token is not written (append) or the affected
+ *     output row is filled with NaN (decode, prefill).
+ *   - Grouping is contiguous: g(h) = h / (H / G), with H a multiple of G.
+ *   - RoPE pairs are interleaved: (x[2i], x[2i+1]) is rotated by p * theta_i.
+ */
+#ifndef GVA_H_
+#define GVA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gva_status {
+  GVA_OK = 0,
+  GVA_ERR_INVALID_ARG = 1,   /* a NULL pointer, a bad size, stride or alignment */
+  GVA_ERR_UNSUPPORTED = 2,   /* valid arguments outside what the kernels implement */
+  GVA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than gva_decode_workspace_bytes */
+  GVA_ERR_HIP = 4            /* a HIP launch failed */
+} gva_status;
+
+typedef enum gva_dtype {
+  GVA_DTYPE_F32 = 0,
+  GVA_DTYPE_BF16 = 1
+} gva_dtype;
+
+/* Bits set in *err_flag by device-side checks (sticky: the library only ORs bits in). */
+enum {
+  GVA_DEVERR_BLOCK = 1,      /* block-table entry outside [0, num_blocks) */
+  GVA_DEVERR_CAPACITY = 2,   /* position >= max_blocks * block_size */
+  GVA_DEVERR_ROPE = 4,       /* position >= max_pos of the RoPE table */
+  GVA_DEVERR_SEQ = 8,        /* sequence index outside [0, B) */
+  GVA_DEVERR_LENGTH = 16     /* negative position or length, or length above max_len */
+};
+
+/* Which decode kernel runs. AUTO picks the MFMA kernel when the shape allows it. */
+typedef enum gva_decode_kernel {
+  GVA_KERNEL_AUTO = 0,
+  GVA_KERNEL_GENERIC = 1,    /* vector-ALU kernel: any supported shape and dtype */
+  GVA_KERNEL_MFMA = 2        /* matrix-core kernel: bf16 cache, see gva_decode */
+} gva_decode_kernel;
+
+/* Model shape in the pages' notation. Limits: 1 <= G <= H, H % G == 0, H <= 256,
+ * 2 <= d_h <= 256 and even, 1 <= d_n <= 512, 2 <= d_r <= 64 and even. */
+typedef struct gva_dims {
+  int32_t H;
+  int32_t G;
+  int32_t d_h;
+  int32_t d_n;
+  int32_t d_r;
+} gva_dims;
+
+/* One layer's cache, paged or contiguous, described by element strides.
+ *   V(blk, tok, g, i) = v [blk * v_stride_block  + tok * v_stride_token  + g * v_stride_group + i]
+ *   kr(blk, tok, i)   = kr[blk * kr_stride_block + tok * kr_stride_token + i]
+ * Position p of sequence b lives in block block_table[b * max_blocks + p / block_size] at
+ * token offset p % block_size. A contiguous cache is one block per sequence with
+ * block_size >= its capacity. Paging only changes where entries live ([kvcache] section 7). */
+typedef struct gva_cache {
+  gva_dtype dtype;                 /* element type of v and kr */
+  void *v;                         /* device, 16-byte aligned */
+  void *kr;                        /* device, 16-byte aligned */
+  int64_t v_stride_block;          /* element strides, each >= 0 */
+  int64_t v_stride_token;
+  int64_t v_stride_group;
+  int64_t kr_stride_block;
+  int64_t kr_stride_token;
+  int64_t num_blocks;              /* blocks in the pool; block ids are in [0, num_blocks) */
+  int32_t block_size;              /* tokens per block, a power of two */
+  int32_t max_blocks;              /* columns of block_table */
+  const int32_t *block_table;      /* device int32 [B][max_blocks] */
+  const double *rope;              /* device float64 [max_pos][d_r / 2][2] = (cos, sin) */
+  int32_t max_pos;                 /* rows of the RoPE table */
+  int32_t *err_flag;               /* device, nullable: sticky GVA_DEVERR_* bits */
+} gva_cache;
+
+/* ---- RoPE table ------------------------------------------------------------------------
+ * Rows p = 0 .. max_pos-1, pairs i = 0 .. d_r/2-1: (cos(p * theta_i), sin(p * theta_i)) with
+ * theta_i = base^(-2i / d_r), evaluated in float64 with the C library's pow, cos and sin.
+ * The positional slice is rotated by position ([review] section 关键技巧二); the frequency
+ * convention is the usual RoPE one. */
+size_t gva_rope_table_bytes(int32_t max_pos, int32_t d_r);
+/* host_out: host float64 buffer of gva_rope_table_bytes(max_pos, d_r) bytes. */
+gva_status gva_rope_table_fill(double *host_out, int32_t max_pos, int32_t d_r, double base);
+
+/* ---- Cache append ([review] section 关键技巧二: the shared positional key is cached already
+ * rotated; [kvcache] section 1: a new token's state is appended before the query reads the
+ * history) -----------------------------------------------------------------------------------
+ * Writes n_tok tokens. Token k belongs to sequence seq[k] in [0, B) at position pos[k]:
+ *   V(slot, g, :) = round(v_new[k][g][:])                    for every group g
+ *   kr(slot, :)   = round(rotate(kr_raw[k][:], pos[k]))      rotation in float64
+ * where round() is one round-to-nearest-even to the cache type and rotate() forms each pair
+ * as (x0*c - x1*s, x0*s + x1*c) with every product and sum rounded to float64 (no fused
+ * multiply-add). The result is bit-exact and independent of launch configuration.
+ *   seq, pos: device int32 [n_tok]. v_new: device float32 [n_tok][G][d_h].
+ *   kr_raw: device float32 [n_tok][d_r]. Two tokens must not target the same slot.
+ * A token with a bad index is skipped and raises its GVA_DEVERR_* bit. */
+gva_status gva_cache_append(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                            int32_t n_tok, const int32_t *seq, const int32_t *pos,
+                            const float *v_new, const float *kr_raw, hipStream_t stream);
+
+/* ---- Query absorption ([review] section 关键技巧一: q~_h = q_nope_h M_h^T once per query
+ * token; section 关键技巧二: the positional slice is rotated at the query's position) --------
+ *   q_abs[k][h][0 .. d_h)         = q~_h,   q~_h[i] = sum_j M[h][i][j] * q_nope[k][h][j]
+ *   q_abs[k][h][d_h .. d_h + d_r) = float32(rotate(q_rope[k][h][:], q_pos[k]))
+ * The q~ part accumulates in float32 (error within d_n * 2^-24 * sum_j |M q|); the rotated
+ * part is one rounding of the float64 rotation.
+ *   q_nope: device float32 [n_q][H][d_n]. q_rope: device float32 [n_q][H][d_r].
+ *   q_pos: device int32 [n_q]. M: device float32 [H][d_h][d_n].
+ *   rope/max_pos: the device RoPE table. q_abs: device float32 [n_q][H][d_h + d_r] (output).
+ * A position outside [0, max_pos) writes NaN into that token's q_abs and raises
+ * GVA_DEVERR_ROPE in *err_flag (nullable). */
+gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_nope,
+                            const float *q_rope, const int32_t *q_pos, const float *M,
+                            const double *rope, int32_t max_pos, float *q_abs,
+                            int32_t *err_flag, hipStream_t stream);
+
+/* ---- Decode ([review] sections 关键技巧一 and 关键技巧二; [kvcache] section 1) -------------------
+ * For every sequence b and head h, over the cached positions j < seq_len[b]:
+ *   s_j = scale * (q~_h . V(j, g(h), :) + r_h . kr(j, :))   with [q~_h ; r_h] = q_abs[b][h]
+ *   out[b][h][:] = sum_j softmax(s)_j V(j, g(h), :),   lse[b][h] = ln sum_j exp(s_j)
+ * The positions are split into num_splits contiguous chunks processed in parallel and merged
+ * through their log-sum-exp. seq_len[b] == 0 gives out = 0 and lse = -inf.
+ *   seq_len: device int32 [B]. max_len: host upper bound on every seq_len[b] (it sizes the
+ *   split plan; a larger length raises GVA_DEVERR_LENGTH and makes that row NaN).
+ *   q_abs: device float32 [B][H][d_h + d_r]. out: device float32 [B][H][d_h].
+ *   lse: device float32 [B][H] or NULL.
+ *   num_splits: 0 = choose automatically, else 1 .. 1024 (rounded down so no chunk is empty
+ *   for a sequence of max_len tokens).
+ *   kernel: GVA_KERNEL_* ; the MFMA kernel needs a bf16 cache, d_h % 32 == 0, d_h <= 256,
+ *   d_r % 8 == 0, d_r <= 32, H / G <= 16, G <= 16, block_size >= 16, every stride a multiple
+ *   of 8 elements (returns GVA_ERR_UNSUPPORTED otherwise).
+ *   workspace: device, 256-byte aligned, at least gva_decode_workspace_bytes(...) bytes. */
+size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
+                                  int32_t num_splits);
+/* The split count gva_decode will use for these arguments (0 on bad arguments). */
+int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,
+                              int32_t num_splits);
+gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                      const int32_t *seq_len, int32_t max_len, const float *q_abs, float scale,
+                      int32_t num_splits, int32_t kernel, void *workspace,
+                      size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
+
+/* ---- Chunked prefill ([summary]: prefill stays a dense, matrix-heavy pass) -----------------
+ * Appends chunk_len new tokens per sequence at positions start[b] .. start[b] + chunk_len - 1
+ * (exactly as gva_cache_append would), then for query i of sequence b, at position
+ * start[b] + i, attends causally to positions 0 .. start[b] + i inclusive with the decode
+ * score above, reading the cache-rounded values.
+ *   start: device int32 [B]; max_start: host upper bound on start[b].
+ *   q_abs: device float32 [B][chunk_len][H][d_h + d_r] (absorbed at positions start[b] + i).
+ *   v_new: device float32 [B][chunk_len][G][d_h]; kr_raw: device float32 [B][chunk_len][d_r].
+ *   out: device float32 [B][chunk_len][H][d_h]; lse: device float32 [B][chunk_len][H] or NULL.
+ * Needs a bf16 cache and the MFMA kernel's shape limits (see gva_decode). */
+gva_status gva_prefill_chunk(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                             const int32_t *start, int32_t max_start, int32_t chunk_len,
+                             const float *q_abs, const float *v_new, const float *kr_raw,
+                             float scale, float *out, float *lse, hipStream_t stream);
+
+/* ---- Diagnostics --------------------------------------------------------------------------- */
+const char *gva_status_string(gva_status status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *gva_last_error(void);
+/* Library version string. */
+const char *gva_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GVA_H_ */

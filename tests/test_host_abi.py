@@ -1,0 +1,215 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every entry point that
+include/gva.h declares, rejects bad arguments before any launch, plans splits, and fills a RoPE
+table bit-identical to the oracle's. None of these tests launches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import gva_oracle as O
+from value_only_kv_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gva.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gb.LIB_PATH):
+        from value_only_kv_amd import _build
+        _build.build()
+    return gb.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gva_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert len(declared) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", gb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(gva_\w+)", out))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    assert sorted(gb.EXPORTED) == declared
+    for f in declared:
+        assert hasattr(L, f)
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in gb.gva_version()
+    for s, name in enumerate(["GVA_OK", "GVA_ERR_INVALID_ARG", "GVA_ERR_UNSUPPORTED",
+                              "GVA_ERR_WORKSPACE", "GVA_ERR_HIP"]):
+        assert L.gva_status_string(s).decode() == name
+
+
+@pytest.mark.parametrize("max_pos,d_r", [(1, 2), (300, 16), (1025, 24), (77, 64)])
+def test_rope_table_bit_identical_to_oracle(L, max_pos, d_r):
+    lib_tab = gb.gva_rope_table_fill(max_pos, d_r, 10000.0)
+    ora_tab = O.rope_table(max_pos, d_r, 10000.0)
+    assert lib_tab.tobytes() == ora_tab.tobytes()
+    assert gb.gva_rope_table_bytes(max_pos, d_r) == ora_tab.nbytes
+
+
+def test_rope_table_rejects_bad_arguments(L):
+    buf = np.empty(64, dtype=np.float64)
+    for args in [(0, 16, 1e4), (4, 3, 1e4), (4, 0, 1e4), (4, 66, 1e4), (4, 16, -1.0),
+                 (4, 16, float("inf"))]:
+        assert L.gva_rope_table_fill(buf.ctypes.data, *args) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_rope_table_fill(None, 4, 16, 1e4) == gb.GVA_ERR_INVALID_ARG
+    assert gb.gva_rope_table_bytes(0, 16) == 0 and gb.gva_rope_table_bytes(4, 5) == 0
+
+
+# ---- validation, with fake (never dereferenced) device addresses ----------------------------
+
+A = 1 << 20  # an aligned fake address
+
+
+def _dims(H=32, G=8, d_h=128, d_n=128, d_r=16):
+    return gb.GvaDims(H, G, d_h, d_n, d_r)
+
+
+def _cache(dtype=gb.GVA_DTYPE_BF16, bs=16, max_blocks=8, num_blocks=64, d=None, **kw):
+    d = d or _dims()
+    s = gb.GvaCacheStruct()
+    s.dtype = dtype
+    s.v, s.kr = A, A + 4096
+    s.v_stride_block = d.G * bs * d.d_h
+    s.v_stride_token = d.d_h
+    s.v_stride_group = bs * d.d_h
+    s.kr_stride_block = bs * d.d_r
+    s.kr_stride_token = d.d_r
+    s.num_blocks, s.block_size, s.max_blocks = num_blocks, bs, max_blocks
+    s.block_table, s.rope, s.max_pos, s.err_flag = A + 8192, A + 16384, 1024, None
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _decode(L, d, c, B=2, seq_len=A, max_len=100, q_abs=A, scale=0.1, S=0, kernel=0, ws=None,
+            ws_bytes=0, out=A, lse=None):
+    return L.gva_decode(ctypes.byref(d), ctypes.byref(c), B, seq_len, max_len, q_abs, scale, S,
+                        kernel, ws, ws_bytes, out, lse, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(H=0), dict(H=257), dict(G=0), dict(G=5), dict(H=12, G=8), dict(d_h=0), dict(d_h=7),
+    dict(d_h=258), dict(d_n=0), dict(d_n=513), dict(d_r=0), dict(d_r=3), dict(d_r=66),
+])
+def test_decode_rejects_bad_dims(L, bad):
+    kw = dict(H=32, G=8, d_h=128, d_n=128, d_r=16)
+    kw.update(bad)
+    d = gb.GvaDims(**kw)
+    assert _decode(L, d, _cache()) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("field,value", [
+    ("dtype", 7), ("v", None), ("kr", None), ("v", A + 2), ("kr", A + 8), ("block_table", None),
+    ("rope", None), ("rope", A + 8), ("max_pos", 0), ("num_blocks", 0), ("block_size", 12),
+    ("block_size", 0), ("max_blocks", 0), ("v_stride_token", -8), ("kr_stride_token", 3),
+    ("kr_stride_token", 8), ("num_blocks", 1 << 40),
+])
+def test_decode_rejects_bad_cache(L, field, value):
+    assert _decode(L, _dims(), _cache(**{field: value})) == gb.GVA_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_call_arguments(L):
+    d, c = _dims(), _cache()
+    assert _decode(L, d, c, B=0) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, seq_len=None) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, q_abs=None) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, q_abs=A + 4) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, out=None) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, max_len=-1) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, max_len=8 * 16 + 1) == gb.GVA_ERR_INVALID_ARG  # beyond capacity
+    assert _decode(L, d, c, scale=0.0) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, scale=float("nan")) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, S=-1) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, S=1025) == gb.GVA_ERR_INVALID_ARG
+    assert _decode(L, d, c, kernel=3) == gb.GVA_ERR_INVALID_ARG
+
+
+def test_decode_workspace_errors(L):
+    d, c = _dims(), _cache(max_blocks=64)
+    need = gb.gva_decode_workspace_bytes(d, 2, 1000, 4)
+    assert need > 0
+    assert _decode(L, d, c, max_len=1000, S=4) == gb.GVA_ERR_WORKSPACE
+    assert _decode(L, d, c, max_len=1000, S=4, ws=A, ws_bytes=need - 1) == gb.GVA_ERR_WORKSPACE
+    assert _decode(L, d, c, max_len=1000, S=4, ws=A + 16, ws_bytes=need) == gb.GVA_ERR_WORKSPACE
+
+
+def test_mfma_kernel_shape_limits(L):
+    # forcing the matrix-core kernel on shapes it does not cover is GVA_ERR_UNSUPPORTED
+    cases = [
+        (_dims(), _cache(dtype=gb.GVA_DTYPE_F32)),
+        (_dims(d_h=48, d_n=48), _cache(d=_dims(d_h=48, d_n=48))),
+        (_dims(d_r=20), _cache(d=_dims(d_r=20), kr_stride_token=24)),
+        (_dims(d_r=40), _cache(d=_dims(d_r=40))),
+        (_dims(H=64, G=2), _cache(d=_dims(H=64, G=2))),
+        (_dims(H=32, G=32), _cache(d=_dims(H=32, G=32))),
+        (_dims(), _cache(bs=8, max_blocks=16)),
+        (_dims(), _cache(v_stride_token=132)),
+    ]
+    for d, c in cases:
+        assert _decode(L, d, c, S=1, kernel=gb.GVA_KERNEL_MFMA) == gb.GVA_ERR_UNSUPPORTED
+
+
+def test_split_planning(L):
+    d = _dims()
+    # automatic: long single sequences get ~one chunk per compute unit, chunks are multiples of 64
+    S = gb.gva_decode_num_splits(d, 1, 131072, 0)
+    assert S == 256
+    assert gb.gva_decode_num_splits(d, 256, 32769, 0) == 17
+    # explicit split counts are kept unless a chunk would start beyond max_len
+    for S in (64, 128, 256):
+        assert gb.gva_decode_num_splits(d, 1, 131072, S) == S
+    assert gb.gva_decode_num_splits(d, 1, 100, 8) == 2        # chunks of 64 positions
+    assert gb.gva_decode_num_splits(d, 1, 0, 0) == 1
+    assert gb.gva_decode_workspace_bytes(d, 1, 131072, 1) == 0
+    ws = gb.gva_decode_workspace_bytes(d, 4, 5000, 8)
+    S = gb.gva_decode_num_splits(d, 4, 5000, 8)
+    assert ws >= 4 * S * 32 * (128 + 2) * 4 and ws % 256 == 0
+    assert gb.gva_decode_num_splits(d, 0, 10, 0) == 0
+
+
+def test_append_and_absorb_validation(L):
+    d, c = _dims(), _cache()
+    app = lambda **kw: L.gva_cache_append(ctypes.byref(d), ctypes.byref(kw.get("c", c)),
+                                          kw.get("B", 2), kw.get("n", 3), kw.get("seq", A),
+                                          kw.get("pos", A), kw.get("v", A), kw.get("kr", A), None)
+    assert app(n=0) == gb.GVA_OK                  # nothing to do, nothing launched
+    assert app(B=0) == gb.GVA_ERR_INVALID_ARG
+    assert app(n=-1) == gb.GVA_ERR_INVALID_ARG
+    assert app(seq=None) == gb.GVA_ERR_INVALID_ARG
+    assert app(v=A + 4) == gb.GVA_ERR_INVALID_ARG
+    assert app(c=_cache(block_size=3)) == gb.GVA_ERR_INVALID_ARG
+    ab = lambda **kw: L.gva_absorb_query(ctypes.byref(kw.get("d", d)), kw.get("n", 2),
+                                         kw.get("qn", A), kw.get("qr", A), kw.get("qp", A),
+                                         kw.get("M", A), kw.get("rope", A), kw.get("mp", 10),
+                                         kw.get("out", A), None, None)
+    assert ab(n=0) == gb.GVA_OK
+    assert ab(n=-2) == gb.GVA_ERR_INVALID_ARG
+    assert ab(M=None) == gb.GVA_ERR_INVALID_ARG
+    assert ab(M=A + 8) == gb.GVA_ERR_INVALID_ARG
+    assert ab(mp=0) == gb.GVA_ERR_INVALID_ARG
+    assert ab(d=_dims(d_n=126)) == gb.GVA_ERR_UNSUPPORTED
+
+
+def test_prefill_validation(L):
+    d, c = _dims(), _cache(max_blocks=64)
+    pf = lambda **kw: L.gva_prefill_chunk(ctypes.byref(kw.get("d", d)), ctypes.byref(kw.get("c", c)),
+                                          2, A, kw.get("ms", 100), kw.get("C", 64), A, A, A,
+                                          kw.get("scale", 0.1), A, None, None)
+    assert pf(C=0) == gb.GVA_OK
+    assert pf(C=-1) == gb.GVA_ERR_INVALID_ARG
+    assert pf(ms=1000) == gb.GVA_ERR_INVALID_ARG           # beyond the table's capacity
+    assert pf(scale=-1.0) == gb.GVA_ERR_INVALID_ARG
+    assert pf(c=_cache(dtype=gb.GVA_DTYPE_F32, max_blocks=64)) == gb.GVA_ERR_UNSUPPORTED

@@ -1,0 +1,121 @@
+// gva_api.hip - the extern "C" entry points of the GVA library: validate on the host (no HIP
+// call before the arguments are known good), plan, then launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "gva_internal.h"
+
+namespace {
+
+gva::DecodeArgs cache_args(const gva_dims *d, const gva_cache *c) {
+  gva::DecodeArgs a{};
+  a.v = c->v;
+  a.kr = c->kr;
+  a.v_sb = c->v_stride_block;
+  a.v_st = c->v_stride_token;
+  a.v_sg = c->v_stride_group;
+  a.kr_sb = c->kr_stride_block;
+  a.kr_st = c->kr_stride_token;
+  a.num_blocks = c->num_blocks;
+  a.log2_bs = __builtin_ctz(static_cast<unsigned>(c->block_size));
+  a.max_blocks = c->max_blocks;
+  a.block_table = c->block_table;
+  a.err_flag = c->err_flag;
+  a.H = d->H;
+  a.G = d->G;
+  a.d_h = d->d_h;
+  a.d_r = d->d_r;
+  return a;
+}
+
+gva_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return GVA_OK;
+  return gva::fail(GVA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+gva_status gva_cache_append(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                            int32_t n_tok, const int32_t *seq, const int32_t *pos,
+                            const float *v_new, const float *kr_raw, hipStream_t stream) {
+  gva_status st = gva::check_append(dims, cache, B, n_tok, seq, pos, v_new, kr_raw);
+  if (st != GVA_OK) return st;
+  return hip_status(gva::launch_append(dims, cache, B, n_tok, seq, pos, v_new, kr_raw, stream),
+                    "cache append launch");
+}
+
+gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_nope,
+                            const float *q_rope, const int32_t *q_pos, const float *M,
+                            const double *rope, int32_t max_pos, float *q_abs,
+                            int32_t *err_flag, hipStream_t stream) {
+  gva_status st = gva::check_absorb(dims, n_q, q_nope, q_rope, q_pos, M, rope, max_pos, q_abs);
+  if (st != GVA_OK) return st;
+  return hip_status(gva::launch_absorb(dims, n_q, q_nope, q_rope, q_pos, M, rope, max_pos, q_abs,
+                                       err_flag, stream),
+                    "absorb launch");
+}
+
+gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                      const int32_t *seq_len, int32_t max_len, const float *q_abs, float scale,
+                      int32_t num_splits, int32_t kernel, void *workspace,
+                      size_t workspace_bytes, float *out, float *lse, hipStream_t stream) {
+  gva::DecodePlan plan{};
+  bool use_mfma = false;
+  gva_status st = gva::check_decode(dims, cache, B, seq_len, max_len, q_abs, scale, num_splits,
+                                    kernel, workspace, workspace_bytes, out, &plan, &use_mfma);
+  if (st != GVA_OK) return st;
+  gva::DecodeArgs a = cache_args(dims, cache);
+  a.B = B;
+  a.seq_len = seq_len;
+  a.max_len = max_len;
+  a.q_abs = q_abs;
+  a.qscale = scale * 1.4426950408889634f;
+  a.num_splits = plan.num_splits;
+  a.chunk = plan.chunk;
+  a.out = out;
+  a.lse = lse;
+  if (plan.num_splits > 1) {
+    char *ws = static_cast<char *>(workspace);
+    a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
+    a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
+    a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+  }
+  hipError_t e = use_mfma ? gva::launch_decode_mfma(a, stream)
+                          : gva::launch_decode_generic(a, cache->dtype == GVA_DTYPE_BF16, stream);
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+  if (plan.num_splits > 1) {
+    e = gva::launch_combine(a, stream);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return GVA_OK;
+}
+
+gva_status gva_prefill_chunk(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                             const int32_t *start, int32_t max_start, int32_t chunk_len,
+                             const float *q_abs, const float *v_new, const float *kr_raw,
+                             float scale, float *out, float *lse, hipStream_t stream) {
+  gva_status st = gva::check_prefill(dims, cache, B, start, max_start, chunk_len, q_abs, v_new,
+                                     kr_raw, scale, out);
+  if (st != GVA_OK) return st;
+  if (chunk_len == 0) return GVA_OK;
+  gva::PrefillArgs p{};
+  p.kv = cache_args(dims, cache);
+  p.kv.B = B;
+  p.kv.qscale = scale * 1.4426950408889634f;
+  p.start = start;
+  p.max_start = max_start;
+  p.chunk_len = chunk_len;
+  p.q_abs = q_abs;
+  p.out = out;
+  p.lse = lse;
+  p.v_new = v_new;
+  p.kr_raw = kr_raw;
+  p.rope = cache->rope;
+  p.max_pos = cache->max_pos;
+  return hip_status(gva::launch_prefill(p, stream), "prefill launch");
+}
+
+}  // extern "C"

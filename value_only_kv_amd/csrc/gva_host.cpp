@@ -1,0 +1,294 @@
+// gva_host.cpp - host side of the GVA library that needs no GPU: argument validation,
+// split planning, the RoPE table and the diagnostics. Compiled by the host C++ compiler;
+// nothing here calls HIP, so every check can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "gva_internal.h"
+
+namespace gva {
+
+namespace {
+thread_local std::string g_last_error;
+
+// The table holds exactly what the C library's separate cos and sin return. Calling them through
+// volatile pointers keeps the compiler from fusing the pair into one sincos call, whose last bit
+// can differ from cos for some arguments.
+double (*volatile g_libm_cos)(double) = cos;
+double (*volatile g_libm_sin)(double) = sin;
+double (*volatile g_libm_pow)(double, double) = pow;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+}  // namespace
+
+const char *last_error_cstr() { return g_last_error.c_str(); }
+
+gva_status fail(gva_status status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+gva_status check_dims(const gva_dims *d) {
+  if (!d) return fail(GVA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->H < 1 || d->H > kMaxH) return fail(GVA_ERR_INVALID_ARG, "H=%d outside [1, %d]", d->H, kMaxH);
+  if (d->G < 1 || d->G > d->H) return fail(GVA_ERR_INVALID_ARG, "G=%d outside [1, H=%d]", d->G, d->H);
+  if (d->H % d->G != 0) return fail(GVA_ERR_INVALID_ARG, "H=%d is not a multiple of G=%d", d->H, d->G);
+  if (d->d_h < 2 || d->d_h > kMaxDh || d->d_h % 2 != 0)
+    return fail(GVA_ERR_INVALID_ARG, "d_h=%d must be even and in [2, %d]", d->d_h, kMaxDh);
+  if (d->d_n < 1 || d->d_n > kMaxDn)
+    return fail(GVA_ERR_INVALID_ARG, "d_n=%d outside [1, %d]", d->d_n, kMaxDn);
+  if (d->d_r < 2 || d->d_r > kMaxDr || d->d_r % 2 != 0)
+    return fail(GVA_ERR_INVALID_ARG, "d_r=%d must be even and in [2, %d]", d->d_r, kMaxDr);
+  return GVA_OK;
+}
+
+gva_status check_cache(const gva_dims *d, const gva_cache *c) {
+  if (!c) return fail(GVA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->dtype != GVA_DTYPE_F32 && c->dtype != GVA_DTYPE_BF16)
+    return fail(GVA_ERR_INVALID_ARG, "unknown cache dtype %d", (int)c->dtype);
+  if (!c->v || !c->kr) return fail(GVA_ERR_INVALID_ARG, "cache v or kr is NULL");
+  if (!aligned(c->v, 16) || !aligned(c->kr, 16))
+    return fail(GVA_ERR_INVALID_ARG, "cache v and kr must be 16-byte aligned");
+  if (!c->block_table) return fail(GVA_ERR_INVALID_ARG, "block_table is NULL");
+  if (!c->rope) return fail(GVA_ERR_INVALID_ARG, "rope table is NULL");
+  if (!aligned(c->rope, 16)) return fail(GVA_ERR_INVALID_ARG, "rope table must be 16-byte aligned");
+  if (c->max_pos < 1) return fail(GVA_ERR_INVALID_ARG, "max_pos=%d must be >= 1", c->max_pos);
+  if (c->num_blocks < 1) return fail(GVA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (c->num_blocks > (int64_t)INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARG, "num_blocks exceeds the int32 block ids of the table");
+  if (!pow2(c->block_size) || c->block_size > (1 << 30))
+    return fail(GVA_ERR_INVALID_ARG, "block_size=%d must be a power of two", c->block_size);
+  if (c->max_blocks < 1) return fail(GVA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  if ((int64_t)c->max_blocks * c->block_size > (int64_t)INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARG, "max_blocks * block_size exceeds int32 positions");
+  const int64_t s[5] = {c->v_stride_block, c->v_stride_token, c->v_stride_group,
+                        c->kr_stride_block, c->kr_stride_token};
+  for (int i = 0; i < 5; ++i) {
+    if (s[i] < 0) return fail(GVA_ERR_INVALID_ARG, "cache strides must be >= 0");
+    if (s[i] % 2 != 0) return fail(GVA_ERR_INVALID_ARG, "cache strides must be even");
+  }
+  // Each row must fit between its neighbours: a token row of a group holds d_h elements and a
+  // positional row d_r elements. (Overlapping layouts are the caller's mistake; these checks
+  // catch the common ones.)
+  if (c->v_stride_group < d->d_h && d->G > 1 && c->v_stride_token < d->d_h)
+    return fail(GVA_ERR_INVALID_ARG, "v strides overlap rows");
+  if (c->kr_stride_token < d->d_r && c->block_size > 1)
+    return fail(GVA_ERR_INVALID_ARG, "kr_stride_token=%lld < d_r=%d",
+                (long long)c->kr_stride_token, d->d_r);
+  return GVA_OK;
+}
+
+gva_status check_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,
+                        const int32_t *seq, const int32_t *pos, const float *v_new,
+                        const float *kr_raw) {
+  gva_status st = check_dims(d);
+  if (st != GVA_OK) return st;
+  if ((st = check_cache(d, c)) != GVA_OK) return st;
+  if (B < 1) return fail(GVA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (n_tok < 0) return fail(GVA_ERR_INVALID_ARG, "n_tok=%d must be >= 0", n_tok);
+  if (n_tok == 0) return GVA_OK;
+  if (!seq || !pos || !v_new || !kr_raw) return fail(GVA_ERR_INVALID_ARG, "append input is NULL");
+  if (!aligned(v_new, 8) || !aligned(kr_raw, 8))
+    return fail(GVA_ERR_INVALID_ARG, "v_new and kr_raw must be 8-byte aligned");
+  return GVA_OK;
+}
+
+gva_status check_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, const float *q_rope,
+                        const int32_t *q_pos, const float *M, const double *rope, int32_t max_pos,
+                        const float *q_abs) {
+  gva_status st = check_dims(d);
+  if (st != GVA_OK) return st;
+  if (n_q < 0) return fail(GVA_ERR_INVALID_ARG, "n_q=%d must be >= 0", n_q);
+  if (n_q == 0) return GVA_OK;
+  if (!q_nope || !q_rope || !q_pos || !M || !rope || !q_abs)
+    return fail(GVA_ERR_INVALID_ARG, "absorb argument is NULL");
+  if (max_pos < 1) return fail(GVA_ERR_INVALID_ARG, "max_pos=%d must be >= 1", max_pos);
+  if (!aligned(q_nope, 4) || !aligned(q_rope, 8) || !aligned(M, 16) || !aligned(q_abs, 8) ||
+      !aligned(rope, 16))
+    return fail(GVA_ERR_INVALID_ARG, "absorb buffers misaligned (M needs 16 bytes)");
+  if (d->d_n % 4 != 0) return fail(GVA_ERR_UNSUPPORTED, "absorb needs d_n %% 4 == 0 (d_n=%d)", d->d_n);
+  return GVA_OK;
+}
+
+bool mfma_supported(const gva_dims *d, const gva_cache *c, const char **why) {
+  const char *w = nullptr;
+  const int hpg = d->H / d->G;
+  if (c->dtype != GVA_DTYPE_BF16) w = "the matrix-core kernel needs a bf16 cache";
+  else if (d->d_h % 32 != 0 || d->d_h > 256) w = "the matrix-core kernel needs d_h % 32 == 0, <= 256";
+  else if (d->d_r % 8 != 0 || d->d_r > 32) w = "the matrix-core kernel needs d_r % 8 == 0, <= 32";
+  else if (hpg > 16) w = "the matrix-core kernel needs H / G <= 16";
+  else if (d->G > 16) w = "the matrix-core kernel needs G <= 16";
+  else if (c->block_size < 16) w = "the matrix-core kernel needs block_size >= 16";
+  else if (c->v_stride_block % 8 || c->v_stride_token % 8 || c->v_stride_group % 8 ||
+           c->kr_stride_block % 8 || c->kr_stride_token % 8)
+    w = "the matrix-core kernel needs strides that are multiples of 8 elements";
+  if (why) *why = w;
+  return w == nullptr;
+}
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
+                 DecodePlan *plan) {
+  if (!d || B < 1 || max_len < 0 || num_splits < 0 || num_splits > kMaxSplits) return false;
+  const int64_t q = kChunkQuantum;
+  int64_t S = num_splits;
+  if (S == 0) {
+    // Enough chunks to give every compute unit work when the batch is small, chunks of at most
+    // 2048 positions for long sequences, and no chunk below 256 positions.
+    const int64_t by_len = (max_len + 2047) / 2048;
+    const int64_t by_cus = (kPlanCUs + B - 1) / B;
+    S = by_len > by_cus ? by_len : by_cus;
+    const int64_t cap = (max_len + 255) / 256;
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    if (S > kMaxSplits) S = kMaxSplits;
+  }
+  int64_t chunk = max_len > 0 ? (max_len + S - 1) / S : q;
+  chunk = (chunk + q - 1) / q * q;
+  if (max_len > 0) S = (max_len + chunk - 1) / chunk;  // no chunk starts at or after max_len
+  if (S < 1) S = 1;
+  plan->num_splits = (int32_t)S;
+  plan->chunk = (int32_t)chunk;
+  if (S == 1) {
+    plan->ws_bytes = 0;
+    plan->off_m = plan->off_l = plan->off_o = 0;
+    return true;
+  }
+  const size_t rows = (size_t)B * (size_t)S * (size_t)d->H;
+  plan->off_o = 0;
+  plan->off_m = round_up(rows * (size_t)d->d_h * 4, 256);
+  plan->off_l = plan->off_m + round_up(rows * 4, 256);
+  plan->ws_bytes = plan->off_l + round_up(rows * 4, 256);
+  return true;
+}
+
+gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
+                        const int32_t *seq_len, int32_t max_len, const float *q_abs,
+                        float scale, int32_t num_splits, int32_t kernel, const void *workspace,
+                        size_t workspace_bytes, const float *out, DecodePlan *plan,
+                        bool *use_mfma) {
+  gva_status st = check_dims(d);
+  if (st != GVA_OK) return st;
+  if ((st = check_cache(d, c)) != GVA_OK) return st;
+  if (B < 1) return fail(GVA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (!seq_len || !q_abs || !out) return fail(GVA_ERR_INVALID_ARG, "decode argument is NULL");
+  if (!aligned(q_abs, 16) || !aligned(out, 16))
+    return fail(GVA_ERR_INVALID_ARG, "q_abs and out must be 16-byte aligned");
+  if (max_len < 0) return fail(GVA_ERR_INVALID_ARG, "max_len=%d must be >= 0", max_len);
+  if ((int64_t)max_len > (int64_t)c->max_blocks * c->block_size)
+    return fail(GVA_ERR_INVALID_ARG, "max_len=%d exceeds the block table's capacity", max_len);
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(GVA_ERR_INVALID_ARG, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
+  if (kernel < GVA_KERNEL_AUTO || kernel > GVA_KERNEL_MFMA)
+    return fail(GVA_ERR_INVALID_ARG, "unknown kernel selector %d", kernel);
+  if (!plan_decode(d, B, max_len, num_splits, plan))
+    return fail(GVA_ERR_INVALID_ARG, "cannot plan the decode split");
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+      return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan->ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const char *why = nullptr;
+  const bool can = mfma_supported(d, c, &why);
+  if (kernel == GVA_KERNEL_MFMA && !can) return fail(GVA_ERR_UNSUPPORTED, "%s", why);
+  *use_mfma = (kernel == GVA_KERNEL_MFMA) || (kernel == GVA_KERNEL_AUTO && can);
+  return GVA_OK;
+}
+
+gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
+                         int32_t max_start, int32_t chunk_len, const float *q_abs,
+                         const float *v_new, const float *kr_raw, float scale, const float *out) {
+  gva_status st = check_dims(d);
+  if (st != GVA_OK) return st;
+  if ((st = check_cache(d, c)) != GVA_OK) return st;
+  if (B < 1) return fail(GVA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (chunk_len < 0) return fail(GVA_ERR_INVALID_ARG, "chunk_len=%d must be >= 0", chunk_len);
+  if (max_start < 0) return fail(GVA_ERR_INVALID_ARG, "max_start=%d must be >= 0", max_start);
+  if ((int64_t)max_start + chunk_len > (int64_t)c->max_blocks * c->block_size)
+    return fail(GVA_ERR_INVALID_ARG, "max_start + chunk_len exceeds the block table's capacity");
+  if (chunk_len == 0) return GVA_OK;
+  if (!start || !q_abs || !v_new || !kr_raw || !out)
+    return fail(GVA_ERR_INVALID_ARG, "prefill argument is NULL");
+  if (!aligned(q_abs, 16) || !aligned(out, 16) || !aligned(v_new, 8) || !aligned(kr_raw, 8))
+    return fail(GVA_ERR_INVALID_ARG, "prefill buffers misaligned");
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARG, "scale must be positive and finite");
+  const char *why = nullptr;
+  if (!mfma_supported(d, c, &why)) return fail(GVA_ERR_UNSUPPORTED, "%s", why);
+  return GVA_OK;
+}
+
+}  // namespace gva
+
+extern "C" {
+
+size_t gva_rope_table_bytes(int32_t max_pos, int32_t d_r) {
+  if (max_pos < 1 || d_r < 2 || d_r % 2 != 0 || d_r > gva::kMaxDr) return 0;
+  return (size_t)max_pos * (size_t)(d_r / 2) * 2 * sizeof(double);
+}
+
+gva_status gva_rope_table_fill(double *host_out, int32_t max_pos, int32_t d_r, double base) {
+  if (!host_out) return gva::fail(GVA_ERR_INVALID_ARG, "host_out is NULL");
+  if (max_pos < 1) return gva::fail(GVA_ERR_INVALID_ARG, "max_pos=%d must be >= 1", max_pos);
+  if (d_r < 2 || d_r % 2 != 0 || d_r > gva::kMaxDr)
+    return gva::fail(GVA_ERR_INVALID_ARG, "d_r=%d must be even and in [2, %d]", d_r, gva::kMaxDr);
+  if (!(base > 0.0) || !isfinite(base)) return gva::fail(GVA_ERR_INVALID_ARG, "base must be > 0");
+  const int half = d_r / 2;
+  for (int i = 0; i < half; ++i) {
+    // theta_i = base^(-2i/d_r): the exponent is the correctly rounded quotient (-2i)/d_r.
+    const double theta = gva::g_libm_pow(base, (-2.0 * (double)i) / (double)d_r);
+    for (int32_t p = 0; p < max_pos; ++p) {
+      const double a = (double)p * theta;
+      host_out[((size_t)p * half + i) * 2 + 0] = gva::g_libm_cos(a);
+      host_out[((size_t)p * half + i) * 2 + 1] = gva::g_libm_sin(a);
+    }
+  }
+  return GVA_OK;
+}
+
+size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
+                                  int32_t num_splits) {
+  if (gva::check_dims(dims) != GVA_OK) return 0;
+  gva::DecodePlan p;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, &p)) return 0;
+  return p.ws_bytes;
+}
+
+int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,
+                              int32_t num_splits) {
+  if (gva::check_dims(dims) != GVA_OK) return 0;
+  gva::DecodePlan p;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, &p)) return 0;
+  return p.num_splits;
+}
+
+const char *gva_status_string(gva_status status) {
+  switch (status) {
+    case GVA_OK: return "GVA_OK";
+    case GVA_ERR_INVALID_ARG: return "GVA_ERR_INVALID_ARG";
+    case GVA_ERR_UNSUPPORTED: return "GVA_ERR_UNSUPPORTED";
+    case GVA_ERR_WORKSPACE: return "GVA_ERR_WORKSPACE";
+    case GVA_ERR_HIP: return "GVA_ERR_HIP";
+  }
+  return "GVA_ERR_UNKNOWN";
+}
+
+const char *gva_last_error(void) { return gva::last_error_cstr(); }
+
+const char *gva_version(void) { return "gva-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// gva_internal.h - declarations shared by the host-side validation/planning code (plain C++,
+// no HIP device code) and the HIP entry points and kernel launchers.
+#ifndef GVA_INTERNAL_H_
+#define GVA_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gva.h"
+
+namespace gva {
+
+// Compute units assumed when planning a split count (MI355X: 256 CUs in 8 XCDs). A fixed
+// value keeps gva_decode_workspace_bytes a pure function of its arguments.
+constexpr int kPlanCUs = 256;
+// Token granularity of a decode chunk: both decode kernels walk a chunk in tiles of this many
+// positions, so chunk boundaries fall on tile boundaries.
+constexpr int kChunkQuantum = 64;
+constexpr int kMaxSplits = 1024;
+constexpr int kMaxH = 256;
+constexpr int kMaxDh = 256;
+constexpr int kMaxDn = 512;
+constexpr int kMaxDr = 64;
+
+const char *last_error_cstr();
+// Records `detail` as the calling thread's last error and returns `status`.
+gva_status fail(gva_status status, const char *fmt, ...);
+
+// Argument checks. None of them touches HIP, so they run (and are tested) without a GPU.
+gva_status check_dims(const gva_dims *d);
+gva_status check_cache(const gva_dims *d, const gva_cache *c);
+gva_status check_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,
+                        const int32_t *seq, const int32_t *pos, const float *v_new,
+                        const float *kr_raw);
+gva_status check_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, const float *q_rope,
+                        const int32_t *q_pos, const float *M, const double *rope, int32_t max_pos,
+                        const float *q_abs);
+
+// Does the matrix-core decode/prefill kernel handle this shape and cache? (No HIP calls.)
+bool mfma_supported(const gva_dims *d, const gva_cache *c, const char **why);
+
+struct DecodePlan {
+  int32_t num_splits;   // chunks per sequence
+  int32_t chunk;        // positions per chunk, a multiple of kChunkQuantum
+  size_t ws_bytes;      // workspace needed (0 when num_splits == 1: output written directly)
+  size_t off_m;         // byte offsets of the partial arrays inside the workspace
+  size_t off_l;
+  size_t off_o;
+};
+
+// Plans the split of positions [0, max_len) into chunks; returns false on bad arguments.
+bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
+                 DecodePlan *plan);
+
+gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
+                        const int32_t *seq_len, int32_t max_len, const float *q_abs,
+                        float scale, int32_t num_splits, int32_t kernel, const void *workspace,
+                        size_t workspace_bytes, const float *out, DecodePlan *plan,
+                        bool *use_mfma);
+
+gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
+                         int32_t max_start, int32_t chunk_len, const float *q_abs,
+                         const float *v_new, const float *kr_raw, float scale, const float *out);
+
+// ---- kernel launchers (defined in the .hip files) -------------------------------------------
+
+struct DecodeArgs {
+  // cache
+  const void *v;
+  const void *kr;
+  int64_t v_sb, v_st, v_sg, kr_sb, kr_st;
+  int64_t num_blocks;
+  int32_t log2_bs;
+  int32_t max_blocks;
+  const int32_t *block_table;
+  int32_t *err_flag;
+  // shape
+  int32_t H, G, d_h, d_r;
+  int32_t B;
+  const int32_t *seq_len;
+  int32_t max_len;
+  const float *q_abs;
+  float qscale;         // softmax scale * log2(e): scores are kept in the base-2 domain
+  int32_t num_splits;
+  int32_t chunk;
+  // outputs: partials (num_splits > 1) or final rows (num_splits == 1)
+  float *part_m;        // [B][S][H]
+  float *part_l;        // [B][S][H]
+  float *part_o;        // [B][S][H][d_h]
+  float *out;           // [B][H][d_h]
+  float *lse;           // [B][H] or nullptr
+};
+
+hipError_t launch_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,
+                         const int32_t *seq, const int32_t *pos, const float *v_new,
+                         const float *kr_raw, hipStream_t stream);
+hipError_t launch_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, const float *q_rope,
+                         const int32_t *q_pos, const float *M, const double *rope,
+                         int32_t max_pos, float *q_abs, int32_t *err_flag, hipStream_t stream);
+hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+  DecodeArgs kv;        // cache description and shape (seq_len unused)
+  const int32_t *start;
+  int32_t max_start;
+  int32_t chunk_len;
+  const float *q_abs;   // [B][C][H][d_h + d_r]
+  const float *v_new;   // [B][C][G][d_h]
+  const float *kr_raw;  // [B][C][d_r]
+  const double *rope;   // RoPE table used by the chunk's append
+  int32_t max_pos;
+  float *out;           // [B][C][H][d_h]
+  float *lse;           // [B][C][H] or nullptr
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace gva
+
+#endif  // GVA_INTERNAL_H_

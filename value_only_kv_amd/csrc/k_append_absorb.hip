@@ -1,0 +1,203 @@
+// k_append_absorb.hip - cache append (values and the shared rotated positional key) and query
+// absorption for Grouped Value Attention.
+//
+// Append: the cache keeps G grouped values and one positional key per token, the latter
+// stored already rotated to the token's position ("GVA：KV 缓存里的 Key 其实可以不存",
+// shibing624.github.io review of arXiv:2609.13285, section 关键技巧二; section 缓存账本).
+// Absorption: q~_h = q_nope_h M_h^T, formed once per query token (same review, section
+// 关键技巧一, the absorption identity).
+#include <hip/hip_runtime.h>
+
+#include "gva_device.h"
+
+namespace {
+
+using gvad::f64_to_bf16_bits;
+using gvad::f64_to_f32_bits;
+
+// One work-group per appended token. Threads stride over the G*d_h/2 value pairs, then over
+// the d_r/2 positional pairs. Values take one rounding fp32 -> cache type (through an exact
+// float64 widening); the positional key is rotated in float64 and rounded once.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_append(gva::DecodeArgs a, int32_t B, const int32_t *seq,
+                                                const int32_t *pos, const float *v_new,
+                                                const float *kr_raw, const double *rope,
+                                                int32_t max_pos) {
+  const int k = blockIdx.x;
+  const int b = seq[k];
+  const int p = pos[k];
+  const int cap = a.max_blocks << a.log2_bs;
+  int32_t err = 0;
+  if (b < 0 || b >= B) err = GVA_DEVERR_SEQ;
+  else if (p < 0) err = GVA_DEVERR_LENGTH;
+  else if (p >= cap) err = GVA_DEVERR_CAPACITY;
+  else if (p >= max_pos) err = GVA_DEVERR_ROPE;
+  int64_t blk = -1;
+  if (!err) {
+    blk = gvad::block_of(a, b, p);
+    if (blk < 0) err = GVA_DEVERR_BLOCK;
+  }
+  if (err) {
+    if (threadIdx.x == 0) gvad::raise_err(a.err_flag, err);
+    return;
+  }
+  const int64_t off = p & ((1 << a.log2_bs) - 1);
+  const int G = a.G, d_h = a.d_h, d_r = a.d_r;
+  const int half_h = d_h >> 1;
+  const float2 *src = reinterpret_cast<const float2 *>(v_new + static_cast<int64_t>(k) * G * d_h);
+  for (int idx = threadIdx.x; idx < G * half_h; idx += blockDim.x) {
+    const int g = idx / half_h;
+    const int i = (idx - g * half_h) * 2;
+    const float2 x = src[idx];
+    const int64_t o = blk * a.v_sb + off * a.v_st + static_cast<int64_t>(g) * a.v_sg + i;
+    if (BF16) {
+      const uint32_t lo = f64_to_bf16_bits(static_cast<double>(x.x));
+      const uint32_t hi = f64_to_bf16_bits(static_cast<double>(x.y));
+      reinterpret_cast<uint32_t *>(const_cast<void *>(a.v))[o >> 1] = lo | (hi << 16);
+    } else {
+      uint2 w;
+      w.x = f64_to_f32_bits(static_cast<double>(x.x));
+      w.y = f64_to_f32_bits(static_cast<double>(x.y));
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(const_cast<void *>(a.v)) + o) = w;
+    }
+  }
+  const int half_r = d_r >> 1;
+  const float2 *ksrc = reinterpret_cast<const float2 *>(kr_raw + static_cast<int64_t>(k) * d_r);
+  const double2 *cs = reinterpret_cast<const double2 *>(rope) + static_cast<int64_t>(p) * half_r;
+  for (int i = threadIdx.x; i < half_r; i += blockDim.x) {
+    const float2 x = ksrc[i];
+    const double2 t = cs[i];
+    double y0, y1;
+    gvad::rotate_pair_f64(static_cast<double>(x.x), static_cast<double>(x.y), t.x, t.y, &y0, &y1);
+    const int64_t o = blk * a.kr_sb + off * a.kr_st + 2 * i;
+    if (BF16) {
+      const uint32_t lo = f64_to_bf16_bits(y0);
+      const uint32_t hi = f64_to_bf16_bits(y1);
+      reinterpret_cast<uint32_t *>(const_cast<void *>(a.kr))[o >> 1] = lo | (hi << 16);
+    } else {
+      uint2 w;
+      w.x = f64_to_f32_bits(y0);
+      w.y = f64_to_f32_bits(y1);
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(const_cast<void *>(a.kr)) + o) = w;
+    }
+  }
+}
+
+// Absorption GEMV. Work-group (h, tile of TQ query tokens): the tile's q_nope rows for head h
+// are staged in LDS; thread i forms q~[i] for all TQ tokens with one pass over row i of M_h
+// (float32, products accumulated in order j = 0 .. d_n-1). The positional slice is rotated at
+// the token's position in float64 and rounded once to float32.
+constexpr int TQ = 8;
+
+__global__ __launch_bounds__(256) void k_absorb(int32_t H, int32_t d_h, int32_t d_n, int32_t d_r,
+                                                int32_t n_q, const float *q_nope,
+                                                const float *q_rope, const int32_t *q_pos,
+                                                const float *M, const double *rope,
+                                                int32_t max_pos, float *q_abs, int32_t *err_flag) {
+  extern __shared__ float qs[];  // [TQ][d_n]
+  const int h = blockIdx.x;
+  const int k0 = blockIdx.y * TQ;
+  const int nt = min(TQ, n_q - k0);
+  const int row = d_h + d_r;
+  for (int idx = threadIdx.x; idx < nt * d_n; idx += blockDim.x) {
+    const int t = idx / d_n;
+    const int j = idx - t * d_n;
+    qs[idx] = q_nope[(static_cast<int64_t>(k0 + t) * H + h) * d_n + j];
+  }
+  __syncthreads();
+  const float4 *Mh = reinterpret_cast<const float4 *>(M + static_cast<int64_t>(h) * d_h * d_n);
+  const int dn4 = d_n >> 2;
+  for (int i = threadIdx.x; i < d_h; i += blockDim.x) {
+    float acc[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) acc[t] = 0.0f;
+    const float4 *mrow = Mh + static_cast<int64_t>(i) * dn4;
+    for (int j4 = 0; j4 < dn4; ++j4) {
+      const float4 m = mrow[j4];
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) {
+        const float *q = qs + t * d_n + 4 * j4;
+        acc[t] = fmaf(m.x, q[0], acc[t]);
+        acc[t] = fmaf(m.y, q[1], acc[t]);
+        acc[t] = fmaf(m.z, q[2], acc[t]);
+        acc[t] = fmaf(m.w, q[3], acc[t]);
+      }
+    }
+    for (int t = 0; t < nt; ++t) {
+      const int p = q_pos[k0 + t];
+      const bool bad = p < 0 || p >= max_pos;
+      q_abs[(static_cast<int64_t>(k0 + t) * H + h) * row + i] = bad ? __int_as_float(0x7fc00000) : acc[t];
+    }
+  }
+  const int half_r = d_r >> 1;
+  for (int idx = threadIdx.x; idx < nt * half_r; idx += blockDim.x) {
+    const int t = idx / half_r;
+    const int i = idx - t * half_r;
+    const int k = k0 + t;
+    const int p = q_pos[k];
+    float2 y;
+    if (p < 0 || p >= max_pos) {
+      y.x = y.y = __int_as_float(0x7fc00000);
+      if (i == 0 && err_flag) atomicOr(err_flag, GVA_DEVERR_ROPE);
+    } else {
+      const float2 x = reinterpret_cast<const float2 *>(q_rope + (static_cast<int64_t>(k) * H + h) * d_r)[i];
+      const double2 t2 = reinterpret_cast<const double2 *>(rope)[static_cast<int64_t>(p) * half_r + i];
+      double y0, y1;
+      gvad::rotate_pair_f64(static_cast<double>(x.x), static_cast<double>(x.y), t2.x, t2.y, &y0, &y1);
+      y.x = gvad::f64_to_f32(y0);
+      y.y = gvad::f64_to_f32(y1);
+    }
+    float *dst = q_abs + (static_cast<int64_t>(k) * H + h) * row + d_h + 2 * i;
+    dst[0] = y.x;
+    dst[1] = y.y;
+  }
+}
+
+}  // namespace
+
+namespace gva {
+
+hipError_t launch_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,
+                         const int32_t *seq, const int32_t *pos, const float *v_new,
+                         const float *kr_raw, hipStream_t stream) {
+  if (n_tok == 0) return hipSuccess;
+  DecodeArgs a{};
+  a.v = c->v;
+  a.kr = c->kr;
+  a.v_sb = c->v_stride_block;
+  a.v_st = c->v_stride_token;
+  a.v_sg = c->v_stride_group;
+  a.kr_sb = c->kr_stride_block;
+  a.kr_st = c->kr_stride_token;
+  a.num_blocks = c->num_blocks;
+  a.log2_bs = __builtin_ctz(static_cast<unsigned>(c->block_size));
+  a.max_blocks = c->max_blocks;
+  a.block_table = c->block_table;
+  a.err_flag = c->err_flag;
+  a.H = d->H;
+  a.G = d->G;
+  a.d_h = d->d_h;
+  a.d_r = d->d_r;
+  const int threads = 256;
+  if (c->dtype == GVA_DTYPE_BF16)
+    hipLaunchKernelGGL(k_append<true>, dim3(n_tok), dim3(threads), 0, stream, a, B, seq, pos, v_new,
+                       kr_raw, c->rope, c->max_pos);
+  else
+    hipLaunchKernelGGL(k_append<false>, dim3(n_tok), dim3(threads), 0, stream, a, B, seq, pos,
+                       v_new, kr_raw, c->rope, c->max_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, const float *q_rope,
+                         const int32_t *q_pos, const float *M, const double *rope,
+                         int32_t max_pos, float *q_abs, int32_t *err_flag, hipStream_t stream) {
+  if (n_q == 0) return hipSuccess;
+  const dim3 grid(d->H, (n_q + TQ - 1) / TQ);
+  const int threads = d->d_h <= 64 ? 64 : (d->d_h <= 128 ? 128 : 256);
+  const size_t lds = static_cast<size_t>(TQ) * d->d_n * sizeof(float);
+  hipLaunchKernelGGL(k_absorb, grid, dim3(threads), lds, stream, d->H, d->d_h, d->d_n, d->d_r, n_q,
+                     q_nope, q_rope, q_pos, M, rope, max_pos, q_abs, err_flag);
+  return hipGetLastError();
+}
+
+}  // namespace gva

@@ -1,0 +1,281 @@
+// k_decode_generic.hip - vector-ALU split decode for Grouped Value Attention, any supported
+// shape and cache type (float32 or bfloat16), and the log-sum-exp combine of the splits.
+//
+// Score of cached position j for head h: q~_h . v_{j,g(h)} + r_h . kr_j, with q~_h the absorbed
+// content query and r_h the rotated positional query ("GVA：KV 缓存里的 Key 其实可以不存",
+// shibing624.github.io review of arXiv:2609.13285, sections 关键技巧一 and 关键技巧二), then a
+// softmax over the cached positions and a weighted sum of the same cached values (agihunt.info
+// summary of the paper; "KV Cache 优化（一）", liumengxuan04.github.io, section 1).
+//
+// One wave per (split, sequence, group, head pass). A chunk is walked in tiles of 64 positions:
+// lane t scores position t of the tile for every head of the pass (one lane per position, no
+// cross-lane reduction), the wave then updates the running max / sum of each head, and the
+// weighted sum runs with lanes over the value dimensions. Scores live in the base-2 domain
+// (the query is pre-multiplied by scale * log2 e), so exponentials are exp2.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "gva_device.h"
+
+namespace {
+
+constexpr int kHeadsPerPass = 16;   // heads of one group handled by one wave
+constexpr int kTile = 64;           // positions per tile (one per lane)
+
+template <bool BF16>
+__device__ __forceinline__ float2 load_pair(const void *base, int64_t off) {
+  if (BF16) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(base)[off >> 1];
+    return make_float2(gvad::bf16_bits_to_f32(w & 0xffffu), gvad::bf16_bits_to_f32(w >> 16));
+  }
+  return *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + off);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_one(const void *base, int64_t off) {
+  if (BF16) return gvad::bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(base)[off]);
+  return reinterpret_cast<const float *>(base)[off];
+}
+
+// Writes the (m, l, o) of a finished chunk, or the final row when there is a single split.
+// o holds DPL values per lane: dims lane, lane + 64, ...
+template <int DPL>
+__device__ __forceinline__ void store_rows(const gva::DecodeArgs &a, int b, int s, int h0, int nh,
+                                           const float *m, const float *l,
+                                           const float (*o)[DPL], bool poison) {
+  const int lane = threadIdx.x;
+  const float qnan = __int_as_float(0x7fc00000);
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    if (a.num_splits == 1) {
+      const float inv = l[hh] > 0.0f ? 1.0f / l[hh] : 0.0f;
+      float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < a.d_h) dst[d] = poison ? qnan : o[hh][k] * inv;
+      }
+      if (a.lse && lane == 0) {
+        float v = l[hh] > 0.0f ? (m[hh] + log2f(l[hh])) * gvad::kLn2 : -INFINITY;
+        a.lse[static_cast<int64_t>(b) * a.H + h] = poison ? qnan : v;
+      }
+    } else {
+      const int64_t row = (static_cast<int64_t>(b) * a.num_splits + s) * a.H + h;
+      float *dst = a.part_o + row * a.d_h;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < a.d_h) dst[d] = o[hh][k];
+      }
+      if (lane == 0) {
+        a.part_m[row] = poison ? qnan : m[hh];
+        a.part_l[row] = l[hh];
+      }
+    }
+  }
+}
+
+template <bool BF16, int DPL>
+__global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int head_passes) {
+  __shared__ float q_s[kHeadsPerPass][gva::kMaxDh + gva::kMaxDr];
+  __shared__ float p_s[kHeadsPerPass][kTile];
+  const int s = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = blockIdx.z / head_passes;
+  const int hp = blockIdx.z - g * head_passes;
+  const int hpg = a.H / a.G;
+  const int h0 = g * hpg + hp * kHeadsPerPass;
+  const int nh = min(kHeadsPerPass, hpg - hp * kHeadsPerPass);
+  const int lane = threadIdx.x;
+  const int d_h = a.d_h, d_r = a.d_r, row = d_h + d_r;
+
+  float m[kHeadsPerPass], l[kHeadsPerPass], o[kHeadsPerPass][DPL];
+#pragma unroll
+  for (int hh = 0; hh < kHeadsPerPass; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[hh][k] = 0.0f;
+  }
+
+  const int len = a.seq_len[b];
+  const int cap = a.max_blocks << a.log2_bs;
+  bool poison = false;
+  if (len < 0 || len > a.max_len || len > cap) {
+    if (lane == 0 && s == 0 && blockIdx.z == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+    store_rows<DPL>(a, b, s, h0, nh, m, l, o, true);
+    return;
+  }
+  const int c0 = s * a.chunk;
+  const int c1 = min(c0 + a.chunk, len);
+  if (c0 >= c1) {
+    store_rows<DPL>(a, b, s, h0, nh, m, l, o, false);
+    return;
+  }
+
+  for (int idx = lane; idx < nh * row; idx += 64) {
+    const int hh = idx / row;
+    const int e = idx - hh * row;
+    q_s[hh][e] = a.q_abs[(static_cast<int64_t>(b) * a.H + h0 + hh) * row + e] * a.qscale;
+  }
+  __syncthreads();
+
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  for (int t0 = c0; t0 < c1; t0 += kTile) {
+    // ---- scores: one position per lane ----
+    const int t = t0 + lane;
+    const bool valid = t < c1;
+    const int tc = valid ? t : c1 - 1;
+    const int64_t blk = gvad::block_of(a, b, tc);
+    if (blk < 0) poison = true;
+    const int64_t blk_s = blk < 0 ? 0 : blk;
+    const int64_t voff = blk_s * a.v_sb + static_cast<int64_t>(tc & bs_mask) * a.v_st +
+                         static_cast<int64_t>(g) * a.v_sg;
+    const int64_t koff = blk_s * a.kr_sb + static_cast<int64_t>(tc & bs_mask) * a.kr_st;
+    float sc[kHeadsPerPass];
+#pragma unroll
+    for (int hh = 0; hh < kHeadsPerPass; ++hh) sc[hh] = 0.0f;
+    for (int i = 0; i < d_h; i += 2) {
+      const float2 x = load_pair<BF16>(a.v, voff + i);
+#pragma unroll
+      for (int hh = 0; hh < kHeadsPerPass; ++hh)
+        if (hh < nh) sc[hh] = fmaf(q_s[hh][i], x.x, fmaf(q_s[hh][i + 1], x.y, sc[hh]));
+    }
+    for (int i = 0; i < d_r; i += 2) {
+      const float2 x = load_pair<BF16>(a.kr, koff + i);
+#pragma unroll
+      for (int hh = 0; hh < kHeadsPerPass; ++hh)
+        if (hh < nh) sc[hh] = fmaf(q_s[hh][d_h + i], x.x, fmaf(q_s[hh][d_h + i + 1], x.y, sc[hh]));
+    }
+    // ---- online softmax over the tile, per head ----
+#pragma unroll
+    for (int hh = 0; hh < kHeadsPerPass; ++hh) {
+      if (hh < nh) {
+        const float sv = valid ? sc[hh] : -INFINITY;
+        const float mn = fmaxf(m[hh], gvad::wave_max(sv));
+        const float alpha = exp2f(m[hh] - mn);
+        const float p = exp2f(sv - mn);
+        l[hh] = l[hh] * alpha + gvad::wave_sum(p);
+        m[hh] = mn;
+        p_s[hh][lane] = p;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[hh][k] *= alpha;
+      }
+    }
+    __syncthreads();
+    // ---- weighted sum: lanes over value dimensions ----
+    const int nt = min(kTile, c1 - t0);
+    for (int j = 0; j < nt; ++j) {
+      const int tj = t0 + j;
+      const int64_t bj = gvad::block_of(a, b, tj);
+      const int64_t bjs = bj < 0 ? 0 : bj;
+      const int64_t vo = bjs * a.v_sb + static_cast<int64_t>(tj & bs_mask) * a.v_st +
+                         static_cast<int64_t>(g) * a.v_sg;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < d_h) {
+          const float x = load_one<BF16>(a.v, vo + d);
+#pragma unroll
+          for (int hh = 0; hh < kHeadsPerPass; ++hh)
+            if (hh < nh) o[hh][k] = fmaf(p_s[hh][j], x, o[hh][k]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // a poisoned split is reported once per wave
+  const bool any_poison = __any(poison);
+  if (any_poison && lane == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
+  store_rows<DPL>(a, b, s, h0, nh, m, l, o, any_poison);
+}
+
+// Combine: one wave per (head, sequence). m* = max over the sequence's non-empty chunks,
+// L = sum l_c 2^(m_c - m*), out = sum o_c 2^(m_c - m*) / L, lse = (m* + log2 L) ln 2.
+__global__ __launch_bounds__(64) void k_combine(gva::DecodeArgs a) {
+  __shared__ float w_s[gva::kMaxSplits];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const float qnan = __int_as_float(0x7fc00000);
+  float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
+  const int len = a.seq_len[b];
+  const int cap = a.max_blocks << a.log2_bs;
+  if (len < 0 || len > a.max_len || len > cap) {
+    for (int d = lane; d < a.d_h; d += 64) dst[d] = qnan;
+    if (a.lse && lane == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
+    return;
+  }
+  const int ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
+  if (ns == 0) {
+    for (int d = lane; d < a.d_h; d += 64) dst[d] = 0.0f;
+    if (a.lse && lane == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
+    return;
+  }
+  const int64_t row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;  // + s * H
+  float mx = -INFINITY;
+  bool bad = false;
+  for (int s = lane; s < ns; s += 64) {
+    const float ms = a.part_m[row0 + static_cast<int64_t>(s) * a.H];
+    if (isnan(ms)) bad = true;
+    mx = fmaxf(mx, ms);
+  }
+  mx = gvad::wave_max(mx);
+  bad = __any(bad);
+  float L = 0.0f;
+  for (int s = lane; s < ns; s += 64) {
+    const int64_t r = row0 + static_cast<int64_t>(s) * a.H;
+    const float f = exp2f(a.part_m[r] - mx);
+    w_s[s] = f;
+    L += a.part_l[r] * f;
+  }
+  L = gvad::wave_sum(L);
+  __syncthreads();
+  const float inv = 1.0f / L;
+  for (int d = lane; d < a.d_h; d += 64) {
+    float acc = 0.0f;
+    for (int s = 0; s < ns; ++s)
+      acc = fmaf(a.part_o[(row0 + static_cast<int64_t>(s) * a.H) * a.d_h + d], w_s[s], acc);
+    dst[d] = bad ? qnan : acc * inv;
+  }
+  if (a.lse && lane == 0)
+    a.lse[static_cast<int64_t>(b) * a.H + h] = bad ? qnan : (mx + log2f(L)) * gvad::kLn2;
+}
+
+}  // namespace
+
+namespace gva {
+
+hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t stream) {
+  const int hpg = a.H / a.G;
+  const int head_passes = (hpg + kHeadsPerPass - 1) / kHeadsPerPass;
+  const dim3 grid(a.num_splits, a.B, a.G * head_passes);
+  const int dpl = (a.d_h + 63) / 64;
+#define GVA_LAUNCH_GENERIC(BF, D)                                                            \
+  hipLaunchKernelGGL((k_decode_generic<BF, D>), grid, dim3(64), 0, stream, a, head_passes)
+  if (bf16) {
+    switch (dpl) {
+      case 1: GVA_LAUNCH_GENERIC(true, 1); break;
+      case 2: GVA_LAUNCH_GENERIC(true, 2); break;
+      case 3: GVA_LAUNCH_GENERIC(true, 3); break;
+      default: GVA_LAUNCH_GENERIC(true, 4); break;
+    }
+  } else {
+    switch (dpl) {
+      case 1: GVA_LAUNCH_GENERIC(false, 1); break;
+      case 2: GVA_LAUNCH_GENERIC(false, 2); break;
+      case 3: GVA_LAUNCH_GENERIC(false, 3); break;
+      default: GVA_LAUNCH_GENERIC(false, 4); break;
+    }
+  }
+#undef GVA_LAUNCH_GENERIC
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_combine, dim3(a.H, a.B), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gva
