@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""GVA decode benchmark on one MI355X.
+
+One step is one pass of the decode hot path over one batch of the ragged paged workload:
+append one token per sequence (gva_cache_append), absorb its query (gva_absorb_query), split
+decode + combine over len_b + 1 cached positions (gva_decode). Inputs are resident in HBM
+before the timed region. The value is the cache bytes the step must read, len (G d_h + d_r) s
+summed over the batch, divided by the step time.
+
+Also measured: the decode kernel alone (HIP events on the library's stream) for the roofline
+line, the long-context single-sequence decode (T = 131072) with cache replicas rotated so the
+256 MB last-level cache cannot serve them, and the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "GVA decode attention cache-read GB/s (% of HBM peak) and seq-steps/s per GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 matrix-core")
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--no-long", action="store_true", help="skip the T=131072 measurement")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+class DeviceCache:
+    """A workload's cache on the device, filled through gva_cache_append with seeded data."""
+
+    def __init__(self, w, lens, fill_seed, torch, gb, synth):
+        self.w = w
+        self.lens = lens
+        self.lay = synth.layout(w, lens)
+        cap = synth.capacity(w, lens)
+        self.max_pos = int(cap.max()) + 1
+        self.dims = gb.GvaDims(w.H, w.G, w.d_h, w.d_n, w.d_r)
+        rope = torch.from_numpy(gb.gva_rope_table_fill(self.max_pos, w.d_r, w.base)).cuda()
+        self.block_table = torch.from_numpy(self.lay.block_table).cuda()
+        lay = self.lay
+        self.cache = gb.GvaCache.allocate(self.dims, w.dtype, lay.num_blocks, lay.block_size,
+                                          self.block_table, rope,
+                                          (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st))
+        # fill positions 0..len_b-1 of every sequence, in batches of tokens
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(fill_seed)
+        seqs = np.repeat(np.arange(w.B, dtype=np.int32), lens)
+        poss = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+        step = 1 << 16
+        for o in range(0, seqs.size, step):
+            n = min(step, seqs.size - o)
+            v = torch.randn((n, w.G, w.d_h), generator=gen, device="cuda")
+            kr = torch.randn((n, w.d_r), generator=gen, device="cuda")
+            gb.gva_cache_append(self.dims, self.cache, w.B,
+                                torch.from_numpy(seqs[o:o + n]).cuda(),
+                                torch.from_numpy(poss[o:o + n]).cuda(), v, kr)
+        torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path shards "
+              "by sequence across GPUs with no exchange, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from value_only_kv_amd import binding as gb
+    from value_only_kv_amd import synth
+
+    gb.lib()  # fails loudly when the HIP library is not built
+    dev = torch.cuda.get_device_name(0)
+    log("device:", dev, "| library:", gb.gva_version())
+
+    # ---------------- ragged paged batch (the headline workload) ----------------
+    w = synth.workload("C4")
+    lens = synth.lengths(w)
+    t_setup = time.time()
+    dc = DeviceCache(w, lens, 1234, torch, gb, synth)
+    log(f"C4 cache filled: {dc.lay.num_blocks} blocks, {int(lens.sum())} tokens, "
+        f"{(dc.cache.v.numel() + dc.cache.kr.numel()) * 2 / 1e9:.2f} GB in {time.time() - t_setup:.1f}s")
+    B, H = w.B, w.H
+    row = w.d_h + w.d_r
+    max_len = int(lens.max()) + 1
+    seq = torch.arange(B, dtype=torch.int32, device="cuda")
+    pos = torch.from_numpy(lens.astype(np.int32)).cuda()          # the appended token's position
+    seq_len = pos + 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    v_new = torch.randn((B, w.G, w.d_h), generator=gen, device="cuda")
+    kr_new = torch.randn((B, w.d_r), generator=gen, device="cuda")
+    q_nope = torch.randn((B, H, w.d_n), generator=gen, device="cuda")
+    q_rope = torch.randn((B, H, w.d_r), generator=gen, device="cuda")
+    M = torch.randn((H, w.d_h, w.d_n), generator=gen, device="cuda") * w.m_sigma
+    q_abs = torch.empty((B, H, row), device="cuda")
+    out = torch.empty((B, H, w.d_h), device="cuda")
+    lse = torch.empty((B, H), device="cuda")
+    S = gb.gva_decode_num_splits(dc.dims, B, max_len, args.splits)
+    wsb = gb.gva_decode_workspace_bytes(dc.dims, B, max_len, args.splits)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gb.gva_cache_append(dc.dims, dc.cache, B, seq, pos, v_new, kr_new, stream=stream)
+        gb.gva_absorb_query(dc.dims, q_nope, q_rope, pos, M, dc.cache.rope, dc.max_pos, q_abs,
+                            stream=stream)
+        gb.gva_decode(dc.dims, dc.cache, B, seq_len, max_len, q_abs, w.scale, out, lse,
+                      num_splits=args.splits, kernel=args.kernel, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    assert torch.isfinite(out).all().item(), "non-finite decode output"
+    assert int(dc.cache.err_flag.item()) == 0, "device error flag raised"
+
+    elem = 2
+    tok_bytes = (w.G * w.d_h + w.d_r) * elem
+    read_bytes = int((lens + 1).sum()) * tok_bytes                 # algorithmic, per step
+    value = read_bytes / t_step / 1e9
+    log(f"C4 step: {t_step * 1e3:.3f} ms, {value:.1f} GB/s, splits={S}")
+
+    # decode launches alone, timed with HIP events on the launch stream
+    n_ev = max(args.steps, 10)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        gb.gva_decode(dc.dims, dc.cache, B, seq_len, max_len, q_abs, w.scale, out, lse,
+                      num_splits=args.splits, kernel=args.kernel, workspace=ws, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_dec = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) / 1e3
+    dec_gbs = read_bytes / t_dec / 1e9
+    log(f"C4 decode (split decode + combine): {t_dec * 1e3:.3f} ms, {dec_gbs:.1f} GB/s")
+
+    result_extra = {}
+    # ---------------- long context, one sequence ----------------
+    if not args.no_long:
+        for d_r, name in ((16, "C3"), (24, "C3r24")):
+            wl = synth.workload(name)
+            lens_l = synth.lengths(wl)
+            reps = [DeviceCache(wl, lens_l, 99 + k, torch, gb, synth) for k in range(3)]
+            ml = int(lens_l.max())
+            qa = torch.randn((1, wl.H, wl.d_h + wl.d_r), generator=gen, device="cuda")
+            sl = torch.from_numpy(lens_l.astype(np.int32)).cuda()
+            o1 = torch.empty((1, wl.H, wl.d_h), device="cuda")
+            rb = int(lens_l.sum()) * (wl.G * wl.d_h + wl.d_r) * 2
+            per_s = {}
+            for S_l in (64, 128, 256):
+                wsb_l = gb.gva_decode_workspace_bytes(reps[0].dims, 1, ml, S_l)
+                ws_l = torch.empty(max(wsb_l, 256) // 4, dtype=torch.float32, device="cuda")
+                for k in range(6):
+                    r = reps[k % 3]
+                    gb.gva_decode(r.dims, r.cache, 1, sl, ml, qa, wl.scale, o1, None,
+                                  num_splits=S_l, kernel=args.kernel, workspace=ws_l, stream=stream)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(30)]
+                for k, (e0, e1) in enumerate(evs):
+                    r = reps[k % 3]
+                    e0.record(stream)
+                    gb.gva_decode(r.dims, r.cache, 1, sl, ml, qa, wl.scale, o1, None,
+                                  num_splits=S_l, kernel=args.kernel, workspace=ws_l, stream=stream)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                ts = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)
+                t_med = ts[len(ts) // 2]
+                per_s[str(S_l)] = {"us": round(t_med * 1e6, 2),
+                                   "GB_s": round(rb / t_med / 1e9, 1),
+                                   "frac_of_hbm_peak": round(rb / t_med / 1e9 / HBM_PEAK_GBS, 4),
+                                   "seq_steps_per_s": round(1.0 / t_med, 1)}
+                log(f"{name} T={ml} S={S_l}: {t_med * 1e6:.1f} us, {rb / t_med / 1e9:.1f} GB/s")
+            result_extra[name] = {"T": ml, "d_r": d_r, "cache_bytes": rb,
+                                  "replicas_rotated": 3, "by_splits": per_s}
+            del reps
+            torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB write, 3 launches")
+
+    # ---------------- CPU oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, lens)
+
+    roofline = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "split decode + combine (gva_decode), ragged paged batch",
+                "bytes_per_launch": read_bytes, "launch_ms": round(t_dec * 1e3, 4)}
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block permutation)",
+        "config": {"workload": "ragged paged batch decode step: B=256, len_b ~ U[512, 32768], "
+                               "append 1 token then decode over len_b+1; H=32, G=8, d_h=d_n=128, "
+                               "d_r=24; bf16 cache in 16-token blocks",
+                   "global_batch": B, "cached_tokens": int((lens + 1).sum()),
+                   "num_splits": S, "parallelism": "single GPU"},
+        "seq_steps_per_s": round(B / t_step, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "decode_only": {"ms": round(t_dec * 1e3, 4), "GB_s": round(dec_gbs, 1),
+                        "seq_steps_per_s": round(B / t_dec, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "long_context": result_extra,
+        "device": dev,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, lens, budget_s=15.0):
+    """The oracle, as it stands, decoding whole sequences of the same workload one by one until
+    the time budget is spent: cache gather (bits -> float64) + absorbed decode of all heads."""
+    from oracle import gva_oracle as O
+    from value_only_kv_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    dims = O.Dims(w.H, w.G, w.d_h, w.d_n, w.d_r)
+    tab = None
+    done_bytes = 0
+    done_seq = 0
+    t_work = 0.0
+    for b in range(w.B):
+        n = int(lens[b]) + 1
+        v, kr_raw = synth.sequence_tokens(w, b, n)
+        # one sequence's own pool (contiguous), filled by the oracle's append
+        pool = O.Pool.empty("bf16", n * w.G * w.d_h, n * w.d_r,
+                            (n * w.G * w.d_h, w.G * w.d_h, w.d_h, n * w.d_r, w.d_r),
+                            1, 1 << int(np.ceil(np.log2(n))), np.zeros((1, 1)))
+        if tab is None or tab.shape[0] < n + 1:
+            tab = O.rope_rows(np.arange(n + 1), w.d_r, w.base)
+        O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr_raw, tab)
+        q = np.random.default_rng(b).standard_normal((w.H, w.d_h + w.d_r))
+        t0 = time.perf_counter()
+        V, kr = O.gather(pool, dims, 0, n)
+        O.decode_sequence(V, kr, dims, q, w.scale)
+        t_work += time.perf_counter() - t0
+        done_bytes += n * (w.G * w.d_h + w.d_r) * 2
+        done_seq += 1
+        if t_work >= budget_s:
+            break
+    gbs = done_bytes / t_work / 1e9
+    log(f"CPU oracle: {done_seq} sequences, {t_work:.1f}s, {gbs:.3f} GB/s, threads={threads}")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seq_steps_per_s": round(done_seq / t_work, 3),
+            "sample": f"first {done_seq} sequences of the ragged batch (len_b + 1 positions each), "
+                      f"decode only (gather + fp64 attention), {t_work:.1f}s of CPU work"}
+
+
+if __name__ == "__main__":
+    main()
