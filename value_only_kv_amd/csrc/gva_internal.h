@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/gva.h"
+#include "gva.h"
 
 namespace gva {
 

@@ -191,55 +191,101 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
   store_rows<DPL>(a, b, s, h0, nh, m, l, o, any_poison);
 }
 
-// Combine: one wave per (head, sequence). m* = max over the sequence's non-empty chunks,
-// L = sum l_c 2^(m_c - m*), out = sum o_c 2^(m_c - m*) / L, lse = (m* + log2 L) ln 2.
-__global__ __launch_bounds__(64) void k_combine(gva::DecodeArgs a) {
+// Combine: one work-group of kCombineWaves waves per (head, sequence). m* = max over the
+// sequence's non-empty chunks, L = sum l_c 2^(m_c - m*), out = sum o_c 2^(m_c - m*) / L and
+// lse = (m* + log2 L) ln 2. The chunk weights are formed once in LDS; wave w then sums chunks
+// w, w + kCombineWaves, ... with its lanes over the value dims, and the waves' sums meet in LDS.
+constexpr int kCombineWaves = 8;
+
+__device__ __forceinline__ float block_max(float v, float *scratch) {
+  v = gvad::wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < kCombineWaves; ++i) r = fmaxf(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *scratch) {
+  v = gvad::wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  float r = 0.0f;
+  for (int i = 0; i < kCombineWaves; ++i) r += scratch[i];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(64 * kCombineWaves) void k_combine(gva::DecodeArgs a) {
   __shared__ float w_s[gva::kMaxSplits];
+  __shared__ float part[kCombineWaves][gva::kMaxDh];
+  __shared__ float scratch[kCombineWaves];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nthr = 64 * kCombineWaves;
   const float qnan = __int_as_float(0x7fc00000);
   float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
   const int len = a.seq_len[b];
   const int cap = a.max_blocks << a.log2_bs;
   if (len < 0 || len > a.max_len || len > cap) {
-    for (int d = lane; d < a.d_h; d += 64) dst[d] = qnan;
-    if (a.lse && lane == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
+    for (int d = tid; d < a.d_h; d += nthr) dst[d] = qnan;
+    if (a.lse && tid == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
     return;
   }
   const int ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
   if (ns == 0) {
-    for (int d = lane; d < a.d_h; d += 64) dst[d] = 0.0f;
-    if (a.lse && lane == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
+    for (int d = tid; d < a.d_h; d += nthr) dst[d] = 0.0f;
+    if (a.lse && tid == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
     return;
   }
   const int64_t row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;  // + s * H
   float mx = -INFINITY;
-  bool bad = false;
-  for (int s = lane; s < ns; s += 64) {
+  int bad = 0;
+  for (int s = tid; s < ns; s += nthr) {
     const float ms = a.part_m[row0 + static_cast<int64_t>(s) * a.H];
-    if (isnan(ms)) bad = true;
+    bad |= isnan(ms) ? 1 : 0;
     mx = fmaxf(mx, ms);
+    w_s[s] = ms;
   }
-  mx = gvad::wave_max(mx);
-  bad = __any(bad);
+  mx = block_max(mx, scratch);
+  bad = block_sum(static_cast<float>(bad), scratch) > 0.0f;
   float L = 0.0f;
-  for (int s = lane; s < ns; s += 64) {
-    const int64_t r = row0 + static_cast<int64_t>(s) * a.H;
-    const float f = exp2f(a.part_m[r] - mx);
+  for (int s = tid; s < ns; s += nthr) {
+    const float f = exp2f(w_s[s] - mx);
     w_s[s] = f;
-    L += a.part_l[r] * f;
+    L += a.part_l[row0 + static_cast<int64_t>(s) * a.H] * f;
   }
-  L = gvad::wave_sum(L);
+  L = block_sum(L, scratch);  // also orders the w_s writes before the reads below
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = wave; s < ns; s += kCombineWaves) {
+    const float f = w_s[s];
+    const float *po = a.part_o + (row0 + static_cast<int64_t>(s) * a.H) * a.d_h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = lane + 64 * k;
+      if (d < a.d_h) acc[k] = fmaf(po[d], f, acc[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = lane + 64 * k;
+    if (d < a.d_h) part[wave][d] = acc[k];
+  }
   __syncthreads();
   const float inv = 1.0f / L;
-  for (int d = lane; d < a.d_h; d += 64) {
-    float acc = 0.0f;
-    for (int s = 0; s < ns; ++s)
-      acc = fmaf(a.part_o[(row0 + static_cast<int64_t>(s) * a.H) * a.d_h + d], w_s[s], acc);
-    dst[d] = bad ? qnan : acc * inv;
+  for (int d = tid; d < a.d_h; d += nthr) {
+    float v = 0.0f;
+    for (int w = 0; w < kCombineWaves; ++w) v += part[w][d];
+    dst[d] = bad ? qnan : v * inv;
   }
-  if (a.lse && lane == 0)
+  if (a.lse && tid == 0)
     a.lse[static_cast<int64_t>(b) * a.H + h] = bad ? qnan : (mx + log2f(L)) * gvad::kLn2;
 }
 
@@ -274,7 +320,7 @@ hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t str
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_combine, dim3(a.H, a.B), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.H, a.B), dim3(64 * kCombineWaves), 0, stream, a);
   return hipGetLastError();
 }
 

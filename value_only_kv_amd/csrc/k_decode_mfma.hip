@@ -15,25 +15,30 @@
 // Layout facts of v_mfma_f32_16x16x32_bf16 used below (checked on the hardware):
 //   A[i][k]: lane i + 16 (k / 8), element k % 8;  B[k][j]: lane j + 16 (k / 8), element k % 8;
 //   D[i][j]: lane j + 16 (i / 4), register i % 4.
-// Write n = lane % 16 and q = lane / 16.
+// Write n = lane % 16 (a row of 16 lanes) and q = lane / 16.
 //
 // One wave per (chunk, sequence, group); a work-group holds several groups of the same chunk,
 // so their reads of the shared positional key hit in cache. A chunk is walked in tiles of 32
 // positions, two blocks of 16 (tb = 0, 1):
 //   1. V rows go straight from HBM into registers in A-operand form: lane (n, q) loads 16 bytes,
 //      8 consecutive dims 32 ks + 8 q .. of position 16 tb + n, for every k-step ks.
-//   2. Scores S^T[t][h] = sum_k V[t][k] Q[h][k] (B = the absorbed query, one column per head).
-//      The query is split into bf16 hi + lo parts, two MFMAs, so it keeps ~16 mantissa bits.
-//      Lane (n, q) then holds head n's scores of positions 16 tb + 4 q + r, r = 0..3.
+//   2. Scores S^T[t][c] = sum_k V[t][k] Q[c][k]. The query keeps ~16 significant bits by being
+//      split into bf16 hi + lo parts. With NH heads per group (NH <= 8) column c < NH holds
+//      head c's hi part and column NH + c its lo part, so one MFMA forms both; a row shift by NH
+//      lanes (DPP) adds them, and lane (NH + c, q) then owns head c's scores of positions
+//      16 tb + 4 q + r, r = 0..3. (Other head counts use separate hi and lo MFMAs; then lane
+//      (c, q) owns head c.)
 //   3. Online softmax per head in the base-2 domain; the tile max needs two lane exchanges.
-//   4. The weighted sum O^T[d][h] = sum_t V[t][d] P[h][t] contracts over positions, so V is
+//   4. The weighted sum O^T[d][c] = sum_t V[t][d] P[c][t] contracts over positions, so V is
 //      needed with positions along K. The matrix core transposes the registers it already has:
 //      V x E, with E a 0/1 selection matrix, returns V[t][d] in D layout (lane (n, q) gets
 //      positions 4 q + r of dim n), exactly, since each output is one product by 1.0. Packing
 //      the two position blocks gives the A operand with K order (q, e) -> 16 (e / 4) + 4 q + e % 4,
 //      which is exactly the order in which each lane already holds its probabilities, so the
-//      B operand (P, hi + lo parts) is built from the lane's own registers.
-//   5. O^T accumulates in registers: lane (n, q) holds head n, dims 16 nb + 4 q + r.
+//      B operand (P split into hi and lo parts, laid out like the query columns) is built from
+//      registers, with one more row shift to place the hi parts.
+//   5. O^T accumulates in registers: lane (n, q) holds column n, dims 16 nb + 4 q + r; the hi
+//      and lo columns are added once, at the end.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -64,66 +69,204 @@ __device__ __forceinline__ unsigned pack2(float x, float y) {
 __device__ __forceinline__ float low_bf16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float high_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): ~16 significant bits in two bf16 operands.
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
-  u32x4 h, l;
+// Lane i of each row of 16 receives lane i - S (row_shr) or i + S (row_shl); lanes with no
+// source receive 0.
+template <int S>
+__device__ __forceinline__ unsigned row_shr(unsigned v) {
+  return static_cast<unsigned>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x110 + S, 0xf, 0xf, true));
+}
+template <int S>
+__device__ __forceinline__ unsigned row_shl(unsigned v) {
+  return static_cast<unsigned>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x100 + S, 0xf, 0xf, true));
+}
+template <int S>
+__device__ __forceinline__ float row_shr_f(float v) {
+  return __uint_as_float(row_shr<S>(__float_as_uint(v)));
+}
+template <int S>
+__device__ __forceinline__ float row_shl_f(float v) {
+  return __uint_as_float(row_shl<S>(__float_as_uint(v)));
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): ~16 significant bits in two bf16 values.
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const unsigned w = pack2(x[2 * i], x[2 * i + 1]);
-    h[i] = w;
-    l[i] = pack2(x[2 * i] - low_bf16(w), x[2 * i + 1] - high_bf16(w));
+    hi[i] = w;
+    lo[i] = pack2(x[2 * i] - low_bf16(w), x[2 * i + 1] - high_bf16(w));
   }
-  hi = as_bf16(h);
-  lo = as_bf16(l);
 }
 
 template <int KS>
 struct Tile {
   u32x4 v[2][KS];   // V rows in A-operand form, per position block and k-step
-  u32x4 kr[2];      // positional key rows in A-operand form (zero where 8 q >= d_r)
+  u32x4 kr[2];      // positional key rows in A-operand form
 };
 
-// Loads the 32 positions starting at t0 (positions >= c1 read position c1 - 1 instead; their
-// scores are masked). Sets *bad when a block-table entry is outside the pool.
+// Block-table entries of the two 16-position blocks of the tile at t0 (clamped to c1 - 1):
+// even lanes hold the first block's entry, odd lanes the second's. The per-lane address makes
+// this a vector load, so it completes in order with the V loads; it is issued a tile ahead and
+// ordered before the previous tile's V loads, so waiting for it never waits for V data in
+// flight. (A scalar load here would share the counter of the cross-lane exchanges and stall.)
+__device__ __forceinline__ int32_t load_pages(const int32_t *__restrict__ bt, int log2_bs, int t0,
+                                              int c1, int lane) {
+  return bt[min(t0 + 16 * (lane & 1), c1 - 1) >> log2_bs];
+}
+
+// Loads the 32 positions starting at t0 as two blocks of 16. Every load is issued
+// unconditionally, so the number of loads in flight is the same on every path and each tile
+// waits only for its own data. A block lies inside one cache block (block_size >= 16 and t0 is a
+// multiple of 16), so one table entry serves all of its lanes. Positions >= c1 read position
+// c1 - 1 instead (finite data from a block that is cached already); their scores are masked, so
+// they add exactly zero. vlane/klane are the lane-invariant parts of the element offsets.
 template <int KS>
-__device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int b, int g, int t0, int c1,
-                                          int n, int q, Tile<KS> &T, bool &bad) {
+__device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, int t0, int c1,
+                                          int n, int64_t vlane, int64_t klane, Tile<KS> &T,
+                                          bool &bad) {
   const int mask = (1 << a.log2_bs) - 1;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
   const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const int t = t0 + 16 * tb + n;
-    const int tc = t < c1 ? t : c1 - 1;
-    const int32_t pb = a.block_table[static_cast<int64_t>(b) * a.max_blocks + (tc >> a.log2_bs)];
+    const int32_t pb = __builtin_amdgcn_readlane(P, tb);
     const bool ok = pb >= 0 && static_cast<int64_t>(pb) < a.num_blocks;
     bad |= !ok;
     const int64_t blk = ok ? pb : 0;
-    const int64_t off = static_cast<int64_t>(tc & mask);
-    const uint16_t *vp = vbase + blk * a.v_sb + off * a.v_st + static_cast<int64_t>(g) * a.v_sg + 8 * q;
+    const int f = min(t0 + 16 * tb, c1 - 1);          // first position read by this block
+    const int rn = min(n, c1 - 1 - f);                 // row within the block (clamped)
+    const int64_t row = static_cast<int64_t>((f & mask) + rn);
+    const uint16_t *vp = vbase + blk * a.v_sb + row * a.v_st + vlane;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = *reinterpret_cast<const u32x4 *>(vp + 32 * ks);
-    if (8 * q < a.d_r) {
-      T.kr[tb] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + off * a.kr_st + 8 * q);
-    } else {
-      T.kr[tb] = u32x4{0u, 0u, 0u, 0u};
-    }
+    T.kr[tb] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + klane);
   }
 }
 
+// Per-wave state of the online softmax and the accumulators.
 template <int KS>
+struct Acc {
+  f32x4 O[2 * KS];
+  float m;
+  float lsum;
+};
+
+// One tile: scores, online softmax and the weighted sum. NH > 0: merged hi/lo columns (see the
+// file comment); NH == 0: separate hi and lo MFMAs with QX = hi and QY = lo.
+template <int KS, int NH>
+__device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, int n, int q,
+                                          const bf16x8 (&QX)[KS], const bf16x8 (&QY)[KS],
+                                          const bf16x8 &RX, const bf16x8 &RY,
+                                          const bf16x8 (&SEL)[2], Acc<KS> &acc) {
+  constexpr int SH = NH > 0 ? NH : 1;
+  f32x4 S[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+    if (NH > 0) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma(as_bf16(cur.v[tb][ks]), QX[ks], s0);
+      s0 = mfma(as_bf16(cur.kr[tb]), RX, s0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s0[r] += row_shr_f<SH>(s0[r]);
+    } else {
+      f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s0 = mfma(as_bf16(cur.v[tb][ks]), QX[ks], s0);
+        s1 = mfma(as_bf16(cur.v[tb][ks]), QY[ks], s1);
+      }
+      s0 = mfma(as_bf16(cur.kr[tb]), RX, s0);
+      s1 = mfma(as_bf16(cur.kr[tb]), RY, s1);
+      s0 += s1;
+    }
+    S[tb] = s0;
+  }
+  if (t0 + kTile > c1) {  // the last tile of the chunk: mask positions >= c1
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (t0 + 16 * tb + 4 * q + r >= c1) S[tb][r] = -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                   fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(acc.m, mt);
+  float alpha = __builtin_amdgcn_exp2f(acc.m - mn);
+  float p[8];
+  float ps = 0.0f;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[4 * tb + r] = __builtin_amdgcn_exp2f(S[tb][r] - mn);
+      ps += p[4 * tb + r];
+    }
+  acc.lsum = acc.lsum * alpha + ps;
+  acc.m = mn;
+  u32x4 ph, pl;
+  split8(p, ph, pl);
+  if (NH > 0) {
+    // hi columns c < NH take the hi parts (and alpha) from their owner lanes NH + c
+    const bool hi_col = n < NH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned h = row_shl<SH>(ph[i]);
+      pl[i] = hi_col ? h : pl[i];
+    }
+    const float a2 = row_shl_f<SH>(alpha);
+    alpha = hi_col ? a2 : alpha;
+  }
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) acc.O[i] *= alpha;
+  }
+  const bf16x8 PX = as_bf16(NH > 0 ? pl : ph);
+  const bf16x8 PY = as_bf16(pl);
+#pragma unroll
+  for (int nb = 0; nb < 2 * KS; ++nb) {
+    const int ks = nb >> 1;
+    const int half = nb & 1;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 T0 = mfma(as_bf16(cur.v[0][ks]), SEL[half], z);
+    const f32x4 T1 = mfma(as_bf16(cur.v[1][ks]), SEL[half], z);
+    u32x4 w;
+    w[0] = pack2(T0[0], T0[1]);
+    w[1] = pack2(T0[2], T0[3]);
+    w[2] = pack2(T1[0], T1[1]);
+    w[3] = pack2(T1[2], T1[3]);
+    const bf16x8 VT = as_bf16(w);
+    acc.O[nb] = mfma(VT, PX, acc.O[nb]);
+    if (NH == 0) acc.O[nb] = mfma(VT, PY, acc.O[nb]);
+  }
+}
+
+template <int KS, int NH>
 __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
+  constexpr int SH = NH > 0 ? NH : 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int q = lane >> 4;
-  const int s = blockIdx.x;
-  const int b = blockIdx.y;
+  // The sequence index varies fastest along the grid: work-groups are dealt to the 8 XCDs in
+  // turn, so every XCD receives an even share of each split column (early split columns are
+  // almost always non-empty, late ones often empty).
+  const int b = blockIdx.x;
+  const int s = blockIdx.y;
   const int g = blockIdx.z * (blockDim.x >> 6) + wave;
   const int nhg = a.H / a.G;
   const int h0 = g * nhg;
-  const bool head_ok = n < nhg;
-  const int row = a.d_h + a.d_r;
+  // the query column of this lane: head c (hi or, with merged columns, lo part)
+  const int c = NH > 0 ? (n < NH ? n : n - NH) : n;
+  const bool col_ok = NH > 0 ? (n < 2 * NH) : (n < nhg);
+  const bool use_lo = NH > 0 && n >= NH;
+  // the lanes that own a head's softmax state and output
+  const bool owner = NH > 0 ? (n >= NH && n < 2 * NH) : (n < nhg);
+  const int row_len = a.d_h + a.d_r;
   const float qnan = __int_as_float(0x7fc00000);
 
   const int len = a.seq_len[b];
@@ -132,32 +275,43 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
   const int c0 = s * a.chunk;
   const int c1 = len_bad ? c0 : min(c0 + a.chunk, len);
 
-  f32x4 O[2 * KS];
+  Acc<KS> acc;
 #pragma unroll
-  for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-  float lsum = 0.0f;
+  for (int i = 0; i < 2 * KS; ++i) acc.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc.m = -INFINITY;
+  acc.lsum = 0.0f;
   bool bad = false;
 
   if (c0 < c1) {
-    // ---- query operands (B layout: column n = head, K group q) ----
-    bf16x8 QH[KS], QL[KS], RH, RL, SEL[2];
-    const float *qp = a.q_abs + (static_cast<int64_t>(b) * a.H + h0 + n) * row;
+    // ---- query operands (B layout: column n, K group q) ----
+    bf16x8 QX[KS], QY[KS], RX, RY, SEL[2];
+    const float *qp =
+        a.q_abs + (static_cast<int64_t>(b) * a.H + h0 + (col_ok ? c : 0)) * row_len;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float x[8];
+      const float4 *src = reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q);
+      const float4 x0 = src[0], x1 = src[1];
+      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = head_ok ? qp[32 * ks + 8 * q + e] * a.qscale : 0.0f;
-      split8(x, QH[ks], QL[ks]);
+      for (int e = 0; e < 8; ++e) x[e] = col_ok ? x[e] * a.qscale : 0.0f;
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      QX[ks] = as_bf16(use_lo ? lo : hi);
+      QY[ks] = as_bf16(lo);
     }
     {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * q + e;
-        x[e] = (head_ok && i < a.d_r) ? qp[a.d_h + i] * a.qscale : 0.0f;
+        x[e] = (col_ok && i < a.d_r) ? qp[a.d_h + i] * a.qscale : 0.0f;
       }
-      split8(x, RH, RL);
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      RX = as_bf16(use_lo ? lo : hi);
+      RY = as_bf16(lo);
     }
     // selection matrices E_half[k][j] = 1 if k == 16 half + j (B layout)
 #pragma unroll
@@ -172,80 +326,40 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
       SEL[half] = as_bf16(w);
     }
 
-    Tile<KS> cur;
-    load_tile<KS>(a, b, g, c0, c1, n, q, cur, bad);
-    for (int t0 = c0; t0 < c1; t0 += kTile) {
-      const bool more = t0 + kTile < c1;
-      Tile<KS> nxt;
-      if (more) load_tile<KS>(a, b, g, t0 + kTile, c1, n, q, nxt, bad);
+    // lane-invariant parts of the element offsets (positional K groups beyond d_r read the
+    // row's last 8 elements; they meet zeros in the query operand)
+    const int64_t vlane = static_cast<int64_t>(g) * a.v_sg + 8 * q;
+    const int64_t klane = min(8 * q, a.d_r - 8);
 
-      // ---- scores ----
-      f32x4 S[2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          acc = mfma(as_bf16(cur.v[tb][ks]), QH[ks], acc);
-          acc = mfma(as_bf16(cur.v[tb][ks]), QL[ks], acc);
-        }
-        acc = mfma(as_bf16(cur.kr[tb]), RH, acc);
-        acc = mfma(as_bf16(cur.kr[tb]), RL, acc);
-        S[tb] = acc;
-      }
-      // ---- online softmax (head n; positions t0 + 16 tb + 4 q + r) ----
-      float mt = -INFINITY;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (t0 + 16 * tb + 4 * q + r >= c1) S[tb][r] = -INFINITY;
-          mt = fmaxf(mt, S[tb][r]);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m, mt);
-      const float alpha = exp2f(m - mn);
-      float p[8];
-      float ps = 0.0f;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[4 * tb + r] = exp2f(S[tb][r] - mn);
-          ps += p[4 * tb + r];
-        }
-      lsum = lsum * alpha + ps;
-      m = mn;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) O[i] *= alpha;
-      }
-      bf16x8 PH, PL;
-      split8(p, PH, PL);
-      // ---- weighted sum: transpose V by the matrix core, then O^T += V^T P^T ----
-#pragma unroll
-      for (int nb = 0; nb < 2 * KS; ++nb) {
-        const int ks = nb >> 1;
-        const int half = nb & 1;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 T0 = mfma(as_bf16(cur.v[0][ks]), SEL[half], z);
-        const f32x4 T1 = mfma(as_bf16(cur.v[1][ks]), SEL[half], z);
-        u32x4 w;
-        w[0] = pack2(T0[0], T0[1]);
-        w[1] = pack2(T0[2], T0[3]);
-        w[2] = pack2(T1[0], T1[1]);
-        w[3] = pack2(T1[2], T1[3]);
-        const bf16x8 VT = as_bf16(w);
-        O[nb] = mfma(VT, PH, O[nb]);
-        O[nb] = mfma(VT, PL, O[nb]);
-      }
-      if (more) cur = nxt;
+    // Two tile buffers in ping-pong (A, Bt): while one tile is computed the other one's loads
+    // are in flight, and no register copies are needed. Issue order per half-step: V loads of
+    // the next tile, then the page entries two tiles ahead, then the math of the current tile.
+    const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+    const int lb = a.log2_bs;
+    Tile<KS> A, Bt;
+    int32_t PA = load_pages(bt, lb, c0, c1, lane);
+    int32_t PB = load_pages(bt, lb, c0 + kTile, c1, lane);
+    load_tile<KS>(a, PA, c0, c1, n, vlane, klane, A, bad);
+    PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
+    for (int t0 = c0; t0 < c1; t0 += 2 * kTile) {
+      const int t1 = t0 + kTile;
+      load_tile<KS>(a, PB, t1, c1, n, vlane, klane, Bt, bad);
+      PB = load_pages(bt, lb, t1 + 2 * kTile, c1, lane);
+      tile_step<KS, NH>(A, t0, c1, n, q, QX, QY, RX, RY, SEL, acc);
+      load_tile<KS>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad);
+      PA = load_pages(bt, lb, t1 + 3 * kTile, c1, lane);
+      if (t1 < c1) tile_step<KS, NH>(Bt, t1, c1, n, q, QX, QY, RX, RY, SEL, acc);
     }
   }
 
-  // ---- epilogue: head n's row; dims 16 nb + 4 q + r ----
-  float ltot = lsum + __shfl_xor(lsum, 16, 64);
+  // ---- epilogue: the owner lanes of head c; dims 16 nb + 4 q + r ----
+  if (NH > 0) {
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc.O[i][r] += row_shr_f<SH>(acc.O[i][r]);
+  }
+  float ltot = acc.lsum + __shfl_xor(acc.lsum, 16, 64);
   ltot += __shfl_xor(ltot, 32, 64);
   const bool any_bad = __any(bad);
   if (lane == 0) {
@@ -253,31 +367,49 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
     if (len_bad && s == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
   }
   const bool poison = any_bad || len_bad;
-  if (!head_ok) return;
-  const int h = h0 + n;
+  if (!owner) return;
+  // chunks past the end of a valid sequence are never read by the combine
+  if (a.num_splits > 1 && !len_bad && c0 >= len) return;
+  const int h = h0 + c;
   if (a.num_splits == 1) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h + 4 * q;
 #pragma unroll
     for (int nb = 0; nb < 2 * KS; ++nb) {
-      f32x4 v = O[nb] * inv;
+      f32x4 v = acc.O[nb] * inv;
       if (poison) v = f32x4{qnan, qnan, qnan, qnan};
       *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
     }
     if (a.lse && q == 0) {
-      const float v = ltot > 0.0f ? (m + log2f(ltot)) * gvad::kLn2 : -INFINITY;
+      const float v = ltot > 0.0f ? (acc.m + log2f(ltot)) * gvad::kLn2 : -INFINITY;
       a.lse[static_cast<int64_t>(b) * a.H + h] = poison ? qnan : v;
     }
   } else {
     const int64_t prow = (static_cast<int64_t>(b) * a.num_splits + s) * a.H + h;
     float *dst = a.part_o + prow * a.d_h + 4 * q;
 #pragma unroll
-    for (int nb = 0; nb < 2 * KS; ++nb) *reinterpret_cast<f32x4 *>(dst + 16 * nb) = O[nb];
+    for (int nb = 0; nb < 2 * KS; ++nb) *reinterpret_cast<f32x4 *>(dst + 16 * nb) = acc.O[nb];
     if (q == 0) {
-      a.part_m[prow] = poison ? qnan : m;
+      a.part_m[prow] = poison ? qnan : acc.m;
       a.part_l[prow] = ltot;
     }
   }
+}
+
+template <int NH>
+hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (a.d_h / 32) {
+    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -292,20 +424,15 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
       wpg = w;
       break;
     }
-  const dim3 grid(a.num_splits, a.B, a.G / wpg);
+  const dim3 grid(a.B, a.num_splits, a.G / wpg);
   const dim3 block(64 * wpg);
-  switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL(k_decode_mfma<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_mfma<2>, grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(k_decode_mfma<3>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(k_decode_mfma<4>, grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL(k_decode_mfma<5>, grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL(k_decode_mfma<6>, grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL(k_decode_mfma<7>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_mfma<8>, grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  switch (a.H / a.G) {
+    case 1: return launch_nh<1>(a, grid, block, stream);
+    case 2: return launch_nh<2>(a, grid, block, stream);
+    case 4: return launch_nh<4>(a, grid, block, stream);
+    case 8: return launch_nh<8>(a, grid, block, stream);
+    default: return launch_nh<0>(a, grid, block, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
