@@ -167,7 +167,7 @@ def test_split_planning(L):
     # automatic: long single sequences get ~one chunk per compute unit, chunks are multiples of 64
     S = gb.gva_decode_num_splits(d, 1, 131072, 0)
     assert S == 256
-    assert gb.gva_decode_num_splits(d, 256, 32769, 0) == 17
+    assert gb.gva_decode_num_splits(d, 256, 32769, 0) == 9
     # explicit split counts are kept unless a chunk would start beyond max_len
     for S in (64, 128, 256):
         assert gb.gva_decode_num_splits(d, 1, 131072, S) == S

@@ -145,8 +145,8 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
   int64_t S = num_splits;
   if (S == 0) {
     // Enough chunks to give every compute unit work when the batch is small, chunks of at most
-    // 2048 positions for long sequences, and no chunk below 256 positions.
-    const int64_t by_len = (max_len + 2047) / 2048;
+    // 4096 positions for long sequences, and no chunk below 256 positions.
+    const int64_t by_len = (max_len + 4095) / 4096;
     const int64_t by_cus = (kPlanCUs + B - 1) / B;
     S = by_len > by_cus ? by_len : by_cus;
     const int64_t cap = (max_len + 255) / 256;

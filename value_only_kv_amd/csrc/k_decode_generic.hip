@@ -191,102 +191,91 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
   store_rows<DPL>(a, b, s, h0, nh, m, l, o, any_poison);
 }
 
-// Combine: one work-group of kCombineWaves waves per (head, sequence). m* = max over the
-// sequence's non-empty chunks, L = sum l_c 2^(m_c - m*), out = sum o_c 2^(m_c - m*) / L and
-// lse = (m* + log2 L) ln 2. The chunk weights are formed once in LDS; wave w then sums chunks
-// w, w + kCombineWaves, ... with its lanes over the value dims, and the waves' sums meet in LDS.
-constexpr int kCombineWaves = 8;
+// Combine: m* = max over a sequence's non-empty chunks, L = sum l_c 2^(m_c - m*),
+// out = sum o_c 2^(m_c - m*) / L and lse = (m* + log2 L) ln 2. One work-group per
+// (64-dim slice, head, sequence) with nw waves (1 .. 16, growing with the split count): the
+// chunk weights 2^(m_c - m*) are formed once in LDS, wave w sums chunks w, w + nw, ... with its
+// lanes over the slice's dims, and the waves' sums meet in LDS.
+constexpr int kCombineMaxWaves = 16;
 
-__device__ __forceinline__ float block_max(float v, float *scratch) {
-  v = gvad::wave_max(v);
+__device__ __forceinline__ float block_reduce(float v, float *scratch, int nw, bool is_max) {
+  v = is_max ? gvad::wave_max(v) : gvad::wave_sum(v);
+  if (nw == 1) return v;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) scratch[wave] = v;
   __syncthreads();
   float r = scratch[0];
-  for (int i = 1; i < kCombineWaves; ++i) r = fmaxf(r, scratch[i]);
+  for (int i = 1; i < nw; ++i) r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
   __syncthreads();
   return r;
 }
 
-__device__ __forceinline__ float block_sum(float v, float *scratch) {
-  v = gvad::wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  float r = 0.0f;
-  for (int i = 0; i < kCombineWaves; ++i) r += scratch[i];
-  __syncthreads();
-  return r;
-}
-
-__global__ __launch_bounds__(64 * kCombineWaves) void k_combine(gva::DecodeArgs a) {
+__global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeArgs a) {
   __shared__ float w_s[gva::kMaxSplits];
-  __shared__ float part[kCombineWaves][gva::kMaxDh];
-  __shared__ float scratch[kCombineWaves];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  __shared__ float part[kCombineMaxWaves][64];
+  __shared__ float scratch[kCombineMaxWaves];
+  const int d0 = 64 * blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int nthr = 64 * kCombineWaves;
+  const int nw = blockDim.x >> 6;
+  const int nthr = blockDim.x;
+  const int d = d0 + lane;
+  const bool dim_ok = d < a.d_h;
   const float qnan = __int_as_float(0x7fc00000);
   float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
+  const bool write_lse = a.lse && tid == 0 && blockIdx.x == 0;
   const int len = a.seq_len[b];
   const int cap = a.max_blocks << a.log2_bs;
   if (len < 0 || len > a.max_len || len > cap) {
-    for (int d = tid; d < a.d_h; d += nthr) dst[d] = qnan;
-    if (a.lse && tid == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
+    if (wave == 0 && dim_ok) dst[d] = qnan;
+    if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
     return;
   }
   const int ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
   if (ns == 0) {
-    for (int d = tid; d < a.d_h; d += nthr) dst[d] = 0.0f;
-    if (a.lse && tid == 0) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
+    if (wave == 0 && dim_ok) dst[d] = 0.0f;
+    if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
     return;
   }
   const int64_t row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;  // + s * H
   float mx = -INFINITY;
-  int bad = 0;
+  float bad = 0.0f;
   for (int s = tid; s < ns; s += nthr) {
     const float ms = a.part_m[row0 + static_cast<int64_t>(s) * a.H];
-    bad |= isnan(ms) ? 1 : 0;
+    bad += isnan(ms) ? 1.0f : 0.0f;
     mx = fmaxf(mx, ms);
     w_s[s] = ms;
   }
-  mx = block_max(mx, scratch);
-  bad = block_sum(static_cast<float>(bad), scratch) > 0.0f;
+  mx = block_reduce(mx, scratch, nw, true);
+  const bool poison = block_reduce(bad, scratch, nw, false) > 0.0f;
   float L = 0.0f;
   for (int s = tid; s < ns; s += nthr) {
     const float f = exp2f(w_s[s] - mx);
     w_s[s] = f;
     L += a.part_l[row0 + static_cast<int64_t>(s) * a.H] * f;
   }
-  L = block_sum(L, scratch);  // also orders the w_s writes before the reads below
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = wave; s < ns; s += kCombineWaves) {
-    const float f = w_s[s];
-    const float *po = a.part_o + (row0 + static_cast<int64_t>(s) * a.H) * a.d_h;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int d = lane + 64 * k;
-      if (d < a.d_h) acc[k] = fmaf(po[d], f, acc[k]);
+  L = block_reduce(L, scratch, nw, false);
+  if (nw == 1) __syncthreads();  // the w_s writes of other lanes must be visible
+  float acc = 0.0f;
+  if (dim_ok) {
+    const float *po = a.part_o + row0 * a.d_h + d;
+    const int64_t step = static_cast<int64_t>(a.H) * a.d_h;
+#pragma unroll 8
+    for (int s = wave; s < ns; s += nw) acc = fmaf(po[s * step], w_s[s], acc);
+  }
+  if (nw > 1) {
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      acc = 0.0f;
+      for (int w = 0; w < nw; ++w) acc += part[w][lane];
     }
   }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int d = lane + 64 * k;
-    if (d < a.d_h) part[wave][d] = acc[k];
-  }
-  __syncthreads();
-  const float inv = 1.0f / L;
-  for (int d = tid; d < a.d_h; d += nthr) {
-    float v = 0.0f;
-    for (int w = 0; w < kCombineWaves; ++w) v += part[w][d];
-    dst[d] = bad ? qnan : v * inv;
-  }
-  if (a.lse && tid == 0)
-    a.lse[static_cast<int64_t>(b) * a.H + h] = bad ? qnan : (mx + log2f(L)) * gvad::kLn2;
+  if (wave == 0 && dim_ok) dst[d] = poison ? qnan : acc / L;
+  if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = poison ? qnan : (mx + log2f(L)) * gvad::kLn2;
 }
 
 }  // namespace
@@ -320,7 +309,9 @@ hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t str
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_combine, dim3(a.H, a.B), dim3(64 * kCombineWaves), 0, stream, a);
+  int nw = a.num_splits / 16;
+  nw = nw < 1 ? 1 : (nw > kCombineMaxWaves ? kCombineMaxWaves : nw);
+  hipLaunchKernelGGL(k_combine, dim3((a.d_h + 63) / 64, a.H, a.B), dim3(64 * nw), 0, stream, a);
   return hipGetLastError();
 }
 
