@@ -1,0 +1,130 @@
+"""GPU parity of gva_prefill_chunk (chunk append + causal attention on matrix cores) against the
+oracle: the appended chunk is bit-exact in the pool, and outputs are within the bf16 tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gva_oracle as O
+from value_only_kv_amd import binding as gb
+from value_only_kv_amd import synth
+from tests.gpu_cases import Case, check_output, lse_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_prefill(c, start, C, q_abs, v_new, kr_new):
+    w = c.w
+    B = w.B
+    st = torch.from_numpy(np.asarray(start, np.int32)).cuda()
+    out = torch.full((B, C, w.H, w.d_h), float("nan"), device="cuda")
+    lse = torch.full((B, C, w.H), float("nan"), device="cuda")
+    gb.gva_prefill_chunk(c.cdims, c.cache, B, st, int(max(start)), C,
+                         torch.from_numpy(np.ascontiguousarray(q_abs, np.float32)).cuda(),
+                         torch.from_numpy(np.ascontiguousarray(v_new, np.float32)).cuda(),
+                         torch.from_numpy(np.ascontiguousarray(kr_new, np.float32)).cuda(),
+                         w.scale, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def _chunk_inputs(w, starts, C):
+    v_new = np.zeros((w.B, C, w.G, w.d_h), np.float32)
+    kr_new = np.zeros((w.B, C, w.d_r), np.float32)
+    for b in range(w.B):
+        v, kr = synth.sequence_tokens(w, b, int(starts[b]) + C)
+        v_new[b], kr_new[b] = v[starts[b]:], kr[starts[b]:]
+    rng = np.random.default_rng(5)
+    q_abs = rng.standard_normal((w.B, C, w.H, w.d_h + w.d_r)).astype(np.float32)
+    return q_abs, v_new, kr_new
+
+
+@pytest.mark.parametrize("shape", [
+    dict(H=8, G=2, d_h=64, d_n=64, d_r=16),        # 4 heads per group
+    dict(H=32, G=8, d_h=128, d_n=128, d_r=24),     # the long-context shape
+    dict(H=6, G=3, d_h=96, d_n=96, d_r=8),         # 2 heads per group, d_h = 3 x 32
+])
+@pytest.mark.parametrize("starts,C", [((100, 37, 0), 70), ((0, 5, 300), 1), ((64, 0, 16), 257)])
+def test_prefill_small_against_oracle(shape, starts, C):
+    w = synth.workload("C5", B=len(starts), T=0, chunk=C, append_one=False,
+                       lengths_uniform=None, **shape)
+    lens = np.asarray(starts, np.int64)
+    c = Case(w, lens=lens)
+    c.append_prefix()                                   # positions 0 .. start_b - 1
+    q_abs, v_new, kr_new = _chunk_inputs(w, starts, C)
+    out, lse = _run_prefill(c, starts, C, q_abs, v_new, kr_new)
+    ref, ref_lse, err = O.prefill(c.pool, c.dims, starts, C, q_abs.astype(np.float64), v_new,
+                                  kr_new, w.scale, c.tab_ora)
+    assert err == 0 and c.err_flag() == 0
+    # the chunk append wrote exactly what the oracle wrote (whole pools, sentinels included)
+    v_bits, kr_bits = c.device_bits()
+    assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
+    check_output(out, ref, "bf16", f"prefill {shape} starts={starts} C={C}")
+    ok, e = lse_ok(lse, ref_lse, 2e-2)
+    assert ok, e
+
+
+def test_prefill_end_to_end_through_absorb():
+    """Queries absorbed on the device at positions start_b + i; the oracle absorbs its own."""
+    w = synth.workload("C5", B=2, T=0, chunk=96, append_one=False, H=16, G=4, d_h=64, d_n=64)
+    starts = np.array([200, 77])
+    c = Case(w, lens=starts)
+    c.append_prefix()
+    C = w.chunk
+    _, v_new, kr_new = _chunk_inputs(w, starts, C)
+    M = synth.weights(w)
+    q_nope, q_rope = synth.queries(w, w.B * C)
+    q_pos = (starts[:, None] + np.arange(C)[None, :]).reshape(-1).astype(np.int32)
+    q_dev = torch.empty((w.B * C, w.H, w.d_h + w.d_r), device="cuda")
+    gb.gva_absorb_query(c.cdims, torch.from_numpy(q_nope).cuda(), torch.from_numpy(q_rope).cuda(),
+                        torch.from_numpy(q_pos).cuda(), torch.from_numpy(M).cuda(), c.tab_lib,
+                        c.max_pos, q_dev)
+    qt, r = O.absorb(q_nope, q_rope, q_pos, M, c.tab_ora)
+    q_ref = O.q_abs_of(qt, r).reshape(w.B, C, w.H, -1)
+    out, _ = _run_prefill(c, starts, C, q_dev.cpu().numpy().reshape(w.B, C, w.H, -1), v_new, kr_new)
+    ref, _, _ = O.prefill(c.pool, c.dims, starts, C, q_ref, v_new, kr_new, w.scale, c.tab_ora)
+    check_output(out, ref, "bf16", "prefill end to end")
+
+
+def test_prefill_c5_full_size_sampled_rows():
+    """B=4 sequences, 8192 cached positions + a 512-token causal chunk, H=32, G=8, d_h=128,
+    d_r=16, 16-token blocks; the oracle checks sampled (sequence, query, head) rows."""
+    w = synth.workload("C5", append_one=False)
+    lens = synth.lengths(w)
+    c = Case(w, lens=lens)
+    c.append_prefix(oracle=False)
+    C = w.chunk
+    starts = lens.astype(np.int64)
+    q_abs, v_new, kr_new = _chunk_inputs(w, starts, C)
+    out, lse = _run_prefill(c, starts, C, q_abs, v_new, kr_new)
+    assert c.err_flag() == 0
+    rng = np.random.default_rng(11)
+    for b in range(w.B):
+        n = int(starts[b]) + C
+        # the oracle's pool for this sequence only: its own append of all n positions
+        v, kr = synth.sequence_tokens(w, b, n)
+        O.append(c.pool, c.dims, np.full(n, b), np.arange(n), v, kr, c.tab_ora)
+        V, krc = O.gather(c.pool, c.dims, b, n)
+        queries = sorted(set([0, 1, C - 1] + list(rng.integers(0, C, size=13))))
+        got, ref = [], []
+        for i in queries:
+            L = int(starts[b]) + i + 1
+            o, l = O.decode_sequence(V[:L], krc[:L], c.dims, q_abs[b, i].astype(np.float64), w.scale)
+            got.append(out[b, i])
+            ref.append(o)
+            ok, e = lse_ok(lse[b, i], l, 2e-2)
+            assert ok, (b, i, e)
+        check_output(np.array(got), np.array(ref), "bf16", f"C5 seq {b}")
+    v_bits, _ = c.device_bits()
+    assert np.array_equal(v_bits, c.pool.v)
+
+
+def test_prefill_bad_start_poisons_rows():
+    w = synth.workload("C5", B=2, T=0, chunk=40, append_one=False, H=8, G=2, d_h=64, d_n=64)
+    starts = np.array([50, 20])
+    c = Case(w, lens=starts)
+    c.append_prefix()
+    q_abs, v_new, kr_new = _chunk_inputs(w, starts, 40)
+    bad = np.array([50, -3])
+    out, lse = _run_prefill(c, bad, 40, q_abs, v_new, kr_new)
+    assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1]))
+    assert c.err_flag() & gb.DEVERR_LENGTH

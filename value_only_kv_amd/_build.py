@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgva.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["gva_api.hip", "k_append_absorb.hip", "k_decode_generic.hip", "k_decode_mfma.hip"]
+HIP_SOURCES = ["gva_api.hip", "k_append_absorb.hip", "k_decode_generic.hip", "k_decode_mfma.hip",
+               "k_prefill.hip"]
 HOST_SOURCES = ["gva_host.cpp"]
 
 HIPCC_FLAGS = [

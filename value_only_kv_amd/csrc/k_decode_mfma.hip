@@ -435,6 +435,4 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
-
 }  // namespace gva

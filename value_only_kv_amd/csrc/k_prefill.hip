@@ -1,0 +1,418 @@
+// k_prefill.hip - chunked causal prefill for Grouped Value Attention on matrix cores (gfx950).
+//
+// A chunk of C new tokens per sequence is appended to the cache first (values and the rotated
+// shared positional key, exactly as the cache-append entry point writes them). Query i of
+// sequence b sits at position start_b + i and attends to positions 0 .. start_b + i, inclusive,
+// with the decode score q~_h . v_{j,g(h)} + r_h . kr_j ("GVA：KV 缓存里的 Key 其实可以不存",
+// shibing624.github.io review of arXiv:2609.13285, sections 关键技巧一 and 关键技巧二). Prefill
+// is a dense, matrix-heavy pass (agihunt.info summary of the paper): the score and the weighted
+// sum are [rows x (d_h + d_r)] x [(d_h + d_r) x keys] and [rows x keys] x [keys x d_h] products
+// with rows = (query, head) pairs of one value group.
+//
+// Work-group: 8 waves, 256 rows of one (sequence, group), rows ordered (query, head) with the
+// head fastest; each wave owns 2 row tiles of 16. Keys are walked in tiles of 32 positions
+// staged once per work-group in LDS (double-buffered, one barrier per tile) in two layouts:
+//   * natural rows [v (d_h) | kr (d_r, zero-padded to 32)], the A operand of the scores
+//     S^T[key][row] = sum_k K[key][k] Q[row][k] (B = the absorbed query, bf16), and
+//   * V^T [d_h][32 keys], the A operand of O^T[dim][row] += sum_key V^T[dim][key] P^T[key][row].
+// The transpose is done by the matrix core: V x E with a 0/1 selection matrix E, exact. Each
+// lane then holds, per row tile, row n = lane % 16 and keys 16 tb + 4 q + r of each 16-key
+// block (q = lane / 16), which is the K order (q, e) -> 16 (e / 4) + 4 q + e % 4 in which V^T is
+// read from LDS, so P feeds the second product from the lane's own registers. Operands are bf16
+// with float32 accumulation; the online softmax runs in float32 in the base-2 domain.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "gva_device.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr int kWaves = 8;
+constexpr int kRowTiles = 2;                       // row tiles of 16 per wave
+constexpr int kRows = kWaves * kRowTiles * 16;     // rows per work-group
+constexpr int kKeyTile = 32;
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ unsigned pack2(float x, float y) {
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));  // RNE, x in low half
+}
+
+// ---- appending the chunk -----------------------------------------------------------------
+
+// Token k of the chunk belongs to sequence k / C at position start[k / C] + k % C. The
+// arithmetic is the cache-append kernel's: one rounding of each value; the positional key
+// rotated in float64 (no fused multiply-add) and rounded once.
+__global__ __launch_bounds__(256) void k_append_chunk(gva::DecodeArgs a, int32_t C,
+                                                      const int32_t *start, const float *v_new,
+                                                      const float *kr_raw, const double *rope,
+                                                      int32_t max_pos) {
+  const int k = blockIdx.x;
+  const int b = k / C;
+  const int p = start[b] + (k - b * C);
+  const int cap = a.max_blocks << a.log2_bs;
+  int32_t err = 0;
+  if (start[b] < 0 || p < 0) err = GVA_DEVERR_LENGTH;
+  else if (p >= cap) err = GVA_DEVERR_CAPACITY;
+  else if (p >= max_pos) err = GVA_DEVERR_ROPE;
+  int64_t blk = -1;
+  if (!err) {
+    blk = gvad::block_of(a, b, p);
+    if (blk < 0) err = GVA_DEVERR_BLOCK;
+  }
+  if (err) {
+    if (threadIdx.x == 0) gvad::raise_err(a.err_flag, err);
+    return;
+  }
+  const int64_t off = p & ((1 << a.log2_bs) - 1);
+  const int half_h = a.d_h >> 1;
+  const float2 *src = reinterpret_cast<const float2 *>(v_new + static_cast<int64_t>(k) * a.G * a.d_h);
+  uint32_t *v32 = reinterpret_cast<uint32_t *>(const_cast<void *>(a.v));
+  for (int idx = threadIdx.x; idx < a.G * half_h; idx += blockDim.x) {
+    const int g = idx / half_h;
+    const int i = (idx - g * half_h) * 2;
+    const float2 x = src[idx];
+    const int64_t o = blk * a.v_sb + off * a.v_st + static_cast<int64_t>(g) * a.v_sg + i;
+    v32[o >> 1] = gvad::f64_to_bf16_bits(static_cast<double>(x.x)) |
+                  (static_cast<uint32_t>(gvad::f64_to_bf16_bits(static_cast<double>(x.y))) << 16);
+  }
+  const int half_r = a.d_r >> 1;
+  const float2 *ksrc = reinterpret_cast<const float2 *>(kr_raw + static_cast<int64_t>(k) * a.d_r);
+  const double2 *cs = reinterpret_cast<const double2 *>(rope) + static_cast<int64_t>(p) * half_r;
+  uint32_t *k32 = reinterpret_cast<uint32_t *>(const_cast<void *>(a.kr));
+  for (int i = threadIdx.x; i < half_r; i += blockDim.x) {
+    const float2 x = ksrc[i];
+    const double2 t = cs[i];
+    double y0, y1;
+    gvad::rotate_pair_f64(static_cast<double>(x.x), static_cast<double>(x.y), t.x, t.y, &y0, &y1);
+    const int64_t o = blk * a.kr_sb + off * a.kr_st + 2 * i;
+    k32[o >> 1] = gvad::f64_to_bf16_bits(y0) |
+                  (static_cast<uint32_t>(gvad::f64_to_bf16_bits(y1)) << 16);
+  }
+}
+
+// ---- attention -----------------------------------------------------------------------------
+
+// LDS tile: natural rows of (KS + 1) * 32 elements (+8 padding against bank conflicts) and the
+// transposed values, d_h rows of 32 keys (+8 padding).
+template <int KS>
+struct TileLds {
+  static constexpr int kNatStride = (KS + 1) * 32 + 8;
+  static constexpr int kVtStride = kKeyTile + 8;
+  static constexpr int kNatElems = kKeyTile * kNatStride;
+  static constexpr int kVtElems = KS * 32 * kVtStride;
+  static constexpr int kElems = kNatElems + kVtElems;
+};
+
+// A unit is 16 keys x 32 elements of the natural rows (k-step ks of key block kb); units
+// ks < KS are values, unit ks == KS the positional key. A wave stages units w, w + 8, ...
+// Each lane holds 16 bytes in A-operand form: key 16 kb + n, elements 32 ks + 8 q .. + 8.
+template <int KS>
+struct Stage {
+  static constexpr int kUnits = 2 * (KS + 1);
+  static constexpr int kPerWave = (kUnits + kWaves - 1) / kWaves;
+  u32x4 u[kPerWave];
+};
+
+template <int KS>
+__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const int32_t *__restrict__ bt,
+                                           int g, int kt0, int kend, int wave, int n, int q,
+                                           Stage<KS> &st) {
+  const int mask = (1 << a.log2_bs) - 1;
+  const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
+  const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
+#pragma unroll
+  for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
+    const int unit = min(wave + kWaves * i, Stage<KS>::kUnits - 1);
+    const int kb = unit & 1;
+    const int ks = unit >> 1;
+    const int key = min(kt0 + 16 * kb + n, kend - 1);   // keys past the end repeat the last
+    const int32_t pb = bt[key >> a.log2_bs];
+    const int64_t blk = (pb >= 0 && static_cast<int64_t>(pb) < a.num_blocks) ? pb : 0;
+    const int64_t row = key & mask;
+    if (ks < KS) {
+      st.u[i] = *reinterpret_cast<const u32x4 *>(vbase + blk * a.v_sb + row * a.v_st +
+                                                 static_cast<int64_t>(g) * a.v_sg + 32 * ks + 8 * q);
+    } else {
+      const int kq = min(8 * q, a.d_r - 8);
+      u32x4 w = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + kq);
+      if (8 * q >= a.d_r) w = u32x4{0u, 0u, 0u, 0u};   // zero padding up to 32
+      st.u[i] = w;
+    }
+  }
+}
+
+template <int KS>
+__device__ __forceinline__ void stage_store(uint16_t *lds, int wave, int n, int q,
+                                            const bf16x8 (&SEL)[2], const Stage<KS> &st) {
+  using L = TileLds<KS>;
+  uint16_t *nat = lds;
+  uint16_t *vt = lds + L::kNatElems;
+#pragma unroll
+  for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
+    const int unit = wave + kWaves * i;
+    if (unit >= Stage<KS>::kUnits) break;              // uniform per wave
+    const int kb = unit & 1;
+    const int ks = unit >> 1;
+    *reinterpret_cast<u32x4 *>(nat + (16 * kb + n) * L::kNatStride + 32 * ks + 8 * q) = st.u[i];
+    if (ks < KS) {
+      // V x E_half: lane (n, q) receives keys 4 q + r of dim 32 ks + 16 half + n, exactly
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 T = mfma(as_bf16(st.u[i]), SEL[half], z);
+        u32x2 w;
+        w[0] = pack2(T[0], T[1]);
+        w[1] = pack2(T[2], T[3]);
+        *reinterpret_cast<u32x2 *>(vt + (32 * ks + 16 * half + n) * L::kVtStride + 16 * kb + 4 * q) = w;
+      }
+    }
+  }
+}
+
+template <int KS>
+__global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
+  using L = TileLds<KS>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][L::kElems];
+  const gva::DecodeArgs &a = p.kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int q = lane >> 4;
+  const int nhg = a.H / a.G;
+  const int C = p.chunk_len;
+  // Work-group -> (row block, group, sequence). Work-groups are dealt to the 8 XCDs in turn;
+  // when the number of (sequence, group) pairs is a multiple of 8, the ids are arranged so that
+  // all row blocks of one pair land on the same XCD, back to back, and share its L2 for the
+  // keys and values they all read.
+  const int nrows = C * nhg;
+  const int nrb = (nrows + kRows - 1) / kRows;
+  const int npairs = a.B * a.G;
+  const int wg = blockIdx.x;
+  int rb, pair;
+  if ((npairs & 7) == 0) {
+    const int j = wg >> 3;
+    rb = j % nrb;
+    pair = (wg & 7) + 8 * (j / nrb);
+  } else {
+    rb = wg % nrb;
+    pair = wg / nrb;
+  }
+  const int g = pair % a.G;
+  const int b = pair / a.G;
+  const int row0 = rb * kRows;
+  if (row0 >= nrows) return;                           // uniform per work-group
+  const int P0 = p.start[b];
+  const int row_len = a.d_h + a.d_r;
+  const float qnan = __int_as_float(0x7fc00000);
+  const int cap = a.max_blocks << a.log2_bs;
+  const bool seq_bad = P0 < 0 || P0 > p.max_start || P0 + C > cap;
+
+  // rows of this wave: tile rt covers rows row0 + 16 (2 wave + rt) + 0..15
+  int qpos[kRowTiles];            // position of this lane's row (as the B column n)
+  bool rvalid[kRowTiles];
+  bf16x8 QB[kRowTiles][KS + 1];
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const int r = row0 + 16 * (kRowTiles * wave + rt) + n;
+    rvalid[rt] = r < nrows;
+    const int rc = rvalid[rt] ? r : nrows - 1;
+    const int qi = rc / nhg;
+    const int h = g * nhg + (rc - qi * nhg);
+    qpos[rt] = P0 + qi;
+    const float *qp = p.q_abs + ((static_cast<int64_t>(b) * C + qi) * a.H + h) * row_len;
+#pragma unroll
+    for (int ks = 0; ks <= KS; ++ks) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x0, x1;
+        if (ks < KS) {
+          x0 = qp[32 * ks + 8 * q + 2 * i];
+          x1 = qp[32 * ks + 8 * q + 2 * i + 1];
+        } else {
+          const int e = 8 * q + 2 * i;
+          x0 = e < a.d_r ? qp[a.d_h + e] : 0.0f;
+          x1 = e + 1 < a.d_r ? qp[a.d_h + e + 1] : 0.0f;
+        }
+        w[i] = pack2(x0 * a.qscale, x1 * a.qscale);
+      }
+      QB[rt][ks] = as_bf16(w);
+    }
+  }
+  bf16x8 SEL[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned lo = (8 * q + 2 * i == 16 * half + n) ? 0x3f80u : 0u;
+      const unsigned hi = (8 * q + 2 * i + 1 == 16 * half + n) ? 0x3f80u : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    SEL[half] = as_bf16(w);
+  }
+
+  f32x4 O[kRowTiles][2 * KS];
+  float m[kRowTiles], lsum[kRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    m[rt] = -INFINITY;
+    lsum[rt] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) O[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // keys 0 .. kend - 1 are seen by some row of this work-group
+  const int last_row = min(row0 + kRows, nrows) - 1;
+  const int kend = seq_bad ? 0 : P0 + last_row / nhg + 1;
+  const int first_q = P0 + row0 / nhg;                 // every key below it is seen by all rows
+  const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+
+  if (kend > 0) {
+    Stage<KS> st;
+    stage_load<KS>(a, bt, g, 0, kend, wave, n, q, st);
+    stage_store<KS>(lds[0], wave, n, q, SEL, st);
+    __syncthreads();
+    int buf = 0;
+    for (int kt0 = 0; kt0 < kend; kt0 += kKeyTile) {
+      const bool more = kt0 + kKeyTile < kend;         // uniform per work-group
+      if (more) stage_load<KS>(a, bt, g, kt0 + kKeyTile, kend, wave, n, q, st);
+      const uint16_t *nat = lds[buf];
+      const uint16_t *vt = lds[buf] + L::kNatElems;
+      // ---- scores S^T[key][row] for both key blocks and both row tiles ----
+      f32x4 S[kRowTiles][2];
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) S[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks <= KS; ++ks) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const u32x4 ka = *reinterpret_cast<const u32x4 *>(nat + (16 * tb + n) * L::kNatStride + 32 * ks + 8 * q);
+#pragma unroll
+          for (int rt = 0; rt < kRowTiles; ++rt) S[rt][tb] = mfma(as_bf16(ka), QB[rt][ks], S[rt][tb]);
+        }
+      }
+      // ---- causal mask (only tiles that reach past the first query), online softmax ----
+      const bool need_mask = kt0 + kKeyTile - 1 > first_q;
+      u32x4 PB[kRowTiles];
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        if (need_mask) {
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (kt0 + 16 * tb + 4 * q + r > qpos[rt]) S[rt][tb][r] = -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(fmaxf(S[rt][0][0], S[rt][0][1]), fmaxf(S[rt][0][2], S[rt][0][3])),
+                         fmaxf(fmaxf(S[rt][1][0], S[rt][1][1]), fmaxf(S[rt][1][2], S[rt][1][3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m[rt], mt);
+        // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
+        const float mref = mn == -INFINITY ? 0.0f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mref);
+        float pv[8];
+        float ps = 0.0f;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pv[4 * tb + r] = __builtin_amdgcn_exp2f(S[rt][tb][r] - mref);
+            ps += pv[4 * tb + r];
+          }
+        lsum[rt] = lsum[rt] * alpha + ps;
+        m[rt] = mn;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) PB[rt][i] = pack2(pv[2 * i], pv[2 * i + 1]);
+      }
+      // ---- O^T[dim][row] += V^T[dim][key] P^T[key][row] ----
+#pragma unroll
+      for (int nb = 0; nb < 2 * KS; ++nb) {
+        const uint16_t *src = vt + (16 * nb + n) * L::kVtStride + 4 * q;
+        u32x4 w;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 16);
+        w[0] = lo[0];
+        w[1] = lo[1];
+        w[2] = hi[0];
+        w[3] = hi[1];
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) O[rt][nb] = mfma(as_bf16(w), as_bf16(PB[rt]), O[rt][nb]);
+      }
+      if (more) stage_store<KS>(lds[buf ^ 1], wave, n, q, SEL, st);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // ---- epilogue: lane (n, q) holds row n of each tile, dims 16 nb + 4 q + r ----
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    float lt = lsum[rt] + __shfl_xor(lsum[rt], 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (!rvalid[rt]) continue;
+    const int r = row0 + 16 * (kRowTiles * wave + rt) + n;
+    const int qi = r / nhg;
+    const int h = g * nhg + (r - qi * nhg);
+    const int64_t orow = (static_cast<int64_t>(b) * C + qi) * a.H + h;
+    float *dst = p.out + orow * a.d_h + 4 * q;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 2 * KS; ++nb) {
+      f32x4 v = O[rt][nb] * inv;
+      if (seq_bad) v = f32x4{qnan, qnan, qnan, qnan};
+      *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
+    }
+    if (p.lse && q == 0)
+      p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (m[rt] + log2f(lt)) * gvad::kLn2 : -INFINITY);
+  }
+  if (seq_bad && threadIdx.x == 0 && rb == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+}
+
+}  // namespace
+
+namespace gva {
+
+hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream) {
+  const DecodeArgs &a = p.kv;
+  const int C = p.chunk_len;
+  hipLaunchKernelGGL(k_append_chunk, dim3(a.B * C), dim3(256), 0, stream, a, C, p.start, p.v_new,
+                     p.kr_raw, p.rope, p.max_pos);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrows = C * (a.H / a.G);
+  const dim3 grid(((nrows + kRows - 1) / kRows) * a.G * a.B);
+  switch (a.d_h / 32) {
+    case 1: hipLaunchKernelGGL(k_prefill<1>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(k_prefill<2>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(k_prefill<3>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(k_prefill<4>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 5: hipLaunchKernelGGL(k_prefill<5>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 6: hipLaunchKernelGGL(k_prefill<6>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 7: hipLaunchKernelGGL(k_prefill<7>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(k_prefill<8>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gva
