@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--no-long", action="store_true", help="skip the T=131072 measurement")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -201,6 +202,11 @@ def main():
             del reps
             torch.cuda.empty_cache()
 
+    # ---------------- chunked prefill + decode mix ----------------
+    prefill = None
+    if not args.no_prefill:
+        prefill = bench_prefill(torch, gb, synth, gen, stream)
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         bcopy = torch.empty_like(a)
@@ -243,9 +249,85 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "long_context": result_extra,
+        "prefill": prefill,
         "device": dev,
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_prefill(torch, gb, synth, gen, stream, iters=20):
+    """Chunked prefill of 512 causal queries over 8192 cached positions for 4 sequences
+    (H=32, G=8, d_h=128, d_r=16, 16-token blocks), then one decode step per sequence."""
+    w = synth.workload("C5")
+    lens = synth.lengths(w)
+    dc = DeviceCache(w, lens, 4321, torch, gb, synth)
+    B, C, H = w.B, w.chunk, w.H
+    row = w.d_h + w.d_r
+    start = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = torch.randn((B, C, H, row), generator=gen, device="cuda")
+    v_new = torch.randn((B, C, w.G, w.d_h), generator=gen, device="cuda")
+    kr_new = torch.randn((B, C, w.d_r), generator=gen, device="cuda")
+    out = torch.empty((B, C, H, w.d_h), device="cuda")
+    lse = torch.empty((B, C, H), device="cuda")
+    ms = int(lens.max())
+
+    def run():
+        gb.gva_prefill_chunk(dc.dims, dc.cache, B, start, ms, C, q, v_new, kr_new, w.scale, out,
+                             lse, stream=stream)
+
+    for _ in range(3):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)[iters // 2]
+    n_pairs = sum(int(lens[b]) * C + C * (C + 1) // 2 for b in range(B))
+    flop = n_pairs * H * (2 * (w.d_h + w.d_r) + 2 * w.d_h)
+    tflops = flop / t / 1e12
+    # the decode step that follows: append one token at start + C, decode over start + C + 1
+    pos = start + C
+    sl = pos + 1
+    seq = torch.arange(B, dtype=torch.int32, device="cuda")
+    v1 = torch.randn((B, w.G, w.d_h), generator=gen, device="cuda")
+    k1 = torch.randn((B, w.d_r), generator=gen, device="cuda")
+    q1 = torch.randn((B, H, row), generator=gen, device="cuda")
+    o1 = torch.empty((B, H, w.d_h), device="cuda")
+    ml = int(lens.max()) + C + 1
+    wsb = gb.gva_decode_workspace_bytes(dc.dims, B, ml, 0)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+
+    def step():
+        gb.gva_cache_append(dc.dims, dc.cache, B, seq, pos, v1, k1, stream=stream)
+        gb.gva_decode(dc.dims, dc.cache, B, sl, ml, q1, w.scale, o1, None, workspace=ws,
+                      stream=stream)
+
+    for _ in range(3):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    td = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)[iters // 2]
+    dec_bytes = int((lens + C + 1).sum()) * (w.G * w.d_h + w.d_r) * 2
+    log(f"C5 prefill: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s "
+        f"({tflops / 2500:.1%} of bf16 dense peak); mix decode step {td * 1e6:.1f} us")
+    assert torch.isfinite(out).all().item()
+    res = {"workload": "4 sequences x (8192 cached + 512 causal queries), H=32, G=8, d_h=d_n=128, "
+                       "d_r=16, bf16 cache in 16-token blocks; chunk append included",
+           "us": round(t * 1e6, 2), "flop": flop, "TFLOP_s": round(tflops, 1),
+           "mfma_util_bf16_dense": round(tflops / 2500.0, 4),
+           "decode_step_after_us": round(td * 1e6, 2),
+           "decode_step_after_GB_s": round(dec_bytes / td / 1e9, 1)}
+    del dc
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, lens, budget_s=15.0):
