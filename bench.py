@@ -148,7 +148,7 @@ def main():
     log(f"C4 step: {t_step * 1e3:.3f} ms, {value:.1f} GB/s, splits={S}")
 
     # decode launches alone, timed with HIP events on the launch stream
-    n_ev = max(args.steps, 10)
+    n_ev = max(args.steps, 100)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_ev)]
     for e0, e1 in ev:
@@ -157,9 +157,19 @@ def main():
                       num_splits=args.splits, kernel=args.kernel, workspace=ws, stream=stream)
         e1.record(stream)
     torch.cuda.synchronize()
-    t_dec = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) / 1e3
+    t_ev = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / 1e3
+    t_dec = float(t_ev.mean())
+    p10, p50, p90 = (float(x) for x in np.percentile(t_ev, [10, 50, 90]))
     dec_gbs = read_bytes / t_dec / 1e9
-    log(f"C4 decode (split decode + combine): {t_dec * 1e3:.3f} ms, {dec_gbs:.1f} GB/s")
+    log(f"C4 decode (split decode + combine): mean {t_dec * 1e3:.3f} ms (p10 {p10 * 1e3:.3f}, "
+        f"median {p50 * 1e3:.3f}, p90 {p90 * 1e3:.3f}), {dec_gbs:.1f} GB/s")
+    # HBM bytes per call from the committed counter runs, when they were taken on these sources
+    # and this configuration
+    traffic = None
+    if args.kernel == 0 and args.splits == 0:
+        from value_only_kv_amd.profile_summary import read_traffic
+        traffic = read_traffic(os.path.join(ROOT, "profiles", "gva_decode_ragged_batch_hbm_traffic.md"),
+                               read_bytes)
 
     result_extra = {}
     # ---------------- long context, one sequence ----------------
@@ -221,9 +231,10 @@ def main():
         cpu = cpu_baseline(w, lens)
 
     roofline = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "split decode + combine (gva_decode), ragged paged batch",
-                "bytes_per_launch": read_bytes, "launch_ms": round(t_dec * 1e3, 4)}
+                "bytes_per_launch": read_bytes, "launch_ms": round(t_dec * 1e3, 4),
+                "traffic_over_algorithmic": (round(traffic / read_bytes, 4) if traffic else None)}
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -245,7 +256,9 @@ def main():
         "seq_steps_per_s": round(B / t_step, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "decode_only": {"ms": round(t_dec * 1e3, 4), "GB_s": round(dec_gbs, 1),
-                        "seq_steps_per_s": round(B / t_dec, 1)},
+                        "seq_steps_per_s": round(B / t_dec, 1), "launches": n_ev,
+                        "ms_p10_p50_p90": [round(p10 * 1e3, 4), round(p50 * 1e3, 4),
+                                           round(p90 * 1e3, 4)]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "long_context": result_extra,

@@ -1,7 +1,7 @@
 """Plain, slow, obviously correct CPU oracle for Grouped Value Attention (GVA) decode.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or executes this
-module: only the tests, the graft smoke check and bench.py's cpu_baseline leg do. It
+module: only the tests, the smoke() check and bench.py's cpu_baseline leg do. It
 shares no code with the HIP library and imports nothing from it; it computes in float64
 with numpy (and Python's libm-backed math module for the RoPE angles).
 
@@ -26,7 +26,7 @@ What the method computes (restated):
     cached positions weights a sum over the same cached values ([summary]; [kvcache] §1,
     the decode-step attention equation).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * RoPE pairs are interleaved (x_{2i}, x_{2i+1}); theta_i = base^(-2i/d_r), base 10000.
   * Rotation is done in float64 with each product and sum rounded separately, and the
     cache stores one round-to-nearest-even of that float64 value.

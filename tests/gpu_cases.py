@@ -13,7 +13,7 @@ from value_only_kv_amd import synth
 
 SENTINEL = {"bf16": 0x7FC1, "f32": 0x7FC00001}   # NaN patterns no append can produce from finite data
 
-# Tolerances for outputs (BASELINE the benchmark spec): bf16 cache with fp32 accumulation -> max-abs 1e-2
+# Tolerances for outputs: bf16 cache with fp32 accumulation -> max-abs 1e-2
 # and relative L2 3e-3 over the whole output; fp32 cache -> max-abs 1e-5.
 TOL_BF16_MAXABS, TOL_BF16_RELL2 = 1e-2, 3e-3
 TOL_F32_MAXABS = 1e-5
