@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    path = os.environ.get("GVA_PARITY_LOG")
+    mod = sys.modules.get("tests.gpu_cases")
+    if not path or mod is None or not mod.ERRORS:
+        return
+    with open(path, "w") as f:
+        f.write("check\tdtype\tmax_abs\trel_l2\n")
+        for what, dtype, err, r in mod.ERRORS:
+            f.write(f"{what}\t{dtype}\t{err:.3e}\t{r:.3e}\n")

@@ -18,6 +18,10 @@ SENTINEL = {"bf16": 0x7FC1, "f32": 0x7FC00001}   # NaN patterns no append can pr
 TOL_BF16_MAXABS, TOL_BF16_RELL2 = 1e-2, 3e-3
 TOL_F32_MAXABS = 1e-5
 
+# (what, max-abs error, relative L2) of every output check in this process; conftest writes it
+# to a file at the end of the session when GVA_PARITY_LOG names one.
+ERRORS = []
+
 
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
@@ -31,10 +35,11 @@ def check_output(got, ref, dtype, what=""):
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), what
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    r = rel_l2(got, ref) if got.size else 0.0
+    ERRORS.append((what, dtype, err, r))
     if dtype == "f32":
         assert err <= TOL_F32_MAXABS, (what, err)
     else:
-        r = rel_l2(got, ref)
         assert err <= TOL_BF16_MAXABS and r <= TOL_BF16_RELL2, (what, err, r)
     return err
 

@@ -17,9 +17,9 @@
 //   D[i][j]: lane j + 16 (i / 4), register i % 4.
 // Write n = lane % 16 (a row of 16 lanes) and q = lane / 16.
 //
-// One wave per (chunk, sequence, group); a work-group holds several groups of the same chunk,
-// so their reads of the shared positional key hit in cache. A chunk is walked in tiles of 32
-// positions, two blocks of 16 (tb = 0, 1):
+// One wave per (chunk, sequence, group); a work-group holds four groups of the same chunk, and
+// the work-groups of one chunk run on the same XCD, so their reads of the shared positional key
+// hit in its L2. A chunk is walked in tiles of 32 positions, two blocks of 16 (tb = 0, 1):
 //   1. V rows go straight from HBM into registers in A-operand form: lane (n, q) loads 16 bytes,
 //      8 consecutive dims 32 ks + 8 q .. of position 16 tb + n, for every k-step ks.
 //   2. Scores S^T[t][c] = sum_k V[t][k] Q[c][k]. The query keeps ~16 significant bits by being
@@ -30,15 +30,16 @@
 //      (c, q) owns head c.)
 //   3. Online softmax per head in the base-2 domain; the tile max needs two lane exchanges.
 //   4. The weighted sum O^T[d][c] = sum_t V[t][d] P[c][t] contracts over positions, so V is
-//      needed with positions along K. The matrix core transposes the registers it already has:
-//      V x E, with E a 0/1 selection matrix, returns V[t][d] in D layout (lane (n, q) gets
-//      positions 4 q + r of dim n), exactly, since each output is one product by 1.0. Packing
-//      the two position blocks gives the A operand with K order (q, e) -> 16 (e / 4) + 4 q + e % 4,
-//      which is exactly the order in which each lane already holds its probabilities, so the
-//      B operand (P split into hi and lo parts, laid out like the query columns) is built from
-//      registers, with one more row shift to place the hi parts.
+//      needed with positions along K. The wave copies its tile rows to a private LDS area and
+//      reads them back with the transposing LDS load (ds_read_b64_tr_b16), which yields V^T in
+//      A-operand form with K order (q, e) -> 16 (e / 4) + 4 q + e % 4. That is exactly the order
+//      in which each lane already holds its probabilities, so the B operand (P split into hi and
+//      lo parts, laid out like the query columns) is built from registers, with one more row
+//      shift to place the hi parts.
 //   5. O^T accumulates in registers: lane (n, q) holds column n, dims 16 nb + 4 q + r; the hi
 //      and lo columns are added once, at the end.
+// Without the transposing products of a matrix-only design the kernel needs 168 registers at
+// d_h = 128, so three four-wave work-groups share a compute unit.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -52,8 +53,30 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kTile = 32;
+// Waves per work-group: 4 lets three work-groups share a CU (one wave per SIMD each) when the
+// kernel fits in 168 registers, which a single 8-wave work-group per CU cannot use.
+constexpr int kGroupWaves = 4;
+
+// Per-wave LDS copy of one tile: 32 rows (positions) of d_h bf16 values, each row padded by 32
+// bytes. The padding puts the four rows that one transposing read touches in every group of 16
+// lanes on different banks.
+template <int KS>
+struct TileLds {
+  static constexpr int kRow = 64 * KS + 32;   // bytes per row
+  static constexpr int kWave = kTile * kRow;  // bytes per wave
+};
+
+// ds_read_b64_tr_b16 (checked on the hardware): in each group of 16 lanes, lanes 4 e + k
+// (k = 0..3) address 4 consecutive 16-bit elements each, together one row of 16; lane i of the
+// group receives element e of its result from row e, column i. So lane L addressing row L / 4,
+// columns 4 (L % 4) .. + 3 of a row-major tile receives column L % 16 of rows 4 (L / 16) .. + 3.
+__device__ __forceinline__ i16x4 read_tr(const uint8_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+}
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -158,9 +181,17 @@ struct Acc {
 template <int KS, int NH>
 __device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, int n, int q,
                                           const bf16x8 (&QX)[KS], const bf16x8 (&QY)[KS],
-                                          const bf16x8 &RX, const bf16x8 &RY,
-                                          const bf16x8 (&SEL)[2], Acc<KS> &acc) {
+                                          const bf16x8 &RX, const bf16x8 &RY, uint8_t *lw_wr,
+                                          const uint8_t *lw_rd, Acc<KS> &acc) {
   constexpr int SH = NH > 0 ? NH : 1;
+  using L = TileLds<KS>;
+  // the tile's V rows go to the wave's LDS copy (row 16 tb + n, columns 32 ks + 8 q ..), to be
+  // read back transposed for the weighted sum
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      *reinterpret_cast<u32x4 *>(lw_wr + tb * 16 * L::kRow + 64 * ks) = cur.v[tb][ks];
   f32x4 S[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -227,19 +258,14 @@ __device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, i
   }
   const bf16x8 PX = as_bf16(NH > 0 ? pl : ph);
   const bf16x8 PY = as_bf16(pl);
+  // V^T in A-operand form, dims 16 nb + n, K order (q, e) -> position 16 (e / 4) + 4 q + e % 4:
+  // the first read gives positions 4 q .. + 3 of block 0, the second the same of block 1.
 #pragma unroll
   for (int nb = 0; nb < 2 * KS; ++nb) {
-    const int ks = nb >> 1;
-    const int half = nb & 1;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 T0 = mfma(as_bf16(cur.v[0][ks]), SEL[half], z);
-    const f32x4 T1 = mfma(as_bf16(cur.v[1][ks]), SEL[half], z);
-    u32x4 w;
-    w[0] = pack2(T0[0], T0[1]);
-    w[1] = pack2(T0[2], T0[3]);
-    w[2] = pack2(T1[0], T1[1]);
-    w[3] = pack2(T1[2], T1[3]);
-    const bf16x8 VT = as_bf16(w);
+    const i16x4 v0 = read_tr(lw_rd + 32 * nb);
+    const i16x4 v1 = read_tr(lw_rd + 16 * L::kRow + 32 * nb);
+    const bf16x8 VT = __builtin_bit_cast(
+        bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
     acc.O[nb] = mfma(VT, PX, acc.O[nb]);
     if (NH == 0) acc.O[nb] = mfma(VT, PY, acc.O[nb]);
   }
@@ -252,12 +278,20 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int q = lane >> 4;
-  // The sequence index varies fastest along the grid: work-groups are dealt to the 8 XCDs in
-  // turn, so every XCD receives an even share of each split column (early split columns are
-  // almost always non-empty, late ones often empty).
-  const int b = blockIdx.x;
-  const int s = blockIdx.y;
-  const int g = blockIdx.z * (blockDim.x >> 6) + wave;
+  // Work-groups are dealt to the 8 XCDs in turn (XCD = id % 8). The nz work-groups that share
+  // one (sequence, split) item take ids 8 apart, so they run on the same XCD at about the same
+  // time and the shared positional key is fetched from HBM once. Along the items the sequence
+  // index varies fastest, so every XCD receives an even share of each split column (early split
+  // columns are almost always non-empty, late ones often empty).
+  const int wpg = blockDim.x >> 6;
+  const int nz = a.G / wpg;
+  const int id = blockIdx.x;
+  const int r8 = id >> 3;
+  const int item = (r8 / nz) * 8 + (id & 7);
+  if (item >= a.B * a.num_splits) return;
+  const int b = item % a.B;
+  const int s = item / a.B;
+  const int g = (r8 % nz) * wpg + wave;
   const int nhg = a.H / a.G;
   const int h0 = g * nhg;
   // the query column of this lane: head c (hi or, with merged columns, lo part)
@@ -284,7 +318,7 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
 
   if (c0 < c1) {
     // ---- query operands (B layout: column n, K group q) ----
-    bf16x8 QX[KS], QY[KS], RX, RY, SEL[2];
+    bf16x8 QX[KS], QY[KS], RX, RY;
     const float *qp =
         a.q_abs + (static_cast<int64_t>(b) * a.H + h0 + (col_ok ? c : 0)) * row_len;
 #pragma unroll
@@ -313,18 +347,12 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
       RX = as_bf16(use_lo ? lo : hi);
       RY = as_bf16(lo);
     }
-    // selection matrices E_half[k][j] = 1 if k == 16 half + j (B layout)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned lo = (8 * q + 2 * i == 16 * half + n) ? 0x3f80u : 0u;
-        const unsigned hi = (8 * q + 2 * i + 1 == 16 * half + n) ? 0x3f80u : 0u;
-        w[i] = lo | (hi << 16);
-      }
-      SEL[half] = as_bf16(w);
-    }
+    // this wave's LDS tile: lane (n, q) writes row n, columns 8 q ..; lane L reads row L / 4,
+    // columns 4 (L % 4) .. (see read_tr)
+    using L = TileLds<KS>;
+    __shared__ __align__(16) uint8_t lds[kGroupWaves * L::kWave];
+    uint8_t *lw_wr = lds + wave * L::kWave + n * L::kRow + 16 * q;
+    const uint8_t *lw_rd = lds + wave * L::kWave + (lane >> 2) * L::kRow + 8 * (lane & 3);
 
     // lane-invariant parts of the element offsets (positional K groups beyond d_r read the
     // row's last 8 elements; they meet zeros in the query operand)
@@ -345,10 +373,10 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
       const int t1 = t0 + kTile;
       load_tile<KS>(a, PB, t1, c1, n, vlane, klane, Bt, bad);
       PB = load_pages(bt, lb, t1 + 2 * kTile, c1, lane);
-      tile_step<KS, NH>(A, t0, c1, n, q, QX, QY, RX, RY, SEL, acc);
+      tile_step<KS, NH>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
       load_tile<KS>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad);
       PA = load_pages(bt, lb, t1 + 3 * kTile, c1, lane);
-      if (t1 < c1) tile_step<KS, NH>(Bt, t1, c1, n, q, QX, QY, RX, RY, SEL, acc);
+      if (t1 < c1) tile_step<KS, NH>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
     }
   }
 
@@ -417,14 +445,15 @@ hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_
 namespace gva {
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
-  // waves per work-group: the largest divisor of G that is at most 8
+  // waves per work-group: the largest divisor of G that is at most kGroupWaves
   int wpg = 1;
-  for (int w = 8; w >= 1; --w)
+  for (int w = kGroupWaves; w >= 1; --w)
     if (a.G % w == 0) {
       wpg = w;
       break;
     }
-  const dim3 grid(a.B, a.num_splits, a.G / wpg);
+  const int64_t items = static_cast<int64_t>(a.B) * a.num_splits;
+  const dim3 grid(static_cast<unsigned>(((items + 7) / 8) * 8 * (a.G / wpg)));
   const dim3 block(64 * wpg);
   switch (a.H / a.G) {
     case 1: return launch_nh<1>(a, grid, block, stream);
