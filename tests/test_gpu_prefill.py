@@ -42,6 +42,7 @@ def _chunk_inputs(w, starts, C):
     dict(H=8, G=2, d_h=64, d_n=64, d_r=16),        # 4 heads per group
     dict(H=32, G=8, d_h=128, d_n=128, d_r=24),     # the long-context shape
     dict(H=6, G=3, d_h=96, d_n=96, d_r=8),         # 2 heads per group, d_h = 3 x 32
+    dict(H=4, G=2, d_h=256, d_n=256, d_r=32),      # one row tile per wave
 ])
 @pytest.mark.parametrize("starts,C", [((100, 37, 0), 70), ((0, 5, 300), 1), ((64, 0, 16), 257)])
 def test_prefill_small_against_oracle(shape, starts, C):

@@ -271,8 +271,16 @@ __device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, i
   }
 }
 
+// Waves per SIMD the register allocation must allow: three where the kernel fits in 168
+// registers without spilling (d_h <= 64, or d_h = 128 with merged hi/lo columns), else two.
 template <int KS, int NH>
-__global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
+constexpr int min_waves_per_simd() {
+  return (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
+}
+
+template <int KS, int NH>
+__global__ __launch_bounds__(64 * kGroupWaves, (min_waves_per_simd<KS, NH>())) void
+k_decode_mfma(gva::DecodeArgs a) {
   constexpr int SH = NH > 0 ? NH : 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -362,6 +370,8 @@ __global__ __launch_bounds__(512) void k_decode_mfma(gva::DecodeArgs a) {
     // Two tile buffers in ping-pong (A, Bt): while one tile is computed the other one's loads
     // are in flight, and no register copies are needed. Issue order per half-step: V loads of
     // the next tile, then the page entries two tiles ahead, then the math of the current tile.
+    // (A third buffer, tried for grids of at most two work-groups per CU, gained nothing: the
+    // loop runs near the streaming rate already.)
     const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
     const int lb = a.log2_bs;
     Tile<KS> A, Bt;

@@ -10,16 +10,17 @@
 // with rows = (query, head) pairs of one value group.
 //
 // Work-group: 8 waves, 256 rows of one (sequence, group), rows ordered (query, head) with the
-// head fastest; each wave owns 2 row tiles of 16. Keys are walked in tiles of 32 positions
-// staged once per work-group in LDS (double-buffered, one barrier per tile) in two layouts:
-//   * natural rows [v (d_h) | kr (d_r, zero-padded to 32)], the A operand of the scores
-//     S^T[key][row] = sum_k K[key][k] Q[row][k] (B = the absorbed query, bf16), and
-//   * V^T [d_h][32 keys], the A operand of O^T[dim][row] += sum_key V^T[dim][key] P^T[key][row].
-// The transpose is done by the matrix core: V x E with a 0/1 selection matrix E, exact. Each
-// lane then holds, per row tile, row n = lane % 16 and keys 16 tb + 4 q + r of each 16-key
-// block (q = lane / 16), which is the K order (q, e) -> 16 (e / 4) + 4 q + e % 4 in which V^T is
-// read from LDS, so P feeds the second product from the lane's own registers. Operands are bf16
-// with float32 accumulation; the online softmax runs in float32 in the base-2 domain.
+// head fastest; each wave owns 2 row tiles of 16. Keys are walked in tiles of 32 positions,
+// loaded two tiles ahead into registers and staged once per work-group in LDS as natural rows
+// [v (d_h) | kr (d_r, zero-padded to 32)] (double-buffered, one barrier per tile). They serve
+//   * the scores S^T[key][row] = sum_k K[key][k] Q[row][k]: A = the natural rows, B = the
+//     absorbed query as a bf16 hi + lo pair (two products), and
+//   * the weighted sum O^T[dim][row] += sum_key V^T[dim][key] P^T[key][row]: A = V^T, read
+//     from the same rows with the transposing LDS load (ds_read_b64_tr_b16), B = P in bf16.
+// Each lane holds, per row tile, row n = lane % 16 and keys 16 tb + 4 q + r of each 16-key
+// block (q = lane / 16), which is the K order (q, e) -> 16 (e / 4) + 4 q + e % 4 in which the
+// transposing load delivers V^T, so P feeds the second product from the lane's own registers.
+// Accumulation and the online softmax (base-2 domain) are float32.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -34,10 +35,15 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 8;
-constexpr int kRowTiles = 2;                       // row tiles of 16 per wave
-constexpr int kRows = kWaves * kRowTiles * 16;     // rows per work-group
+// Row tiles of 16 per wave: two up to d_h = 128, one above (register budget).
+template <int KS>
+constexpr int row_tiles() { return KS <= 4 ? 2 : 1; }
+template <int KS>
+constexpr int rows_per_group() { return kWaves * row_tiles<KS>() * 16; }
 constexpr int kKeyTile = 32;
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -47,6 +53,15 @@ __device__ __forceinline__ bf16x8 as_bf16(const u32x4 &u) { return __builtin_bit
 __device__ __forceinline__ unsigned pack2(float x, float y) {
   const f32x2 v = {x, y};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));  // RNE, x in low half
+}
+__device__ __forceinline__ float low_bf16(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float high_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ds_read_b64_tr_b16 (checked on the hardware): in each group of 16 lanes, lanes 4 e + k
+// (k = 0..3) address 4 consecutive 16-bit elements each, together one row of 16; lane i of the
+// group receives element e of its result from row e, column i.
+__device__ __forceinline__ i16x4 read_tr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
 // ---- appending the chunk -----------------------------------------------------------------
@@ -104,15 +119,12 @@ __global__ __launch_bounds__(256) void k_append_chunk(gva::DecodeArgs a, int32_t
 
 // ---- attention -----------------------------------------------------------------------------
 
-// LDS tile: natural rows of (KS + 1) * 32 elements (+8 padding against bank conflicts) and the
-// transposed values, d_h rows of 32 keys (+8 padding).
+// LDS tile: 32 natural rows of (KS + 1) * 32 elements, each padded by 16 elements so that the
+// four rows one transposing read touches in a group of 16 lanes fall on different banks.
 template <int KS>
 struct TileLds {
-  static constexpr int kNatStride = (KS + 1) * 32 + 8;
-  static constexpr int kVtStride = kKeyTile + 8;
-  static constexpr int kNatElems = kKeyTile * kNatStride;
-  static constexpr int kVtElems = KS * 32 * kVtStride;
-  static constexpr int kElems = kNatElems + kVtElems;
+  static constexpr int kNatStride = (KS + 1) * 32 + 16;
+  static constexpr int kElems = kKeyTile * kNatStride;
 };
 
 // A unit is 16 keys x 32 elements of the natural rows (k-step ks of key block kb); units
@@ -154,11 +166,9 @@ __device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const int32
 }
 
 template <int KS>
-__device__ __forceinline__ void stage_store(uint16_t *lds, int wave, int n, int q,
-                                            const bf16x8 (&SEL)[2], const Stage<KS> &st) {
+__device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int q,
+                                            const Stage<KS> &st) {
   using L = TileLds<KS>;
-  uint16_t *nat = lds;
-  uint16_t *vt = lds + L::kNatElems;
 #pragma unroll
   for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
     const int unit = wave + kWaves * i;
@@ -166,24 +176,14 @@ __device__ __forceinline__ void stage_store(uint16_t *lds, int wave, int n, int 
     const int kb = unit & 1;
     const int ks = unit >> 1;
     *reinterpret_cast<u32x4 *>(nat + (16 * kb + n) * L::kNatStride + 32 * ks + 8 * q) = st.u[i];
-    if (ks < KS) {
-      // V x E_half: lane (n, q) receives keys 4 q + r of dim 32 ks + 16 half + n, exactly
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 T = mfma(as_bf16(st.u[i]), SEL[half], z);
-        u32x2 w;
-        w[0] = pack2(T[0], T[1]);
-        w[1] = pack2(T[2], T[3]);
-        *reinterpret_cast<u32x2 *>(vt + (32 * ks + 16 * half + n) * L::kVtStride + 16 * kb + 4 * q) = w;
-      }
-    }
   }
 }
 
 template <int KS>
 __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   using L = TileLds<KS>;
+  constexpr int kRowTiles = row_tiles<KS>();
+  constexpr int kRows = rows_per_group<KS>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][L::kElems];
   const gva::DecodeArgs &a = p.kv;
   const int lane = threadIdx.x & 63;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   // rows of this wave: tile rt covers rows row0 + 16 (2 wave + rt) + 0..15
   int qpos[kRowTiles];            // position of this lane's row (as the B column n)
   bool rvalid[kRowTiles];
-  bf16x8 QB[kRowTiles][KS + 1];
+  bf16x8 QH[kRowTiles][KS + 1], QL[kRowTiles][KS + 1];   // query hi and lo parts (B operand)
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
     const int r = row0 + 16 * (kRowTiles * wave + rt) + n;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     const float *qp = p.q_abs + ((static_cast<int64_t>(b) * C + qi) * a.H + h) * row_len;
 #pragma unroll
     for (int ks = 0; ks <= KS; ++ks) {
-      u32x4 w;
+      u32x4 hi, lo;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x0, x1;
@@ -246,22 +246,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
           x0 = e < a.d_r ? qp[a.d_h + e] : 0.0f;
           x1 = e + 1 < a.d_r ? qp[a.d_h + e + 1] : 0.0f;
         }
-        w[i] = pack2(x0 * a.qscale, x1 * a.qscale);
+        x0 *= a.qscale;
+        x1 *= a.qscale;
+        const unsigned w = pack2(x0, x1);
+        hi[i] = w;
+        lo[i] = pack2(x0 - low_bf16(w), x1 - high_bf16(w));
       }
-      QB[rt][ks] = as_bf16(w);
+      QH[rt][ks] = as_bf16(hi);
+      QL[rt][ks] = as_bf16(lo);
     }
-  }
-  bf16x8 SEL[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned lo = (8 * q + 2 * i == 16 * half + n) ? 0x3f80u : 0u;
-      const unsigned hi = (8 * q + 2 * i + 1 == 16 * half + n) ? 0x3f80u : 0u;
-      w[i] = lo | (hi << 16);
-    }
-    SEL[half] = as_bf16(w);
   }
 
   f32x4 O[kRowTiles][2 * KS];
@@ -279,88 +272,102 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   const int kend = seq_bad ? 0 : P0 + last_row / nhg + 1;
   const int first_q = P0 + row0 / nhg;                 // every key below it is seen by all rows
   const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  // transposing-read address of this lane: row lane / 4, columns 4 (lane % 4) ..
+  const int tr_off = (lane >> 2) * L::kNatStride + 4 * (lane & 3);
 
-  if (kend > 0) {
-    Stage<KS> st;
-    stage_load<KS>(a, bt, g, 0, kend, wave, n, q, st);
-    stage_store<KS>(lds[0], wave, n, q, SEL, st);
-    __syncthreads();
-    int buf = 0;
-    for (int kt0 = 0; kt0 < kend; kt0 += kKeyTile) {
-      const bool more = kt0 + kKeyTile < kend;         // uniform per work-group
-      if (more) stage_load<KS>(a, bt, g, kt0 + kKeyTile, kend, wave, n, q, st);
-      const uint16_t *nat = lds[buf];
-      const uint16_t *vt = lds[buf] + L::kNatElems;
-      // ---- scores S^T[key][row] for both key blocks and both row tiles ----
-      f32x4 S[kRowTiles][2];
+  // One key tile: scores, mask, online softmax, weighted sum, on the LDS rows in nat.
+  auto tile = [&](const uint16_t *nat, int kt0) {
+    f32x4 S[kRowTiles][2];
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt)
+    for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) S[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < 2; ++tb) S[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks <= KS; ++ks) {
+    for (int ks = 0; ks <= KS; ++ks) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const u32x4 ka = *reinterpret_cast<const u32x4 *>(nat + (16 * tb + n) * L::kNatStride + 32 * ks + 8 * q);
+      for (int tb = 0; tb < 2; ++tb) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(nat + (16 * tb + n) * L::kNatStride +
+                                                          32 * ks + 8 * q);
 #pragma unroll
-          for (int rt = 0; rt < kRowTiles; ++rt) S[rt][tb] = mfma(as_bf16(ka), QB[rt][ks], S[rt][tb]);
+        for (int rt = 0; rt < kRowTiles; ++rt) {
+          S[rt][tb] = mfma(as_bf16(ka), QH[rt][ks], S[rt][tb]);
+          S[rt][tb] = mfma(as_bf16(ka), QL[rt][ks], S[rt][tb]);
         }
       }
-      // ---- causal mask (only tiles that reach past the first query), online softmax ----
-      const bool need_mask = kt0 + kKeyTile - 1 > first_q;
-      u32x4 PB[kRowTiles];
+    }
+    // causal mask (only tiles that reach past the first query), online softmax
+    const bool need_mask = kt0 + kKeyTile - 1 > first_q;
+    u32x4 PB[kRowTiles];
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        if (need_mask) {
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (kt0 + 16 * tb + 4 * q + r > qpos[rt]) S[rt][tb][r] = -INFINITY;
-        }
-        float mt = fmaxf(fmaxf(fmaxf(S[rt][0][0], S[rt][0][1]), fmaxf(S[rt][0][2], S[rt][0][3])),
-                         fmaxf(fmaxf(S[rt][1][0], S[rt][1][1]), fmaxf(S[rt][1][2], S[rt][1][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(m[rt], mt);
-        // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
-        const float mref = mn == -INFINITY ? 0.0f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mref);
-        float pv[8];
-        float ps = 0.0f;
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      if (need_mask) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pv[4 * tb + r] = __builtin_amdgcn_exp2f(S[rt][tb][r] - mref);
-            ps += pv[4 * tb + r];
-          }
-        lsum[rt] = lsum[rt] * alpha + ps;
-        m[rt] = mn;
-        if (__any(alpha != 1.0f)) {
+          for (int r = 0; r < 4; ++r)
+            if (kt0 + 16 * tb + 4 * q + r > qpos[rt]) S[rt][tb][r] = -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(fmaxf(S[rt][0][0], S[rt][0][1]), fmaxf(S[rt][0][2], S[rt][0][3])),
+                       fmaxf(fmaxf(S[rt][1][0], S[rt][1][1]), fmaxf(S[rt][1][2], S[rt][1][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m[rt], mt);
+      // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
+      const float mref = mn == -INFINITY ? 0.0f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m[rt] - mref);
+      float pv[8];
+      float ps = 0.0f;
 #pragma unroll
-          for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha;
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[4 * tb + r] = __builtin_amdgcn_exp2f(S[rt][tb][r] - mref);
+          ps += pv[4 * tb + r];
         }
+      lsum[rt] = lsum[rt] * alpha + ps;
+      m[rt] = mn;
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) PB[rt][i] = pack2(pv[2 * i], pv[2 * i + 1]);
+        for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha;
       }
-      // ---- O^T[dim][row] += V^T[dim][key] P^T[key][row] ----
 #pragma unroll
-      for (int nb = 0; nb < 2 * KS; ++nb) {
-        const uint16_t *src = vt + (16 * nb + n) * L::kVtStride + 4 * q;
-        u32x4 w;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 16);
-        w[0] = lo[0];
-        w[1] = lo[1];
-        w[2] = hi[0];
-        w[3] = hi[1];
+      for (int i = 0; i < 4; ++i) PB[rt][i] = pack2(pv[2 * i], pv[2 * i + 1]);
+    }
+    // O^T[dim][row] += V^T[dim][key] P^T[key][row]; V^T of dims 16 nb .. read transposed:
+    // the first read gives keys 4 q .. + 3 of block 0, the second the same of block 1
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) O[rt][nb] = mfma(as_bf16(w), as_bf16(PB[rt]), O[rt][nb]);
-      }
-      if (more) stage_store<KS>(lds[buf ^ 1], wave, n, q, SEL, st);
+    for (int nb = 0; nb < 2 * KS; ++nb) {
+      const i16x4 v0 = read_tr(nat + tr_off + 16 * nb);
+      const i16x4 v1 = read_tr(nat + tr_off + 16 * L::kNatStride + 16 * nb);
+      const bf16x8 VT = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) O[rt][nb] = mfma(VT, as_bf16(PB[rt]), O[rt][nb]);
+    }
+  };
+
+  if (kend > 0) {
+    // Tiles are loaded two ahead: while tile i is computed, tile i + 1 waits in registers (to
+    // be stored into the other LDS buffer) and tile i + 2 is in flight. The two register stages
+    // alternate roles, so the loop is unrolled by two.
+    Stage<KS> s0, s1;
+    stage_load<KS>(a, bt, g, 0, kend, wave, n, q, s0);
+    if (kKeyTile < kend) stage_load<KS>(a, bt, g, kKeyTile, kend, wave, n, q, s1);
+    stage_store<KS>(lds[0], wave, n, q, s0);
+    __syncthreads();
+    for (int kt0 = 0; kt0 < kend; kt0 += 2 * kKeyTile) {
+      // tile kt0 in lds[0]; tile kt0 + 32 in s1; s0 free
+      if (kt0 + 2 * kKeyTile < kend) stage_load<KS>(a, bt, g, kt0 + 2 * kKeyTile, kend, wave, n, q, s0);
+      tile(lds[0], kt0);
+      if (kt0 + kKeyTile >= kend) break;               // uniform per work-group
+      stage_store<KS>(lds[1], wave, n, q, s1);
       __syncthreads();
-      buf ^= 1;
+      // tile kt0 + 32 in lds[1]; tile kt0 + 64 in s0; s1 free
+      if (kt0 + 3 * kKeyTile < kend) stage_load<KS>(a, bt, g, kt0 + 3 * kKeyTile, kend, wave, n, q, s1);
+      tile(lds[1], kt0 + kKeyTile);
+      if (kt0 + 2 * kKeyTile >= kend) break;
+      stage_store<KS>(lds[0], wave, n, q, s0);
+      __syncthreads();
     }
   }
 
@@ -400,16 +407,18 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrows = C * (a.H / a.G);
-  const dim3 grid(((nrows + kRows - 1) / kRows) * a.G * a.B);
+  const int64_t pairs = static_cast<int64_t>(a.G) * a.B;
+  auto grid = [&](int rows) { return dim3(static_cast<unsigned>((nrows + rows - 1) / rows * pairs)); };
+  const dim3 block(64 * kWaves);
   switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL(k_prefill<1>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(k_prefill<2>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(k_prefill<3>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(k_prefill<4>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 5: hipLaunchKernelGGL(k_prefill<5>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 6: hipLaunchKernelGGL(k_prefill<6>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 7: hipLaunchKernelGGL(k_prefill<7>, grid, dim3(64 * kWaves), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(k_prefill<8>, grid, dim3(64 * kWaves), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(k_prefill<1>, grid(rows_per_group<1>()), block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(k_prefill<2>, grid(rows_per_group<2>()), block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(k_prefill<3>, grid(rows_per_group<3>()), block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(k_prefill<4>, grid(rows_per_group<4>()), block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL(k_prefill<5>, grid(rows_per_group<5>()), block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL(k_prefill<6>, grid(rows_per_group<6>()), block, 0, stream, p); break;
+    case 7: hipLaunchKernelGGL(k_prefill<7>, grid(rows_per_group<7>()), block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(k_prefill<8>, grid(rows_per_group<8>()), block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
