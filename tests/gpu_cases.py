@@ -151,5 +151,6 @@ def lse_ok(got, ref, tol):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     both_inf = np.isneginf(got) & np.isneginf(ref)
-    d = np.abs(np.where(both_inf, 0.0, got - ref))
+    with np.errstate(invalid="ignore"):
+        d = np.abs(np.where(both_inf, 0.0, got - ref))
     return bool(np.all(d <= tol)), float(np.max(d)) if d.size else 0.0

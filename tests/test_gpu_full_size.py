@@ -1,0 +1,127 @@
+"""GPU parity at the full sizes the benchmark runs, in its launch configuration (automatic split
+count), on outputs the oracle computes one sequence at a time.
+
+* One sequence of T = 131072 cached positions (H=32, G=8, d_h=d_n=128, d_r=16 and 24), decoded
+  with 64, 128 and 256 splits and the automatic count: every head against the oracle.
+* The ragged paged batch (B=256, lengths U[512, 32768], d_r=24, 16-token blocks in a seeded
+  permutation of the pool): append one token per sequence, absorb the queries, decode over
+  len_b + 1 positions. Six sampled sequences (the longest, the shortest and four drawn at random)
+  carry the seeded synthetic tokens and are checked against the oracle; the other sequences are
+  filled with device random values, which only they read.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gva_oracle as O
+from value_only_kv_amd import binding as gb
+from value_only_kv_amd import synth
+from tests.gpu_cases import Case, absorbed_queries, check_output, lse_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _device_absorb(cdims, w, q_nope, q_rope, q_pos, M, tab, max_pos):
+    n = q_nope.shape[0]
+    out = torch.empty((n, w.H, w.d_h + w.d_r), device="cuda")
+    gb.gva_absorb_query(cdims, torch.from_numpy(q_nope).cuda(), torch.from_numpy(q_rope).cuda(),
+                        torch.from_numpy(np.asarray(q_pos, np.int32)).cuda(),
+                        torch.from_numpy(M).cuda(), tab, max_pos, out)
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["C3", "C3r24"])
+def test_long_context_full_size(name):
+    w = synth.workload(name)
+    c = Case(w, sentinel=False)
+    c.append_prefix()
+    T = int(c.lens[0])
+    q_ref, (M, q_nope, q_rope) = absorbed_queries(w, 1, [T], c.tab_ora)
+    q_dev = _device_absorb(c.cdims, w, q_nope, q_rope, [T], M, c.tab_lib, c.max_pos)
+    ref, ref_lse = c.oracle_decode([T], q_ref)
+    for S in (64, 128, 256, 0):
+        out, lse = c.decode([T], q_dev, num_splits=S)
+        check_output(out, ref, "bf16", f"{name} T={T} S={S}")
+        ok, e = lse_ok(lse, ref_lse, 1e-3)
+        assert ok, (S, e)
+    assert c.err_flag() == 0
+
+
+def test_ragged_batch_full_size_sampled_sequences():
+    w = synth.workload("C4")
+    lens = synth.lengths(w)
+    lay = synth.layout(w, lens)
+    B, G, d_h, d_r, H = w.B, w.G, w.d_h, w.d_r, w.H
+    cdims = gb.GvaDims(H, G, d_h, w.d_n, d_r)
+    dims = O.Dims(H, G, d_h, w.d_n, d_r)
+    max_pos = int(synth.capacity(w, lens).max()) + 1
+    tab_lib = torch.from_numpy(gb.gva_rope_table_fill(max_pos, d_r, w.base)).cuda()
+    cache = gb.GvaCache.allocate(cdims, w.dtype, lay.num_blocks, lay.block_size,
+                                 torch.from_numpy(lay.block_table).cuda(), tab_lib,
+                                 (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st))
+    rng = np.random.default_rng(17)
+    sampled = sorted({int(np.argmax(lens)), int(np.argmin(lens)),
+                      *(int(x) for x in rng.choice(B, 4, replace=False))})
+    print(f"sampled sequences {sampled}, lengths {[int(lens[b]) for b in sampled]}", flush=True)
+
+    # filler: positions 0 .. len_b - 1 of the other sequences, device random values
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    others = [b for b in range(B) if b not in sampled]
+    seqs = np.repeat(np.asarray(others, np.int32), lens[others])
+    poss = np.concatenate([np.arange(lens[b], dtype=np.int32) for b in others])
+    for o in range(0, seqs.size, 1 << 16):
+        n = min(1 << 16, seqs.size - o)
+        gb.gva_cache_append(cdims, cache, B, torch.from_numpy(seqs[o:o + n]).cuda(),
+                            torch.from_numpy(poss[o:o + n]).cuda(),
+                            torch.randn((n, G, d_h), generator=gen, device="cuda"),
+                            torch.randn((n, d_r), generator=gen, device="cuda"))
+    # sampled sequences: their seeded tokens; position len_b is appended by the step below
+    toks = {}
+    for b in sampled:
+        n = int(lens[b])
+        v, kr = synth.sequence_tokens(w, b, n + 1)
+        toks[b] = (v, kr)
+        gb.gva_cache_append(cdims, cache, B, torch.full((n,), b, dtype=torch.int32).cuda(),
+                            torch.arange(n, dtype=torch.int32).cuda(),
+                            torch.from_numpy(v[:n]).cuda(), torch.from_numpy(kr[:n]).cuda())
+    # the step: append one token per sequence at position len_b, absorb, decode over len_b + 1
+    v_step = torch.randn((B, G, d_h), generator=gen, device="cuda")
+    k_step = torch.randn((B, d_r), generator=gen, device="cuda")
+    for b in sampled:
+        v_step[b] = torch.from_numpy(toks[b][0][-1]).cuda()
+        k_step[b] = torch.from_numpy(toks[b][1][-1]).cuda()
+    pos = lens.astype(np.int32)
+    gb.gva_cache_append(cdims, cache, B, torch.arange(B, dtype=torch.int32).cuda(),
+                        torch.from_numpy(pos).cuda(), v_step, k_step)
+    M = synth.weights(w)
+    q_nope, q_rope = synth.queries(w, B)
+    q_dev = _device_absorb(cdims, w, q_nope, q_rope, pos, M, tab_lib, max_pos)
+    seq_len = torch.from_numpy(pos + 1).cuda()
+    max_len = int(pos.max()) + 1
+    out = torch.full((B, H, d_h), float("nan"), device="cuda")
+    lse = torch.full((B, H), float("nan"), device="cuda")
+    wsb = gb.gva_decode_workspace_bytes(cdims, B, max_len, 0)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    gb.gva_decode(cdims, cache, B, seq_len, max_len, torch.from_numpy(q_dev).cuda(), w.scale,
+                  out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out))
+
+    tab_ora = O.rope_rows(np.arange(max_pos), d_r, w.base)
+    for b in sampled:
+        n = int(lens[b]) + 1
+        v, kr = toks[b]
+        # the oracle's own contiguous pool for this sequence
+        pool = O.Pool.empty("bf16", n * G * d_h, n * d_r, (n * G * d_h, G * d_h, d_h, n * d_r, d_r),
+                            1, 1 << int(np.ceil(np.log2(n))), np.zeros((1, 1)))
+        O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr, tab_ora)
+        V, krc = O.gather(pool, dims, 0, n)
+        qt, r = O.absorb(q_nope[b:b + 1], q_rope[b:b + 1], pos[b:b + 1], M, tab_ora)
+        q_ref = O.q_abs_of(qt, r)[0]
+        ref, ref_lse = O.decode_sequence(V, krc, dims, q_ref, w.scale)
+        check_output(out[b], ref, "bf16", f"ragged batch seq {b} len {n}")
+        ok, e = lse_ok(lse[b], ref_lse, 1e-3)
+        assert ok, (b, e)
