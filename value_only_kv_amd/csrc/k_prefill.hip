@@ -295,26 +295,37 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
         }
       }
     }
-    // causal mask (only tiles that reach past the first query), online softmax
+    // causal mask (only tiles that reach past the first query), online softmax; the two row
+    // tiles go through each stage together so their latencies overlap
     const bool need_mask = kt0 + kKeyTile - 1 > first_q;
-    u32x4 PB[kRowTiles];
+    if (need_mask) {
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      if (need_mask) {
+      for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (kt0 + 16 * tb + 4 * q + r > qpos[rt]) S[rt][tb][r] = -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(fmaxf(S[rt][0][0], S[rt][0][1]), fmaxf(S[rt][0][2], S[rt][0][3])),
-                       fmaxf(fmaxf(S[rt][1][0], S[rt][1][1]), fmaxf(S[rt][1][2], S[rt][1][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m[rt], mt);
+    }
+    float mt[kRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt)
+      mt[rt] = fmaxf(fmaxf(fmaxf(S[rt][0][0], S[rt][0][1]), fmaxf(S[rt][0][2], S[rt][0][3])),
+                     fmaxf(fmaxf(S[rt][1][0], S[rt][1][1]), fmaxf(S[rt][1][2], S[rt][1][3])));
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) mt[rt] = gvad::xor16_max(mt[rt]);
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) mt[rt] = gvad::xor32_max(mt[rt]);
+    u32x4 PB[kRowTiles];
+    float alpha[kRowTiles];
+    bool rescale = false;
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      const float mn = fmaxf(m[rt], mt[rt]);
       // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
       const float mref = mn == -INFINITY ? 0.0f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m[rt] - mref);
+      alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mref);
+      rescale |= alpha[rt] != 1.0f;
       float pv[8];
       float ps = 0.0f;
 #pragma unroll
@@ -324,14 +335,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
           pv[4 * tb + r] = __builtin_amdgcn_exp2f(S[rt][tb][r] - mref);
           ps += pv[4 * tb + r];
         }
-      lsum[rt] = lsum[rt] * alpha + ps;
+      lsum[rt] = lsum[rt] * alpha[rt] + ps;
       m[rt] = mn;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha;
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) PB[rt][i] = pack2(pv[2 * i], pv[2 * i + 1]);
+    }
+    if (__any(rescale)) {
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha[rt];
     }
     // O^T[dim][row] += V^T[dim][key] P^T[key][row]; V^T of dims 16 nb .. read transposed:
     // the first read gives keys 4 q .. + 3 of block 0, the second the same of block 1
@@ -374,8 +387,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   // ---- epilogue: lane (n, q) holds row n of each tile, dims 16 nb + 4 q + r ----
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
-    float lt = lsum[rt] + __shfl_xor(lsum[rt], 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = gvad::xor32_sum(gvad::xor16_sum(lsum[rt]));
     if (!rvalid[rt]) continue;
     const int r = row0 + 16 * (kRowTiles * wave + rt) + n;
     const int qi = r / nhg;

@@ -29,7 +29,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 # Sources whose change invalidates stored decode counters.
 DECODE_SOURCES = ("csrc/k_decode_mfma.hip", "csrc/k_decode_generic.hip", "csrc/gva_api.hip",
-                  "csrc/gva_host.cpp", "csrc/gva_internal.h")
+                  "csrc/gva_host.cpp", "csrc/gva_internal.h", "csrc/gva_device.h")
 
 
 def sources_sha256(paths=DECODE_SOURCES) -> str:
