@@ -119,6 +119,9 @@ def main():
     out = torch.empty((B, H, w.d_h), device="cuda")
     lse = torch.empty((B, H), device="cuda")
     S = gb.gva_decode_num_splits(dc.dims, B, max_len, args.splits)
+    R = gb.gva_decode_num_ranges(dc.dims, B, max_len) if args.splits == 0 and args.kernel != 1 else 0
+    plan = (f"balanced: {R} equal tile ranges over all sequences" if R > 0
+            else f"split: {S} chunks per sequence")
     wsb = gb.gva_decode_workspace_bytes(dc.dims, B, max_len, args.splits)
     ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -145,7 +148,7 @@ def main():
     tok_bytes = (w.G * w.d_h + w.d_r) * elem
     read_bytes = int((lens + 1).sum()) * tok_bytes                 # algorithmic, per step
     value = read_bytes / t_step / 1e9
-    log(f"C4 step: {t_step * 1e3:.3f} ms, {value:.1f} GB/s, splits={S}")
+    log(f"C4 step: {t_step * 1e3:.3f} ms, {value:.1f} GB/s, {plan}")
 
     # decode launches alone, timed with HIP events on the launch stream
     n_ev = max(args.steps, 100)
@@ -252,7 +255,7 @@ def main():
                                "append 1 token then decode over len_b+1; H=32, G=8, d_h=d_n=128, "
                                "d_r=24; bf16 cache in 16-token blocks",
                    "global_batch": B, "cached_tokens": int((lens + 1).sum()),
-                   "num_splits": S, "parallelism": "single GPU"},
+                   "decode_plan": plan, "parallelism": "single GPU"},
         "seq_steps_per_s": round(B / t_step, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "decode_only": {"ms": round(t_dec * 1e3, 4), "GB_s": round(dec_gbs, 1),

@@ -154,7 +154,11 @@ gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_no
  *   s_j = scale * (q~_h . V(j, g(h), :) + r_h . kr(j, :))   with [q~_h ; r_h] = q_abs[b][h]
  *   out[b][h][:] = sum_j softmax(s)_j V(j, g(h), :),   lse[b][h] = ln sum_j exp(s_j)
  * The positions are split into num_splits contiguous chunks processed in parallel and merged
- * through their log-sum-exp. seq_len[b] == 0 gives out = 0 and lse = -inf.
+ * through their log-sum-exp. With num_splits == 0 (automatic) the matrix-core kernel instead
+ * cuts the 32-position tiles of all sequences, taken in sequence order, into equal ranges (see
+ * gva_decode_num_ranges), so every work-group gets the same amount of cache to read whatever
+ * the lengths; the chunks of one sequence are merged the same way.
+ * seq_len[b] == 0 gives out = 0 and lse = -inf.
  *   seq_len: device int32 [B]. max_len: host upper bound on every seq_len[b] (it sizes the
  *   split plan; a larger length raises GVA_DEVERR_LENGTH and makes that row NaN).
  *   q_abs: device float32 [B][H][d_h + d_r]. out: device float32 [B][H][d_h].
@@ -167,9 +171,13 @@ gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_no
  *   workspace: device, 256-byte aligned, at least gva_decode_workspace_bytes(...) bytes. */
 size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
                                   int32_t num_splits);
-/* The split count gva_decode will use for these arguments (0 on bad arguments). */
+/* The split count gva_decode will use for these arguments with per-sequence chunks (an
+ * explicit num_splits, or the vector-ALU kernel); 0 on bad arguments. */
 int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,
                               int32_t num_splits);
+/* The number of equal tile ranges of the matrix-core kernel's automatic plan (num_splits == 0);
+ * 0 on bad arguments or when that plan falls back to per-sequence chunks. */
+int32_t gva_decode_num_ranges(const gva_dims *dims, int32_t B, int32_t max_len);
 gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
                       const int32_t *seq_len, int32_t max_len, const float *q_abs, float scale,
                       int32_t num_splits, int32_t kernel, void *workspace,

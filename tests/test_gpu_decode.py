@@ -176,3 +176,34 @@ def test_split_counts_one_to_many(kernel):
     for S in (1, 2, 5, 16, 33, 64, 1024):
         out, _ = c.decode(c.lens, q, num_splits=S, kernel=kernel)
         check_output(out, ref, "bf16", f"S={S}")
+
+
+def test_balanced_ranges_edge_lengths():
+    """The matrix-core kernel's automatic plan cuts the tiles of all sequences into equal ranges:
+    empty sequences, single positions and tile-boundary lengths, and a plan with more ranges than
+    the sequences have tiles (max_len far above the actual lengths)."""
+    c = _ragged_case(B=40, lo=0, hi=2000)
+    lens = c.lens.copy()
+    lens[:12] = [0, 1, 31, 32, 33, 0, 0, 64, 65, 0, 1, 2]
+    ml = int(c.lens.max())
+    assert gb.gva_decode_num_ranges(c.cdims, c.w.B, ml) > 1
+    q = synth.direct_q_abs(c.w, c.w.B)
+    out, lse = c.decode(lens, q, num_splits=0, kernel=MFMA, max_len=ml)
+    ref, ref_lse = c.oracle_decode(lens, q.astype(np.float64))
+    check_output(out, ref, "bf16", "balanced edge lengths")
+    ok, e = lse_ok(lse, ref_lse, 1e-3)
+    assert ok, e
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+    # a cache sized for ~4000 positions, decoded over a few positions per sequence
+    big = _ragged_case(B=3, lo=4000, hi=4100)
+    lens = np.array([1, 5, 40])
+    ml = int(big.lens.min())
+    q = synth.direct_q_abs(big.w, big.w.B)
+    R = gb.gva_decode_num_ranges(big.cdims, big.w.B, ml)
+    assert R > int(np.sum((lens + 31) // 32))
+    out, lse = big.decode(lens, q, num_splits=0, kernel=MFMA, max_len=ml)
+    ref, ref_lse = big.oracle_decode(lens, q.astype(np.float64))
+    check_output(out, ref, "bf16", "more ranges than tiles")
+    ok, e = lse_ok(lse, ref_lse, 1e-3)
+    assert ok, e

@@ -183,6 +183,24 @@ def test_split_planning(L):
     assert gb.gva_decode_num_splits(d, 0, 10, 0) == 0
 
 
+def test_balanced_range_planning(L):
+    """The matrix-core kernel's automatic plan: equal tile ranges, at most one pass of three
+    four-wave work-groups per compute unit over 256 CUs (G=8 -> two work-groups per range), at
+    least 128 ranges or ranges of 32 tiles, never more ranges than tiles, and none for a single
+    sequence."""
+    d = _dims()
+    assert gb.gva_decode_num_ranges(d, 256, 32769) == 384
+    assert gb.gva_decode_num_ranges(d, 4, 8705) == 128
+    assert gb.gva_decode_num_ranges(d, 16, 4096) == 128                # 2048 tiles / 32 < 128
+    assert gb.gva_decode_num_ranges(d, 64, 32768) == 384               # 65536 tiles: one pass
+    assert gb.gva_decode_num_ranges(d, 3, 40) == 6                     # one tile per range
+    assert gb.gva_decode_num_ranges(d, 1, 131072) == 0
+    assert gb.gva_decode_num_ranges(d, 2, 0) == 0
+    # the workspace query covers both plans
+    ws = gb.gva_decode_workspace_bytes(d, 256, 32769, 0)
+    assert ws >= (384 + 256) * 32 * (128 + 2) * 4 + 257 * 4
+
+
 def test_append_and_absorb_validation(L):
     d, c = _dims(), _cache()
     app = lambda **kw: L.gva_cache_append(ctypes.byref(d), ctypes.byref(kw.get("c", c)),

@@ -27,7 +27,8 @@ DEVERR_BLOCK, DEVERR_CAPACITY, DEVERR_ROPE, DEVERR_SEQ, DEVERR_LENGTH = 1, 2, 4,
 
 EXPORTED = [
     "gva_rope_table_bytes", "gva_rope_table_fill", "gva_cache_append", "gva_absorb_query",
-    "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode", "gva_prefill_chunk",
+    "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
+    "gva_prefill_chunk",
     "gva_status_string", "gva_last_error", "gva_version",
 ]
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.gva_decode_workspace_bytes.restype = c_size_t
     L.gva_decode_num_splits.argtypes = [POINTER(GvaDims), c_int32, c_int32, c_int32]
     L.gva_decode_num_splits.restype = c_int32
+    L.gva_decode_num_ranges.argtypes = [POINTER(GvaDims), c_int32, c_int32]
+    L.gva_decode_num_ranges.restype = c_int32
     L.gva_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32, P,
                              c_float, c_int32, c_int32, P, c_size_t, P, P, P]
     L.gva_decode.restype = c_int32
@@ -167,6 +170,10 @@ def gva_decode_workspace_bytes(dims: GvaDims, B: int, max_len: int, num_splits: 
 
 def gva_decode_num_splits(dims: GvaDims, B: int, max_len: int, num_splits: int = 0) -> int:
     return int(lib().gva_decode_num_splits(ctypes.byref(dims), B, max_len, num_splits))
+
+
+def gva_decode_num_ranges(dims: GvaDims, B: int, max_len: int) -> int:
+    return int(lib().gva_decode_num_ranges(ctypes.byref(dims), B, max_len))
 
 
 def gva_decode(dims: GvaDims, cache: "GvaCache", B: int, seq_len, max_len: int, q_abs,

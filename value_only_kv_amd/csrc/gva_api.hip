@@ -75,18 +75,21 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
   a.qscale = scale * 1.4426950408889634f;
   a.num_splits = plan.num_splits;
   a.chunk = plan.chunk;
+  a.num_ranges = plan.num_ranges;
   a.out = out;
   a.lse = lse;
-  if (plan.num_splits > 1) {
+  const bool partials = plan.num_splits > 1 || plan.num_ranges > 0;
+  if (partials) {
     char *ws = static_cast<char *>(workspace);
     a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
     a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
     a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+    if (plan.num_ranges > 0) a.tile_prefix = reinterpret_cast<int32_t *>(ws + plan.off_prefix);
   }
   hipError_t e = use_mfma ? gva::launch_decode_mfma(a, stream)
                           : gva::launch_decode_generic(a, cache->dtype == GVA_DTYPE_BF16, stream);
   if (e != hipSuccess) return hip_status(e, "decode launch");
-  if (plan.num_splits > 1) {
+  if (partials) {
     e = gva::launch_combine(a, stream);
     if (e != hipSuccess) return hip_status(e, "combine launch");
   }

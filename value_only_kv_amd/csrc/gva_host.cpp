@@ -139,16 +139,37 @@ bool mfma_supported(const gva_dims *d, const gva_cache *c, const char **why) {
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
-                 DecodePlan *plan) {
+                 bool balanced, DecodePlan *plan) {
   if (!d || B < 1 || max_len < 0 || num_splits < 0 || num_splits > kMaxSplits) return false;
+  *plan = DecodePlan{};
+  const int64_t tiles_max = static_cast<int64_t>(B) * ((max_len + kTilePositions - 1) / kTilePositions);
+  if (balanced && num_splits == 0 && B > 1 && tiles_max > 0 &&
+      tiles_max < (int64_t(1) << 31) && d->G > 0) {
+    // Equal ranges over all sequences' tiles: at most one pass of work-groups over the device;
+    // fewer for small batches, down to kPlanCUs / 2 ranges or ranges of kMinTilesPerRange tiles
+    // (assuming every sequence at max_len), whichever is more. A single sequence gets the same
+    // cut from the split grid, without the search for its range.
+    const int64_t nz = d->G / decode_waves_per_group(d->G);
+    const int64_t by_size = (tiles_max + kMinTilesPerRange - 1) / kMinTilesPerRange;
+    int64_t R = by_size > kPlanCUs / 2 ? by_size : kPlanCUs / 2;
+    if (R > kBalancedWorkGroups / nz) R = kBalancedWorkGroups / nz;
+    if (R > tiles_max) R = tiles_max;
+    if (R > kMaxSplits) R = kMaxSplits;
+    if (R < 1) R = 1;
+    plan->num_ranges = (int32_t)R;
+    const size_t rows = (size_t)(R + B) * (size_t)d->H;
+    plan->off_o = 0;
+    plan->off_m = round_up(rows * (size_t)d->d_h * 4, 256);
+    plan->off_l = plan->off_m + round_up(rows * 4, 256);
+    plan->off_prefix = plan->off_l + round_up(rows * 4, 256);
+    plan->ws_bytes = plan->off_prefix + round_up((size_t)(B + 1) * 4, 256);
+    return true;
+  }
   const int64_t q = kChunkQuantum;
   int64_t S = num_splits;
   if (S == 0) {
     // Chunks of at most 2048 positions for long sequences, at least kPlanCUs / 2 (sequence,
-    // chunk) items when the batch is small (each item is G/4 work-groups of four waves, and a
-    // compute unit runs up to three of them), and no chunk below 256 positions. Measured on the
-    // ragged batch (B = 256, lengths up to 32769): 12 to 16 chunks per sequence beat 8 and 32;
-    // on one sequence of 131072 positions 128 chunks beat 256.
+    // chunk) items when the batch is small, and no chunk below 256 positions.
     const int64_t by_len = (max_len + 2047) / 2048;
     const int64_t by_cus = (kPlanCUs / 2 + B - 1) / B;
     S = by_len > by_cus ? by_len : by_cus;
@@ -163,11 +184,7 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
   if (S < 1) S = 1;
   plan->num_splits = (int32_t)S;
   plan->chunk = (int32_t)chunk;
-  if (S == 1) {
-    plan->ws_bytes = 0;
-    plan->off_m = plan->off_l = plan->off_o = 0;
-    return true;
-  }
+  if (S == 1) return true;
   const size_t rows = (size_t)B * (size_t)S * (size_t)d->H;
   plan->off_o = 0;
   plan->off_m = round_up(rows * (size_t)d->d_h * 4, 256);
@@ -197,7 +214,11 @@ gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
     return fail(GVA_ERR_INVALID_ARG, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
   if (kernel < GVA_KERNEL_AUTO || kernel > GVA_KERNEL_MFMA)
     return fail(GVA_ERR_INVALID_ARG, "unknown kernel selector %d", kernel);
-  if (!plan_decode(d, B, max_len, num_splits, plan))
+  const char *why = nullptr;
+  const bool can = mfma_supported(d, c, &why);
+  if (kernel == GVA_KERNEL_MFMA && !can) return fail(GVA_ERR_UNSUPPORTED, "%s", why);
+  *use_mfma = (kernel == GVA_KERNEL_MFMA) || (kernel == GVA_KERNEL_AUTO && can);
+  if (!plan_decode(d, B, max_len, num_splits, *use_mfma, plan))
     return fail(GVA_ERR_INVALID_ARG, "cannot plan the decode split");
   if (plan->ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan->ws_bytes)
@@ -205,10 +226,6 @@ gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
-  const char *why = nullptr;
-  const bool can = mfma_supported(d, c, &why);
-  if (kernel == GVA_KERNEL_MFMA && !can) return fail(GVA_ERR_UNSUPPORTED, "%s", why);
-  *use_mfma = (kernel == GVA_KERNEL_MFMA) || (kernel == GVA_KERNEL_AUTO && can);
   return GVA_OK;
 }
 
@@ -266,17 +283,26 @@ gva_status gva_rope_table_fill(double *host_out, int32_t max_pos, int32_t d_r, d
 size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
                                   int32_t num_splits) {
   if (gva::check_dims(dims) != GVA_OK) return 0;
-  gva::DecodePlan p;
-  if (!gva::plan_decode(dims, B, max_len, num_splits, &p)) return 0;
-  return p.ws_bytes;
+  // enough for either kernel's plan (the cache decides which one runs)
+  gva::DecodePlan p, pb;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, false, &p)) return 0;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, true, &pb)) return 0;
+  return p.ws_bytes > pb.ws_bytes ? p.ws_bytes : pb.ws_bytes;
 }
 
 int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,
                               int32_t num_splits) {
   if (gva::check_dims(dims) != GVA_OK) return 0;
   gva::DecodePlan p;
-  if (!gva::plan_decode(dims, B, max_len, num_splits, &p)) return 0;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, false, &p)) return 0;
   return p.num_splits;
+}
+
+int32_t gva_decode_num_ranges(const gva_dims *dims, int32_t B, int32_t max_len) {
+  if (gva::check_dims(dims) != GVA_OK) return 0;
+  gva::DecodePlan p;
+  if (!gva::plan_decode(dims, B, max_len, 0, true, &p)) return 0;
+  return p.num_ranges;
 }
 
 const char *gva_status_string(gva_status status) {

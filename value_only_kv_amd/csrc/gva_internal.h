@@ -16,6 +16,20 @@ constexpr int kPlanCUs = 256;
 // Token granularity of a decode chunk: both decode kernels walk a chunk in tiles of this many
 // positions, so chunk boundaries fall on tile boundaries.
 constexpr int kChunkQuantum = 64;
+// Balanced mode: work-groups the automatic plan fills the device with (3 resident four-wave
+// work-groups on each of kPlanCUs compute units), and the fewest tiles a range should hold.
+constexpr int kBalancedWorkGroups = 3 * kPlanCUs;
+constexpr int kMinTilesPerRange = 32;
+constexpr int kTilePositions = 32;
+// Waves (value groups) per work-group of the matrix-core decode kernel: the largest divisor of
+// G that is at most 4. Four lets three work-groups share a CU (one wave per SIMD each) when the
+// kernel fits in 168 registers, which one 8-wave work-group per CU cannot use.
+constexpr int kDecodeGroupWaves = 4;
+inline int decode_waves_per_group(int G) {
+  for (int w = kDecodeGroupWaves; w > 1; --w)
+    if (G % w == 0) return w;
+  return 1;
+}
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxH = 256;
 constexpr int kMaxDh = 256;
@@ -40,17 +54,21 @@ gva_status check_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, con
 bool mfma_supported(const gva_dims *d, const gva_cache *c, const char **why);
 
 struct DecodePlan {
-  int32_t num_splits;   // chunks per sequence
-  int32_t chunk;        // positions per chunk, a multiple of kChunkQuantum
+  int32_t num_splits;   // split grid: chunks per sequence (0 in balanced mode)
+  int32_t chunk;        // split grid: positions per chunk, a multiple of kChunkQuantum
+  int32_t num_ranges;   // balanced mode: equal ranges over all sequences' tiles (0: split grid)
   size_t ws_bytes;      // workspace needed (0 when num_splits == 1: output written directly)
   size_t off_m;         // byte offsets of the partial arrays inside the workspace
   size_t off_l;
   size_t off_o;
+  size_t off_prefix;    // balanced mode: the per-sequence tile prefix, int32 [B + 1]
 };
 
-// Plans the split of positions [0, max_len) into chunks; returns false on bad arguments.
+// Plans the split of positions [0, max_len) into chunks (balanced == false), or the cut of all
+// sequences' 32-position tiles into equal ranges (balanced == true, the matrix-core kernel's
+// automatic mode); returns false on bad arguments.
 bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
-                 DecodePlan *plan);
+                 bool balanced, DecodePlan *plan);
 
 gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
                         const int32_t *seq_len, int32_t max_len, const float *q_abs,
@@ -83,10 +101,12 @@ struct DecodeArgs {
   float qscale;         // softmax scale * log2(e): scores are kept in the base-2 domain
   int32_t num_splits;
   int32_t chunk;
-  // outputs: partials (num_splits > 1) or final rows (num_splits == 1)
-  float *part_m;        // [B][S][H]
-  float *part_l;        // [B][S][H]
-  float *part_o;        // [B][S][H][d_h]
+  int32_t num_ranges;   // > 0: balanced mode (matrix-core kernel), see plan_decode
+  int32_t *tile_prefix; // balanced mode: [B + 1], written by the decode kernel
+  // outputs: partials (num_splits > 1, or balanced mode) or final rows (num_splits == 1)
+  float *part_m;        // split grid [B][S][H]; balanced mode [R + B][H]
+  float *part_l;        // same rows as part_m
+  float *part_o;        // same rows as part_m, [d_h] each
   float *out;           // [B][H][d_h]
   float *lse;           // [B][H] or nullptr
 };

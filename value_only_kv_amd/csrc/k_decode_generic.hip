@@ -232,15 +232,39 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   if (len < 0 || len > a.max_len || len > cap) {
     if (wave == 0 && dim_ok) dst[d] = qnan;
     if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
+    if (a.num_ranges > 0 && tid == 0 && blockIdx.x == 0 && h == 0)
+      gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
     return;
   }
-  const int ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
+  // the sequence's partials: rows row0 + s H for s < ns
+  int ns;
+  int64_t row0;
+  if (a.num_ranges > 0) {
+    // balanced mode: the ranges holding tiles [P[b], P[b + 1]) are those containing its first
+    // and last tile (with Re = min(R, T) ranges, range r starts at tile r T / Re and is never
+    // empty), and range r wrote row (r + b) H + h
+    const int64_t pb = a.tile_prefix[b];
+    const int64_t pe = a.tile_prefix[b + 1];
+    const int64_t T = a.tile_prefix[a.B];
+    const int64_t Re = T < a.num_ranges ? T : a.num_ranges;
+    if (pe <= pb) {
+      ns = 0;
+      row0 = 0;
+    } else {
+      const int64_t r_first = ((pb + 1) * Re - 1) / T;
+      const int64_t r_last = (pe * Re - 1) / T;
+      ns = static_cast<int>(r_last - r_first + 1);
+      row0 = (r_first + b) * a.H + h;
+    }
+  } else {
+    ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
+    row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;
+  }
   if (ns == 0) {
     if (wave == 0 && dim_ok) dst[d] = 0.0f;
     if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
     return;
   }
-  const int64_t row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;  // + s * H
   float mx = -INFINITY;
   float bad = 0.0f;
   for (int s = tid; s < ns; s += nthr) {
@@ -309,7 +333,9 @@ hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t str
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  int nw = a.num_splits / 16;
+  // waves grow with the partials per sequence (balanced mode: about R / B + 1 of them)
+  const int per_seq = a.num_ranges > 0 ? a.num_ranges / a.B + 1 : a.num_splits;
+  int nw = per_seq / 16;
   nw = nw < 1 ? 1 : (nw > kCombineMaxWaves ? kCombineMaxWaves : nw);
   hipLaunchKernelGGL(k_combine, dim3((a.d_h + 63) / 64, a.H, a.B), dim3(64 * nw), 0, stream, a);
   return hipGetLastError();

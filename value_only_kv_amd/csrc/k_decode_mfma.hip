@@ -57,9 +57,7 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kTile = 32;
-// Waves per work-group: 4 lets three work-groups share a CU (one wave per SIMD each) when the
-// kernel fits in 168 registers, which a single 8-wave work-group per CU cannot use.
-constexpr int kGroupWaves = 4;
+constexpr int kGroupWaves = gva::kDecodeGroupWaves;
 
 // Per-wave LDS copy of one tile: 32 rows (positions) of d_h bf16 values, each row padded by 32
 // bytes. The padding puts the four rows that one transposing read touches in every group of 16
@@ -278,28 +276,19 @@ constexpr int min_waves_per_simd() {
   return (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
 }
 
+// One chunk of positions [c0, c1) of sequence b for value group g (one wave): scores, online
+// softmax and weighted sum over its tiles, then the partial (m, l, o) of each of the group's heads
+// h at workspace row prow0 + h or, when `direct`, the final output row. len_bad makes the output
+// row NaN (its chunk is empty). lds is the work-group's LDS tile area.
 template <int KS, int NH>
-__global__ __launch_bounds__(64 * kGroupWaves, (min_waves_per_simd<KS, NH>())) void
-k_decode_mfma(gva::DecodeArgs a) {
+__device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g, int c0, int c1,
+                                          bool len_bad, bool direct, int64_t prow0,
+                                          uint8_t *lds) {
   constexpr int SH = NH > 0 ? NH : 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int q = lane >> 4;
-  // Work-groups are dealt to the 8 XCDs in turn (XCD = id % 8). The nz work-groups that share
-  // one (sequence, split) item take ids 8 apart, so they run on the same XCD at about the same
-  // time and the shared positional key is fetched from HBM once. Along the items the sequence
-  // index varies fastest, so every XCD receives an even share of each split column (early split
-  // columns are almost always non-empty, late ones often empty).
-  const int wpg = blockDim.x >> 6;
-  const int nz = a.G / wpg;
-  const int id = blockIdx.x;
-  const int r8 = id >> 3;
-  const int item = (r8 / nz) * 8 + (id & 7);
-  if (item >= a.B * a.num_splits) return;
-  const int b = item % a.B;
-  const int s = item / a.B;
-  const int g = (r8 % nz) * wpg + wave;
   const int nhg = a.H / a.G;
   const int h0 = g * nhg;
   // the query column of this lane: head c (hi or, with merged columns, lo part)
@@ -310,12 +299,6 @@ k_decode_mfma(gva::DecodeArgs a) {
   const bool owner = NH > 0 ? (n >= NH && n < 2 * NH) : (n < nhg);
   const int row_len = a.d_h + a.d_r;
   const float qnan = __int_as_float(0x7fc00000);
-
-  const int len = a.seq_len[b];
-  const int cap = a.max_blocks << a.log2_bs;
-  const bool len_bad = len < 0 || len > a.max_len || len > cap;
-  const int c0 = s * a.chunk;
-  const int c1 = len_bad ? c0 : min(c0 + a.chunk, len);
 
   Acc<KS> acc;
 #pragma unroll
@@ -358,7 +341,6 @@ k_decode_mfma(gva::DecodeArgs a) {
     // this wave's LDS tile: lane (n, q) writes row n, columns 8 q ..; lane L reads row L / 4,
     // columns 4 (L % 4) .. (see read_tr)
     using L = TileLds<KS>;
-    __shared__ __align__(16) uint8_t lds[kGroupWaves * L::kWave];
     uint8_t *lw_wr = lds + wave * L::kWave + n * L::kRow + 16 * q;
     const uint8_t *lw_rd = lds + wave * L::kWave + (lane >> 2) * L::kRow + 8 * (lane & 3);
 
@@ -400,16 +382,14 @@ k_decode_mfma(gva::DecodeArgs a) {
   float ltot = acc.lsum + __shfl_xor(acc.lsum, 16, 64);
   ltot += __shfl_xor(ltot, 32, 64);
   const bool any_bad = __any(bad);
-  if (lane == 0) {
-    if (any_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
-    if (len_bad && s == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
-  }
+  if (lane == 0 && any_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
   const bool poison = any_bad || len_bad;
   if (!owner) return;
-  // chunks past the end of a valid sequence are never read by the combine
-  if (a.num_splits > 1 && !len_bad && c0 >= len) return;
+  // empty chunks (past the end of a sequence, or of a sequence with a bad length) are never
+  // read by the combine
+  if (!direct && c0 >= c1) return;
   const int h = h0 + c;
-  if (a.num_splits == 1) {
+  if (direct) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h + 4 * q;
 #pragma unroll
@@ -423,7 +403,7 @@ k_decode_mfma(gva::DecodeArgs a) {
       a.lse[static_cast<int64_t>(b) * a.H + h] = poison ? qnan : v;
     }
   } else {
-    const int64_t prow = (static_cast<int64_t>(b) * a.num_splits + s) * a.H + h;
+    const int64_t prow = prow0 + h;
     float *dst = a.part_o + prow * a.d_h + 4 * q;
 #pragma unroll
     for (int nb = 0; nb < 2 * KS; ++nb) *reinterpret_cast<f32x4 *>(dst + 16 * nb) = acc.O[nb];
@@ -434,20 +414,175 @@ k_decode_mfma(gva::DecodeArgs a) {
   }
 }
 
-template <int NH>
-hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+
+// Values the whole wave agrees on, moved to scalar registers (they come out of LDS or from
+// per-lane arithmetic, so the compiler cannot know they are uniform).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int tiles_of(const gva::DecodeArgs &a, int b, int cap) {
+  const int len = a.seq_len[b];
+  return (len >= 0 && len <= a.max_len && len <= cap) ? (len + kTile - 1) / kTile : 0;
+}
+
+template <int KS, int NH, bool BALANCED>
+__global__ __launch_bounds__(64 * kGroupWaves, (min_waves_per_simd<KS, NH>())) void
+k_decode_mfma(gva::DecodeArgs a) {
+  using L = TileLds<KS>;
+  __shared__ __align__(16) uint8_t lds[kGroupWaves * L::kWave];
+  __shared__ int64_t s_part[kGroupWaves];
+  __shared__ int32_t s_found_b;
+  __shared__ int32_t s_len[64 * kGroupWaves];
+  __shared__ int64_t s_found_p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // Work-groups are dealt to the 8 XCDs in turn (XCD = id % 8). The nz work-groups that share
+  // one work item (they cover the same positions for different value groups) take ids 8 apart,
+  // so they run on the same XCD at about the same time and the shared positional key is fetched
+  // from HBM once.
+  const int wpg = blockDim.x >> 6;
+  const int nz = a.G / wpg;
+  const int id = blockIdx.x;
+  const int r8 = id >> 3;
+  const int g = (r8 % nz) * wpg + wave;
+  const int item = (r8 / nz) * 8 + (id & 7);
+  const int cap = a.max_blocks << a.log2_bs;
+
+  if constexpr (!BALANCED) {
+    // Split grid: item = (split s, sequence b) with b fastest, so every XCD receives an even
+    // share of each split column (early columns are almost always non-empty, late ones often
+    // empty). Chunk s covers positions [s chunk, (s + 1) chunk).
+    if (item >= a.B * a.num_splits) return;
+    const int b = item % a.B;
+    const int s = item / a.B;
+    const int len = a.seq_len[b];
+    const bool len_bad = len < 0 || len > a.max_len || len > cap;
+    if (len_bad && s == 0 && g == 0 && lane == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+    const int c0 = s * a.chunk;
+    const int c1 = len_bad ? c0 : min(c0 + a.chunk, len);
+    run_chunk<KS, NH>(a, b, g, c0, c1, len_bad, a.num_splits == 1,
+                      (static_cast<int64_t>(b) * a.num_splits + s) * a.H, lds);
+  } else {
+
+  // Balanced ranges: the 32-position tiles of all sequences, concatenated in sequence order
+  // (T of them), are cut into Re = min(num_ranges, T) equal ranges; range r = item covers tiles
+  // [r T / Re, (r + 1) T / Re), never empty. A range that spans several sequences does one chunk per sequence;
+  // the chunk of range r in sequence b writes its partials at workspace rows (r + b) H + h, so
+  // the chunks of one sequence occupy consecutive rows. Range 0 of the first group block also
+  // writes the tile prefix P[b] (and P[B] = T) for the combine.
+  const int R = a.num_ranges;
+  if (item >= R) return;
+  const bool writer = item == 0 && r8 % nz == 0;
+  const int nthr = blockDim.x;
+  // total tile count (with at most one sequence per thread, each length is read once and kept:
+  // in a register for the scans, in LDS for the walk over the ranges)
+  const bool one_pass = a.B <= nthr;
+  int t_own = 0;
+  int64_t mine = 0;
+  if (one_pass) {
+    if (tid < a.B) {
+      const int len = a.seq_len[tid];
+      s_len[tid] = len;
+      t_own = (len >= 0 && len <= a.max_len && len <= cap) ? (len + kTile - 1) / kTile : 0;
+    }
+    mine = t_own;
+  } else {
+    for (int b = tid; b < a.B; b += nthr) mine += tiles_of(a, b, cap);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) s_part[wave] = mine;
+  if (tid == 0) s_found_b = -1;
+  __syncthreads();
+  int64_t T = 0;
+  for (int w = 0; w < wpg; ++w) T += s_part[w];
+  T = uniform(T);
+  // with fewer tiles than ranges, one tile per range (no range is empty)
+  const int64_t Re = T < R ? T : R;
+  const bool has_range = item < Re;
+  const int64_t start = has_range ? static_cast<int64_t>(item) * T / Re : 0;
+  const int64_t end = has_range ? static_cast<int64_t>(item + 1) * T / Re : 0;
+  if (!writer && !has_range) return;                   // uniform per work-group
+  // the sequence holding tile `start`: a running block-wide prefix over the sequences
+  int64_t base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += nthr) {
+    __syncthreads();                                   // s_part reuse
+    const int b = b0 + tid;
+    const int t = one_pass ? t_own : (b < a.B ? tiles_of(a, b, cap) : 0);
+    int incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) s_part[wave] = incl;
+    __syncthreads();
+    int64_t before = base;
+    int64_t chunk_total = 0;
+    for (int w = 0; w < wpg; ++w) {
+      if (w < wave) before += s_part[w];
+      chunk_total += s_part[w];
+    }
+    const int64_t p_excl = before + incl - t;
+    if (writer && b < a.B) a.tile_prefix[b] = static_cast<int32_t>(p_excl);
+    if (has_range && t > 0 && p_excl <= start && start < p_excl + t) {
+      s_found_b = b;
+      s_found_p = p_excl;
+    }
+    base += chunk_total;
+    __syncthreads();
+    if (!writer && s_found_b >= 0) break;              // uniform per work-group
+  }
+  if (writer && tid == 0) a.tile_prefix[a.B] = static_cast<int32_t>(T);
+  if (!has_range) return;
+  auto len_of = [&](int b) { return uniform(one_pass ? s_len[b] : a.seq_len[b]); };
+  auto tiles_b_of = [&](int b) {
+    const int len = len_of(b);
+    return (len >= 0 && len <= a.max_len && len <= cap) ? (len + kTile - 1) / kTile : 0;
+  };
+  int b = uniform(s_found_b);
+  int64_t pb = uniform(s_found_p);                     // first tile of sequence b
+  int64_t t = start;
+  while (t < end) {
+    const int tiles_b = tiles_b_of(b);
+    const int64_t seg_end = min(end, pb + tiles_b);
+    const int len = len_of(b);
+    const int c0 = static_cast<int>(t - pb) * kTile;
+    const int c1 = min(static_cast<int>(seg_end - pb) * kTile, len);
+    run_chunk<KS, NH>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H, lds);
+    t = seg_end;
+    pb += tiles_b;
+    ++b;
+    while (t < end && tiles_b_of(b) == 0) ++b;        // sequences without tiles hold no range
+  }
+  }
+}
+
+template <int NH, bool BAL>
+hipError_t launch_mode(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH, BAL>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH, BAL>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH, BAL>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH, BAL>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH, BAL>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH, BAL>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH, BAL>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH, BAL>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int NH>
+hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+  return a.num_ranges > 0 ? launch_mode<NH, true>(a, grid, block, stream)
+                          : launch_mode<NH, false>(a, grid, block, stream);
 }
 
 }  // namespace
@@ -455,14 +590,8 @@ hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_
 namespace gva {
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
-  // waves per work-group: the largest divisor of G that is at most kGroupWaves
-  int wpg = 1;
-  for (int w = kGroupWaves; w >= 1; --w)
-    if (a.G % w == 0) {
-      wpg = w;
-      break;
-    }
-  const int64_t items = static_cast<int64_t>(a.B) * a.num_splits;
+  const int wpg = decode_waves_per_group(a.G);
+  const int64_t items = a.num_ranges > 0 ? a.num_ranges : static_cast<int64_t>(a.B) * a.num_splits;
   const dim3 grid(static_cast<unsigned>(((items + 7) / 8) * 8 * (a.G / wpg)));
   const dim3 block(64 * wpg);
   switch (a.H / a.G) {
