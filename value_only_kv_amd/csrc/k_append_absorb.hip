@@ -83,71 +83,101 @@ __global__ __launch_bounds__(256) void k_append(gva::DecodeArgs a, int32_t B, co
   }
 }
 
-// Absorption GEMV. Work-group (h, tile of TQ query tokens): the tile's q_nope rows for head h
-// are staged in LDS; thread i forms q~[i] for all TQ tokens with one pass over row i of M_h
-// (float32, products accumulated in order j = 0 .. d_n-1). The positional slice is rotated at
-// the token's position in float64 and rounded once to float32.
-constexpr int TQ = 8;
+// Absorption, q~[t][i] = sum_j M_h[i][j] q_nope[t][h][j]: for every head a small GEMM of the
+// d_h x d_n map by the d_n x n queries. Work-group (head h, tile of kAbsQ query tokens, tile of
+// kAbsRows rows of M_h): both operand tiles are staged in LDS, 128 columns at a time, with
+// coalesced loads (rows padded by 4 floats so that the 16-byte reads of 8 consecutive rows hit
+// 8 different bank groups);
+// thread (i, tq) forms q~ for row i and tokens tq, tq + 8, tq + 16, tq + 24, accumulating the
+// float32 products in order j = 0 .. d_n - 1. The work-groups with row tile 0 also rotate the
+// positional slice at the token's position in float64 and round it once to float32.
+constexpr int kAbsQ = 32;
+constexpr int kAbsRows = 32;
+constexpr int kAbsThreads = 256;
 
-__global__ __launch_bounds__(256) void k_absorb(int32_t H, int32_t d_h, int32_t d_n, int32_t d_r,
-                                                int32_t n_q, const float *q_nope,
-                                                const float *q_rope, const int32_t *q_pos,
-                                                const float *M, const double *rope,
-                                                int32_t max_pos, float *q_abs, int32_t *err_flag) {
-  extern __shared__ float qs[];  // [TQ][d_n]
+__global__ __launch_bounds__(kAbsThreads) void k_absorb(int32_t H, int32_t d_h, int32_t d_n,
+                                                        int32_t d_r, int32_t n_q,
+                                                        const float *q_nope, const float *q_rope,
+                                                        const int32_t *q_pos, const float *M,
+                                                        const double *rope, int32_t max_pos,
+                                                        float *q_abs, int32_t *err_flag) {
+  constexpr int kJ4 = 32;                      // d_n is walked in chunks of 128 (32 float4)
+  constexpr int kStride4 = kJ4 + 1;            // row stride in float4 (4 floats of padding)
+  __shared__ float4 qs[kAbsQ * kStride4];
+  __shared__ float4 ms[kAbsRows * kStride4];
   const int h = blockIdx.x;
-  const int k0 = blockIdx.y * TQ;
-  const int nt = min(TQ, n_q - k0);
-  const int row = d_h + d_r;
-  for (int idx = threadIdx.x; idx < nt * d_n; idx += blockDim.x) {
-    const int t = idx / d_n;
-    const int j = idx - t * d_n;
-    qs[idx] = q_nope[(static_cast<int64_t>(k0 + t) * H + h) * d_n + j];
-  }
-  __syncthreads();
-  const float4 *Mh = reinterpret_cast<const float4 *>(M + static_cast<int64_t>(h) * d_h * d_n);
+  const int k0 = blockIdx.y * kAbsQ;
+  const int i0 = blockIdx.z * kAbsRows;
+  const int nt = min(kAbsQ, n_q - k0);
+  const int ni = min(kAbsRows, d_h - i0);
   const int dn4 = d_n >> 2;
-  for (int i = threadIdx.x; i < d_h; i += blockDim.x) {
-    float acc[TQ];
+  const int row = d_h + d_r;
+  const int tid = threadIdx.x;
+  const int i = tid >> 3;                      // row of the tile
+  const int tq = tid & 7;                      // tokens tq + 8 k
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const float4 *Mh = reinterpret_cast<const float4 *>(M + (static_cast<int64_t>(h) * d_h + i0) * d_n);
+  for (int jc = 0; jc < dn4; jc += kJ4) {
+    const int nj = min(kJ4, dn4 - jc);
+    for (int idx = tid; idx < kAbsQ * kJ4; idx += kAbsThreads) {
+      const int t = idx / kJ4;
+      const int j4 = idx - t * kJ4;
+      float4 v = {0.f, 0.f, 0.f, 0.f};
+      if (t < nt && j4 < nj)
+        v = reinterpret_cast<const float4 *>(q_nope + (static_cast<int64_t>(k0 + t) * H + h) * d_n)[jc + j4];
+      qs[t * kStride4 + j4] = v;
+    }
+    for (int idx = tid; idx < kAbsRows * kJ4; idx += kAbsThreads) {
+      const int r = idx / kJ4;
+      const int j4 = idx - r * kJ4;
+      float4 v = {0.f, 0.f, 0.f, 0.f};
+      if (r < ni && j4 < nj) v = Mh[static_cast<int64_t>(r) * dn4 + jc + j4];
+      ms[r * kStride4 + j4] = v;
+    }
+    __syncthreads();
+    for (int j4 = 0; j4 < nj; ++j4) {
+      const float4 m = ms[i * kStride4 + j4];
 #pragma unroll
-    for (int t = 0; t < TQ; ++t) acc[t] = 0.0f;
-    const float4 *mrow = Mh + static_cast<int64_t>(i) * dn4;
-    for (int j4 = 0; j4 < dn4; ++j4) {
-      const float4 m = mrow[j4];
-#pragma unroll
-      for (int t = 0; t < TQ; ++t) {
-        const float *q = qs + t * d_n + 4 * j4;
-        acc[t] = fmaf(m.x, q[0], acc[t]);
-        acc[t] = fmaf(m.y, q[1], acc[t]);
-        acc[t] = fmaf(m.z, q[2], acc[t]);
-        acc[t] = fmaf(m.w, q[3], acc[t]);
+      for (int k = 0; k < 4; ++k) {
+        const float4 q = qs[(tq + 8 * k) * kStride4 + j4];
+        acc[k] = fmaf(m.x, q.x, acc[k]);
+        acc[k] = fmaf(m.y, q.y, acc[k]);
+        acc[k] = fmaf(m.z, q.z, acc[k]);
+        acc[k] = fmaf(m.w, q.w, acc[k]);
       }
     }
-    for (int t = 0; t < nt; ++t) {
+    __syncthreads();
+  }
+  if (i < ni) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = tq + 8 * k;
+      if (t >= nt) continue;
       const int p = q_pos[k0 + t];
       const bool bad = p < 0 || p >= max_pos;
-      q_abs[(static_cast<int64_t>(k0 + t) * H + h) * row + i] = bad ? __int_as_float(0x7fc00000) : acc[t];
+      q_abs[(static_cast<int64_t>(k0 + t) * H + h) * row + i0 + i] = bad ? __int_as_float(0x7fc00000) : acc[k];
     }
   }
+  if (blockIdx.z != 0) return;
   const int half_r = d_r >> 1;
-  for (int idx = threadIdx.x; idx < nt * half_r; idx += blockDim.x) {
+  for (int idx = tid; idx < nt * half_r; idx += kAbsThreads) {
     const int t = idx / half_r;
-    const int i = idx - t * half_r;
+    const int r = idx - t * half_r;
     const int k = k0 + t;
     const int p = q_pos[k];
     float2 y;
     if (p < 0 || p >= max_pos) {
       y.x = y.y = __int_as_float(0x7fc00000);
-      if (i == 0 && err_flag) atomicOr(err_flag, GVA_DEVERR_ROPE);
+      if (r == 0 && err_flag) atomicOr(err_flag, GVA_DEVERR_ROPE);
     } else {
-      const float2 x = reinterpret_cast<const float2 *>(q_rope + (static_cast<int64_t>(k) * H + h) * d_r)[i];
-      const double2 t2 = reinterpret_cast<const double2 *>(rope)[static_cast<int64_t>(p) * half_r + i];
+      const float2 x = reinterpret_cast<const float2 *>(q_rope + (static_cast<int64_t>(k) * H + h) * d_r)[r];
+      const double2 t2 = reinterpret_cast<const double2 *>(rope)[static_cast<int64_t>(p) * half_r + r];
       double y0, y1;
       gvad::rotate_pair_f64(static_cast<double>(x.x), static_cast<double>(x.y), t2.x, t2.y, &y0, &y1);
       y.x = gvad::f64_to_f32(y0);
       y.y = gvad::f64_to_f32(y1);
     }
-    float *dst = q_abs + (static_cast<int64_t>(k) * H + h) * row + d_h + 2 * i;
+    float *dst = q_abs + (static_cast<int64_t>(k) * H + h) * row + d_h + 2 * r;
     dst[0] = y.x;
     dst[1] = y.y;
   }
@@ -192,11 +222,9 @@ hipError_t launch_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, co
                          const int32_t *q_pos, const float *M, const double *rope,
                          int32_t max_pos, float *q_abs, int32_t *err_flag, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  const dim3 grid(d->H, (n_q + TQ - 1) / TQ);
-  const int threads = d->d_h <= 64 ? 64 : (d->d_h <= 128 ? 128 : 256);
-  const size_t lds = static_cast<size_t>(TQ) * d->d_n * sizeof(float);
-  hipLaunchKernelGGL(k_absorb, grid, dim3(threads), lds, stream, d->H, d->d_h, d->d_n, d->d_r, n_q,
-                     q_nope, q_rope, q_pos, M, rope, max_pos, q_abs, err_flag);
+  const dim3 grid(d->H, (n_q + kAbsQ - 1) / kAbsQ, (d->d_h + kAbsRows - 1) / kAbsRows);
+  hipLaunchKernelGGL(k_absorb, grid, dim3(kAbsThreads), 0, stream, d->H, d->d_h, d->d_n, d->d_r,
+                     n_q, q_nope, q_rope, q_pos, M, rope, max_pos, q_abs, err_flag);
   return hipGetLastError();
 }
 
