@@ -400,6 +400,29 @@ def decode_materialized(V: np.ndarray, kr: np.ndarray, dims: Dims, q_nope_b, r_b
 
 
 # --------------------------------------------------------------------------------------
+# GQA comparator: what a matched grouped-query model caches and reads per step, G keys and
+# G values per token ([kvcache] section 4: the query heads of a group share one key head and
+# one value head), decoded with the textbook step ([kvcache] section 1). Keys are cached as
+# the model produced them (any rotation already applied), so the score of head h at cached
+# position j is scale * q_h . k_{j, g(h)}.
+# --------------------------------------------------------------------------------------
+
+
+def gqa_decode_sequence(K: np.ndarray, V: np.ndarray, dims: Dims, q_b, scale: float):
+    """One sequence; K, V [n, G, d_h] (the cached values in float64), q_b [H, d_h]."""
+    q_b = np.asarray(q_b, dtype=np.float64)
+    out = np.zeros((dims.H, dims.d_h))
+    lse = np.full(dims.H, -np.inf)
+    if V.shape[0] == 0:
+        return out, lse
+    for h in range(dims.H):
+        g = dims.group_of(h)
+        s = scale * (K[:, g, :] @ q_b[h])
+        out[h], lse[h], _ = softmax_attend(s, V[:, g, :])
+    return out, lse
+
+
+# --------------------------------------------------------------------------------------
 # O7: chunked prefill.  The chunk's tokens are appended first (O4); query i of sequence b
 # sits at position start_b + i and attends to positions 0..start_b + i (inclusive), over
 # the cache-rounded values ([summary]: prefill is a dense, matrix-heavy pass).
@@ -497,6 +520,11 @@ def kv_cache_bytes(layers: int, batch: int, T: int, kv_heads: int, d_h: int,
                    elem_bytes: int) -> int:
     """Bytes of a key/value cache with kv_heads key heads and as many value heads."""
     return 2 * layers * batch * T * kv_heads * d_h * elem_bytes
+
+
+def gqa_decode_bytes(len_b: int, G: int, d_h: int, elem_bytes: int) -> int:
+    """Cache bytes one GQA decode step of a sequence reads: every key and value, once."""
+    return len_b * gqa_cache_scalars(1, G, d_h) * elem_bytes
 
 
 def gva_decode_bytes(len_b: int, G: int, d_h: int, d_r: int, elem_bytes: int) -> int:

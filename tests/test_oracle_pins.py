@@ -524,3 +524,64 @@ def test_synthetic_m_scale_is_matched():
     v, _ = synth.sequence_tokens(w, 0, 4096)
     K = np.einsum("ti,hik->htk", v[:, 0, :].astype(np.float64), M)
     assert abs(np.sqrt(np.mean(K ** 2)) - 1.0) < 0.02
+
+
+# ----------------------------------------------------------------------------------------
+# GQA comparator (the cache a matched grouped-query model keeps)
+# ----------------------------------------------------------------------------------------
+
+
+def test_gqa_comparator_worked_example():
+    """The [kvcache] section 3 example is itself an MQA step: G = 1 key/value head."""
+    g = _golden("kvcache_mqa_worked_example.json")
+    K = np.array(g["keys"], dtype=np.float64)[:, None, :]
+    V = np.array(g["values"], dtype=np.float64)[:, None, :]
+    dims = O.Dims(H=1, G=1, d_h=2, d_n=2, d_r=0)
+    for case in g["cases"]:
+        o, lse = O.gqa_decode_sequence(K, V, dims, np.array([case["query"]], float), g["scale"])
+        assert [round(x, 1) for x in o[0]] == case["output_1dp"]
+        e2 = math.exp(2.0)
+        assert abs(lse[0] - math.log(e2 + 1)) < 1e-15
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gqa_comparator_against_sdpa(seed):
+    """A library routine: scaled_dot_product_attention in float64 with the group's key and value
+    repeated for each of its heads."""
+    rng = np.random.default_rng(seed)
+    H, G, n, d_h = 8, 2, 37, 16
+    K = rng.standard_normal((n, G, d_h))
+    V = rng.standard_normal((n, G, d_h))
+    q = rng.standard_normal((H, d_h))
+    dims = O.Dims(H=H, G=G, d_h=d_h, d_n=d_h, d_r=0)
+    out, lse = O.gqa_decode_sequence(K, V, dims, q, 0.3)
+    per = H // G
+    Kh = torch.from_numpy(np.repeat(K.transpose(1, 0, 2), per, axis=0))   # [H, n, d_h]
+    Vh = torch.from_numpy(np.repeat(V.transpose(1, 0, 2), per, axis=0))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :], Kh, Vh, scale=0.3)[:, 0, :].numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    s = 0.3 * np.einsum("hd,hnd->hn", q, Kh.numpy())
+    assert np.allclose(lse, np.log(np.exp(s).sum(-1)), rtol=0, atol=1e-12)
+
+
+def test_gqa_with_keys_equal_values_is_gva_with_identity_map():
+    """Shared K = V ([review] 第一次尝试) is both a GQA cache with K = V and a GVA cache with
+    M_h = I and no positional slice: the two decode definitions must agree."""
+    rng = np.random.default_rng(4)
+    H, G, n, d = 6, 3, 23, 8
+    V = rng.standard_normal((n, G, d))
+    q = rng.standard_normal((H, d))
+    dims = O.Dims(H=H, G=G, d_h=d, d_n=d, d_r=0)
+    a, la = O.gqa_decode_sequence(V, V, dims, q, 0.5)
+    b, lb = O.decode_sequence(V, np.zeros((n, 0)), dims, q, 0.5)
+    assert np.allclose(a, b, rtol=0, atol=1e-13) and np.allclose(la, lb, rtol=0, atol=1e-13)
+
+
+def test_gqa_bytes_against_kvcache_page():
+    """The per-token byte count a GQA step reads is the [kvcache] section 5 figure: 8 KV heads
+    of 128 fp16 values, keys and values, 4 KiB per token per layer for MHA-8 (= GQA with G = 8)."""
+    assert O.gqa_decode_bytes(1, 8, 128, 2) == 4096
+    assert O.gqa_decode_bytes(1, 1, 128, 2) == 512
+    # the GVA step at the ragged-batch shape reads 2096 B per token, 51.2% of GQA's 4096 B
+    assert O.gva_decode_bytes(1, 8, 128, 24, 2) == 2096
