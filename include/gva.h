@@ -198,6 +198,24 @@ gva_status gva_prefill_chunk(const gva_dims *dims, const gva_cache *cache, int32
                              const float *q_abs, const float *v_new, const float *kr_raw,
                              float scale, float *out, float *lse, hipStream_t stream);
 
+/* ---- GQA comparator ([kvcache] section 4: the query heads of a group share one key head and one
+ * value head; [kvcache] section 1: the decode step) ------------------------------------------
+ * Decodes the cache a matched grouped-query model would keep - G keys and G values per token,
+ * 2 G d_h scalars instead of GVA's G d_h + d_r - on the same matrix-core kernel, work plan and
+ * combine as gva_decode, so the two can be timed side by side:
+ *   out[b][h][:] = sum_j softmax_j(scale * q[b][h] . K(j, g(h), :)) V(j, g(h), :)
+ *   dims: as for gva_decode (H, G, d_h are used; the shape limits of the matrix-core kernel
+ *   apply). values: a bf16 cache as for gva_decode holding the value pool; its positional-key
+ *   pool and RoPE table are not read. keys: device, 16-byte aligned, the key pool, laid out
+ *   exactly like values->v (same strides, block table and dtype).
+ *   q: device float32 [B][H][d_h], already rotated like the cached keys.
+ *   workspace: at least gva_decode_workspace_bytes(dims, B, max_len, 0) bytes.
+ * Errors as for gva_decode. */
+gva_status gva_gqa_decode(const gva_dims *dims, const gva_cache *values, const void *keys,
+                          int32_t B, const int32_t *seq_len, int32_t max_len, const float *q,
+                          float scale, void *workspace, size_t workspace_bytes, float *out,
+                          float *lse, hipStream_t stream);
+
 /* ---- Diagnostics --------------------------------------------------------------------------- */
 const char *gva_status_string(gva_status status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */

@@ -28,7 +28,7 @@ DEVERR_BLOCK, DEVERR_CAPACITY, DEVERR_ROPE, DEVERR_SEQ, DEVERR_LENGTH = 1, 2, 4,
 EXPORTED = [
     "gva_rope_table_bytes", "gva_rope_table_fill", "gva_cache_append", "gva_absorb_query",
     "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
-    "gva_prefill_chunk",
+    "gva_prefill_chunk", "gva_gqa_decode",
     "gva_status_string", "gva_last_error", "gva_version",
 ]
 
@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.gva_prefill_chunk.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32,
                                     c_int32, P, P, P, c_float, P, P, P]
     L.gva_prefill_chunk.restype = c_int32
+    L.gva_gqa_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), P, c_int32, P, c_int32,
+                                 P, c_float, P, c_size_t, P, P, P]
+    L.gva_gqa_decode.restype = c_int32
     L.gva_status_string.argtypes = [c_int32]
     L.gva_status_string.restype = c_char_p
     L.gva_last_error.argtypes = []
@@ -191,6 +194,15 @@ def gva_prefill_chunk(dims: GvaDims, cache: "GvaCache", B: int, start, max_start
     _check(lib().gva_prefill_chunk(ctypes.byref(dims), ctypes.byref(cache.struct), B, _ptr(start),
                                    max_start, chunk_len, _ptr(q_abs), _ptr(v_new), _ptr(kr_raw),
                                    scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def gva_gqa_decode(dims: GvaDims, values: "GvaCache", keys, B: int, seq_len, max_len: int, q,
+                   scale: float, out, lse=None, workspace=None, stream=None) -> None:
+    """The GQA comparator: keys is a tensor laid out exactly like values.v."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gva_gqa_decode(ctypes.byref(dims), ctypes.byref(values.struct), _ptr(keys), B,
+                                _ptr(seq_len), max_len, _ptr(q), scale, _ptr(workspace), ws_bytes,
+                                _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def gva_version() -> str:

@@ -96,6 +96,48 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
   return GVA_OK;
 }
 
+gva_status gva_gqa_decode(const gva_dims *dims, const gva_cache *values, const void *keys,
+                          int32_t B, const int32_t *seq_len, int32_t max_len, const float *q,
+                          float scale, void *workspace, size_t workspace_bytes, float *out,
+                          float *lse, hipStream_t stream) {
+  if (!keys || reinterpret_cast<uintptr_t>(keys) % 16 != 0)
+    return gva::fail(GVA_ERR_INVALID_ARG, "keys must be a 16-byte aligned device pointer");
+  gva::DecodePlan plan{};
+  bool use_mfma = false;
+  gva_status st = gva::check_decode(dims, values, B, seq_len, max_len, q, scale, 0,
+                                    GVA_KERNEL_MFMA, workspace, workspace_bytes, out, &plan,
+                                    &use_mfma);
+  if (st != GVA_OK) return st;
+  gva::DecodeArgs a = cache_args(dims, values);
+  a.k = keys;
+  a.d_r = 0;                          // the query rows are [q_h] (d_h wide), no positional part
+  a.B = B;
+  a.seq_len = seq_len;
+  a.max_len = max_len;
+  a.q_abs = q;
+  a.qscale = scale * 1.4426950408889634f;
+  a.num_splits = plan.num_splits;
+  a.chunk = plan.chunk;
+  a.num_ranges = plan.num_ranges;
+  a.out = out;
+  a.lse = lse;
+  const bool partials = plan.num_splits > 1 || plan.num_ranges > 0;
+  if (partials) {
+    char *ws = static_cast<char *>(workspace);
+    a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
+    a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
+    a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+    if (plan.num_ranges > 0) a.tile_prefix = reinterpret_cast<int32_t *>(ws + plan.off_prefix);
+  }
+  hipError_t e = gva::launch_decode_mfma(a, stream);
+  if (e != hipSuccess) return hip_status(e, "comparator decode launch");
+  if (partials) {
+    e = gva::launch_combine(a, stream);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return GVA_OK;
+}
+
 gva_status gva_prefill_chunk(const gva_dims *dims, const gva_cache *cache, int32_t B,
                              const int32_t *start, int32_t max_start, int32_t chunk_len,
                              const float *q_abs, const float *v_new, const float *kr_raw,

@@ -86,6 +86,7 @@ struct DecodeArgs {
   // cache
   const void *v;
   const void *kr;
+  const void *k;        // GQA comparator only: key pool, same layout as v (nullptr for GVA)
   int64_t v_sb, v_st, v_sg, kr_sb, kr_st;
   int64_t num_blocks;
   int32_t log2_bs;

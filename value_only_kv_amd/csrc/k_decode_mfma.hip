@@ -121,10 +121,12 @@ __device__ __forceinline__ void split8(const float (&x)[8], u32x4 &hi, u32x4 &lo
   }
 }
 
-template <int KS>
+// GQA == true is the comparator: a cache of G keys and G values per token, where the score
+// contracts the key rows (d_h wide) instead of [value row | positional key row].
+template <int KS, bool GQA>
 struct Tile {
-  u32x4 v[2][KS];   // V rows in A-operand form, per position block and k-step
-  u32x4 kr[2];      // positional key rows in A-operand form
+  u32x4 v[2][KS];                  // V rows in A-operand form, per position block and k-step
+  u32x4 x[2][GQA ? KS : 1];        // GVA: positional key rows; GQA: key rows, like v
 };
 
 // Block-table entries of the two 16-position blocks of the tile at t0 (clamped to c1 - 1):
@@ -143,9 +145,9 @@ __device__ __forceinline__ int32_t load_pages(const int32_t *__restrict__ bt, in
 // multiple of 16), so one table entry serves all of its lanes. Positions >= c1 read position
 // c1 - 1 instead (finite data from a block that is cached already); their scores are masked, so
 // they add exactly zero. vlane/klane are the lane-invariant parts of the element offsets.
-template <int KS>
+template <int KS, bool GQA>
 __device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, int t0, int c1,
-                                          int n, int64_t vlane, int64_t klane, Tile<KS> &T,
+                                          int n, int64_t vlane, int64_t klane, Tile<KS, GQA> &T,
                                           bool &bad) {
   const int mask = (1 << a.log2_bs) - 1;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
@@ -162,7 +164,15 @@ __device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, i
     const uint16_t *vp = vbase + blk * a.v_sb + row * a.v_st + vlane;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = *reinterpret_cast<const u32x4 *>(vp + 32 * ks);
-    T.kr[tb] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + klane);
+    if constexpr (GQA) {
+      const uint16_t *kp = static_cast<const uint16_t *>(a.k) + (vp - vbase);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) T.x[tb][ks] = *reinterpret_cast<const u32x4 *>(kp + 32 * ks);
+      (void)kbase;
+      (void)klane;
+    } else {
+      T.x[tb][0] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + klane);
+    }
   }
 }
 
@@ -176,8 +186,8 @@ struct Acc {
 
 // One tile: scores, online softmax and the weighted sum. NH > 0: merged hi/lo columns (see the
 // file comment); NH == 0: separate hi and lo MFMAs with QX = hi and QY = lo.
-template <int KS, int NH>
-__device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, int n, int q,
+template <int KS, int NH, bool GQA>
+__device__ __forceinline__ void tile_step(const Tile<KS, GQA> &cur, int t0, int c1, int n, int q,
                                           const bf16x8 (&QX)[KS], const bf16x8 (&QY)[KS],
                                           const bf16x8 &RX, const bf16x8 &RY, uint8_t *lw_wr,
                                           const uint8_t *lw_rd, Acc<KS> &acc) {
@@ -194,21 +204,25 @@ __device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, i
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+    // the score operand: the value rows plus the positional key (GVA) or the key rows (GQA)
+    const u32x4 *sx = GQA ? cur.x[tb] : cur.v[tb];
     if (NH > 0) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s0 = mfma(as_bf16(cur.v[tb][ks]), QX[ks], s0);
-      s0 = mfma(as_bf16(cur.kr[tb]), RX, s0);
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma(as_bf16(sx[ks]), QX[ks], s0);
+      if (!GQA) s0 = mfma(as_bf16(cur.x[tb][0]), RX, s0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) s0[r] += row_shr_f<SH>(s0[r]);
     } else {
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s0 = mfma(as_bf16(cur.v[tb][ks]), QX[ks], s0);
-        s1 = mfma(as_bf16(cur.v[tb][ks]), QY[ks], s1);
+        s0 = mfma(as_bf16(sx[ks]), QX[ks], s0);
+        s1 = mfma(as_bf16(sx[ks]), QY[ks], s1);
       }
-      s0 = mfma(as_bf16(cur.kr[tb]), RX, s0);
-      s1 = mfma(as_bf16(cur.kr[tb]), RY, s1);
+      if (!GQA) {
+        s0 = mfma(as_bf16(cur.x[tb][0]), RX, s0);
+        s1 = mfma(as_bf16(cur.x[tb][0]), RY, s1);
+      }
       s0 += s1;
     }
     S[tb] = s0;
@@ -271,16 +285,16 @@ __device__ __forceinline__ void tile_step(const Tile<KS> &cur, int t0, int c1, i
 
 // Waves per SIMD the register allocation must allow: three where the kernel fits in 168
 // registers without spilling (d_h <= 64, or d_h = 128 with merged hi/lo columns), else two.
-template <int KS, int NH>
+template <int KS, int NH, bool GQA>
 constexpr int min_waves_per_simd() {
-  return (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
+  return !GQA && (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
 }
 
 // One chunk of positions [c0, c1) of sequence b for value group g (one wave): scores, online
 // softmax and weighted sum over its tiles, then the partial (m, l, o) of each of the group's heads
 // h at workspace row prow0 + h or, when `direct`, the final output row. len_bad makes the output
 // row NaN (its chunk is empty). lds is the work-group's LDS tile area.
-template <int KS, int NH>
+template <int KS, int NH, bool GQA>
 __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g, int c0, int c1,
                                           bool len_bad, bool direct, int64_t prow0,
                                           uint8_t *lds) {
@@ -356,19 +370,19 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
     // loop runs near the streaming rate already.)
     const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
     const int lb = a.log2_bs;
-    Tile<KS> A, Bt;
+    Tile<KS, GQA> A, Bt;
     int32_t PA = load_pages(bt, lb, c0, c1, lane);
     int32_t PB = load_pages(bt, lb, c0 + kTile, c1, lane);
-    load_tile<KS>(a, PA, c0, c1, n, vlane, klane, A, bad);
+    load_tile<KS, GQA>(a, PA, c0, c1, n, vlane, klane, A, bad);
     PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
     for (int t0 = c0; t0 < c1; t0 += 2 * kTile) {
       const int t1 = t0 + kTile;
-      load_tile<KS>(a, PB, t1, c1, n, vlane, klane, Bt, bad);
+      load_tile<KS, GQA>(a, PB, t1, c1, n, vlane, klane, Bt, bad);
       PB = load_pages(bt, lb, t1 + 2 * kTile, c1, lane);
-      tile_step<KS, NH>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
-      load_tile<KS>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad);
+      tile_step<KS, NH, GQA>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
+      load_tile<KS, GQA>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad);
       PA = load_pages(bt, lb, t1 + 3 * kTile, c1, lane);
-      if (t1 < c1) tile_step<KS, NH>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
+      if (t1 < c1) tile_step<KS, NH, GQA>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
     }
   }
 
@@ -429,8 +443,8 @@ __device__ __forceinline__ int tiles_of(const gva::DecodeArgs &a, int b, int cap
   return (len >= 0 && len <= a.max_len && len <= cap) ? (len + kTile - 1) / kTile : 0;
 }
 
-template <int KS, int NH, bool BALANCED>
-__global__ __launch_bounds__(64 * kGroupWaves, (min_waves_per_simd<KS, NH>())) void
+template <int KS, int NH, bool BALANCED, bool GQA>
+__global__ __launch_bounds__(64 * kGroupWaves, (min_waves_per_simd<KS, NH, GQA>())) void
 k_decode_mfma(gva::DecodeArgs a) {
   using L = TileLds<KS>;
   __shared__ __align__(16) uint8_t lds[kGroupWaves * L::kWave];
@@ -465,7 +479,7 @@ k_decode_mfma(gva::DecodeArgs a) {
     if (len_bad && s == 0 && g == 0 && lane == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
     const int c0 = s * a.chunk;
     const int c1 = len_bad ? c0 : min(c0 + a.chunk, len);
-    run_chunk<KS, NH>(a, b, g, c0, c1, len_bad, a.num_splits == 1,
+    run_chunk<KS, NH, GQA>(a, b, g, c0, c1, len_bad, a.num_splits == 1,
                       (static_cast<int64_t>(b) * a.num_splits + s) * a.H, lds);
   } else {
 
@@ -554,7 +568,7 @@ k_decode_mfma(gva::DecodeArgs a) {
     const int len = len_of(b);
     const int c0 = static_cast<int>(t - pb) * kTile;
     const int c1 = min(static_cast<int>(seg_end - pb) * kTile, len);
-    run_chunk<KS, NH>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H, lds);
+    run_chunk<KS, NH, GQA>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H, lds);
     t = seg_end;
     pb += tiles_b;
     ++b;
@@ -563,17 +577,17 @@ k_decode_mfma(gva::DecodeArgs a) {
   }
 }
 
-template <int NH, bool BAL>
+template <int NH, bool BAL, bool GQA>
 hipError_t launch_mode(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH, BAL>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH, BAL>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH, BAL>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH, BAL>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH, BAL>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH, BAL>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH, BAL>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH, BAL>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH, BAL, GQA>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -581,8 +595,12 @@ hipError_t launch_mode(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStrea
 
 template <int NH>
 hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
-  return a.num_ranges > 0 ? launch_mode<NH, true>(a, grid, block, stream)
-                          : launch_mode<NH, false>(a, grid, block, stream);
+  if (a.k) {
+    return a.num_ranges > 0 ? launch_mode<NH, true, true>(a, grid, block, stream)
+                            : launch_mode<NH, false, true>(a, grid, block, stream);
+  }
+  return a.num_ranges > 0 ? launch_mode<NH, true, false>(a, grid, block, stream)
+                          : launch_mode<NH, false, false>(a, grid, block, stream);
 }
 
 }  // namespace

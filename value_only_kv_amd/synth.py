@@ -226,6 +226,14 @@ def sequence_tokens(w: Workload, b: int, n_tok: int):
     return v, kr
 
 
+def comparator_keys(w: Workload, b: int, n_tok: int) -> np.ndarray:
+    """Keys of sequence b for a matched GQA cache (the comparator): [n_tok, G, d_h] float32 drawn
+    from N(0, 1) on a stream of their own, [1000 + k, b, 2], position by position."""
+    rng = np.random.default_rng(np.random.SeedSequence([1000 + w.index, b, 2]))
+    x = rng.standard_normal(size=(n_tok, w.G * w.d_h), dtype=np.float64).astype(np.float32)
+    return np.ascontiguousarray(x.reshape(n_tok, w.G, w.d_h))
+
+
 def decode_query_positions(w: Workload, lens: np.ndarray) -> np.ndarray:
     """Position of each sequence's query token: the next position after the cached ones."""
     return lens.astype(np.int32)
