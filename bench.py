@@ -8,8 +8,9 @@ before the timed region. The value is the cache bytes the step must read, len (G
 summed over the batch, divided by the step time.
 
 Also measured: the decode kernel alone (HIP events on the library's stream) for the roofline
-line, the long-context single-sequence decode (T = 131072) with cache replicas rotated so the
-256 MB last-level cache cannot serve them, and the CPU oracle on a bounded sample.
+line, the GQA comparator (the cache a matched grouped-query model keeps) on the same batch, the
+long-context single-sequence decode (T = 131072) with cache replicas rotated so the 256 MB
+last-level cache cannot serve them, the chunked prefill, and the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ def parse():
     p.add_argument("--no-long", action="store_true", help="skip the T=131072 measurement")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    p.add_argument("--no-gqa", action="store_true", help="skip the GQA comparator measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -174,6 +176,40 @@ def main():
         traffic = read_traffic(os.path.join(ROOT, "profiles", "gva_decode_ragged_batch_hbm_traffic.md"),
                                read_bytes)
 
+    # ---------------- GQA comparator on the same batch ----------------
+    # The cache a matched grouped-query model keeps: the same value pool plus a key pool of the
+    # same layout (G keys per token instead of one shared positional key), decoded by the same
+    # kernel skeleton, plan and combine; its own cache bytes are 2 G d_h per token.
+    gqa = None
+    if not args.no_gqa:
+        keys = torch.randn(dc.cache.v.shape, generator=gen, device="cuda").to(torch.bfloat16)
+        q_g = torch.randn((B, H, w.d_h), generator=gen, device="cuda")
+        for _ in range(3):
+            gb.gva_gqa_decode(dc.dims, dc.cache, keys, B, seq_len, max_len, q_g, w.scale, out, lse,
+                              workspace=ws, stream=stream)
+        evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_ev)]
+        for e0, e1 in evg:
+            e0.record(stream)
+            gb.gva_gqa_decode(dc.dims, dc.cache, keys, B, seq_len, max_len, q_g, w.scale, out, lse,
+                              workspace=ws, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t_gqa = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evg])) / 1e3
+        gqa_bytes = int((lens + 1).sum()) * 2 * w.G * w.d_h * 2
+        gqa = {"workload": "same batch, lengths and paged layout; keys [T][G][d_h] bf16 in place "
+                           "of the shared positional key",
+               "ms": round(t_gqa * 1e3, 4), "cache_bytes": gqa_bytes,
+               "GB_s": round(gqa_bytes / t_gqa / 1e9, 1),
+               "frac_of_hbm_peak": round(gqa_bytes / t_gqa / 1e9 / HBM_PEAK_GBS, 4),
+               "seq_steps_per_s": round(B / t_gqa, 1),
+               "gva_bytes_over_gqa_bytes": round(read_bytes / gqa_bytes, 4),
+               "gva_speedup_over_gqa": round(t_gqa / t_dec, 3)}
+        log(f"GQA comparator decode: {t_gqa * 1e3:.3f} ms ({gqa_bytes / t_gqa / 1e9:.1f} GB/s of its "
+            f"{gqa_bytes / 1e9:.2f} GB); GVA decode is {t_gqa / t_dec:.2f}x faster")
+        del keys
+        torch.cuda.empty_cache()
+
     result_extra = {}
     # ---------------- long context, one sequence ----------------
     if not args.no_long:
@@ -266,6 +302,7 @@ def main():
         "cpu_baseline": cpu,
         "long_context": result_extra,
         "prefill": prefill,
+        "gqa_comparator": gqa,
         "device": dev,
     }
     print(json.dumps(res), flush=True)
