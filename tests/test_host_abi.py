@@ -165,12 +165,12 @@ def test_mfma_kernel_shape_limits(L):
 def test_split_planning(L):
     d = _dims()
     # automatic: a single sequence gets 128 chunks, long sequences chunks of at most 2048
-    # positions (rounded up to multiples of 64), short ones no chunk below 256 positions
+    # positions (rounded up to multiples of 64), short ones chunks down to 64 positions
     S = gb.gva_decode_num_splits(d, 1, 131072, 0)
     assert S == 128
     assert gb.gva_decode_num_splits(d, 256, 32769, 0) == 17     # chunks of 1984 positions
     assert gb.gva_decode_num_splits(d, 8, 4097, 0) == 13         # 16 asked, chunks of 320
-    assert gb.gva_decode_num_splits(d, 1, 1000, 0) == 4          # chunks of 256
+    assert gb.gva_decode_num_splits(d, 1, 1000, 0) == 16         # chunks of 64
     # explicit split counts are kept unless a chunk would start beyond max_len
     for S in (64, 128, 256):
         assert gb.gva_decode_num_splits(d, 1, 131072, S) == S

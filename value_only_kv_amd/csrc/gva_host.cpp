@@ -168,12 +168,13 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
   const int64_t q = kChunkQuantum;
   int64_t S = num_splits;
   if (S == 0) {
-    // Chunks of at most 2048 positions for long sequences, at least kPlanCUs / 2 (sequence,
-    // chunk) items when the batch is small, and no chunk below 256 positions.
+    // Chunks of at most 2048 positions for long sequences, and at least kPlanCUs / 2
+    // (sequence, chunk) items when the batch is small, down to chunks of kChunkQuantum
+    // positions (short sequences are latency-bound: more, shorter chunks finish sooner).
     const int64_t by_len = (max_len + 2047) / 2048;
     const int64_t by_cus = (kPlanCUs / 2 + B - 1) / B;
     S = by_len > by_cus ? by_len : by_cus;
-    const int64_t cap = (max_len + 255) / 256;
+    const int64_t cap = (max_len + q - 1) / q;
     if (S > cap) S = cap;
     if (S < 1) S = 1;
     if (S > kMaxSplits) S = kMaxSplits;

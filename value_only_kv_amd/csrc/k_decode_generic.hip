@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kHeadsPerPass = 16;   // heads of one group handled by one wave
 constexpr int kTile = 64;           // positions per tile (one per lane)
+constexpr int kPvBatch = 16;        // positions whose values are loaded together
 
 template <bool BF16>
 __device__ __forceinline__ float2 load_pair(const void *base, int64_t off) {
@@ -76,10 +77,13 @@ __device__ __forceinline__ void store_rows(const gva::DecodeArgs &a, int b, int 
   }
 }
 
-template <bool BF16, int DPL>
+// NHP: heads per wave, a power of two covering the group's heads of this pass; the heads past
+// nh are computed with a zero query and never stored, so the loops over heads have no branches.
+template <bool BF16, int DPL, int NHP>
 __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int head_passes) {
-  __shared__ float q_s[kHeadsPerPass][gva::kMaxDh + gva::kMaxDr];
-  __shared__ float p_s[kHeadsPerPass][kTile];
+  __shared__ float q_s[NHP][gva::kMaxDh + gva::kMaxDr];
+  __shared__ float p_s[NHP][kTile];
+  __shared__ int64_t vo_s[kTile];
   const int s = blockIdx.x;
   const int b = blockIdx.y;
   const int g = blockIdx.z / head_passes;
@@ -90,9 +94,9 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
   const int lane = threadIdx.x;
   const int d_h = a.d_h, d_r = a.d_r, row = d_h + d_r;
 
-  float m[kHeadsPerPass], l[kHeadsPerPass], o[kHeadsPerPass][DPL];
+  float m[NHP], l[NHP], o[NHP][DPL];
 #pragma unroll
-  for (int hh = 0; hh < kHeadsPerPass; ++hh) {
+  for (int hh = 0; hh < NHP; ++hh) {
     m[hh] = -INFINITY;
     l[hh] = 0.0f;
 #pragma unroll
@@ -114,10 +118,11 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
     return;
   }
 
-  for (int idx = lane; idx < nh * row; idx += 64) {
+  for (int idx = lane; idx < NHP * row; idx += 64) {
     const int hh = idx / row;
     const int e = idx - hh * row;
-    q_s[hh][e] = a.q_abs[(static_cast<int64_t>(b) * a.H + h0 + hh) * row + e] * a.qscale;
+    q_s[hh][e] = hh < nh ? a.q_abs[(static_cast<int64_t>(b) * a.H + h0 + hh) * row + e] * a.qscale
+                         : 0.0f;
   }
   __syncthreads();
 
@@ -133,53 +138,59 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
     const int64_t voff = blk_s * a.v_sb + static_cast<int64_t>(tc & bs_mask) * a.v_st +
                          static_cast<int64_t>(g) * a.v_sg;
     const int64_t koff = blk_s * a.kr_sb + static_cast<int64_t>(tc & bs_mask) * a.kr_st;
-    float sc[kHeadsPerPass];
+    vo_s[lane] = voff;                         // the weighted sum reads the rows from here
+    float sc[NHP];
 #pragma unroll
-    for (int hh = 0; hh < kHeadsPerPass; ++hh) sc[hh] = 0.0f;
+    for (int hh = 0; hh < NHP; ++hh) sc[hh] = 0.0f;
+#pragma unroll 16
     for (int i = 0; i < d_h; i += 2) {
       const float2 x = load_pair<BF16>(a.v, voff + i);
 #pragma unroll
-      for (int hh = 0; hh < kHeadsPerPass; ++hh)
-        if (hh < nh) sc[hh] = fmaf(q_s[hh][i], x.x, fmaf(q_s[hh][i + 1], x.y, sc[hh]));
+      for (int hh = 0; hh < NHP; ++hh) sc[hh] = fmaf(q_s[hh][i], x.x, fmaf(q_s[hh][i + 1], x.y, sc[hh]));
     }
+#pragma unroll 4
     for (int i = 0; i < d_r; i += 2) {
       const float2 x = load_pair<BF16>(a.kr, koff + i);
 #pragma unroll
-      for (int hh = 0; hh < kHeadsPerPass; ++hh)
-        if (hh < nh) sc[hh] = fmaf(q_s[hh][d_h + i], x.x, fmaf(q_s[hh][d_h + i + 1], x.y, sc[hh]));
+      for (int hh = 0; hh < NHP; ++hh)
+        sc[hh] = fmaf(q_s[hh][d_h + i], x.x, fmaf(q_s[hh][d_h + i + 1], x.y, sc[hh]));
     }
     // ---- online softmax over the tile, per head ----
 #pragma unroll
-    for (int hh = 0; hh < kHeadsPerPass; ++hh) {
-      if (hh < nh) {
-        const float sv = valid ? sc[hh] : -INFINITY;
-        const float mn = fmaxf(m[hh], gvad::wave_max(sv));
-        const float alpha = exp2f(m[hh] - mn);
-        const float p = exp2f(sv - mn);
-        l[hh] = l[hh] * alpha + gvad::wave_sum(p);
-        m[hh] = mn;
-        p_s[hh][lane] = p;
+    for (int hh = 0; hh < NHP; ++hh) {
+      const float sv = valid ? sc[hh] : -INFINITY;
+      const float mn = fmaxf(m[hh], gvad::wave_max(sv));
+      const float alpha = exp2f(m[hh] - mn);
+      const float p = exp2f(sv - mn);
+      l[hh] = l[hh] * alpha + gvad::wave_sum(p);
+      m[hh] = mn;
+      p_s[hh][lane] = p;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[hh][k] *= alpha;
-      }
+      for (int k = 0; k < DPL; ++k) o[hh][k] *= alpha;
     }
     __syncthreads();
     // ---- weighted sum: lanes over value dimensions ----
+    // The row offsets come from LDS (no block-table lookups in this loop), and the values of 16
+    // positions are loaded before their products, so a tile costs four load round trips.
     const int nt = min(kTile, c1 - t0);
-    for (int j = 0; j < nt; ++j) {
-      const int tj = t0 + j;
-      const int64_t bj = gvad::block_of(a, b, tj);
-      const int64_t bjs = bj < 0 ? 0 : bj;
-      const int64_t vo = bjs * a.v_sb + static_cast<int64_t>(tj & bs_mask) * a.v_st +
-                         static_cast<int64_t>(g) * a.v_sg;
+    for (int j0 = 0; j0 < nt; j0 += kPvBatch) {
+      float x[kPvBatch][DPL];
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) {
-        const int d = lane + 64 * k;
-        if (d < d_h) {
-          const float x = load_one<BF16>(a.v, vo + d);
+      for (int u = 0; u < kPvBatch; ++u)
 #pragma unroll
-          for (int hh = 0; hh < kHeadsPerPass; ++hh)
-            if (hh < nh) o[hh][k] = fmaf(p_s[hh][j], x, o[hh][k]);
+        for (int k = 0; k < DPL; ++k) {
+          const int d = lane + 64 * k;
+          x[u][k] = (j0 + u < nt && d < d_h) ? load_one<BF16>(a.v, vo_s[j0 + u] + d) : 0.0f;
+        }
+#pragma unroll
+      for (int u = 0; u < kPvBatch; ++u) {
+        if (j0 + u < nt) {
+#pragma unroll
+          for (int hh = 0; hh < NHP; ++hh) {
+            const float pj = p_s[hh][j0 + u];
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) o[hh][k] = fmaf(pj, x[u][k], o[hh][k]);
+          }
         }
       }
     }
@@ -306,29 +317,38 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
 
 namespace gva {
 
+template <bool BF16, int DPL>
+void launch_generic_nhp(const DecodeArgs &a, dim3 grid, int head_passes, int nhp,
+                        hipStream_t stream) {
+  switch (nhp) {
+    case 1: hipLaunchKernelGGL((k_decode_generic<BF16, DPL, 1>), grid, dim3(64), 0, stream, a, head_passes); break;
+    case 2: hipLaunchKernelGGL((k_decode_generic<BF16, DPL, 2>), grid, dim3(64), 0, stream, a, head_passes); break;
+    case 4: hipLaunchKernelGGL((k_decode_generic<BF16, DPL, 4>), grid, dim3(64), 0, stream, a, head_passes); break;
+    case 8: hipLaunchKernelGGL((k_decode_generic<BF16, DPL, 8>), grid, dim3(64), 0, stream, a, head_passes); break;
+    default: hipLaunchKernelGGL((k_decode_generic<BF16, DPL, 16>), grid, dim3(64), 0, stream, a, head_passes); break;
+  }
+}
+
+template <bool BF16>
+void launch_generic_dpl(const DecodeArgs &a, dim3 grid, int head_passes, int nhp,
+                        hipStream_t stream) {
+  switch ((a.d_h + 63) / 64) {
+    case 1: launch_generic_nhp<BF16, 1>(a, grid, head_passes, nhp, stream); break;
+    case 2: launch_generic_nhp<BF16, 2>(a, grid, head_passes, nhp, stream); break;
+    case 3: launch_generic_nhp<BF16, 3>(a, grid, head_passes, nhp, stream); break;
+    default: launch_generic_nhp<BF16, 4>(a, grid, head_passes, nhp, stream); break;
+  }
+}
+
 hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t stream) {
   const int hpg = a.H / a.G;
   const int head_passes = (hpg + kHeadsPerPass - 1) / kHeadsPerPass;
   const dim3 grid(a.num_splits, a.B, a.G * head_passes);
-  const int dpl = (a.d_h + 63) / 64;
-#define GVA_LAUNCH_GENERIC(BF, D)                                                            \
-  hipLaunchKernelGGL((k_decode_generic<BF, D>), grid, dim3(64), 0, stream, a, head_passes)
-  if (bf16) {
-    switch (dpl) {
-      case 1: GVA_LAUNCH_GENERIC(true, 1); break;
-      case 2: GVA_LAUNCH_GENERIC(true, 2); break;
-      case 3: GVA_LAUNCH_GENERIC(true, 3); break;
-      default: GVA_LAUNCH_GENERIC(true, 4); break;
-    }
-  } else {
-    switch (dpl) {
-      case 1: GVA_LAUNCH_GENERIC(false, 1); break;
-      case 2: GVA_LAUNCH_GENERIC(false, 2); break;
-      case 3: GVA_LAUNCH_GENERIC(false, 3); break;
-      default: GVA_LAUNCH_GENERIC(false, 4); break;
-    }
-  }
-#undef GVA_LAUNCH_GENERIC
+  const int nh_max = hpg < kHeadsPerPass ? hpg : kHeadsPerPass;
+  int nhp = 1;
+  while (nhp < nh_max) nhp <<= 1;
+  if (bf16) launch_generic_dpl<true>(a, grid, head_passes, nhp, stream);
+  else launch_generic_dpl<false>(a, grid, head_passes, nhp, stream);
   return hipGetLastError();
 }
 
