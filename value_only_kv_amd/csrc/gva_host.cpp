@@ -146,12 +146,13 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
   if (balanced && num_splits == 0 && B > 1 && tiles_max > 0 &&
       tiles_max < (int64_t(1) << 31) && d->G > 0) {
     // Equal ranges over all sequences' tiles: at most one pass of work-groups over the device;
-    // fewer for small batches, down to kPlanCUs / 2 ranges or ranges of kMinTilesPerRange tiles
-    // (assuming every sequence at max_len), whichever is more. A single sequence gets the same
-    // cut from the split grid, without the search for its range.
+    // fewer for small batches, down to one work-group per compute unit (kPlanCUs / nz ranges)
+    // or ranges of kMinTilesPerRange tiles (assuming every sequence at max_len), whichever is
+    // more. A single sequence gets the same cut from the split grid, without the search for
+    // its range.
     const int64_t nz = d->G / decode_waves_per_group(d->G);
     const int64_t by_size = (tiles_max + kMinTilesPerRange - 1) / kMinTilesPerRange;
-    int64_t R = by_size > kPlanCUs / 2 ? by_size : kPlanCUs / 2;
+    int64_t R = by_size > kPlanCUs / nz ? by_size : kPlanCUs / nz;
     if (R > kBalancedWorkGroups / nz) R = kBalancedWorkGroups / nz;
     if (R > tiles_max) R = tiles_max;
     if (R > kMaxSplits) R = kMaxSplits;
