@@ -17,9 +17,11 @@
 //   D[i][j]: lane j + 16 (i / 4), register i % 4.
 // Write n = lane % 16 (a row of 16 lanes) and q = lane / 16.
 //
-// One wave per (chunk, sequence, group); a work-group holds four groups of the same chunk, and
-// the work-groups of one chunk run on the same XCD, so their reads of the shared positional key
-// hit in its L2. A chunk is walked in tiles of 32 positions, two blocks of 16 (tb = 0, 1):
+// One wave per (chunk, group); a work-group holds four groups of the same chunk, and the
+// work-groups of one chunk run on the same XCD, so their reads of the shared positional key hit
+// in its L2. Chunks come from one of two work plans (see the kernel): per-sequence splits, or
+// equal ranges over the tiles of all sequences (balanced). A chunk is walked in tiles of 32
+// positions, two blocks of 16 (tb = 0, 1):
 //   1. V rows go straight from HBM into registers in A-operand form: lane (n, q) loads 16 bytes,
 //      8 consecutive dims 32 ks + 8 q .. of position 16 tb + n, for every k-step ks.
 //   2. Scores S^T[t][c] = sum_k V[t][k] Q[c][k]. The query keeps ~16 significant bits by being
@@ -38,8 +40,12 @@
 //      shift to place the hi parts.
 //   5. O^T accumulates in registers: lane (n, q) holds column n, dims 16 nb + 4 q + r; the hi
 //      and lo columns are added once, at the end.
-// Without the transposing products of a matrix-only design the kernel needs 168 registers at
-// d_h = 128, so three four-wave work-groups share a compute unit.
+// The kernel needs 168 registers at d_h = 128, so three four-wave work-groups share a compute
+// unit (transposing V with selection-matrix MFMAs instead of the LDS load needed 250).
+//
+// The same template, with GQA = true, decodes the comparator cache of a matched grouped-query
+// model (G keys and G values per token): the score then contracts key rows loaded beside the
+// value rows, and there is no positional term.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
