@@ -9,15 +9,17 @@
 // sum are [rows x (d_h + d_r)] x [(d_h + d_r) x keys] and [rows x keys] x [keys x d_h] products
 // with rows = (query, head) pairs of one value group.
 //
-// Work-group: 8 waves, 256 rows of one (sequence, group), rows ordered (query, head) with the
-// head fastest; each wave owns 2 row tiles of 16. Keys are walked in tiles of 32 positions,
+// Work-group: 16 waves (8 for d_h above 128) of one (sequence, group), each owning a tile of
+// 16 rows, rows ordered (query, head) with the head fastest; the work-group is the only one on
+// its compute unit, and its 16 waves (four per SIMD) hide each other's latencies. Keys are
+// walked in tiles of 32 positions,
 // loaded two tiles ahead into registers and staged once per work-group in LDS as natural rows
 // [v (d_h) | kr (d_r, zero-padded to 32)] (double-buffered, one barrier per tile). They serve
 //   * the scores S^T[key][row] = sum_k K[key][k] Q[row][k]: A = the natural rows, B = the
 //     absorbed query as a bf16 hi + lo pair (two products), and
 //   * the weighted sum O^T[dim][row] += sum_key V^T[dim][key] P^T[key][row]: A = V^T, read
 //     from the same rows with the transposing LDS load (ds_read_b64_tr_b16), B = P in bf16.
-// Each lane holds, per row tile, row n = lane % 16 and keys 16 tb + 4 q + r of each 16-key
+// Each lane holds row n = lane % 16 of its wave's tile and keys 16 tb + 4 q + r of each 16-key
 // block (q = lane / 16), which is the K order (q, e) -> 16 (e / 4) + 4 q + e % 4 in which the
 // transposing load delivers V^T, so P feeds the second product from the lane's own registers.
 // Accumulation and the online softmax (base-2 domain) are float32.
@@ -38,12 +40,12 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 8;
-// Row tiles of 16 per wave: two up to d_h = 128, one above (register budget).
+// One row tile of 16 per wave; 16 waves up to d_h = 128 (128 registers each, four waves per
+// SIMD), 8 above, where the query and the accumulators need more registers.
 template <int KS>
-constexpr int row_tiles() { return KS <= 4 ? 2 : 1; }
+constexpr int waves() { return KS <= 4 ? 16 : 8; }
 template <int KS>
-constexpr int rows_per_group() { return kWaves * row_tiles<KS>() * 16; }
+constexpr int rows_per_group() { return waves<KS>() * 16; }
 constexpr int kKeyTile = 32;
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -128,12 +130,12 @@ struct TileLds {
 };
 
 // A unit is 16 keys x 32 elements of the natural rows (k-step ks of key block kb); units
-// ks < KS are values, unit ks == KS the positional key. A wave stages units w, w + 8, ...
+// ks < KS are values, unit ks == KS the positional key. Wave w stages units w, w + waves, ...
 // Each lane holds 16 bytes in A-operand form: key 16 kb + n, elements 32 ks + 8 q .. + 8.
 template <int KS>
 struct Stage {
   static constexpr int kUnits = 2 * (KS + 1);
-  static constexpr int kPerWave = (kUnits + kWaves - 1) / kWaves;
+  static constexpr int kPerWave = (kUnits + waves<KS>() - 1) / waves<KS>();
   u32x4 u[kPerWave];
 };
 
@@ -146,7 +148,7 @@ __device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const int32
   const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
 #pragma unroll
   for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
-    const int unit = min(wave + kWaves * i, Stage<KS>::kUnits - 1);
+    const int unit = min(wave + waves<KS>() * i, Stage<KS>::kUnits - 1);
     const int kb = unit & 1;
     const int ks = unit >> 1;
     const int key = min(kt0 + 16 * kb + n, kend - 1);   // keys past the end repeat the last
@@ -171,7 +173,7 @@ __device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int 
   using L = TileLds<KS>;
 #pragma unroll
   for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
-    const int unit = wave + kWaves * i;
+    const int unit = wave + waves<KS>() * i;
     if (unit >= Stage<KS>::kUnits) break;              // uniform per wave
     const int kb = unit & 1;
     const int ks = unit >> 1;
@@ -180,9 +182,8 @@ __device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int 
 }
 
 template <int KS>
-__global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
+__global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p) {
   using L = TileLds<KS>;
-  constexpr int kRowTiles = row_tiles<KS>();
   constexpr int kRows = rows_per_group<KS>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][L::kElems];
   const gva::DecodeArgs &a = p.kv;
@@ -219,18 +220,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   const int cap = a.max_blocks << a.log2_bs;
   const bool seq_bad = P0 < 0 || P0 > p.max_start || P0 + C > cap;
 
-  // rows of this wave: tile rt covers rows row0 + 16 (2 wave + rt) + 0..15
-  int qpos[kRowTiles];            // position of this lane's row (as the B column n)
-  bool rvalid[kRowTiles];
-  bf16x8 QH[kRowTiles][KS + 1], QL[kRowTiles][KS + 1];   // query hi and lo parts (B operand)
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r = row0 + 16 * (kRowTiles * wave + rt) + n;
-    rvalid[rt] = r < nrows;
-    const int rc = rvalid[rt] ? r : nrows - 1;
+  // the row tile of this wave: rows row0 + 16 wave + 0..15; this lane's row (the B column) is n
+  const int r = row0 + 16 * wave + n;
+  const bool rvalid = r < nrows;
+  int qpos;                       // position of this lane's query
+  bf16x8 QH[KS + 1], QL[KS + 1];  // query hi and lo parts (B operand)
+  {
+    const int rc = rvalid ? r : nrows - 1;
     const int qi = rc / nhg;
     const int h = g * nhg + (rc - qi * nhg);
-    qpos[rt] = P0 + qi;
+    qpos = P0 + qi;
     const float *qp = p.q_abs + ((static_cast<int64_t>(b) * C + qi) * a.H + h) * row_len;
 #pragma unroll
     for (int ks = 0; ks <= KS; ++ks) {
@@ -252,20 +251,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
         hi[i] = w;
         lo[i] = pack2(x0 - low_bf16(w), x1 - high_bf16(w));
       }
-      QH[rt][ks] = as_bf16(hi);
-      QL[rt][ks] = as_bf16(lo);
+      QH[ks] = as_bf16(hi);
+      QL[ks] = as_bf16(lo);
     }
   }
 
-  f32x4 O[kRowTiles][2 * KS];
-  float m[kRowTiles], lsum[kRowTiles];
+  f32x4 O[2 * KS];
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    m[rt] = -INFINITY;
-    lsum[rt] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) O[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.0f;
 
   // keys 0 .. kend - 1 are seen by some row of this work-group
   const int last_row = min(row0 + kRows, nrows) - 1;
@@ -277,74 +271,49 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
 
   // One key tile: scores, mask, online softmax, weighted sum, on the LDS rows in nat.
   auto tile = [&](const uint16_t *nat, int kt0) {
-    f32x4 S[kRowTiles][2];
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) S[rt][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks <= KS; ++ks) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const u32x4 ka = *reinterpret_cast<const u32x4 *>(nat + (16 * tb + n) * L::kNatStride +
                                                           32 * ks + 8 * q);
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
-          S[rt][tb] = mfma(as_bf16(ka), QH[rt][ks], S[rt][tb]);
-          S[rt][tb] = mfma(as_bf16(ka), QL[rt][ks], S[rt][tb]);
-        }
+        S[tb] = mfma(as_bf16(ka), QH[ks], S[tb]);
+        S[tb] = mfma(as_bf16(ka), QL[ks], S[tb]);
       }
     }
-    // causal mask (only tiles that reach past the first query), online softmax; the two row
-    // tiles go through each stage together so their latencies overlap
-    const bool need_mask = kt0 + kKeyTile - 1 > first_q;
-    if (need_mask) {
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kt0 + 16 * tb + 4 * q + r > qpos[rt]) S[rt][tb][r] = -INFINITY;
-    }
-    float mt[kRowTiles];
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
-      mt[rt] = fmaxf(fmaxf(fmaxf(S[rt][0][0], S[rt][0][1]), fmaxf(S[rt][0][2], S[rt][0][3])),
-                     fmaxf(fmaxf(S[rt][1][0], S[rt][1][1]), fmaxf(S[rt][1][2], S[rt][1][3])));
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) mt[rt] = gvad::xor16_max(mt[rt]);
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) mt[rt] = gvad::xor32_max(mt[rt]);
-    u32x4 PB[kRowTiles];
-    float alpha[kRowTiles];
-    bool rescale = false;
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      const float mn = fmaxf(m[rt], mt[rt]);
-      // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
-      const float mref = mn == -INFINITY ? 0.0f : mn;
-      alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mref);
-      rescale |= alpha[rt] != 1.0f;
-      float pv[8];
-      float ps = 0.0f;
+    // causal mask (only tiles that reach past the first query), online softmax
+    if (kt0 + kKeyTile - 1 > first_q) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[4 * tb + r] = __builtin_amdgcn_exp2f(S[rt][tb][r] - mref);
-          ps += pv[4 * tb + r];
-        }
-      lsum[rt] = lsum[rt] * alpha[rt] + ps;
-      m[rt] = mn;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) PB[rt][i] = pack2(pv[2 * i], pv[2 * i + 1]);
+        for (int e = 0; e < 4; ++e)
+          if (kt0 + 16 * tb + 4 * q + e > qpos) S[tb][e] = -INFINITY;
     }
-    if (__any(rescale)) {
+    float mt = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+    mt = gvad::xor32_max(gvad::xor16_max(mt));
+    const float mn = fmaxf(m, mt);
+    // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
+    const float mref = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
+    float pv[8];
+    float ps = 0.0f;
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha[rt];
+      for (int e = 0; e < 4; ++e) {
+        pv[4 * tb + e] = __builtin_amdgcn_exp2f(S[tb][e] - mref);
+        ps += pv[4 * tb + e];
+      }
+    lsum = lsum * alpha + ps;
+    m = mn;
+    u32x4 PB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) PB[i] = pack2(pv[2 * i], pv[2 * i + 1]);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) O[i] *= alpha;
     }
     // O^T[dim][row] += V^T[dim][key] P^T[key][row]; V^T of dims 16 nb .. read transposed:
     // the first read gives keys 4 q .. + 3 of block 0, the second the same of block 1
@@ -354,8 +323,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
       const i16x4 v1 = read_tr(nat + tr_off + 16 * L::kNatStride + 16 * nb);
       const bf16x8 VT = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) O[rt][nb] = mfma(VT, as_bf16(PB[rt]), O[rt][nb]);
+      O[nb] = mfma(VT, as_bf16(PB), O[nb]);
     }
   };
 
@@ -384,12 +352,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     }
   }
 
-  // ---- epilogue: lane (n, q) holds row n of each tile, dims 16 nb + 4 q + r ----
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const float lt = gvad::xor32_sum(gvad::xor16_sum(lsum[rt]));
-    if (!rvalid[rt]) continue;
-    const int r = row0 + 16 * (kRowTiles * wave + rt) + n;
+  // ---- epilogue: lane (n, q) holds row n, dims 16 nb + 4 q + e ----
+  const float lt = gvad::xor32_sum(gvad::xor16_sum(lsum));
+  if (rvalid) {
     const int qi = r / nhg;
     const int h = g * nhg + (r - qi * nhg);
     const int64_t orow = (static_cast<int64_t>(b) * C + qi) * a.H + h;
@@ -397,12 +362,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
     for (int nb = 0; nb < 2 * KS; ++nb) {
-      f32x4 v = O[rt][nb] * inv;
+      f32x4 v = O[nb] * inv;
       if (seq_bad) v = f32x4{qnan, qnan, qnan, qnan};
       *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
     }
     if (p.lse && q == 0)
-      p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (m[rt] + log2f(lt)) * gvad::kLn2 : -INFINITY);
+      p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (m + log2f(lt)) * gvad::kLn2 : -INFINITY);
   }
   if (seq_bad && threadIdx.x == 0 && rb == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
 }
@@ -421,16 +386,15 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream) {
   const int nrows = C * (a.H / a.G);
   const int64_t pairs = static_cast<int64_t>(a.G) * a.B;
   auto grid = [&](int rows) { return dim3(static_cast<unsigned>((nrows + rows - 1) / rows * pairs)); };
-  const dim3 block(64 * kWaves);
   switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL(k_prefill<1>, grid(rows_per_group<1>()), block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(k_prefill<2>, grid(rows_per_group<2>()), block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(k_prefill<3>, grid(rows_per_group<3>()), block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(k_prefill<4>, grid(rows_per_group<4>()), block, 0, stream, p); break;
-    case 5: hipLaunchKernelGGL(k_prefill<5>, grid(rows_per_group<5>()), block, 0, stream, p); break;
-    case 6: hipLaunchKernelGGL(k_prefill<6>, grid(rows_per_group<6>()), block, 0, stream, p); break;
-    case 7: hipLaunchKernelGGL(k_prefill<7>, grid(rows_per_group<7>()), block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(k_prefill<8>, grid(rows_per_group<8>()), block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(k_prefill<1>, grid(rows_per_group<1>()), dim3(64 * waves<1>()), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(k_prefill<2>, grid(rows_per_group<2>()), dim3(64 * waves<2>()), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(k_prefill<3>, grid(rows_per_group<3>()), dim3(64 * waves<3>()), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(k_prefill<4>, grid(rows_per_group<4>()), dim3(64 * waves<4>()), 0, stream, p); break;
+    case 5: hipLaunchKernelGGL(k_prefill<5>, grid(rows_per_group<5>()), dim3(64 * waves<5>()), 0, stream, p); break;
+    case 6: hipLaunchKernelGGL(k_prefill<6>, grid(rows_per_group<6>()), dim3(64 * waves<6>()), 0, stream, p); break;
+    case 7: hipLaunchKernelGGL(k_prefill<7>, grid(rows_per_group<7>()), dim3(64 * waves<7>()), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(k_prefill<8>, grid(rows_per_group<8>()), dim3(64 * waves<8>()), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
