@@ -130,8 +130,11 @@ struct TileLds {
 };
 
 // A unit is 16 keys x 32 elements of the natural rows (k-step ks of key block kb); units
-// ks < KS are values, unit ks == KS the positional key. Wave w stages units w, w + waves, ...
-// Each lane holds 16 bytes in A-operand form: key 16 kb + n, elements 32 ks + 8 q .. + 8.
+// ks < KS are values, unit ks == KS the positional key. Wave w stages units w, w + waves, ...;
+// waves past the last unit load a copy of it and store nothing. Each lane holds 16 bytes in
+// A-operand form: key 16 kb + n, elements 32 ks + 8 q .. + 8. Every load is unconditional
+// (keys past the end repeat the last), so the compiler can count the loads in flight exactly
+// and wait only for the one it needs.
 template <int KS>
 struct Stage {
   static constexpr int kUnits = 2 * (KS + 1);
@@ -139,8 +142,33 @@ struct Stage {
   u32x4 u[kPerWave];
 };
 
+// Block-table entries of the keys a wave's units read in one tile. They are loaded one stage
+// before the data loads that use them, so that waiting for them does not also wait for the
+// tile still in flight (memory loads complete in order).
 template <int KS>
-__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const int32_t *__restrict__ bt,
+struct StagePages {
+  int32_t pb[Stage<KS>::kPerWave];
+};
+
+template <int KS>
+__device__ __forceinline__ int stage_unit(int wave, int i) {
+  return min(wave + waves<KS>() * i, Stage<KS>::kUnits - 1);
+}
+// keys past the end repeat the last
+__device__ __forceinline__ int stage_key(int kt0, int unit, int n, int kend) {
+  return min(kt0 + 16 * (unit & 1) + n, kend - 1);
+}
+
+template <int KS>
+__device__ __forceinline__ void stage_pages(const gva::DecodeArgs &a, const int32_t *__restrict__ bt,
+                                            int kt0, int kend, int wave, int n, StagePages<KS> &pg) {
+#pragma unroll
+  for (int i = 0; i < Stage<KS>::kPerWave; ++i)
+    pg.pb[i] = bt[stage_key(kt0, stage_unit<KS>(wave, i), n, kend) >> a.log2_bs];
+}
+
+template <int KS>
+__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const StagePages<KS> &pg,
                                            int g, int kt0, int kend, int wave, int n, int q,
                                            Stage<KS> &st) {
   const int mask = (1 << a.log2_bs) - 1;
@@ -148,27 +176,21 @@ __device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const int32
   const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
 #pragma unroll
   for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
-    const int unit = min(wave + waves<KS>() * i, Stage<KS>::kUnits - 1);
-    const int kb = unit & 1;
+    const int unit = stage_unit<KS>(wave, i);
     const int ks = unit >> 1;
-    const int key = min(kt0 + 16 * kb + n, kend - 1);   // keys past the end repeat the last
-    const int32_t pb = bt[key >> a.log2_bs];
+    const int32_t pb = pg.pb[i];
     const int64_t blk = (pb >= 0 && static_cast<int64_t>(pb) < a.num_blocks) ? pb : 0;
-    const int64_t row = key & mask;
-    if (ks < KS) {
-      st.u[i] = *reinterpret_cast<const u32x4 *>(vbase + blk * a.v_sb + row * a.v_st +
-                                                 static_cast<int64_t>(g) * a.v_sg + 32 * ks + 8 * q);
-    } else {
-      const int kq = min(8 * q, a.d_r - 8);
-      u32x4 w = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + kq);
-      if (8 * q >= a.d_r) w = u32x4{0u, 0u, 0u, 0u};   // zero padding up to 32
-      st.u[i] = w;
-    }
+    const int64_t row = stage_key(kt0, unit, n, kend) & mask;
+    // lanes with 8 q >= d_r read the last 8 positional-key elements; the store zeroes them
+    const uint16_t *src =
+        ks < KS ? vbase + blk * a.v_sb + row * a.v_st + static_cast<int64_t>(g) * a.v_sg + 32 * ks + 8 * q
+                : kbase + blk * a.kr_sb + row * a.kr_st + min(8 * q, a.d_r - 8);
+    st.u[i] = *reinterpret_cast<const u32x4 *>(src);
   }
 }
 
 template <int KS>
-__device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int q,
+__device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int q, int d_r,
                                             const Stage<KS> &st) {
   using L = TileLds<KS>;
 #pragma unroll
@@ -177,7 +199,9 @@ __device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int 
     if (unit >= Stage<KS>::kUnits) break;              // uniform per wave
     const int kb = unit & 1;
     const int ks = unit >> 1;
-    *reinterpret_cast<u32x4 *>(nat + (16 * kb + n) * L::kNatStride + 32 * ks + 8 * q) = st.u[i];
+    u32x4 w = st.u[i];
+    if (ks == KS && 8 * q >= d_r) w = u32x4{0u, 0u, 0u, 0u};   // zero padding up to 32
+    *reinterpret_cast<u32x4 *>(nat + (16 * kb + n) * L::kNatStride + 32 * ks + 8 * q) = w;
   }
 }
 
@@ -188,7 +212,7 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][L::kElems];
   const gva::DecodeArgs &a = p.kv;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int n = lane & 15;
   const int q = lane >> 4;
   const int nhg = a.H / a.G;
@@ -332,22 +356,29 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
     // be stored into the other LDS buffer) and tile i + 2 is in flight. The two register stages
     // alternate roles, so the loop is unrolled by two.
     Stage<KS> s0, s1;
-    stage_load<KS>(a, bt, g, 0, kend, wave, n, q, s0);
-    if (kKeyTile < kend) stage_load<KS>(a, bt, g, kKeyTile, kend, wave, n, q, s1);
-    stage_store<KS>(lds[0], wave, n, q, s0);
+    StagePages<KS> p0, p1;
+    stage_pages<KS>(a, bt, 0, kend, wave, n, p0);
+    stage_pages<KS>(a, bt, kKeyTile, kend, wave, n, p1);
+    stage_load<KS>(a, p0, g, 0, kend, wave, n, q, s0);
+    stage_pages<KS>(a, bt, 2 * kKeyTile, kend, wave, n, p0);
+    stage_load<KS>(a, p1, g, kKeyTile, kend, wave, n, q, s1);
+    stage_pages<KS>(a, bt, 3 * kKeyTile, kend, wave, n, p1);
+    stage_store<KS>(lds[0], wave, n, q, a.d_r, s0);
     __syncthreads();
     for (int kt0 = 0; kt0 < kend; kt0 += 2 * kKeyTile) {
-      // tile kt0 in lds[0]; tile kt0 + 32 in s1; s0 free
-      if (kt0 + 2 * kKeyTile < kend) stage_load<KS>(a, bt, g, kt0 + 2 * kKeyTile, kend, wave, n, q, s0);
+      // tile kt0 in lds[0]; tile kt0 + 32 in s1; s0 free; p0 holds the pages of kt0 + 64
+      stage_load<KS>(a, p0, g, kt0 + 2 * kKeyTile, kend, wave, n, q, s0);
+      stage_pages<KS>(a, bt, kt0 + 4 * kKeyTile, kend, wave, n, p0);
       tile(lds[0], kt0);
       if (kt0 + kKeyTile >= kend) break;               // uniform per work-group
-      stage_store<KS>(lds[1], wave, n, q, s1);
+      stage_store<KS>(lds[1], wave, n, q, a.d_r, s1);
       __syncthreads();
-      // tile kt0 + 32 in lds[1]; tile kt0 + 64 in s0; s1 free
-      if (kt0 + 3 * kKeyTile < kend) stage_load<KS>(a, bt, g, kt0 + 3 * kKeyTile, kend, wave, n, q, s1);
+      // tile kt0 + 32 in lds[1]; tile kt0 + 64 in s0; s1 free; p1 holds the pages of kt0 + 96
+      stage_load<KS>(a, p1, g, kt0 + 3 * kKeyTile, kend, wave, n, q, s1);
+      stage_pages<KS>(a, bt, kt0 + 5 * kKeyTile, kend, wave, n, p1);
       tile(lds[1], kt0 + kKeyTile);
       if (kt0 + 2 * kKeyTile >= kend) break;
-      stage_store<KS>(lds[0], wave, n, q, s0);
+      stage_store<KS>(lds[0], wave, n, q, a.d_r, s0);
       __syncthreads();
     }
   }
