@@ -22,7 +22,9 @@
 // Each lane holds row n = lane % 16 of its wave's tile and keys 16 tb + 4 q + r of each 16-key
 // block (q = lane / 16), which is the K order (q, e) -> 16 (e / 4) + 4 q + e % 4 in which the
 // transposing load delivers V^T, so P feeds the second product from the lane's own registers.
-// Accumulation and the online softmax (base-2 domain) are float32.
+// Accumulation and the online softmax (base-2 domain) are float32. The softmax keeps a lazily
+// raised reference maximum per row: the scores accumulate on top of minus the reference, and the
+// reference (with the rescaling of the sums) moves only when a score passes it by more than 8.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -65,6 +67,30 @@ __device__ __forceinline__ float high_bf16(unsigned w) { return __uint_as_float(
 __device__ __forceinline__ i16x4 read_tr(const uint16_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
+
+// Plain v_max_f32 / v_max3_f32: scores come straight from the matrix cores or are -inf, never
+// signalling NaNs, so the operand canonicalisation the compiler adds around fmaxf is not needed.
+__device__ __forceinline__ float max2(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ float max3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+// Row maximum over the 16-lane groups (lanes n, n + 16, n + 32, n + 48 hold one row).
+__device__ __forceinline__ float row_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
+// The reference maximum of a row is raised only when a score passes it by more than this
+// (base-2 domain), so the unnormalised probabilities stay below 2^8.
+constexpr float kLazyRescale = 8.0f;
 
 // ---- appending the chunk -----------------------------------------------------------------
 
@@ -167,25 +193,46 @@ __device__ __forceinline__ void stage_pages(const gva::DecodeArgs &a, const int3
     pg.pb[i] = bt[stage_key(kt0, stage_unit<KS>(wave, i), n, kend) >> a.log2_bs];
 }
 
+// Where this lane's units read: a fixed base pointer and the per-block and per-token strides of
+// the value or positional-key rows (the units, and so the choice, are fixed per wave).
 template <int KS>
-__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const StagePages<KS> &pg,
-                                           int g, int kt0, int kend, int wave, int n, int q,
-                                           Stage<KS> &st) {
-  const int mask = (1 << a.log2_bs) - 1;
-  const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
-  const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
+struct StageSrc {
+  const uint16_t *base[Stage<KS>::kPerWave];
+  int64_t sb[Stage<KS>::kPerWave], st[Stage<KS>::kPerWave];
+};
+
+template <int KS>
+__device__ __forceinline__ StageSrc<KS> stage_src(const gva::DecodeArgs &a, int g, int wave, int q) {
+  StageSrc<KS> src;
 #pragma unroll
   for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
-    const int unit = stage_unit<KS>(wave, i);
-    const int ks = unit >> 1;
+    const int ks = stage_unit<KS>(wave, i) >> 1;
+    if (ks < KS) {
+      src.base[i] = static_cast<const uint16_t *>(a.v) + static_cast<int64_t>(g) * a.v_sg + 32 * ks + 8 * q;
+      src.sb[i] = a.v_sb;
+      src.st[i] = a.v_st;
+    } else {
+      // lanes with 8 q >= d_r read the last 8 positional-key elements; the store zeroes them
+      src.base[i] = static_cast<const uint16_t *>(a.kr) + min(8 * q, a.d_r - 8);
+      src.sb[i] = a.kr_sb;
+      src.st[i] = a.kr_st;
+    }
+  }
+  return src;
+}
+
+template <int KS>
+__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const StageSrc<KS> &src,
+                                           const StagePages<KS> &pg, int kt0, int kend, int wave,
+                                           int n, Stage<KS> &st) {
+  const int mask = (1 << a.log2_bs) - 1;
+#pragma unroll
+  for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
     const int32_t pb = pg.pb[i];
-    const int64_t blk = (pb >= 0 && static_cast<int64_t>(pb) < a.num_blocks) ? pb : 0;
-    const int64_t row = stage_key(kt0, unit, n, kend) & mask;
-    // lanes with 8 q >= d_r read the last 8 positional-key elements; the store zeroes them
-    const uint16_t *src =
-        ks < KS ? vbase + blk * a.v_sb + row * a.v_st + static_cast<int64_t>(g) * a.v_sg + 32 * ks + 8 * q
-                : kbase + blk * a.kr_sb + row * a.kr_st + min(8 * q, a.d_r - 8);
-    st.u[i] = *reinterpret_cast<const u32x4 *>(src);
+    // block ids are below 2^31 (checked on the host): one unsigned compare covers both ends
+    const int64_t blk = static_cast<uint32_t>(pb) < static_cast<uint32_t>(a.num_blocks) ? pb : 0;
+    const int64_t row = stage_key(kt0, stage_unit<KS>(wave, i), n, kend) & mask;
+    st.u[i] = *reinterpret_cast<const u32x4 *>(src.base[i] + blk * src.sb[i] + row * src.st[i]);
   }
 }
 
@@ -283,7 +330,11 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
   f32x4 O[2 * KS];
 #pragma unroll
   for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.0f;
+  // Online softmax with a lazily raised reference: mref is the row's reference maximum (base 2),
+  // -inf until the row's first unmasked key. The scores of a tile accumulate on top of negm =
+  // -mref (0 while mref = -inf), so the probabilities are exp2 of the accumulators directly.
+  float mref = -INFINITY, lsum = 0.0f;
+  f32x4 negm = {0.f, 0.f, 0.f, 0.f};
 
   // keys 0 .. kend - 1 are seen by some row of this work-group
   const int last_row = min(row0 + kRows, nrows) - 1;
@@ -295,7 +346,7 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
 
   // One key tile: scores, mask, online softmax, weighted sum, on the LDS rows in nat.
   auto tile = [&](const uint16_t *nat, int kt0) {
-    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 S[2] = {negm, negm};
 #pragma unroll
     for (int ks = 0; ks <= KS; ++ks) {
 #pragma unroll
@@ -306,7 +357,7 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
         S[tb] = mfma(as_bf16(ka), QL[ks], S[tb]);
       }
     }
-    // causal mask (only tiles that reach past the first query), online softmax
+    // causal mask (only tiles that reach past the first query)
     if (kt0 + kKeyTile - 1 > first_q) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -314,31 +365,33 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
         for (int e = 0; e < 4; ++e)
           if (kt0 + 16 * tb + 4 * q + e > qpos) S[tb][e] = -INFINITY;
     }
-    float mt = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-    mt = gvad::xor32_max(gvad::xor16_max(mt));
-    const float mn = fmaxf(m, mt);
-    // a row whose keys so far are all masked keeps m = -inf; use 0 as its reference
-    const float mref = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
+    // tile maximum relative to the reference
+    const float mt = row_max(max2(max3(S[0][0], S[0][1], S[0][2]),
+                                  max3(S[0][3], S[1][0], max3(S[1][1], S[1][2], S[1][3]))));
+    const bool raise = mt > kLazyRescale || (mref == -INFINITY && mt != -INFINITY);
+    if (__any(raise)) {   // rare after the first tiles: move the reference to the tile maximum
+      const float delta = raise ? mt : 0.0f;
+      const float mnew = mref == -INFINITY ? mt : mref + delta;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;   // 0 from -inf
+      mref = raise ? mnew : mref;
+      negm = raise ? f32x4{-mnew, -mnew, -mnew, -mnew} : negm;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) O[i] *= alpha;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) S[tb] -= delta;
+    }
     float pv[8];
-    float ps = 0.0f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pv[4 * tb + e] = __builtin_amdgcn_exp2f(S[tb][e] - mref);
-        ps += pv[4 * tb + e];
+        pv[4 * tb + e] = __builtin_amdgcn_exp2f(S[tb][e]);
+        lsum += pv[4 * tb + e];
       }
-    lsum = lsum * alpha + ps;
-    m = mn;
     u32x4 PB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) PB[i] = pack2(pv[2 * i], pv[2 * i + 1]);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) O[i] *= alpha;
-    }
     // O^T[dim][row] += V^T[dim][key] P^T[key][row]; V^T of dims 16 nb .. read transposed:
     // the first read gives keys 4 q .. + 3 of block 0, the second the same of block 1
 #pragma unroll
@@ -354,32 +407,43 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
   if (kend > 0) {
     // Tiles are loaded two ahead: while tile i is computed, tile i + 1 waits in registers (to
     // be stored into the other LDS buffer) and tile i + 2 is in flight. The two register stages
-    // alternate roles, so the loop is unrolled by two.
+    // alternate roles, so the loop runs over pairs of tiles; it has no early exit, so that the
+    // number of loads in flight is the same on every path into its head, and the last one or
+    // two tiles follow it. Loads past the last tile read its keys again and are not used.
+    const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+    const StageSrc<KS> src = stage_src<KS>(a, g, wave, q);
     Stage<KS> s0, s1;
     StagePages<KS> p0, p1;
     stage_pages<KS>(a, bt, 0, kend, wave, n, p0);
     stage_pages<KS>(a, bt, kKeyTile, kend, wave, n, p1);
-    stage_load<KS>(a, p0, g, 0, kend, wave, n, q, s0);
+    stage_load<KS>(a, src, p0, 0, kend, wave, n, s0);
     stage_pages<KS>(a, bt, 2 * kKeyTile, kend, wave, n, p0);
-    stage_load<KS>(a, p1, g, kKeyTile, kend, wave, n, q, s1);
+    stage_load<KS>(a, src, p1, kKeyTile, kend, wave, n, s1);
     stage_pages<KS>(a, bt, 3 * kKeyTile, kend, wave, n, p1);
     stage_store<KS>(lds[0], wave, n, q, a.d_r, s0);
     __syncthreads();
-    for (int kt0 = 0; kt0 < kend; kt0 += 2 * kKeyTile) {
-      // tile kt0 in lds[0]; tile kt0 + 32 in s1; s0 free; p0 holds the pages of kt0 + 64
-      stage_load<KS>(a, p0, g, kt0 + 2 * kKeyTile, kend, wave, n, q, s0);
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      const int kt0 = t * kKeyTile;
+      // tile t in lds[0]; tile t + 1 in s1; s0 free; p0 holds the pages of tile t + 2
+      stage_load<KS>(a, src, p0, kt0 + 2 * kKeyTile, kend, wave, n, s0);
       stage_pages<KS>(a, bt, kt0 + 4 * kKeyTile, kend, wave, n, p0);
       tile(lds[0], kt0);
-      if (kt0 + kKeyTile >= kend) break;               // uniform per work-group
       stage_store<KS>(lds[1], wave, n, q, a.d_r, s1);
       __syncthreads();
-      // tile kt0 + 32 in lds[1]; tile kt0 + 64 in s0; s1 free; p1 holds the pages of kt0 + 96
-      stage_load<KS>(a, p1, g, kt0 + 3 * kKeyTile, kend, wave, n, q, s1);
+      // tile t + 1 in lds[1]; tile t + 2 in s0; s1 free; p1 holds the pages of tile t + 3
+      stage_load<KS>(a, src, p1, kt0 + 3 * kKeyTile, kend, wave, n, s1);
       stage_pages<KS>(a, bt, kt0 + 5 * kKeyTile, kend, wave, n, p1);
       tile(lds[1], kt0 + kKeyTile);
-      if (kt0 + 2 * kKeyTile >= kend) break;
       stage_store<KS>(lds[0], wave, n, q, a.d_r, s0);
       __syncthreads();
+    }
+    // one or two tiles left: tile t in lds[0], tile t + 1 (if any) in s1
+    tile(lds[0], t * kKeyTile);
+    if (t + 1 < ntiles) {                              // uniform per work-group
+      stage_store<KS>(lds[1], wave, n, q, a.d_r, s1);
+      __syncthreads();
+      tile(lds[1], (t + 1) * kKeyTile);
     }
   }
 
@@ -398,7 +462,7 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
       *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
     }
     if (p.lse && q == 0)
-      p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (m + log2f(lt)) * gvad::kLn2 : -INFINITY);
+      p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (mref + log2f(lt)) * gvad::kLn2 : -INFINITY);
   }
   if (seq_bad && threadIdx.x == 0 && rb == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
 }
