@@ -178,6 +178,29 @@ def test_split_counts_one_to_many(kernel):
         check_output(out, ref, "bf16", f"S={S}")
 
 
+def test_combine_many_rows_for_one_sequence():
+    """A batch whose plan has few partial rows per sequence on average (so the combine takes one
+    wave per (sequence, head)) but one long sequence among short ones, which spans more than 64
+    ranges: the combine walks its rows 64 at a time."""
+    c = _ragged_case(B=32, lo=4096, hi=4100)
+    lens = np.array([4096] + [1 + 3 * i for i in range(31)])
+    ml = int(lens.max())
+    R = gb.gva_decode_num_ranges(c.cdims, c.w.B, ml)
+    assert R // c.w.B + 1 <= 16
+    tiles = (lens + 31) // 32
+    P = np.concatenate([[0], np.cumsum(tiles)])
+    T = int(P[-1])
+    Re = min(R, T)
+    rows_long = (int(P[1]) * Re - 1) // T - ((int(P[0]) + 1) * Re - 1) // T + 1
+    assert rows_long > 64
+    q = synth.direct_q_abs(c.w, c.w.B)
+    out, lse = c.decode(lens, q, num_splits=0, kernel=MFMA, max_len=ml)
+    ref, ref_lse = c.oracle_decode(lens, q.astype(np.float64))
+    check_output(out, ref, "bf16", "one long sequence among short ones")
+    ok, e = lse_ok(lse, ref_lse, 1e-3)
+    assert ok, e
+
+
 def test_balanced_ranges_edge_lengths():
     """The matrix-core kernel's automatic plan cuts the tiles of all sequences into equal ranges:
     empty sequences, single positions and tile-boundary lengths, and a plan with more ranges than

@@ -208,6 +208,8 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
 // chunk weights 2^(m_c - m*) are formed once in LDS, wave w sums chunks w, w + nw, ... with its
 // lanes over the slice's dims, and the waves' sums meet in LDS.
 constexpr int kCombineMaxWaves = 16;
+// partial rows per sequence up to which the combine takes one wave per (sequence, head)
+constexpr int kCombineWaveRows = 16;
 
 __device__ __forceinline__ float block_reduce(float v, float *scratch, int nw, bool is_max) {
   v = is_max ? gvad::wave_max(v) : gvad::wave_sum(v);
@@ -219,6 +221,32 @@ __device__ __forceinline__ float block_reduce(float v, float *scratch, int nw, b
   for (int i = 1; i < nw; ++i) r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
   __syncthreads();
   return r;
+}
+
+// The partial rows of (sequence b, head h): rows row0 + s H for s < ns.
+__device__ __forceinline__ void partial_rows(const gva::DecodeArgs &a, int b, int h, int len,
+                                             int &ns, int64_t &row0) {
+  if (a.num_ranges > 0) {
+    // balanced mode: the ranges holding tiles [P[b], P[b + 1]) are those containing its first
+    // and last tile (with Re = min(R, T) ranges, range r starts at tile r T / Re and is never
+    // empty), and range r wrote row (r + b) H + h
+    const int64_t pb = a.tile_prefix[b];
+    const int64_t pe = a.tile_prefix[b + 1];
+    const int64_t T = a.tile_prefix[a.B];
+    const int64_t Re = T < a.num_ranges ? T : a.num_ranges;
+    if (pe <= pb) {
+      ns = 0;
+      row0 = 0;
+    } else {
+      const int64_t r_first = ((pb + 1) * Re - 1) / T;
+      const int64_t r_last = (pe * Re - 1) / T;
+      ns = static_cast<int>(r_last - r_first + 1);
+      row0 = (r_first + b) * a.H + h;
+    }
+  } else {
+    ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
+    row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;
+  }
 }
 
 __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeArgs a) {
@@ -247,30 +275,9 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
       gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
     return;
   }
-  // the sequence's partials: rows row0 + s H for s < ns
   int ns;
   int64_t row0;
-  if (a.num_ranges > 0) {
-    // balanced mode: the ranges holding tiles [P[b], P[b + 1]) are those containing its first
-    // and last tile (with Re = min(R, T) ranges, range r starts at tile r T / Re and is never
-    // empty), and range r wrote row (r + b) H + h
-    const int64_t pb = a.tile_prefix[b];
-    const int64_t pe = a.tile_prefix[b + 1];
-    const int64_t T = a.tile_prefix[a.B];
-    const int64_t Re = T < a.num_ranges ? T : a.num_ranges;
-    if (pe <= pb) {
-      ns = 0;
-      row0 = 0;
-    } else {
-      const int64_t r_first = ((pb + 1) * Re - 1) / T;
-      const int64_t r_last = (pe * Re - 1) / T;
-      ns = static_cast<int>(r_last - r_first + 1);
-      row0 = (r_first + b) * a.H + h;
-    }
-  } else {
-    ns = min(a.num_splits, (len + a.chunk - 1) / a.chunk);
-    row0 = static_cast<int64_t>(b) * a.num_splits * a.H + h;
-  }
+  partial_rows(a, b, h, len, ns, row0);
   if (ns == 0) {
     if (wave == 0 && dim_ok) dst[d] = 0.0f;
     if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
@@ -313,6 +320,78 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = poison ? qnan : (mx + log2f(L)) * gvad::kLn2;
 }
 
+
+// One wave per (sequence, head), four heads per work-group, for sequences with few partial rows
+// (the balanced plan gives about R / B + 1 of them): no LDS and no barriers, so the chain of
+// dependent loads is the length and prefix, then m, l and o. Lane s holds row s's m and l (rows
+// are taken 64 at a time); lane i accumulates dims i, i + 64, ... of the output. Same
+// arithmetic as k_combine: m and lse in the base-2 domain, weights 2^(m_s - max).
+template <int DPL>
+__global__ __launch_bounds__(256) void k_combine_wave(gva::DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (h >= a.H) return;                                // uniform per wave
+  const float qnan = __int_as_float(0x7fc00000);
+  float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
+  float *lse = a.lse ? a.lse + static_cast<int64_t>(b) * a.H + h : nullptr;
+  const int len = a.seq_len[b];
+  const int cap = a.max_blocks << a.log2_bs;
+  if (len < 0 || len > a.max_len || len > cap) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = qnan;
+    if (lse && lane == 0) *lse = qnan;
+    if (a.num_ranges > 0 && lane == 0 && h == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+    return;
+  }
+  int ns;
+  int64_t row0;
+  partial_rows(a, b, h, len, ns, row0);
+  const int64_t step = a.H;                            // rows of one (sequence, head) are H apart
+  // maximum of m over the rows (and whether any is NaN)
+  float mx = -INFINITY;
+  bool poison = false;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float ms = s0 + lane < ns ? a.part_m[row0 + (s0 + lane) * step] : -INFINITY;
+    poison |= __any(isnan(ms));
+    mx = fmaxf(mx, gvad::wave_max(ms));
+  }
+  float acc[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
+  float L = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.0f;
+    if (s < ns) {
+      w = exp2f(a.part_m[row0 + s * step] - mx);
+      L += a.part_l[row0 + s * step] * w;
+    }
+    const int nc = min(64, ns - s0);
+    const float *po = a.part_o + (row0 + static_cast<int64_t>(s0) * step) * a.d_h + lane;
+#pragma unroll 4
+    for (int j = 0; j < nc; ++j) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+      for (int k = 0; k < DPL; ++k)
+        if (lane + 64 * k < a.d_h) acc[k] = fmaf(po[j * step * a.d_h + 64 * k], wj, acc[k]);
+    }
+  }
+  L = gvad::wave_sum(L);
+  if (ns == 0) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = 0.0f;
+    if (lse && lane == 0) *lse = -INFINITY;
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k)
+    if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = poison ? qnan : acc[k] / L;
+  if (lse && lane == 0) *lse = poison ? qnan : (mx + log2f(L)) * gvad::kLn2;
+}
+
 }  // namespace
 
 namespace gva {
@@ -353,8 +432,19 @@ hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t str
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  // waves grow with the partials per sequence (balanced mode: about R / B + 1 of them)
+  // waves grow with the partials per sequence (balanced mode: about R / B + 1 of them); with
+  // few of them, one wave per (sequence, head)
   const int per_seq = a.num_ranges > 0 ? a.num_ranges / a.B + 1 : a.num_splits;
+  if (per_seq <= kCombineWaveRows) {
+    const dim3 grid((a.H + 3) / 4, a.B);
+    switch ((a.d_h + 63) / 64) {
+      case 1: hipLaunchKernelGGL(k_combine_wave<1>, grid, dim3(256), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(k_combine_wave<2>, grid, dim3(256), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(k_combine_wave<3>, grid, dim3(256), 0, stream, a); break;
+      default: hipLaunchKernelGGL(k_combine_wave<4>, grid, dim3(256), 0, stream, a); break;
+    }
+    return hipGetLastError();
+  }
   int nw = per_seq / 16;
   nw = nw < 1 ? 1 : (nw > kCombineMaxWaves ? kCombineMaxWaves : nw);
   hipLaunchKernelGGL(k_combine, dim3((a.d_h + 63) / 64, a.H, a.B), dim3(64 * nw), 0, stream, a);
