@@ -322,12 +322,15 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
 
 
 // One wave per (sequence, head), four heads per work-group, for sequences with few partial rows
-// (the balanced plan gives about R / B + 1 of them): no LDS and no barriers, so the chain of
-// dependent loads is the length and prefix, then m, l and o. Lane s holds row s's m and l (rows
-// are taken 64 at a time); lane i accumulates dims i, i + 64, ... of the output. Same
-// arithmetic as k_combine: m and lse in the base-2 domain, weights 2^(m_s - max).
+// (the balanced plan gives about R / B + 1 of them): no LDS and no barriers. The length and the
+// tile prefix are loaded together; then m, l and the first kPre rows of o are all in flight at
+// once (rows past the last read the last row again, with weight 0), so the common case waits
+// for two rounds of loads. Lane s holds row s's m and l (rows are taken 64 at a time); lane i
+// accumulates dims i, i + 64, ... of the output. Same arithmetic as k_combine: m and lse in the
+// base-2 domain, weights 2^(m_s - max).
 template <int DPL>
 __global__ __launch_bounds__(256) void k_combine_wave(gva::DecodeArgs a) {
+  constexpr int kPre = 4;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int b = blockIdx.y;
@@ -336,56 +339,69 @@ __global__ __launch_bounds__(256) void k_combine_wave(gva::DecodeArgs a) {
   float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
   float *lse = a.lse ? a.lse + static_cast<int64_t>(b) * a.H + h : nullptr;
   const int len = a.seq_len[b];
-  const int cap = a.max_blocks << a.log2_bs;
-  if (len < 0 || len > a.max_len || len > cap) {
-#pragma unroll
-    for (int k = 0; k < DPL; ++k)
-      if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = qnan;
-    if (lse && lane == 0) *lse = qnan;
-    if (a.num_ranges > 0 && lane == 0 && h == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
-    return;
-  }
   int ns;
   int64_t row0;
   partial_rows(a, b, h, len, ns, row0);
+  const int cap = a.max_blocks << a.log2_bs;
+  const bool bad = len < 0 || len > a.max_len || len > cap;
+  if (bad || ns == 0) {                                // NaN for a bad length, else empty: 0, -inf
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = bad ? qnan : 0.0f;
+    if (lse && lane == 0) *lse = bad ? qnan : -INFINITY;
+    if (bad && a.num_ranges > 0 && lane == 0 && h == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+    return;
+  }
   const int64_t step = a.H;                            // rows of one (sequence, head) are H apart
-  // maximum of m over the rows (and whether any is NaN)
-  float mx = -INFINITY;
-  bool poison = false;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const float ms = s0 + lane < ns ? a.part_m[row0 + (s0 + lane) * step] : -INFINITY;
-    poison |= __any(isnan(ms));
-    mx = fmaxf(mx, gvad::wave_max(ms));
+  const float *po = a.part_o + row0 * a.d_h + lane;
+  const int64_t ostep = step * a.d_h;
+  // first rows of o, in flight together with m and l
+  float opre[kPre][DPL];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j)
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      opre[j][k] = lane + 64 * k < a.d_h ? po[min(j, ns - 1) * ostep + 64 * k] : 0.0f;
+  float ms = lane < ns ? a.part_m[row0 + lane * step] : -INFINITY;
+  float ls = lane < ns ? a.part_l[row0 + lane * step] : 0.0f;
+  // maximum of m over all rows (and whether any is NaN)
+  bool poison = __any(isnan(ms));
+  float mx = gvad::wave_max(ms);
+  for (int s0 = 64; s0 < ns; s0 += 64) {
+    const float m2 = s0 + lane < ns ? a.part_m[row0 + (s0 + lane) * step] : -INFINITY;
+    poison |= __any(isnan(m2));
+    mx = fmaxf(mx, gvad::wave_max(m2));
   }
   float acc[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
   float L = 0.0f;
   for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    float w = 0.0f;
-    if (s < ns) {
-      w = exp2f(a.part_m[row0 + s * step] - mx);
-      L += a.part_l[row0 + s * step] * w;
+    if (s0 > 0) {
+      ms = s0 + lane < ns ? a.part_m[row0 + (s0 + lane) * step] : -INFINITY;
+      ls = s0 + lane < ns ? a.part_l[row0 + (s0 + lane) * step] : 0.0f;
     }
+    const float w = s0 + lane < ns ? exp2f(ms - mx) : 0.0f;
+    L += ls * w;
     const int nc = min(64, ns - s0);
-    const float *po = a.part_o + (row0 + static_cast<int64_t>(s0) * step) * a.d_h + lane;
+    int j = 0;
+    if (s0 == 0) {
+#pragma unroll
+      for (; j < kPre; ++j) {
+        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(opre[j][k], wj, acc[k]);
+      }
+    }
 #pragma unroll 4
-    for (int j = 0; j < nc; ++j) {
+    for (; j < nc; ++j) {
       const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
 #pragma unroll
       for (int k = 0; k < DPL; ++k)
-        if (lane + 64 * k < a.d_h) acc[k] = fmaf(po[j * step * a.d_h + 64 * k], wj, acc[k]);
+        if (lane + 64 * k < a.d_h) acc[k] = fmaf(po[(s0 + j) * ostep + 64 * k], wj, acc[k]);
     }
   }
   L = gvad::wave_sum(L);
-  if (ns == 0) {
-#pragma unroll
-    for (int k = 0; k < DPL; ++k)
-      if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = 0.0f;
-    if (lse && lane == 0) *lse = -INFINITY;
-    return;
-  }
 #pragma unroll
   for (int k = 0; k < DPL; ++k)
     if (lane + 64 * k < a.d_h) dst[lane + 64 * k] = poison ? qnan : acc[k] / L;
