@@ -183,6 +183,31 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
                       int32_t num_splits, int32_t kernel, void *workspace,
                       size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
 
+/* ---- One decode step ([kvcache] section 1: each step appends the new token's state, then the
+ * query reads the whole history; [review] sections 关键技巧一 and 关键技巧二) ------------------
+ * For B sequences that each receive one token, does what gva_cache_append (token b to
+ * sequence b at pos[b]), gva_absorb_query (query b at pos[b], with the cache's RoPE table and
+ * err_flag) and gva_decode would do in that order, with the same arithmetic and bit-identical
+ * results. The append and the absorption touch disjoint data and run as one launch, so a step
+ * takes one launch fewer than the three calls; that is what counts for small batches, whose
+ * step is a few microseconds of work.
+ *   pos: device int32 [B], the new token's position (its sequence's length before the step).
+ *   v_new: device float32 [B][G][d_h]; kr_raw: device float32 [B][d_r].
+ *   q_nope: device float32 [B][H][d_n]; q_rope: device float32 [B][H][d_r];
+ *   M: device float32 [H][d_h][d_n].
+ *   seq_len: device int32 [B], the positions the decode reads (pos[b] + 1 to include the new
+ *   token); max_len, scale, num_splits, kernel, workspace, out, lse: as for gva_decode
+ *   (workspace sized by gva_decode_workspace_bytes).
+ *   q_abs: device float32 [B][H][d_h + d_r], written with the absorbed queries and then read
+ *   by the decode (16-byte aligned).
+ * Errors found on the device raise the same GVA_DEVERR_* bits as the three calls. */
+gva_status gva_decode_step(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                           const int32_t *pos, const float *v_new, const float *kr_raw,
+                           const float *q_nope, const float *q_rope, const float *M,
+                           const int32_t *seq_len, int32_t max_len, float scale,
+                           int32_t num_splits, int32_t kernel, float *q_abs, void *workspace,
+                           size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
+
 /* ---- Chunked prefill ([summary]: prefill stays a dense, matrix-heavy pass) -----------------
  * Appends chunk_len new tokens per sequence at positions start[b] .. start[b] + chunk_len - 1
  * (exactly as gva_cache_append would), then for query i of sequence b, at position

@@ -1,0 +1,133 @@
+"""GPU parity of gva_decode_step (append + absorb in one launch, then decode): bit-identical to
+the three separate calls, and within the bf16/fp32 bars of the oracle's append, absorption and
+decode in float64."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gva_oracle as O
+from value_only_kv_amd import binding as gb
+from value_only_kv_amd import synth
+from tests.gpu_cases import Case, absorbed_queries, check_output, lse_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, **kw):
+    w = synth.workload(name, **kw)
+    c = Case(w)
+    c.append_prefix()
+    return c
+
+
+def _step_inputs(c, seed):
+    """New tokens (one per sequence, at position lens[b]) and their queries."""
+    w = c.w
+    rng = np.random.default_rng(np.random.SeedSequence([4242, seed]))
+    v_new = rng.standard_normal((w.B, w.G, w.d_h)).astype(np.float32)
+    kr_raw = rng.standard_normal((w.B, w.d_r)).astype(np.float32)
+    pos = c.lens.astype(np.int64)
+    q_ref, (M, q_nope, q_rope) = absorbed_queries(w, w.B, pos, c.tab_ora)
+    return pos, v_new, kr_raw, M, q_nope, q_rope, q_ref
+
+
+def _t(x, dtype=None):
+    a = np.ascontiguousarray(x if dtype is None else np.asarray(x, dtype))
+    return torch.from_numpy(a).cuda()
+
+
+def _run_step(c, pos, v_new, kr_raw, M, q_nope, q_rope, num_splits, fused, kernel=gb.GVA_KERNEL_AUTO):
+    w = c.w
+    B, H = w.B, w.H
+    sl = pos + 1
+    ml = int(sl.max())
+    pos_t, sl_t = _t(pos, np.int32), _t(sl, np.int32)
+    qa = torch.full((B, H, w.d_h + w.d_r), float("nan"), device="cuda")
+    out = torch.full((B, H, w.d_h), float("nan"), device="cuda")
+    lse = torch.full((B, H), float("nan"), device="cuda")
+    wsb = gb.gva_decode_workspace_bytes(c.cdims, B, ml, num_splits)
+    ws = torch.empty(max(wsb, 256) // 4, device="cuda") if wsb else None
+    args = tuple(_t(x, np.float32) for x in (v_new, kr_raw, q_nope, q_rope, M))
+    if fused:
+        gb.gva_decode_step(c.cdims, c.cache, B, pos_t, *args[:2], *args[2:], sl_t, ml, w.scale, qa,
+                           out, lse, num_splits=num_splits, kernel=kernel, workspace=ws)
+    else:
+        seq = _t(np.arange(B), np.int32)
+        gb.gva_cache_append(c.cdims, c.cache, B, seq, pos_t, args[0], args[1])
+        gb.gva_absorb_query(c.cdims, args[2], args[3], pos_t, args[4], c.tab_lib, c.max_pos, qa,
+                            err_flag=c.cache.err_flag)
+        gb.gva_decode(c.cdims, c.cache, B, sl_t, ml, qa, w.scale, out, lse,
+                      num_splits=num_splits, kernel=kernel, workspace=ws)
+    torch.cuda.synchronize()
+    return qa.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+
+
+SHAPES = [
+    pytest.param("C1", dict(append_one=True, block_size=512), 1, id="C1-fp32"),
+    pytest.param("C2", dict(append_one=True, block_size=8192), 0, id="C2-bf16-auto"),
+    pytest.param("C2", dict(append_one=True, block_size=8192), 3, id="C2-bf16-S3"),
+    pytest.param("C4", dict(B=9, lengths_uniform=(0, 700)), 0, id="ragged-paged-balanced"),
+    pytest.param("C4", dict(B=9, lengths_uniform=(0, 700)), 2, id="ragged-paged-S2"),
+]
+
+
+@pytest.mark.parametrize("name,kw,num_splits", SHAPES)
+def test_step_matches_separate_calls(name, kw, num_splits):
+    """Same cache bytes, same absorbed queries, same outputs, bit for bit."""
+    a, b = _case(name, **kw), _case(name, **kw)
+    pos, v_new, kr_raw, M, q_nope, q_rope, _ = _step_inputs(a, 1)
+    qa1, o1, l1 = _run_step(a, pos, v_new, kr_raw, M, q_nope, q_rope, num_splits, fused=False)
+    qa2, o2, l2 = _run_step(b, pos, v_new, kr_raw, M, q_nope, q_rope, num_splits, fused=True)
+    va, ka = a.device_bits()
+    vb, kb = b.device_bits()
+    assert np.array_equal(va, vb) and np.array_equal(ka, kb)
+    assert qa1.tobytes() == qa2.tobytes()
+    assert o1.tobytes() == o2.tobytes() and l1.tobytes() == l2.tobytes()
+    assert a.err_flag() == 0 and b.err_flag() == 0
+
+
+@pytest.mark.parametrize("name,kw,num_splits", SHAPES)
+def test_step_against_oracle(name, kw, num_splits):
+    c = _case(name, **kw)
+    pos, v_new, kr_raw, M, q_nope, q_rope, q_ref = _step_inputs(c, 2)
+    qa, out, lse = _run_step(c, pos, v_new, kr_raw, M, q_nope, q_rope, num_splits, fused=True)
+    # the oracle appends the same tokens into its own pool; the cache bytes must agree exactly
+    O.append(c.pool, c.dims, np.arange(c.w.B), pos, v_new, kr_raw, c.tab_ora)
+    v_dev, k_dev = c.device_bits()
+    assert np.array_equal(v_dev, c.pool.v) and np.array_equal(k_dev, c.pool.kr)
+    # the absorbed queries: float32 accumulation against float64
+    assert np.max(np.abs(qa - q_ref)) <= 1e-4 * max(1.0, float(np.max(np.abs(q_ref))))
+    ref, ref_lse = c.oracle_decode(pos + 1, q_ref)
+    dtype = "f32" if c.w.dtype == "f32" else "bf16"
+    check_output(out, ref, dtype, f"step {name} S={num_splits}")
+    ok, e = lse_ok(lse, ref_lse, 1e-5 if dtype == "f32" else 1e-3)
+    assert ok, e
+
+
+def test_step_flags_a_position_outside_the_rope_table():
+    """A new token beyond the RoPE table: its append is skipped, its query row is NaN, the
+    other sequences are unaffected and the ROPE bit is raised."""
+    c = _case("C4", B=4, lengths_uniform=(100, 300))
+    pos, v_new, kr_raw, M, q_nope, q_rope, q_ref = _step_inputs(c, 3)
+    bad = pos.copy()
+    bad[2] = c.max_pos + 3
+    w = c.w
+    B, H = w.B, w.H
+    sl = pos + 1
+    ml = int(sl.max())
+    qa = torch.full((B, H, w.d_h + w.d_r), 0.0, device="cuda")
+    out = torch.empty((B, H, w.d_h), device="cuda")
+    wsb = gb.gva_decode_workspace_bytes(c.cdims, B, ml, 0)
+    ws = torch.empty(max(wsb, 256) // 4, device="cuda")
+    gb.gva_decode_step(c.cdims, c.cache, B, _t(bad, np.int32),
+                       *(_t(x, np.float32) for x in (v_new, kr_raw, q_nope, q_rope, M)),
+                       _t(sl, np.int32), ml, w.scale, qa, out, workspace=ws)
+    torch.cuda.synchronize()
+    assert c.err_flag() & gb.DEVERR_ROPE
+    qa = qa.cpu().numpy()
+    out = out.cpu().numpy()
+    assert np.all(np.isnan(qa[2])) and np.all(np.isnan(out[2]))
+    good = [0, 1, 3]
+    O.append(c.pool, c.dims, np.array(good), pos[good], v_new[good], kr_raw[good], c.tab_ora)
+    ref, _ = c.oracle_decode(sl, q_ref, seqs=good)
+    check_output(out[good], ref[good], "bf16", "healthy sequences")

@@ -224,6 +224,38 @@ def test_append_and_absorb_validation(L):
     assert ab(d=_dims(d_n=126)) == gb.GVA_ERR_UNSUPPORTED
 
 
+def test_decode_step_validation(L):
+    """Every call here fails validation on the host, before anything is launched."""
+    d, c = _dims(), _cache()
+    def st(**kw):
+        return L.gva_decode_step(ctypes.byref(kw.get("d", d)), ctypes.byref(kw.get("c", c)),
+                                 kw.get("B", 2), kw.get("pos", A), kw.get("v", A),
+                                 kw.get("kr", A), kw.get("qn", A), kw.get("qr", A), kw.get("M", A),
+                                 kw.get("sl", A), kw.get("ml", 100), kw.get("scale", 0.1),
+                                 kw.get("S", 0), kw.get("kernel", 0), kw.get("qa", A),
+                                 kw.get("ws", None), kw.get("wsb", 0), kw.get("out", A), None, None)
+    assert st(B=0) == gb.GVA_ERR_INVALID_ARG
+    assert st(pos=None) == gb.GVA_ERR_INVALID_ARG
+    assert st(v=None) == gb.GVA_ERR_INVALID_ARG
+    assert st(kr=A + 4) == gb.GVA_ERR_INVALID_ARG
+    assert st(qn=None) == gb.GVA_ERR_INVALID_ARG
+    assert st(M=A + 8) == gb.GVA_ERR_INVALID_ARG
+    assert st(qa=None) == gb.GVA_ERR_INVALID_ARG
+    assert st(qa=A + 8) == gb.GVA_ERR_INVALID_ARG          # the decode reads q_abs 16-aligned
+    assert st(sl=None) == gb.GVA_ERR_INVALID_ARG
+    assert st(out=None) == gb.GVA_ERR_INVALID_ARG
+    assert st(scale=0.0) == gb.GVA_ERR_INVALID_ARG
+    assert st(ml=8 * 16 + 1) == gb.GVA_ERR_INVALID_ARG      # beyond the table's capacity
+    assert st(S=1025) == gb.GVA_ERR_INVALID_ARG
+    assert st(d=_dims(d_n=126)) == gb.GVA_ERR_UNSUPPORTED   # the absorption's float4 rows
+    assert st(c=_cache(rope=None)) == gb.GVA_ERR_INVALID_ARG
+    assert st(c=_cache(max_pos=0)) == gb.GVA_ERR_INVALID_ARG
+    # the automatic plan of a bf16 batch needs a workspace
+    assert st() == gb.GVA_ERR_WORKSPACE
+    assert st(ws=A + 64, wsb=1 << 30) == gb.GVA_ERR_WORKSPACE   # not 256-byte aligned
+    assert b"workspace" in L.gva_last_error()
+
+
 def test_prefill_validation(L):
     d, c = _dims(), _cache(max_blocks=64)
     pf = lambda **kw: L.gva_prefill_chunk(ctypes.byref(kw.get("d", d)), ctypes.byref(kw.get("c", c)),

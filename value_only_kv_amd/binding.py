@@ -28,7 +28,7 @@ DEVERR_BLOCK, DEVERR_CAPACITY, DEVERR_ROPE, DEVERR_SEQ, DEVERR_LENGTH = 1, 2, 4,
 EXPORTED = [
     "gva_rope_table_bytes", "gva_rope_table_fill", "gva_cache_append", "gva_absorb_query",
     "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
-    "gva_prefill_chunk", "gva_gqa_decode",
+    "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode",
     "gva_status_string", "gva_last_error", "gva_version",
 ]
 
@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
     L.gva_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32, P,
                              c_float, c_int32, c_int32, P, c_size_t, P, P, P]
     L.gva_decode.restype = c_int32
+    L.gva_decode_step.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, P, P, P,
+                                  P, P, P, c_int32, c_float, c_int32, c_int32, P, P, c_size_t, P,
+                                  P, P]
+    L.gva_decode_step.restype = c_int32
     L.gva_prefill_chunk.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32,
                                     c_int32, P, P, P, c_float, P, P, P]
     L.gva_prefill_chunk.restype = c_int32
@@ -186,6 +190,19 @@ def gva_decode(dims: GvaDims, cache: "GvaCache", B: int, seq_len, max_len: int, 
     _check(lib().gva_decode(ctypes.byref(dims), ctypes.byref(cache.struct), B, _ptr(seq_len),
                             max_len, _ptr(q_abs), scale, num_splits, kernel, _ptr(workspace),
                             ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def gva_decode_step(dims: GvaDims, cache: "GvaCache", B: int, pos, v_new, kr_raw, q_nope, q_rope,
+                    M, seq_len, max_len: int, scale: float, q_abs, out, lse=None,
+                    num_splits: int = 0, kernel: int = GVA_KERNEL_AUTO, workspace=None,
+                    stream=None) -> None:
+    """Append + absorb (one launch) + decode for one new token per sequence."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gva_decode_step(ctypes.byref(dims), ctypes.byref(cache.struct), B, _ptr(pos),
+                                 _ptr(v_new), _ptr(kr_raw), _ptr(q_nope), _ptr(q_rope), _ptr(M),
+                                 _ptr(seq_len), max_len, scale, num_splits, kernel, _ptr(q_abs),
+                                 _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                 _stream(stream)))
 
 
 def gva_prefill_chunk(dims: GvaDims, cache: "GvaCache", B: int, start, max_start: int,

@@ -34,6 +34,40 @@ gva_status hip_status(hipError_t e, const char *what) {
   return gva::fail(GVA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Decode + combine launches for a checked call and its plan.
+gva_status launch_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                         const int32_t *seq_len, int32_t max_len, const float *q_abs, float scale,
+                         const gva::DecodePlan &plan, bool use_mfma, void *workspace, float *out,
+                         float *lse, hipStream_t stream) {
+  gva::DecodeArgs a = cache_args(dims, cache);
+  a.B = B;
+  a.seq_len = seq_len;
+  a.max_len = max_len;
+  a.q_abs = q_abs;
+  a.qscale = scale * 1.4426950408889634f;
+  a.num_splits = plan.num_splits;
+  a.chunk = plan.chunk;
+  a.num_ranges = plan.num_ranges;
+  a.out = out;
+  a.lse = lse;
+  const bool partials = plan.num_splits > 1 || plan.num_ranges > 0;
+  if (partials) {
+    char *ws = static_cast<char *>(workspace);
+    a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
+    a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
+    a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+    if (plan.num_ranges > 0) a.tile_prefix = reinterpret_cast<int32_t *>(ws + plan.off_prefix);
+  }
+  hipError_t e = use_mfma ? gva::launch_decode_mfma(a, stream)
+                          : gva::launch_decode_generic(a, cache->dtype == GVA_DTYPE_BF16, stream);
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+  if (partials) {
+    e = gva::launch_combine(a, stream);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return GVA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,33 +101,29 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
   gva_status st = gva::check_decode(dims, cache, B, seq_len, max_len, q_abs, scale, num_splits,
                                     kernel, workspace, workspace_bytes, out, &plan, &use_mfma);
   if (st != GVA_OK) return st;
-  gva::DecodeArgs a = cache_args(dims, cache);
-  a.B = B;
-  a.seq_len = seq_len;
-  a.max_len = max_len;
-  a.q_abs = q_abs;
-  a.qscale = scale * 1.4426950408889634f;
-  a.num_splits = plan.num_splits;
-  a.chunk = plan.chunk;
-  a.num_ranges = plan.num_ranges;
-  a.out = out;
-  a.lse = lse;
-  const bool partials = plan.num_splits > 1 || plan.num_ranges > 0;
-  if (partials) {
-    char *ws = static_cast<char *>(workspace);
-    a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
-    a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
-    a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
-    if (plan.num_ranges > 0) a.tile_prefix = reinterpret_cast<int32_t *>(ws + plan.off_prefix);
-  }
-  hipError_t e = use_mfma ? gva::launch_decode_mfma(a, stream)
-                          : gva::launch_decode_generic(a, cache->dtype == GVA_DTYPE_BF16, stream);
-  if (e != hipSuccess) return hip_status(e, "decode launch");
-  if (partials) {
-    e = gva::launch_combine(a, stream);
-    if (e != hipSuccess) return hip_status(e, "combine launch");
-  }
-  return GVA_OK;
+  return launch_decode(dims, cache, B, seq_len, max_len, q_abs, scale, plan, use_mfma, workspace,
+                       out, lse, stream);
+}
+
+gva_status gva_decode_step(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                           const int32_t *pos, const float *v_new, const float *kr_raw,
+                           const float *q_nope, const float *q_rope, const float *M,
+                           const int32_t *seq_len, int32_t max_len, float scale,
+                           int32_t num_splits, int32_t kernel, float *q_abs, void *workspace,
+                           size_t workspace_bytes, float *out, float *lse, hipStream_t stream) {
+  gva_status st = gva::check_step(dims, cache, B, pos, v_new, kr_raw, q_nope, q_rope, M, q_abs);
+  if (st != GVA_OK) return st;
+  gva::DecodePlan plan{};
+  bool use_mfma = false;
+  st = gva::check_decode(dims, cache, B, seq_len, max_len, q_abs, scale, num_splits, kernel,
+                         workspace, workspace_bytes, out, &plan, &use_mfma);
+  if (st != GVA_OK) return st;
+  hipError_t e = gva::launch_step_prep(cache_args(dims, cache), cache->dtype == GVA_DTYPE_BF16, B,
+                                       pos, v_new, kr_raw, cache->rope, cache->max_pos, dims->d_n,
+                                       q_nope, q_rope, M, q_abs, stream);
+  if (e != hipSuccess) return hip_status(e, "step append and absorb launch");
+  return launch_decode(dims, cache, B, seq_len, max_len, q_abs, scale, plan, use_mfma, workspace,
+                       out, lse, stream);
 }
 
 gva_status gva_gqa_decode(const gva_dims *dims, const gva_cache *values, const void *keys,

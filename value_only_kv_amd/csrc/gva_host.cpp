@@ -231,6 +231,19 @@ gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
   return GVA_OK;
 }
 
+gva_status check_step(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *pos,
+                      const float *v_new, const float *kr_raw, const float *q_nope,
+                      const float *q_rope, const float *M, const float *q_abs) {
+  gva_status st = check_dims(d);
+  if (st != GVA_OK) return st;
+  if ((st = check_cache(d, c)) != GVA_OK) return st;
+  if (B < 1) return fail(GVA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (!pos || !v_new || !kr_raw) return fail(GVA_ERR_INVALID_ARG, "step append input is NULL");
+  if (!aligned(v_new, 8) || !aligned(kr_raw, 8))
+    return fail(GVA_ERR_INVALID_ARG, "v_new and kr_raw must be 8-byte aligned");
+  return check_absorb(d, B, q_nope, q_rope, pos, M, c->rope, c->max_pos, q_abs);
+}
+
 gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
                          int32_t max_start, int32_t chunk_len, const float *q_abs,
                          const float *v_new, const float *kr_raw, float scale, const float *out) {

@@ -76,6 +76,12 @@ gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
                         size_t workspace_bytes, const float *out, DecodePlan *plan,
                         bool *use_mfma);
 
+// The append and absorption parts of a decode step: token b goes to sequence b at pos[b], and
+// query b is absorbed at the same position with the cache's RoPE table.
+gva_status check_step(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *pos,
+                      const float *v_new, const float *kr_raw, const float *q_nope,
+                      const float *q_rope, const float *M, const float *q_abs);
+
 gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
                          int32_t max_start, int32_t chunk_len, const float *q_abs,
                          const float *v_new, const float *kr_raw, float scale, const float *out);
@@ -118,6 +124,11 @@ hipError_t launch_append(const gva_dims *d, const gva_cache *c, int32_t B, int32
 hipError_t launch_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, const float *q_rope,
                          const int32_t *q_pos, const float *M, const double *rope,
                          int32_t max_pos, float *q_abs, int32_t *err_flag, hipStream_t stream);
+// One launch: append token b to sequence b at pos[b] (b < B) and absorb query b at pos[b].
+hipError_t launch_step_prep(const DecodeArgs &a, bool bf16, int32_t B, const int32_t *pos,
+                            const float *v_new, const float *kr_raw, const double *rope,
+                            int32_t max_pos, int32_t d_n, const float *q_nope, const float *q_rope,
+                            const float *M, float *q_abs, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);

@@ -17,19 +17,15 @@ using gvad::f64_to_f32_bits;
 
 // One work-group per appended token. Threads stride over the G*d_h/2 value pairs, then over
 // the d_r/2 positional pairs. Values take one rounding fp32 -> cache type (through an exact
-// float64 widening); the positional key is rotated in float64 and rounded once.
+// float64 widening); the positional key is rotated in float64 and rounded once. Token k of the
+// inputs goes to sequence b (checked by the caller to lie in [0, B)) at position p.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_append(gva::DecodeArgs a, int32_t B, const int32_t *seq,
-                                                const int32_t *pos, const float *v_new,
-                                                const float *kr_raw, const double *rope,
-                                                int32_t max_pos) {
-  const int k = blockIdx.x;
-  const int b = seq[k];
-  const int p = pos[k];
+__device__ __forceinline__ void append_one(const gva::DecodeArgs &a, int k, int b, int p,
+                                           const float *v_new, const float *kr_raw,
+                                           const double *rope, int32_t max_pos) {
   const int cap = a.max_blocks << a.log2_bs;
   int32_t err = 0;
-  if (b < 0 || b >= B) err = GVA_DEVERR_SEQ;
-  else if (p < 0) err = GVA_DEVERR_LENGTH;
+  if (p < 0) err = GVA_DEVERR_LENGTH;
   else if (p >= cap) err = GVA_DEVERR_CAPACITY;
   else if (p >= max_pos) err = GVA_DEVERR_ROPE;
   int64_t blk = -1;
@@ -83,6 +79,20 @@ __global__ __launch_bounds__(256) void k_append(gva::DecodeArgs a, int32_t B, co
   }
 }
 
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_append(gva::DecodeArgs a, int32_t B, const int32_t *seq,
+                                                const int32_t *pos, const float *v_new,
+                                                const float *kr_raw, const double *rope,
+                                                int32_t max_pos) {
+  const int k = blockIdx.x;
+  const int b = seq[k];
+  if (b < 0 || b >= B) {
+    if (threadIdx.x == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_SEQ);
+    return;
+  }
+  append_one<BF16>(a, k, b, pos[k], v_new, kr_raw, rope, max_pos);
+}
+
 // Absorption, q~[t][i] = sum_j M_h[i][j] q_nope[t][h][j]: for every head a small GEMM of the
 // d_h x d_n map by the d_n x n queries. Work-group (head h, tile of kAbsQ query tokens, tile of
 // kAbsRows rows of M_h): both operand tiles are staged in LDS, 128 columns at a time, with
@@ -95,19 +105,32 @@ constexpr int kAbsQ = 32;
 constexpr int kAbsRows = 32;
 constexpr int kAbsThreads = 256;
 
-__global__ __launch_bounds__(kAbsThreads) void k_absorb(int32_t H, int32_t d_h, int32_t d_n,
-                                                        int32_t d_r, int32_t n_q,
-                                                        const float *q_nope, const float *q_rope,
-                                                        const int32_t *q_pos, const float *M,
-                                                        const double *rope, int32_t max_pos,
-                                                        float *q_abs, int32_t *err_flag) {
+struct AbsorbArgs {
+  int32_t H, d_h, d_n, d_r, n_q;
+  const float *q_nope, *q_rope;
+  const int32_t *q_pos;
+  const float *M;
+  const double *rope;
+  int32_t max_pos;
+  float *q_abs;
+  int32_t *err_flag;
+};
+
+// Tile (head h, query tile ty, row tile tz) of the absorption.
+__device__ __forceinline__ void absorb_tile(const AbsorbArgs &x, int h, int ty, int tz) {
   constexpr int kJ4 = 32;                      // d_n is walked in chunks of 128 (32 float4)
   constexpr int kStride4 = kJ4 + 1;            // row stride in float4 (4 floats of padding)
   __shared__ float4 qs[kAbsQ * kStride4];
   __shared__ float4 ms[kAbsRows * kStride4];
-  const int h = blockIdx.x;
-  const int k0 = blockIdx.y * kAbsQ;
-  const int i0 = blockIdx.z * kAbsRows;
+  const int H = x.H, d_h = x.d_h, d_n = x.d_n, d_r = x.d_r, n_q = x.n_q;
+  const float *q_nope = x.q_nope, *q_rope = x.q_rope, *M = x.M;
+  const int32_t *q_pos = x.q_pos;
+  const double *rope = x.rope;
+  const int32_t max_pos = x.max_pos;
+  float *q_abs = x.q_abs;
+  int32_t *err_flag = x.err_flag;
+  const int k0 = ty * kAbsQ;
+  const int i0 = tz * kAbsRows;
   const int nt = min(kAbsQ, n_q - k0);
   const int ni = min(kAbsRows, d_h - i0);
   const int dn4 = d_n >> 2;
@@ -158,7 +181,7 @@ __global__ __launch_bounds__(kAbsThreads) void k_absorb(int32_t H, int32_t d_h, 
       q_abs[(static_cast<int64_t>(k0 + t) * H + h) * row + i0 + i] = bad ? __int_as_float(0x7fc00000) : acc[k];
     }
   }
-  if (blockIdx.z != 0) return;
+  if (tz != 0) return;
   const int half_r = d_r >> 1;
   for (int idx = tid; idx < nt * half_r; idx += kAbsThreads) {
     const int t = idx / half_r;
@@ -181,6 +204,30 @@ __global__ __launch_bounds__(kAbsThreads) void k_absorb(int32_t H, int32_t d_h, 
     dst[0] = y.x;
     dst[1] = y.y;
   }
+}
+
+__global__ __launch_bounds__(kAbsThreads) void k_absorb(AbsorbArgs x) {
+  absorb_tile(x, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The append and the absorption of one decode step in one launch (they touch disjoint data):
+// work-group k < B appends token k to sequence k at position pos[k]; the others are the
+// absorption's tiles, head fastest, then query tile, then row tile (query k sits at pos[k]).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_step_prep(gva::DecodeArgs a, int32_t B, const int32_t *pos,
+                                                   const float *v_new, const float *kr_raw,
+                                                   const double *rope, int32_t max_pos,
+                                                   AbsorbArgs x, int32_t n_qt) {
+  const int id = blockIdx.x;
+  if (id < B) {
+    append_one<BF16>(a, id, id, pos[id], v_new, kr_raw, rope, max_pos);
+    return;
+  }
+  const int r = id - B;
+  const int h = r % x.H;
+  const int ty = (r / x.H) % n_qt;
+  const int tz = r / (x.H * n_qt);
+  absorb_tile(x, h, ty, tz);
 }
 
 }  // namespace
@@ -223,8 +270,27 @@ hipError_t launch_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, co
                          int32_t max_pos, float *q_abs, int32_t *err_flag, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
   const dim3 grid(d->H, (n_q + kAbsQ - 1) / kAbsQ, (d->d_h + kAbsRows - 1) / kAbsRows);
-  hipLaunchKernelGGL(k_absorb, grid, dim3(kAbsThreads), 0, stream, d->H, d->d_h, d->d_n, d->d_r,
-                     n_q, q_nope, q_rope, q_pos, M, rope, max_pos, q_abs, err_flag);
+  const AbsorbArgs x{d->H, d->d_h, d->d_n, d->d_r, n_q, q_nope, q_rope, q_pos, M, rope, max_pos,
+                     q_abs, err_flag};
+  hipLaunchKernelGGL(k_absorb, grid, dim3(kAbsThreads), 0, stream, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_prep(const DecodeArgs &a, bool bf16, int32_t B, const int32_t *pos,
+                            const float *v_new, const float *kr_raw, const double *rope,
+                            int32_t max_pos, int32_t d_n, const float *q_nope, const float *q_rope,
+                            const float *M, float *q_abs, hipStream_t stream) {
+  const int n_qt = (B + kAbsQ - 1) / kAbsQ;
+  const int n_rt = (a.d_h + kAbsRows - 1) / kAbsRows;
+  const AbsorbArgs x{a.H, a.d_h, d_n, a.d_r, B, q_nope, q_rope, pos, M, rope, max_pos, q_abs,
+                     a.err_flag};
+  const dim3 grid(static_cast<unsigned>(B + a.H * n_qt * n_rt));
+  if (bf16)
+    hipLaunchKernelGGL(k_step_prep<true>, grid, dim3(256), 0, stream, a, B, pos, v_new, kr_raw,
+                       rope, max_pos, x, n_qt);
+  else
+    hipLaunchKernelGGL(k_step_prep<false>, grid, dim3(256), 0, stream, a, B, pos, v_new, kr_raw,
+                       rope, max_pos, x, n_qt);
   return hipGetLastError();
 }
 
