@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     p.add_argument("--no-gqa", action="store_true", help="skip the GQA comparator measurement")
+    p.add_argument("--no-small", action="store_true", help="skip the small-batch step latencies")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -129,11 +130,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        gb.gva_cache_append(dc.dims, dc.cache, B, seq, pos, v_new, kr_new, stream=stream)
-        gb.gva_absorb_query(dc.dims, q_nope, q_rope, pos, M, dc.cache.rope, dc.max_pos, q_abs,
-                            stream=stream)
-        gb.gva_decode(dc.dims, dc.cache, B, seq_len, max_len, q_abs, w.scale, out, lse,
-                      num_splits=args.splits, kernel=args.kernel, workspace=ws, stream=stream)
+        # append + absorb (one launch), then the decode
+        gb.gva_decode_step(dc.dims, dc.cache, B, pos, v_new, kr_new, q_nope, q_rope, M, seq_len,
+                           max_len, w.scale, q_abs, out, lse, num_splits=args.splits,
+                           kernel=args.kernel, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -256,6 +256,11 @@ def main():
     if not args.no_prefill:
         prefill = bench_prefill(torch, gb, synth, gen, stream)
 
+    # ---------------- small-batch step latency ----------------
+    small = None
+    if not args.no_small:
+        small = bench_small(torch, gb, synth, gen, stream)
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         bcopy = torch.empty_like(a)
@@ -302,6 +307,7 @@ def main():
         "cpu_baseline": cpu,
         "long_context": result_extra,
         "prefill": prefill,
+        "small_batch_step": small,
         "gqa_comparator": gqa,
         "device": dev,
     }
@@ -380,6 +386,67 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
            "decode_step_after_GB_s": round(dec_bytes / td / 1e9, 1)}
     del dc
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_small(torch, gb, synth, gen, stream, iters=50):
+    """Latency of one decode step (append one token per sequence, absorb, decode) at the
+    small-batch shapes, as three calls and as gva_decode_step (append and absorb in one launch).
+    Median of HIP-event times on the launch stream."""
+    res = {}
+    shapes = (("C2", dict(append_one=True, block_size=8192),
+               "B=8, T=4096 (+1 appended), H=16, G=4, d_h=d_n=64, d_r=16, bf16 contiguous"),
+              ("C1", dict(append_one=True, block_size=512),
+               "B=1, T=256 (+1 appended), H=8, G=4, d_h=d_n=64, d_r=16, fp32 contiguous"))
+    for name, kw, desc in shapes:
+        w = synth.workload(name, **kw)
+        lens = synth.lengths(w)
+        dc = DeviceCache(w, lens, 99, torch, gb, synth)
+        B, H = w.B, w.H
+        seq = torch.arange(B, dtype=torch.int32, device="cuda")
+        pos = torch.from_numpy(lens.astype(np.int32)).cuda()
+        sl = pos + 1
+        ml = int(lens.max()) + 1
+        v = torch.randn((B, w.G, w.d_h), generator=gen, device="cuda")
+        kr = torch.randn((B, w.d_r), generator=gen, device="cuda")
+        qn = torch.randn((B, H, w.d_n), generator=gen, device="cuda")
+        qr = torch.randn((B, H, w.d_r), generator=gen, device="cuda")
+        M = torch.randn((H, w.d_h, w.d_n), generator=gen, device="cuda") * w.m_sigma
+        qa = torch.empty((B, H, w.d_h + w.d_r), device="cuda")
+        out = torch.empty((B, H, w.d_h), device="cuda")
+        lse = torch.empty((B, H), device="cuda")
+        wsb = gb.gva_decode_workspace_bytes(dc.dims, B, ml, 0)
+        ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+
+        def three_calls():
+            gb.gva_cache_append(dc.dims, dc.cache, B, seq, pos, v, kr, stream=stream)
+            gb.gva_absorb_query(dc.dims, qn, qr, pos, M, dc.cache.rope, dc.max_pos, qa,
+                                stream=stream)
+            gb.gva_decode(dc.dims, dc.cache, B, sl, ml, qa, w.scale, out, lse, workspace=ws,
+                          stream=stream)
+
+        def fused():
+            gb.gva_decode_step(dc.dims, dc.cache, B, pos, v, kr, qn, qr, M, sl, ml, w.scale, qa,
+                               out, lse, workspace=ws, stream=stream)
+
+        r = {"workload": desc}
+        for label, fn in (("three_calls_us", three_calls), ("decode_step_us", fused)):
+            for _ in range(5):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(iters)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            r[label] = round(sorted(e0.elapsed_time(e1) for e0, e1 in evs)[iters // 2] * 1e3, 1)
+        assert torch.isfinite(out).all().item() and int(dc.cache.err_flag.item()) == 0
+        log(f"{name} step ({desc}): three calls {r['three_calls_us']} us, "
+            f"gva_decode_step {r['decode_step_us']} us")
+        res[name] = r
+        del dc
+        torch.cuda.empty_cache()
     return res
 
 
