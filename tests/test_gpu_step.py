@@ -64,6 +64,10 @@ def _run_step(c, pos, v_new, kr_raw, M, q_nope, q_rope, num_splits, fused, kerne
 
 SHAPES = [
     pytest.param("C1", dict(append_one=True, block_size=512), 1, id="C1-fp32"),
+    pytest.param("C4", dict(B=3, lengths_uniform=(200, 400), d_h=256, d_n=256, H=8, G=2, d_r=16),
+                 0, id="d_h-256"),
+    pytest.param("C4", dict(B=5, lengths_uniform=(100, 900), H=32, G=4), 0, id="eight-heads-per-group"),
+    pytest.param("C4", dict(B=40, lengths_uniform=(0, 300)), 0, id="forty-sequences"),
     pytest.param("C2", dict(append_one=True, block_size=8192), 0, id="C2-bf16-auto"),
     pytest.param("C2", dict(append_one=True, block_size=8192), 3, id="C2-bf16-S3"),
     pytest.param("C4", dict(B=9, lengths_uniform=(0, 700)), 0, id="ragged-paged-balanced"),
@@ -131,3 +135,23 @@ def test_step_flags_a_position_outside_the_rope_table():
     O.append(c.pool, c.dims, np.array(good), pos[good], v_new[good], kr_raw[good], c.tab_ora)
     ref, _ = c.oracle_decode(sl, q_ref, seqs=good)
     check_output(out[good], ref[good], "bf16", "healthy sequences")
+
+
+def test_step_with_empty_histories():
+    """Sequences whose new token is their first (pos = 0): the step appends it and the decode
+    reads that one position, so the output is the token's own values."""
+    w = synth.workload("C4", B=12, lengths_uniform=(0, 300))
+    lens = synth.lengths(w).copy()
+    lens[[0, 3, 7]] = 0
+    c = Case(w, lens=lens)
+    c.append_prefix()
+    pos, v_new, kr_raw, M, q_nope, q_rope, q_ref = _step_inputs(c, 4)
+    qa, out, lse = _run_step(c, pos, v_new, kr_raw, M, q_nope, q_rope, 0, fused=True)
+    O.append(c.pool, c.dims, np.arange(w.B), pos, v_new, kr_raw, c.tab_ora)
+    ref, ref_lse = c.oracle_decode(pos + 1, q_ref)
+    check_output(out, ref, "bf16", "empty histories")
+    ok, e = lse_ok(lse, ref_lse, 1e-3)
+    assert ok, e
+    V, _ = O.gather(c.pool, c.dims, 3, 1)
+    for h in range(w.H):
+        assert np.allclose(out[3, h], V[0, c.dims.group_of(h)], rtol=0, atol=1e-6)
