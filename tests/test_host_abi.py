@@ -184,19 +184,24 @@ def test_split_planning(L):
 
 
 def test_balanced_range_planning(L):
-    """The matrix-core kernel's automatic plan: equal tile ranges, at most one pass of three
-    four-wave work-groups per compute unit over 256 CUs (G=8 -> two work-groups per range), at
-    least 128 ranges or ranges of 32 tiles, never more ranges than tiles, and none for a single
-    sequence."""
+    """The matrix-core kernel's automatic plan: equal tile ranges, one pass of work-groups over
+    256 CUs, never more ranges than tiles, and none for a single sequence. With G a multiple of
+    8 a range is one 8-wave work-group (one per CU, sharing the positional key), so 256 ranges;
+    with G = 4, three four-wave work-groups per CU, so up to 768 ranges, at least 256 or ranges
+    of 32 tiles."""
     d = _dims()
-    assert gb.gva_decode_num_ranges(d, 256, 32769) == 384
-    assert gb.gva_decode_num_ranges(d, 4, 8705) == 128
-    assert gb.gva_decode_num_ranges(d, 16, 4096) == 128                # 2048 tiles / 32 < 128
-    assert gb.gva_decode_num_ranges(d, 64, 32768) == 384               # 65536 tiles: one pass
+    assert gb.gva_decode_num_ranges(d, 256, 32769) == 256
+    assert gb.gva_decode_num_ranges(d, 4, 8705) == 256
+    assert gb.gva_decode_num_ranges(d, 16, 4096) == 256                # 2048 tiles / 32 < 256
+    assert gb.gva_decode_num_ranges(d, 64, 32768) == 256               # one pass
     assert gb.gva_decode_num_ranges(d, 3, 40) == 6                     # one tile per range
     assert gb.gva_decode_num_ranges(d, 1, 131072) == 0
     assert gb.gva_decode_num_ranges(d, 2, 0) == 0
-    # the workspace query covers both plans
+    d4 = _dims(H=16, G=4, d_h=64, d_n=64)
+    assert gb.gva_decode_num_ranges(d4, 256, 32769) == 768             # 3 x 256 four-wave groups
+    assert gb.gva_decode_num_ranges(d4, 8, 4097) == 256                # 1032 tiles / 32 < 256
+    # the workspace query covers every plan, the GQA comparator's too (two four-wave
+    # work-groups per range at G = 8: up to 384 ranges)
     ws = gb.gva_decode_workspace_bytes(d, 256, 32769, 0)
     assert ws >= (384 + 256) * 32 * (128 + 2) * 4 + 257 * 4
 

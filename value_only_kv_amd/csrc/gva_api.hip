@@ -136,7 +136,7 @@ gva_status gva_gqa_decode(const gva_dims *dims, const gva_cache *values, const v
   bool use_mfma = false;
   gva_status st = gva::check_decode(dims, values, B, seq_len, max_len, q, scale, 0,
                                     GVA_KERNEL_MFMA, workspace, workspace_bytes, out, &plan,
-                                    &use_mfma);
+                                    &use_mfma, false);
   if (st != GVA_OK) return st;
   gva::DecodeArgs a = cache_args(dims, values);
   a.k = keys;

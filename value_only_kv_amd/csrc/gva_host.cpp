@@ -139,7 +139,7 @@ bool mfma_supported(const gva_dims *d, const gva_cache *c, const char **why) {
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
-                 bool balanced, DecodePlan *plan) {
+                 bool balanced, DecodePlan *plan, bool share_key) {
   if (!d || B < 1 || max_len < 0 || num_splits < 0 || num_splits > kMaxSplits) return false;
   *plan = DecodePlan{};
   const int64_t tiles_max = static_cast<int64_t>(B) * ((max_len + kTilePositions - 1) / kTilePositions);
@@ -150,10 +150,11 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
     // or ranges of kMinTilesPerRange tiles (assuming every sequence at max_len), whichever is
     // more. A single sequence gets the same cut from the split grid, without the search for
     // its range.
-    const int64_t nz = d->G / decode_waves_per_group(d->G);
+    const BalancedLayout lay = balanced_layout(d->G, share_key);
+    const int64_t nz = d->G / lay.waves;
     const int64_t by_size = (tiles_max + kMinTilesPerRange - 1) / kMinTilesPerRange;
     int64_t R = by_size > kPlanCUs / nz ? by_size : kPlanCUs / nz;
-    if (R > kBalancedWorkGroups / nz) R = kBalancedWorkGroups / nz;
+    if (R > kPlanCUs * lay.groups_per_cu / nz) R = kPlanCUs * lay.groups_per_cu / nz;
     if (R > tiles_max) R = tiles_max;
     if (R > kMaxSplits) R = kMaxSplits;
     if (R < 1) R = 1;
@@ -199,7 +200,7 @@ gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
                         const int32_t *seq_len, int32_t max_len, const float *q_abs,
                         float scale, int32_t num_splits, int32_t kernel, const void *workspace,
                         size_t workspace_bytes, const float *out, DecodePlan *plan,
-                        bool *use_mfma) {
+                        bool *use_mfma, bool share_key) {
   gva_status st = check_dims(d);
   if (st != GVA_OK) return st;
   if ((st = check_cache(d, c)) != GVA_OK) return st;
@@ -220,7 +221,7 @@ gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
   const bool can = mfma_supported(d, c, &why);
   if (kernel == GVA_KERNEL_MFMA && !can) return fail(GVA_ERR_UNSUPPORTED, "%s", why);
   *use_mfma = (kernel == GVA_KERNEL_MFMA) || (kernel == GVA_KERNEL_AUTO && can);
-  if (!plan_decode(d, B, max_len, num_splits, *use_mfma, plan))
+  if (!plan_decode(d, B, max_len, num_splits, *use_mfma, plan, share_key))
     return fail(GVA_ERR_INVALID_ARG, "cannot plan the decode split");
   if (plan->ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan->ws_bytes)
@@ -298,11 +299,14 @@ gva_status gva_rope_table_fill(double *host_out, int32_t max_pos, int32_t d_r, d
 size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
                                   int32_t num_splits) {
   if (gva::check_dims(dims) != GVA_OK) return 0;
-  // enough for either kernel's plan (the cache decides which one runs)
-  gva::DecodePlan p, pb;
+  // enough for either kernel's plan (the cache decides which one runs), and for the GQA
+  // comparator's balanced plan
+  gva::DecodePlan p, pb, pq;
   if (!gva::plan_decode(dims, B, max_len, num_splits, false, &p)) return 0;
   if (!gva::plan_decode(dims, B, max_len, num_splits, true, &pb)) return 0;
-  return p.ws_bytes > pb.ws_bytes ? p.ws_bytes : pb.ws_bytes;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, true, &pq, false)) return 0;
+  size_t ws = p.ws_bytes > pb.ws_bytes ? p.ws_bytes : pb.ws_bytes;
+  return ws > pq.ws_bytes ? ws : pq.ws_bytes;
 }
 
 int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,

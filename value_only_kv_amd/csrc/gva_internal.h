@@ -30,6 +30,19 @@ inline int decode_waves_per_group(int G) {
     if (G % w == 0) return w;
   return 1;
 }
+// The balanced plan of the GVA decode (not the GQA comparator) with G a multiple of 8 runs
+// 8-wave work-groups, one per CU: the eight value groups of a range share one work-group, so
+// its shared positional key is read from HBM once (by one wave, into LDS) instead of once per
+// wave. Other cases use the four-wave layout above, three work-groups per CU.
+constexpr int kSharedKeyWaves = 8;
+struct BalancedLayout {
+  int waves;            // waves (value groups) per work-group
+  int groups_per_cu;    // resident work-groups per CU the plan fills
+};
+inline BalancedLayout balanced_layout(int G, bool share_key) {
+  if (share_key && G % kSharedKeyWaves == 0) return {kSharedKeyWaves, 1};
+  return {decode_waves_per_group(G), kBalancedWorkGroups / kPlanCUs};
+}
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxH = 256;
 constexpr int kMaxDh = 256;
@@ -68,13 +81,13 @@ struct DecodePlan {
 // sequences' 32-position tiles into equal ranges (balanced == true, the matrix-core kernel's
 // automatic mode); returns false on bad arguments.
 bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
-                 bool balanced, DecodePlan *plan);
+                 bool balanced, DecodePlan *plan, bool share_key = true);
 
 gva_status check_decode(const gva_dims *d, const gva_cache *c, int32_t B,
                         const int32_t *seq_len, int32_t max_len, const float *q_abs,
                         float scale, int32_t num_splits, int32_t kernel, const void *workspace,
                         size_t workspace_bytes, const float *out, DecodePlan *plan,
-                        bool *use_mfma);
+                        bool *use_mfma, bool share_key = true);
 
 // The append and absorption parts of a decode step: token b goes to sequence b at pos[b], and
 // query b is absorbed at the same position with the cache's RoPE table.

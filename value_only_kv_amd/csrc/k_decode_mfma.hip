@@ -17,11 +17,15 @@
 //   D[i][j]: lane j + 16 (i / 4), register i % 4.
 // Write n = lane % 16 (a row of 16 lanes) and q = lane / 16.
 //
-// One wave per (chunk, group); a work-group holds four groups of the same chunk, and the
-// work-groups of one chunk run on the same XCD, so their reads of the shared positional key hit
-// in its L2. Chunks come from one of two work plans (see the kernel): per-sequence splits, or
-// equal ranges over the tiles of all sequences (balanced). A chunk is walked in tiles of 32
-// positions, two blocks of 16 (tb = 0, 1):
+// One wave per (chunk, group). Chunks come from one of two work plans (see the kernel):
+// per-sequence splits, or equal ranges over the tiles of all sequences (balanced). In the
+// balanced plan with G a multiple of 8, a work-group holds eight groups of the same range (one
+// work-group per CU) and only its wave 0 fetches the shared positional key; it passes each tile's
+// key to the other seven through LDS, one barrier per tile. Concurrent misses on the same line
+// are not merged by the caches, so letting every wave fetch the key read it two to three times
+// from HBM (2.9% more traffic on the ragged batch). Otherwise a work-group holds four groups
+// and every wave fetches the key, and the work-groups of one chunk take ids 8 apart so that they
+// run on the same XCD. A chunk is walked in tiles of 32 positions, two blocks of 16 (tb = 0, 1):
 //   1. V rows go straight from HBM into registers in A-operand form: lane (n, q) loads 16 bytes,
 //      8 consecutive dims 32 ks + 8 q .. of position 16 tb + n, for every k-step ks.
 //   2. Scores S^T[t][c] = sum_k V[t][k] Q[c][k]. The query keeps ~16 significant bits by being
@@ -40,8 +44,9 @@
 //      shift to place the hi parts.
 //   5. O^T accumulates in registers: lane (n, q) holds column n, dims 16 nb + 4 q + r; the hi
 //      and lo columns are added once, at the end.
-// The kernel needs 168 registers at d_h = 128, so three four-wave work-groups share a compute
-// unit (transposing V with selection-matrix MFMAs instead of the LDS load needed 250).
+// The four-wave layout needs 168 registers at d_h = 128, so three work-groups share a compute
+// unit (transposing V with selection-matrix MFMAs instead of the LDS load needed 250); the
+// eight-wave layout is alone on its CU and may use up to 256.
 //
 // The same template, with GQA = true, decodes the comparator cache of a matched grouped-query
 // model (G keys and G values per token): the score then contracts key rows loaded beside the
@@ -151,10 +156,13 @@ __device__ __forceinline__ int32_t load_pages(const int32_t *__restrict__ bt, in
 // multiple of 16), so one table entry serves all of its lanes. Positions >= c1 read position
 // c1 - 1 instead (finite data from a block that is cached already); their scores are masked, so
 // they add exactly zero. vlane/klane are the lane-invariant parts of the element offsets.
-template <int KS, bool GQA>
+// SHARE: only the waves with fetch_key read the positional key (the others read a row of their
+// own work-group, kown, which stays in cache, and take the key from LDS instead); every load is
+// still issued, so the loads in flight stay the same on every path.
+template <int KS, bool GQA, bool SHARE>
 __device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, int t0, int c1,
                                           int n, int64_t vlane, int64_t klane, Tile<KS, GQA> &T,
-                                          bool &bad) {
+                                          bool &bad, bool fetch_key, int64_t kown) {
   const int mask = (1 << a.log2_bs) - 1;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
   const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
@@ -176,8 +184,11 @@ __device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, i
       for (int ks = 0; ks < KS; ++ks) T.x[tb][ks] = *reinterpret_cast<const u32x4 *>(kp + 32 * ks);
       (void)kbase;
       (void)klane;
+      (void)fetch_key;
+      (void)kown;
     } else {
-      T.x[tb][0] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + klane);
+      const int64_t koff = !SHARE || fetch_key ? blk * a.kr_sb + row * a.kr_st : kown;
+      T.x[tb][0] = *reinterpret_cast<const u32x4 *>(kbase + koff + klane);
     }
   }
 }
@@ -192,11 +203,14 @@ struct Acc {
 
 // One tile: scores, online softmax and the weighted sum. NH > 0: merged hi/lo columns (see the
 // file comment); NH == 0: separate hi and lo MFMAs with QX = hi and QY = lo.
-template <int KS, int NH, bool GQA>
+// SHARE: the positional key comes from the work-group's LDS copy (this lane's 16 bytes of
+// block 0 at kx, of block 1 at kx + 1024) instead of the tile's registers.
+template <int KS, int NH, bool GQA, bool SHARE>
 __device__ __forceinline__ void tile_step(const Tile<KS, GQA> &cur, int t0, int c1, int n, int q,
                                           const bf16x8 (&QX)[KS], const bf16x8 (&QY)[KS],
                                           const bf16x8 &RX, const bf16x8 &RY, uint8_t *lw_wr,
-                                          const uint8_t *lw_rd, Acc<KS> &acc) {
+                                          const uint8_t *lw_rd, Acc<KS> &acc,
+                                          const uint8_t *kx) {
   constexpr int SH = NH > 0 ? NH : 1;
   using L = TileLds<KS>;
   // the tile's V rows go to the wave's LDS copy (row 16 tb + n, columns 32 ks + 8 q ..), to be
@@ -212,10 +226,12 @@ __device__ __forceinline__ void tile_step(const Tile<KS, GQA> &cur, int t0, int 
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
     // the score operand: the value rows plus the positional key (GVA) or the key rows (GQA)
     const u32x4 *sx = GQA ? cur.x[tb] : cur.v[tb];
+    // the positional key rows (GVA)
+    const u32x4 kx_tb = SHARE ? *reinterpret_cast<const u32x4 *>(kx + 1024 * tb) : cur.x[tb][0];
     if (NH > 0) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) s0 = mfma(as_bf16(sx[ks]), QX[ks], s0);
-      if (!GQA) s0 = mfma(as_bf16(cur.x[tb][0]), RX, s0);
+      if (!GQA) s0 = mfma(as_bf16(kx_tb), RX, s0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) s0[r] += row_shr_f<SH>(s0[r]);
     } else {
@@ -226,8 +242,8 @@ __device__ __forceinline__ void tile_step(const Tile<KS, GQA> &cur, int t0, int 
         s1 = mfma(as_bf16(sx[ks]), QY[ks], s1);
       }
       if (!GQA) {
-        s0 = mfma(as_bf16(cur.x[tb][0]), RX, s0);
-        s1 = mfma(as_bf16(cur.x[tb][0]), RY, s1);
+        s0 = mfma(as_bf16(kx_tb), RX, s0);
+        s1 = mfma(as_bf16(kx_tb), RY, s1);
       }
       s0 += s1;
     }
@@ -291,22 +307,23 @@ __device__ __forceinline__ void tile_step(const Tile<KS, GQA> &cur, int t0, int 
 
 // Waves per SIMD the register allocation must allow: three where the kernel fits in 168
 // registers without spilling (d_h <= 64, or d_h = 128 with merged hi/lo columns), else two.
-template <int KS, int NH, bool GQA>
+template <int KS, int NH, bool GQA, int WAVES>
 constexpr int min_waves_per_simd() {
-  return !GQA && (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
+  // an 8-wave work-group is alone on its CU (two waves per SIMD) whatever its registers
+  return WAVES == 8 ? 2 : !GQA && (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
 }
 
 // One chunk of positions [c0, c1) of sequence b for value group g (one wave): scores, online
 // softmax and weighted sum over its tiles, then the partial (m, l, o) of each of the group's heads
 // h at workspace row prow0 + h or, when `direct`, the final output row. len_bad makes the output
 // row NaN (its chunk is empty). lds is the work-group's LDS tile area.
-template <int KS, int NH, bool GQA>
+template <int KS, int NH, bool GQA, bool SHARE>
 __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g, int c0, int c1,
                                           bool len_bad, bool direct, int64_t prow0,
-                                          uint8_t *lds) {
+                                          uint8_t *lds, uint8_t *kbuf) {
   constexpr int SH = NH > 0 ? NH : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int q = lane >> 4;
   const int nhg = a.H / a.G;
@@ -376,19 +393,42 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
     // loop runs near the streaming rate already.)
     const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
     const int lb = a.log2_bs;
+    // SHARE: wave 0 fetches each tile's positional key and stores it in the work-group's key
+    // buffer (two tiles, 2 KB each: block tb, lane l at 1024 tb + 16 l); one barrier per tile
+    // publishes it. The buffer of tile t + 1 is written after tile t's step and after every
+    // wave has passed the barrier that ended tile t - 1, its last reader.
+    const bool fetch_key = wave == 0;
+    const int64_t kown = SHARE ? static_cast<int64_t>(blockIdx.x % a.num_blocks) * a.kr_sb : 0;
+    uint8_t *kb0 = kbuf;
+    uint8_t *kb1 = kbuf + 2048;
+    auto publish = [&](uint8_t *kb, const Tile<KS, GQA> &T) {
+      if constexpr (SHARE) {
+        if (fetch_key) {
+          *reinterpret_cast<u32x4 *>(kb + 16 * lane) = T.x[0][0];
+          *reinterpret_cast<u32x4 *>(kb + 1024 + 16 * lane) = T.x[1][0];
+        }
+        __syncthreads();
+      }
+    };
     Tile<KS, GQA> A, Bt;
     int32_t PA = load_pages(bt, lb, c0, c1, lane);
     int32_t PB = load_pages(bt, lb, c0 + kTile, c1, lane);
-    load_tile<KS, GQA>(a, PA, c0, c1, n, vlane, klane, A, bad);
+    load_tile<KS, GQA, SHARE>(a, PA, c0, c1, n, vlane, klane, A, bad, fetch_key, kown);
     PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
+    publish(kb0, A);
     for (int t0 = c0; t0 < c1; t0 += 2 * kTile) {
       const int t1 = t0 + kTile;
-      load_tile<KS, GQA>(a, PB, t1, c1, n, vlane, klane, Bt, bad);
+      load_tile<KS, GQA, SHARE>(a, PB, t1, c1, n, vlane, klane, Bt, bad, fetch_key, kown);
       PB = load_pages(bt, lb, t1 + 2 * kTile, c1, lane);
-      tile_step<KS, NH, GQA>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
-      load_tile<KS, GQA>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad);
+      tile_step<KS, NH, GQA, SHARE>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc,
+                                    kb0 + 16 * lane);
+      publish(kb1, Bt);
+      load_tile<KS, GQA, SHARE>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad, fetch_key, kown);
       PA = load_pages(bt, lb, t1 + 3 * kTile, c1, lane);
-      if (t1 < c1) tile_step<KS, NH, GQA>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc);
+      if (t1 < c1)                                     // uniform per work-group
+        tile_step<KS, NH, GQA, SHARE>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc,
+                                      kb1 + 16 * lane);
+      publish(kb0, A);
     }
   }
 
@@ -449,22 +489,26 @@ __device__ __forceinline__ int tiles_of(const gva::DecodeArgs &a, int b, int cap
   return (len >= 0 && len <= a.max_len && len <= cap) ? (len + kTile - 1) / kTile : 0;
 }
 
-template <int KS, int NH, bool BALANCED, bool GQA>
-__global__ __launch_bounds__(64 * kGroupWaves, (min_waves_per_simd<KS, NH, GQA>())) void
+// WAVES: the most waves (value groups) a work-group has; 8 only for the GVA balanced plan,
+// whose work-groups then share the positional key through LDS (SHARE).
+template <int KS, int NH, bool BALANCED, bool GQA, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, (min_waves_per_simd<KS, NH, GQA, WAVES>())) void
 k_decode_mfma(gva::DecodeArgs a) {
   using L = TileLds<KS>;
-  __shared__ __align__(16) uint8_t lds[kGroupWaves * L::kWave];
-  __shared__ int64_t s_part[kGroupWaves];
+  constexpr bool SHARE = WAVES == 8 && BALANCED && !GQA;
+  __shared__ __align__(16) uint8_t lds[WAVES * L::kWave];
+  __shared__ __align__(16) uint8_t kbuf[SHARE ? 4096 : 16];
+  __shared__ int64_t s_part[WAVES];
   __shared__ int32_t s_found_b;
-  __shared__ int32_t s_len[64 * kGroupWaves];
+  __shared__ int32_t s_len[64 * WAVES];
   __shared__ int64_t s_found_p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   // Work-groups are dealt to the 8 XCDs in turn (XCD = id % 8). The nz work-groups that share
   // one work item (they cover the same positions for different value groups) take ids 8 apart,
-  // so they run on the same XCD at about the same time and the shared positional key is fetched
-  // from HBM once.
+  // so they run on the same XCD at about the same time (their reads of the shared positional key
+  // still miss together about half the time).
   const int wpg = blockDim.x >> 6;
   const int nz = a.G / wpg;
   const int id = blockIdx.x;
@@ -485,8 +529,8 @@ k_decode_mfma(gva::DecodeArgs a) {
     if (len_bad && s == 0 && g == 0 && lane == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
     const int c0 = s * a.chunk;
     const int c1 = len_bad ? c0 : min(c0 + a.chunk, len);
-    run_chunk<KS, NH, GQA>(a, b, g, c0, c1, len_bad, a.num_splits == 1,
-                      (static_cast<int64_t>(b) * a.num_splits + s) * a.H, lds);
+    run_chunk<KS, NH, GQA, SHARE>(a, b, g, c0, c1, len_bad, a.num_splits == 1,
+                      (static_cast<int64_t>(b) * a.num_splits + s) * a.H, lds, kbuf);
   } else {
 
   // Balanced ranges: the 32-position tiles of all sequences, concatenated in sequence order
@@ -574,7 +618,7 @@ k_decode_mfma(gva::DecodeArgs a) {
     const int len = len_of(b);
     const int c0 = static_cast<int>(t - pb) * kTile;
     const int c1 = min(static_cast<int>(seg_end - pb) * kTile, len);
-    run_chunk<KS, NH, GQA>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H, lds);
+    run_chunk<KS, NH, GQA, SHARE>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H, lds, kbuf);
     t = seg_end;
     pb += tiles_b;
     ++b;
@@ -583,17 +627,17 @@ k_decode_mfma(gva::DecodeArgs a) {
   }
 }
 
-template <int NH, bool BAL, bool GQA>
+template <int NH, bool BAL, bool GQA, int W>
 hipError_t launch_mode(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH, BAL, GQA>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH, BAL, GQA>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_mfma<1, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_mfma<2, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_decode_mfma<3, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_mfma<4, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((k_decode_mfma<5, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_decode_mfma<6, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((k_decode_mfma<7, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_mfma<8, NH, BAL, GQA, W>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -602,11 +646,13 @@ hipError_t launch_mode(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStrea
 template <int NH>
 hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   if (a.k) {
-    return a.num_ranges > 0 ? launch_mode<NH, true, true>(a, grid, block, stream)
-                            : launch_mode<NH, false, true>(a, grid, block, stream);
+    return a.num_ranges > 0 ? launch_mode<NH, true, true, kGroupWaves>(a, grid, block, stream)
+                            : launch_mode<NH, false, true, kGroupWaves>(a, grid, block, stream);
   }
-  return a.num_ranges > 0 ? launch_mode<NH, true, false>(a, grid, block, stream)
-                          : launch_mode<NH, false, false>(a, grid, block, stream);
+  if (a.num_ranges == 0) return launch_mode<NH, false, false, kGroupWaves>(a, grid, block, stream);
+  return block.x == 64u * gva::kSharedKeyWaves
+             ? launch_mode<NH, true, false, gva::kSharedKeyWaves>(a, grid, block, stream)
+             : launch_mode<NH, true, false, kGroupWaves>(a, grid, block, stream);
 }
 
 }  // namespace
@@ -614,7 +660,9 @@ hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_
 namespace gva {
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
-  const int wpg = decode_waves_per_group(a.G);
+  // the GVA balanced plan's layout (as plan_decode chose it), else four-wave work-groups
+  const int wpg = a.num_ranges > 0 && !a.k ? balanced_layout(a.G, true).waves
+                                           : decode_waves_per_group(a.G);
   const int64_t items = a.num_ranges > 0 ? a.num_ranges : static_cast<int64_t>(a.B) * a.num_splits;
   const dim3 grid(static_cast<unsigned>(((items + 7) / 8) * 8 * (a.G / wpg)));
   const dim3 block(64 * wpg);
