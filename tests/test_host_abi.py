@@ -186,13 +186,14 @@ def test_split_planning(L):
 def test_balanced_range_planning(L):
     """The matrix-core kernel's automatic plan: equal tile ranges, one pass of work-groups over
     256 CUs, never more ranges than tiles, and none for a single sequence. With G a multiple of
-    8 a range is one 8-wave work-group (one per CU, sharing the positional key), so 256 ranges;
-    with G = 4, three four-wave work-groups per CU, so up to 768 ranges, at least 256 or ranges
-    of 32 tiles."""
+    8 and at least 256 ranges of 32 tiles, a range is one 8-wave work-group (one per CU, sharing
+    the positional key), so 256 ranges; otherwise three four-wave work-groups per CU, so up to
+    3 * 256 / (G / 4) ranges, at least 256 / (G / 4) or ranges of 32 tiles."""
     d = _dims()
     assert gb.gva_decode_num_ranges(d, 256, 32769) == 256
-    assert gb.gva_decode_num_ranges(d, 4, 8705) == 256
-    assert gb.gva_decode_num_ranges(d, 16, 4096) == 256                # 2048 tiles / 32 < 256
+    assert gb.gva_decode_num_ranges(d, 8, 32768) == 256                # 8192 tiles: shared key
+    assert gb.gva_decode_num_ranges(d, 4, 8705) == 128                 # 1092 tiles: four-wave
+    assert gb.gva_decode_num_ranges(d, 16, 4096) == 128                # 2048 tiles / 32 < 128
     assert gb.gva_decode_num_ranges(d, 64, 32768) == 256               # one pass
     assert gb.gva_decode_num_ranges(d, 3, 40) == 6                     # one tile per range
     assert gb.gva_decode_num_ranges(d, 1, 131072) == 0

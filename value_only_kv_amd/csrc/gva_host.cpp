@@ -150,7 +150,7 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
     // or ranges of kMinTilesPerRange tiles (assuming every sequence at max_len), whichever is
     // more. A single sequence gets the same cut from the split grid, without the search for
     // its range.
-    const BalancedLayout lay = balanced_layout(d->G, share_key);
+    const BalancedLayout lay = balanced_layout(d->G, share_key, tiles_max);
     const int64_t nz = d->G / lay.waves;
     const int64_t by_size = (tiles_max + kMinTilesPerRange - 1) / kMinTilesPerRange;
     int64_t R = by_size > kPlanCUs / nz ? by_size : kPlanCUs / nz;

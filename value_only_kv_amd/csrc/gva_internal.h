@@ -30,17 +30,21 @@ inline int decode_waves_per_group(int G) {
     if (G % w == 0) return w;
   return 1;
 }
-// The balanced plan of the GVA decode (not the GQA comparator) with G a multiple of 8 runs
-// 8-wave work-groups, one per CU: the eight value groups of a range share one work-group, so
-// its shared positional key is read from HBM once (by one wave, into LDS) instead of once per
-// wave. Other cases use the four-wave layout above, three work-groups per CU.
+// The balanced plan of the GVA decode (not the GQA comparator) with G a multiple of 8 and
+// enough tiles for ranges of kMinTilesPerRange tiles runs 8-wave work-groups, one per CU: the
+// eight value groups of a range share one work-group, so its shared positional key is read from
+// HBM once (by one wave, into LDS) instead of once per wave. Smaller batches (a few tiles per
+// range, where the per-tile barrier costs more than the key's bytes) and other G use the
+// four-wave layout above, three work-groups per CU. tiles_max = B * ceil(max_len / 32).
 constexpr int kSharedKeyWaves = 8;
 struct BalancedLayout {
   int waves;            // waves (value groups) per work-group
   int groups_per_cu;    // resident work-groups per CU the plan fills
 };
-inline BalancedLayout balanced_layout(int G, bool share_key) {
-  if (share_key && G % kSharedKeyWaves == 0) return {kSharedKeyWaves, 1};
+inline BalancedLayout balanced_layout(int G, bool share_key, int64_t tiles_max) {
+  if (share_key && G % kSharedKeyWaves == 0 &&
+      tiles_max >= static_cast<int64_t>(kPlanCUs) * kMinTilesPerRange)
+    return {kSharedKeyWaves, 1};
   return {decode_waves_per_group(G), kBalancedWorkGroups / kPlanCUs};
 }
 constexpr int kMaxSplits = 1024;

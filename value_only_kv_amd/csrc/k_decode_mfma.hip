@@ -661,7 +661,8 @@ namespace gva {
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
   // the GVA balanced plan's layout (as plan_decode chose it), else four-wave work-groups
-  const int wpg = a.num_ranges > 0 && !a.k ? balanced_layout(a.G, true).waves
+  const int64_t tiles_max = static_cast<int64_t>(a.B) * ((a.max_len + kTile - 1) / kTile);
+  const int wpg = a.num_ranges > 0 && !a.k ? balanced_layout(a.G, true, tiles_max).waves
                                            : decode_waves_per_group(a.G);
   const int64_t items = a.num_ranges > 0 ? a.num_ranges : static_cast<int64_t>(a.B) * a.num_splits;
   const dim3 grid(static_cast<unsigned>(((items + 7) / 8) * 8 * (a.G / wpg)));
