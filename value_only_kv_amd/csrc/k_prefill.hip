@@ -9,17 +9,17 @@
 // sum are [rows x (d_h + d_r)] x [(d_h + d_r) x keys] and [rows x keys] x [keys x d_h] products
 // with rows = (query, head) pairs of one value group.
 //
-// Work-group: 16 waves (8 for d_h above 128) of one (sequence, group), each owning a tile of
-// 16 rows, rows ordered (query, head) with the head fastest; the work-group is the only one on
-// its compute unit, and its 16 waves (four per SIMD) hide each other's latencies. Keys are
-// walked in tiles of 32 positions,
+// Work-group: 8 waves of one (sequence, group), two per SIMD, rows ordered (query, head) with
+// the head fastest. Up to d_h = 128 each wave owns two tiles of 16 rows, so every operand it
+// reads from LDS feeds the products of both (half the LDS instructions per product of one tile
+// per wave); above, one. Keys are walked in tiles of 32 positions,
 // loaded two tiles ahead into registers and staged once per work-group in LDS as natural rows
 // [v (d_h) | kr (d_r, zero-padded to 32)] (double-buffered, one barrier per tile). They serve
 //   * the scores S^T[key][row] = sum_k K[key][k] Q[row][k]: A = the natural rows, B = the
 //     absorbed query as a bf16 hi + lo pair (two products), and
 //   * the weighted sum O^T[dim][row] += sum_key V^T[dim][key] P^T[key][row]: A = V^T, read
 //     from the same rows with the transposing LDS load (ds_read_b64_tr_b16), B = P in bf16.
-// Each lane holds row n = lane % 16 of its wave's tile and keys 16 tb + 4 q + r of each 16-key
+// Each lane holds row n = lane % 16 of each of its wave's row tiles and keys 16 tb + 4 q + r of each 16-key
 // block (q = lane / 16), which is the K order (q, e) -> 16 (e / 4) + 4 q + e % 4 in which the
 // transposing load delivers V^T, so P feeds the second product from the lane's own registers.
 // Accumulation and the online softmax (base-2 domain) are float32. The softmax keeps a lazily
@@ -42,12 +42,15 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// One row tile of 16 per wave; 16 waves up to d_h = 128 (128 registers each, four waves per
-// SIMD), 8 above, where the query and the accumulators need more registers.
+// Eight waves per work-group, two per SIMD (up to 256 registers each). Each wave owns RT row
+// tiles of 16 rows: two up to d_h = 128, so that every LDS read of a key or V^T operand feeds
+// the products of both, and one above, where the query and the accumulators need the
+// registers.
+constexpr int kWaves = 8;
 template <int KS>
-constexpr int waves() { return KS <= 4 ? 16 : 8; }
+constexpr int row_tiles() { return KS <= 4 ? 2 : 1; }
 template <int KS>
-constexpr int rows_per_group() { return waves<KS>() * 16; }
+constexpr int rows_per_group() { return kWaves * 16 * row_tiles<KS>(); }
 constexpr int kKeyTile = 32;
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -161,52 +164,54 @@ struct TileLds {
 // A-operand form: key 16 kb + n, elements 32 ks + 8 q .. + 8. Every load is unconditional
 // (keys past the end repeat the last), so the compiler can count the loads in flight exactly
 // and wait only for the one it needs.
-template <int KS>
+template <int KS, int W>
 struct Stage {
   static constexpr int kUnits = 2 * (KS + 1);
-  static constexpr int kPerWave = (kUnits + waves<KS>() - 1) / waves<KS>();
+  static constexpr int kPerWave = (kUnits + W - 1) / W;
   u32x4 u[kPerWave];
 };
 
 // Block-table entries of the keys a wave's units read in one tile. They are loaded one stage
 // before the data loads that use them, so that waiting for them does not also wait for the
 // tile still in flight (memory loads complete in order).
-template <int KS>
+template <int KS, int W>
 struct StagePages {
-  int32_t pb[Stage<KS>::kPerWave];
+  int32_t pb[Stage<KS, W>::kPerWave];
 };
 
-template <int KS>
+template <int KS, int W>
 __device__ __forceinline__ int stage_unit(int wave, int i) {
-  return min(wave + waves<KS>() * i, Stage<KS>::kUnits - 1);
+  return min(wave + W * i, Stage<KS, W>::kUnits - 1);
 }
 // keys past the end repeat the last
 __device__ __forceinline__ int stage_key(int kt0, int unit, int n, int kend) {
   return min(kt0 + 16 * (unit & 1) + n, kend - 1);
 }
 
-template <int KS>
+template <int KS, int W>
 __device__ __forceinline__ void stage_pages(const gva::DecodeArgs &a, const int32_t *__restrict__ bt,
-                                            int kt0, int kend, int wave, int n, StagePages<KS> &pg) {
+                                            int kt0, int kend, int wave, int n,
+                                            StagePages<KS, W> &pg) {
 #pragma unroll
-  for (int i = 0; i < Stage<KS>::kPerWave; ++i)
-    pg.pb[i] = bt[stage_key(kt0, stage_unit<KS>(wave, i), n, kend) >> a.log2_bs];
+  for (int i = 0; i < Stage<KS, W>::kPerWave; ++i)
+    pg.pb[i] = bt[stage_key(kt0, stage_unit<KS, W>(wave, i), n, kend) >> a.log2_bs];
 }
 
 // Where this lane's units read: a fixed base pointer and the per-block and per-token strides of
 // the value or positional-key rows (the units, and so the choice, are fixed per wave).
-template <int KS>
+template <int KS, int W>
 struct StageSrc {
-  const uint16_t *base[Stage<KS>::kPerWave];
-  int64_t sb[Stage<KS>::kPerWave], st[Stage<KS>::kPerWave];
+  const uint16_t *base[Stage<KS, W>::kPerWave];
+  int64_t sb[Stage<KS, W>::kPerWave], st[Stage<KS, W>::kPerWave];
 };
 
-template <int KS>
-__device__ __forceinline__ StageSrc<KS> stage_src(const gva::DecodeArgs &a, int g, int wave, int q) {
-  StageSrc<KS> src;
+template <int KS, int W>
+__device__ __forceinline__ StageSrc<KS, W> stage_src(const gva::DecodeArgs &a, int g, int wave,
+                                                     int q) {
+  StageSrc<KS, W> src;
 #pragma unroll
-  for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
-    const int ks = stage_unit<KS>(wave, i) >> 1;
+  for (int i = 0; i < Stage<KS, W>::kPerWave; ++i) {
+    const int ks = stage_unit<KS, W>(wave, i) >> 1;
     if (ks < KS) {
       src.base[i] = static_cast<const uint16_t *>(a.v) + static_cast<int64_t>(g) * a.v_sg + 32 * ks + 8 * q;
       src.sb[i] = a.v_sb;
@@ -221,29 +226,29 @@ __device__ __forceinline__ StageSrc<KS> stage_src(const gva::DecodeArgs &a, int 
   return src;
 }
 
-template <int KS>
-__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const StageSrc<KS> &src,
-                                           const StagePages<KS> &pg, int kt0, int kend, int wave,
-                                           int n, Stage<KS> &st) {
+template <int KS, int W>
+__device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const StageSrc<KS, W> &src,
+                                           const StagePages<KS, W> &pg, int kt0, int kend,
+                                           int wave, int n, Stage<KS, W> &st) {
   const int mask = (1 << a.log2_bs) - 1;
 #pragma unroll
-  for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
+  for (int i = 0; i < Stage<KS, W>::kPerWave; ++i) {
     const int32_t pb = pg.pb[i];
     // block ids are below 2^31 (checked on the host): one unsigned compare covers both ends
     const int64_t blk = static_cast<uint32_t>(pb) < static_cast<uint32_t>(a.num_blocks) ? pb : 0;
-    const int64_t row = stage_key(kt0, stage_unit<KS>(wave, i), n, kend) & mask;
+    const int64_t row = stage_key(kt0, stage_unit<KS, W>(wave, i), n, kend) & mask;
     st.u[i] = *reinterpret_cast<const u32x4 *>(src.base[i] + blk * src.sb[i] + row * src.st[i]);
   }
 }
 
-template <int KS>
+template <int KS, int W>
 __device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int q, int d_r,
-                                            const Stage<KS> &st) {
+                                            const Stage<KS, W> &st) {
   using L = TileLds<KS>;
 #pragma unroll
-  for (int i = 0; i < Stage<KS>::kPerWave; ++i) {
-    const int unit = wave + waves<KS>() * i;
-    if (unit >= Stage<KS>::kUnits) break;              // uniform per wave
+  for (int i = 0; i < Stage<KS, W>::kPerWave; ++i) {
+    const int unit = wave + W * i;
+    if (unit >= Stage<KS, W>::kUnits) break;           // uniform per wave
     const int kb = unit & 1;
     const int ks = unit >> 1;
     u32x4 w = st.u[i];
@@ -253,8 +258,10 @@ __device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int 
 }
 
 template <int KS>
-__global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p) {
+__global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   using L = TileLds<KS>;
+  constexpr int W = kWaves;
+  constexpr int RT = row_tiles<KS>();
   constexpr int kRows = rows_per_group<KS>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][L::kElems];
   const gva::DecodeArgs &a = p.kv;
@@ -291,16 +298,17 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
   const int cap = a.max_blocks << a.log2_bs;
   const bool seq_bad = P0 < 0 || P0 > p.max_start || P0 + C > cap;
 
-  // the row tile of this wave: rows row0 + 16 wave + 0..15; this lane's row (the B column) is n
-  const int r = row0 + 16 * wave + n;
-  const bool rvalid = r < nrows;
-  int qpos;                       // position of this lane's query
-  bf16x8 QH[KS + 1], QL[KS + 1];  // query hi and lo parts (B operand)
-  {
-    const int rc = rvalid ? r : nrows - 1;
+  // Row tile rt of this wave: rows row0 + 16 (RT wave + rt) + 0..15; this lane's row (the B
+  // column) is n of each.
+  int qpos[RT];                            // position of this lane's query in row tile rt
+  bf16x8 QH[RT][KS + 1], QL[RT][KS + 1];   // query hi and lo parts (B operand)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = row0 + 16 * (RT * wave + rt) + n;
+    const int rc = r < nrows ? r : nrows - 1;
     const int qi = rc / nhg;
     const int h = g * nhg + (rc - qi * nhg);
-    qpos = P0 + qi;
+    qpos[rt] = P0 + qi;
     const float *qp = p.q_abs + ((static_cast<int64_t>(b) * C + qi) * a.H + h) * row_len;
 #pragma unroll
     for (int ks = 0; ks <= KS; ++ks) {
@@ -322,19 +330,26 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
         hi[i] = w;
         lo[i] = pack2(x0 - low_bf16(w), x1 - high_bf16(w));
       }
-      QH[ks] = as_bf16(hi);
-      QL[ks] = as_bf16(lo);
+      QH[rt][ks] = as_bf16(hi);
+      QL[rt][ks] = as_bf16(lo);
     }
   }
 
-  f32x4 O[2 * KS];
+  f32x4 O[RT][2 * KS];
 #pragma unroll
-  for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) O[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Online softmax with a lazily raised reference: mref is the row's reference maximum (base 2),
   // -inf until the row's first unmasked key. The scores of a tile accumulate on top of negm =
   // -mref (0 while mref = -inf), so the probabilities are exp2 of the accumulators directly.
-  float mref = -INFINITY, lsum = 0.0f;
-  f32x4 negm = {0.f, 0.f, 0.f, 0.f};
+  float mref[RT], lsum[RT], negm[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    mref[rt] = -INFINITY;
+    lsum[rt] = 0.0f;
+    negm[rt] = 0.0f;
+  }
 
   // keys 0 .. kend - 1 are seen by some row of this work-group
   const int last_row = min(row0 + kRows, nrows) - 1;
@@ -344,63 +359,90 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
   // transposing-read address of this lane: row lane / 4, columns 4 (lane % 4) ..
   const int tr_off = (lane >> 2) * L::kNatStride + 4 * (lane & 3);
 
-  // One key tile: scores, mask, online softmax, weighted sum, on the LDS rows in nat.
-  auto tile = [&](const uint16_t *nat, int kt0) {
-    f32x4 S[2] = {negm, negm};
+  f32x4 S[RT][2];   // scores of the current tile, from its products to its softmax
+  u32x4 PB[RT];     // its probabilities (bf16 pairs), from its softmax to its weighted sum
+
+  // Score products of the tile in nat (starting at key kt0), and its causal mask.
+  auto scores = [&](const uint16_t *nat, int kt0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) S[rt][0] = S[rt][1] = f32x4{negm[rt], negm[rt], negm[rt], negm[rt]};
 #pragma unroll
     for (int ks = 0; ks <= KS; ++ks) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const u32x4 ka = *reinterpret_cast<const u32x4 *>(nat + (16 * tb + n) * L::kNatStride +
                                                           32 * ks + 8 * q);
-        S[tb] = mfma(as_bf16(ka), QH[ks], S[tb]);
-        S[tb] = mfma(as_bf16(ka), QL[ks], S[tb]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          S[rt][tb] = mfma(as_bf16(ka), QH[rt][ks], S[rt][tb]);
+          S[rt][tb] = mfma(as_bf16(ka), QL[rt][ks], S[rt][tb]);
+        }
       }
     }
     // causal mask (only tiles that reach past the first query)
     if (kt0 + kKeyTile - 1 > first_q) {
 #pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kt0 + 16 * tb + 4 * q + e > qpos[rt]) S[rt][tb][e] = -INFINITY;
+    }
+  };
+  // Online softmax of the scores S into PB (and the rare move of the reference).
+  auto softmax = [&]() {
+    float mt[RT];
+    bool raise[RT];
+    bool any_raise = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const f32x4 &s0 = S[rt][0], &s1 = S[rt][1];
+      mt[rt] = row_max(max2(max3(s0[0], s0[1], s0[2]), max3(s0[3], s1[0], max3(s1[1], s1[2], s1[3]))));
+      raise[rt] = mt[rt] > kLazyRescale || (mref[rt] == -INFINITY && mt[rt] != -INFINITY);
+      any_raise = any_raise || raise[rt];
+    }
+    if (__any(any_raise)) {   // rare after the first tiles: move the reference to the tile maximum
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float delta = raise[rt] ? mt[rt] : 0.0f;
+        const float mnew = mref[rt] == -INFINITY ? mt[rt] : mref[rt] + delta;
+        const float alpha = raise[rt] ? __builtin_amdgcn_exp2f(mref[rt] - mnew) : 1.0f;   // 0 from -inf
+        mref[rt] = raise[rt] ? mnew : mref[rt];
+        negm[rt] = raise[rt] ? -mnew : negm[rt];
+        lsum[rt] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) S[rt][tb] -= delta;
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float pv[8];
+#pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (kt0 + 16 * tb + 4 * q + e > qpos) S[tb][e] = -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          pv[4 * tb + e] = __builtin_amdgcn_exp2f(S[rt][tb][e]);
+          lsum[rt] += pv[4 * tb + e];
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) PB[rt][i] = pack2(pv[2 * i], pv[2 * i + 1]);
     }
-    // tile maximum relative to the reference
-    const float mt = row_max(max2(max3(S[0][0], S[0][1], S[0][2]),
-                                  max3(S[0][3], S[1][0], max3(S[1][1], S[1][2], S[1][3]))));
-    const bool raise = mt > kLazyRescale || (mref == -INFINITY && mt != -INFINITY);
-    if (__any(raise)) {   // rare after the first tiles: move the reference to the tile maximum
-      const float delta = raise ? mt : 0.0f;
-      const float mnew = mref == -INFINITY ? mt : mref + delta;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;   // 0 from -inf
-      mref = raise ? mnew : mref;
-      negm = raise ? f32x4{-mnew, -mnew, -mnew, -mnew} : negm;
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) O[i] *= alpha;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) S[tb] -= delta;
-    }
-    float pv[8];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pv[4 * tb + e] = __builtin_amdgcn_exp2f(S[tb][e]);
-        lsum += pv[4 * tb + e];
-      }
-    u32x4 PB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) PB[i] = pack2(pv[2 * i], pv[2 * i + 1]);
-    // O^T[dim][row] += V^T[dim][key] P^T[key][row]; V^T of dims 16 nb .. read transposed:
-    // the first read gives keys 4 q .. + 3 of block 0, the second the same of block 1
+  };
+  // Weighted sum of the tile in nat with PB: O^T[dim][row] += V^T[dim][key] P^T[key][row]; V^T
+  // of dims 16 nb .. read transposed: the first read gives keys 4 q .. + 3 of block 0, the
+  // second the same of block 1.
+  auto weighted_sum = [&](const uint16_t *nat) {
 #pragma unroll
     for (int nb = 0; nb < 2 * KS; ++nb) {
       const i16x4 v0 = read_tr(nat + tr_off + 16 * nb);
       const i16x4 v1 = read_tr(nat + tr_off + 16 * L::kNatStride + 16 * nb);
       const bf16x8 VT = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      O[nb] = mfma(VT, as_bf16(PB), O[nb]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) O[rt][nb] = mfma(VT, as_bf16(PB[rt]), O[rt][nb]);
     }
   };
 
@@ -410,59 +452,68 @@ __global__ __launch_bounds__(64 * waves<KS>()) void k_prefill(gva::PrefillArgs p
     // alternate roles, so the loop runs over pairs of tiles; it has no early exit, so that the
     // number of loads in flight is the same on every path into its head, and the last one or
     // two tiles follow it. Loads past the last tile read its keys again and are not used.
+    auto tile = [&](const uint16_t *nat, int kt0) {
+      scores(nat, kt0);
+      softmax();
+      weighted_sum(nat);
+    };
     const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
-    const StageSrc<KS> src = stage_src<KS>(a, g, wave, q);
-    Stage<KS> s0, s1;
-    StagePages<KS> p0, p1;
-    stage_pages<KS>(a, bt, 0, kend, wave, n, p0);
-    stage_pages<KS>(a, bt, kKeyTile, kend, wave, n, p1);
-    stage_load<KS>(a, src, p0, 0, kend, wave, n, s0);
-    stage_pages<KS>(a, bt, 2 * kKeyTile, kend, wave, n, p0);
-    stage_load<KS>(a, src, p1, kKeyTile, kend, wave, n, s1);
-    stage_pages<KS>(a, bt, 3 * kKeyTile, kend, wave, n, p1);
-    stage_store<KS>(lds[0], wave, n, q, a.d_r, s0);
+    const StageSrc<KS, W> src = stage_src<KS, W>(a, g, wave, q);
+    Stage<KS, W> s0, s1;
+    StagePages<KS, W> p0, p1;
+    stage_pages<KS, W>(a, bt, 0, kend, wave, n, p0);
+    stage_pages<KS, W>(a, bt, kKeyTile, kend, wave, n, p1);
+    stage_load<KS, W>(a, src, p0, 0, kend, wave, n, s0);
+    stage_pages<KS, W>(a, bt, 2 * kKeyTile, kend, wave, n, p0);
+    stage_load<KS, W>(a, src, p1, kKeyTile, kend, wave, n, s1);
+    stage_pages<KS, W>(a, bt, 3 * kKeyTile, kend, wave, n, p1);
+    stage_store<KS, W>(lds[0], wave, n, q, a.d_r, s0);
     __syncthreads();
     int t = 0;
     for (; t + 2 < ntiles; t += 2) {
       const int kt0 = t * kKeyTile;
       // tile t in lds[0]; tile t + 1 in s1; s0 free; p0 holds the pages of tile t + 2
-      stage_load<KS>(a, src, p0, kt0 + 2 * kKeyTile, kend, wave, n, s0);
-      stage_pages<KS>(a, bt, kt0 + 4 * kKeyTile, kend, wave, n, p0);
+      stage_load<KS, W>(a, src, p0, kt0 + 2 * kKeyTile, kend, wave, n, s0);
+      stage_pages<KS, W>(a, bt, kt0 + 4 * kKeyTile, kend, wave, n, p0);
       tile(lds[0], kt0);
-      stage_store<KS>(lds[1], wave, n, q, a.d_r, s1);
+      stage_store<KS, W>(lds[1], wave, n, q, a.d_r, s1);
       __syncthreads();
       // tile t + 1 in lds[1]; tile t + 2 in s0; s1 free; p1 holds the pages of tile t + 3
-      stage_load<KS>(a, src, p1, kt0 + 3 * kKeyTile, kend, wave, n, s1);
-      stage_pages<KS>(a, bt, kt0 + 5 * kKeyTile, kend, wave, n, p1);
+      stage_load<KS, W>(a, src, p1, kt0 + 3 * kKeyTile, kend, wave, n, s1);
+      stage_pages<KS, W>(a, bt, kt0 + 5 * kKeyTile, kend, wave, n, p1);
       tile(lds[1], kt0 + kKeyTile);
-      stage_store<KS>(lds[0], wave, n, q, a.d_r, s0);
+      stage_store<KS, W>(lds[0], wave, n, q, a.d_r, s0);
       __syncthreads();
     }
     // one or two tiles left: tile t in lds[0], tile t + 1 (if any) in s1
     tile(lds[0], t * kKeyTile);
     if (t + 1 < ntiles) {                              // uniform per work-group
-      stage_store<KS>(lds[1], wave, n, q, a.d_r, s1);
+      stage_store<KS, W>(lds[1], wave, n, q, a.d_r, s1);
       __syncthreads();
       tile(lds[1], (t + 1) * kKeyTile);
     }
   }
 
-  // ---- epilogue: lane (n, q) holds row n, dims 16 nb + 4 q + e ----
-  const float lt = gvad::xor32_sum(gvad::xor16_sum(lsum));
-  if (rvalid) {
-    const int qi = r / nhg;
-    const int h = g * nhg + (r - qi * nhg);
-    const int64_t orow = (static_cast<int64_t>(b) * C + qi) * a.H + h;
-    float *dst = p.out + orow * a.d_h + 4 * q;
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  // ---- epilogue: lane (n, q) holds row n of each row tile, dims 16 nb + 4 q + e ----
 #pragma unroll
-    for (int nb = 0; nb < 2 * KS; ++nb) {
-      f32x4 v = O[nb] * inv;
-      if (seq_bad) v = f32x4{qnan, qnan, qnan, qnan};
-      *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lt = gvad::xor32_sum(gvad::xor16_sum(lsum[rt]));
+    const int r = row0 + 16 * (RT * wave + rt) + n;
+    if (r < nrows) {
+      const int qi = r / nhg;
+      const int h = g * nhg + (r - qi * nhg);
+      const int64_t orow = (static_cast<int64_t>(b) * C + qi) * a.H + h;
+      float *dst = p.out + orow * a.d_h + 4 * q;
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2 * KS; ++nb) {
+        f32x4 v = O[rt][nb] * inv;
+        if (seq_bad) v = f32x4{qnan, qnan, qnan, qnan};
+        *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
+      }
+      if (p.lse && q == 0)
+        p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (mref[rt] + log2f(lt)) * gvad::kLn2 : -INFINITY);
     }
-    if (p.lse && q == 0)
-      p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (mref + log2f(lt)) * gvad::kLn2 : -INFINITY);
   }
   if (seq_bad && threadIdx.x == 0 && rb == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
 }
@@ -481,17 +532,23 @@ hipError_t launch_prefill(const PrefillArgs &p, hipStream_t stream) {
   const int nrows = C * (a.H / a.G);
   const int64_t pairs = static_cast<int64_t>(a.G) * a.B;
   auto grid = [&](int rows) { return dim3(static_cast<unsigned>((nrows + rows - 1) / rows * pairs)); };
+#define GVA_PREFILL_CASE(KS)                                                                  \
+  case KS:                                                                                    \
+    hipLaunchKernelGGL(k_prefill<KS>, grid(rows_per_group<KS>()), dim3(64 * kWaves), 0,       \
+                       stream, p);                                                            \
+    break;
   switch (a.d_h / 32) {
-    case 1: hipLaunchKernelGGL(k_prefill<1>, grid(rows_per_group<1>()), dim3(64 * waves<1>()), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(k_prefill<2>, grid(rows_per_group<2>()), dim3(64 * waves<2>()), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(k_prefill<3>, grid(rows_per_group<3>()), dim3(64 * waves<3>()), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(k_prefill<4>, grid(rows_per_group<4>()), dim3(64 * waves<4>()), 0, stream, p); break;
-    case 5: hipLaunchKernelGGL(k_prefill<5>, grid(rows_per_group<5>()), dim3(64 * waves<5>()), 0, stream, p); break;
-    case 6: hipLaunchKernelGGL(k_prefill<6>, grid(rows_per_group<6>()), dim3(64 * waves<6>()), 0, stream, p); break;
-    case 7: hipLaunchKernelGGL(k_prefill<7>, grid(rows_per_group<7>()), dim3(64 * waves<7>()), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(k_prefill<8>, grid(rows_per_group<8>()), dim3(64 * waves<8>()), 0, stream, p); break;
+    GVA_PREFILL_CASE(1)
+    GVA_PREFILL_CASE(2)
+    GVA_PREFILL_CASE(3)
+    GVA_PREFILL_CASE(4)
+    GVA_PREFILL_CASE(5)
+    GVA_PREFILL_CASE(6)
+    GVA_PREFILL_CASE(7)
+    GVA_PREFILL_CASE(8)
     default: return hipErrorInvalidValue;
   }
+#undef GVA_PREFILL_CASE
   return hipGetLastError();
 }
 
