@@ -423,6 +423,50 @@ def gqa_decode_sequence(K: np.ndarray, V: np.ndarray, dims: Dims, q_b, scale: fl
 
 
 # --------------------------------------------------------------------------------------
+# Non-absorbable variant (comparator).  The scale-matched row applies ordinary RoPE to the
+# reconstructed content key, which is why its map cannot be absorbed into the query
+# ([summary], the scale-matched + query RMSNorm row; [review] section 第二次尝试 for
+# K_h = V_g M_h). Its cache holds the G value streams only: position enters through the key.
+# Head h's key at position j is k_{h,j} = R_j (M_h^T v_{j,g(h)}) (width d_n), its query at
+# position p is R_p q_h, and s_j = scale (R_p q_h) . k_{h,j}; the softmax and the weighted sum
+# over the cached values are O6's.
+# Readings: RoPE over all d_n dims of the key, interleaved pairs, theta_i = base^(-2i/d_n)
+# (O1's convention at width d_n); the query arrives already normalised (the row's query
+# RMSNorm acts before attention, on the query projection).
+# --------------------------------------------------------------------------------------
+
+
+def recon_decode_sequence(V: np.ndarray, dims: Dims, q_b, p: int, M, scale: float,
+                          base: float = 10000.0, key_pos=None):
+    """One sequence; V [n, G, d_h] (cached values, float64), q_b [H, d_n], M [H, d_h, d_n].
+
+    The query sits at position p; key j sits at key_pos[j] (default j).
+    Returns out [H, d_h] and lse [H] (float64).
+    """
+    q_b = np.asarray(q_b, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    n = V.shape[0]
+    out = np.zeros((dims.H, dims.d_h))
+    lse = np.full(dims.H, -np.inf)
+    if n == 0:
+        return out, lse
+    kp = np.arange(n) if key_pos is None else np.asarray(key_pos)
+    cs_k = rope_rows(kp, dims.d_n, base)                   # [n, d_n/2, 2]
+    cs_q = rope_rows(np.array([p]), dims.d_n, base)[0]     # [d_n/2, 2]
+    for h in range(dims.H):
+        g = dims.group_of(h)
+        K = rotate(V[:, g, :] @ M[h], cs_k)                # k_{h,j} = R_j (M_h^T v_j), [n, d_n]
+        s = scale * (K @ rotate(q_b[h], cs_q))
+        out[h], lse[h], _ = softmax_attend(s, V[:, g, :])
+    return out, lse
+
+
+def recon_decode_flops(len_b: int, H: int, d_h: int, d_n: int) -> int:
+    """Multiply-adds x 2 of one step of one sequence: key rebuild, score and weighted sum."""
+    return H * len_b * (2 * d_h * d_n + 2 * d_n + 2 * d_h)
+
+
+# --------------------------------------------------------------------------------------
 # O7: chunked prefill.  The chunk's tokens are appended first (O4); query i of sequence b
 # sits at position start_b + i and attends to positions 0..start_b + i (inclusive), over
 # the cache-rounded values ([summary]: prefill is a dense, matrix-heavy pass).

@@ -585,3 +585,74 @@ def test_gqa_bytes_against_kvcache_page():
     assert O.gqa_decode_bytes(1, 1, 128, 2) == 512
     # the GVA step at the ragged-batch shape reads 2096 B per token, 51.2% of GQA's 4096 B
     assert O.gva_decode_bytes(1, 8, 128, 24, 2) == 2096
+
+
+# ----------------------------------------------------------------------------------------
+# Non-absorbable variant: ordinary RoPE on the reconstructed key
+# ----------------------------------------------------------------------------------------
+
+
+def test_recon_decode_closed_form_two_tokens():
+    """Worked by hand. d_h = 1, d_n = 2 (one pair, theta_0 = 1), two cached values v = (1, 2)
+    at positions 0 and 1, the query q = (1, 0) at p = 1, scale 1.
+    With M = [1, 0] the key is k_j = v_j (cos j, sin j) and s_j = v_j cos(j - 1); with
+    M = [0, 1] it is v_j (-sin j, cos j) and s_j = v_j sin(1 - j)."""
+    dims = O.Dims(H=1, G=1, d_h=1, d_n=2, d_r=0)
+    V = np.array([[[1.0]], [[2.0]]])
+    q = np.array([[1.0, 0.0]])
+    for M, s in (([1.0, 0.0], (math.cos(1.0), 2.0)), ([0.0, 1.0], (math.sin(1.0), 0.0))):
+        out, lse = O.recon_decode_sequence(V, dims, q, 1, np.array([[M]]), 1.0)
+        e0, e1 = math.exp(s[0]), math.exp(s[1])
+        assert abs(out[0, 0] - (e0 * 1.0 + e1 * 2.0) / (e0 + e1)) < 1e-15
+        assert abs(lse[0] - math.log(e0 + e1)) < 1e-15
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_recon_decode_against_complex_relative_angles(seed):
+    """An independent definition: the key k = M_h^T v (einsum over the named index), pairs as
+    complex numbers, and the score Re(sum_i conj(q_i) k_i e^{i (j - p) theta_i}), which is what
+    rotating the key by j and the query by p gives. d_h != d_n, so a transposed map fails."""
+    rng = np.random.default_rng(seed)
+    H, G, n, d_h, d_n, p, base, scale = 4, 2, 19, 6, 8, 25, 10000.0, 0.4
+    V = rng.standard_normal((n, G, d_h))
+    M = rng.standard_normal((H, d_h, d_n))
+    q = rng.standard_normal((H, d_n))
+    dims = O.Dims(H=H, G=G, d_h=d_h, d_n=d_n, d_r=0)
+    out, lse = O.recon_decode_sequence(V, dims, q, p, M, scale, base)
+    theta = np.array([math.pow(base, -2.0 * i / d_n) for i in range(d_n // 2)])
+    for h in range(H):
+        g = h // (H // G)
+        k = np.einsum("ni,ik->nk", V[:, g, :], M[h])
+        kc = k[:, 0::2] + 1j * k[:, 1::2]
+        qc = q[h, 0::2] + 1j * q[h, 1::2]
+        rel = np.exp(1j * (np.arange(n)[:, None] - p) * theta[None, :])
+        s = scale * np.real((np.conj(qc)[None, :] * kc * rel).sum(-1))
+        ls = logsumexp(s)
+        assert abs(lse[h] - ls) < 1e-12
+        assert np.allclose(out[h], np.exp(s - ls) @ V[:, g, :], rtol=0, atol=1e-12)
+
+
+def test_recon_decode_depends_only_on_relative_position():
+    """RoPE on both sides makes the score a function of p - j: moving the query and every key
+    by the same offset changes nothing (a rotation dropped on either side breaks this)."""
+    rng = np.random.default_rng(7)
+    H, G, n, d_h, d_n = 4, 2, 11, 8, 8
+    V = rng.standard_normal((n, G, d_h))
+    M = rng.standard_normal((H, d_h, d_n))
+    q = rng.standard_normal((H, d_n))
+    dims = O.Dims(H=H, G=G, d_h=d_h, d_n=d_n, d_r=0)
+    a, la = O.recon_decode_sequence(V, dims, q, n, M, 0.3)
+    b, lb = O.recon_decode_sequence(V, dims, q, n + 1000, M, 0.3, key_pos=np.arange(n) + 1000)
+    assert np.allclose(a, b, rtol=0, atol=1e-10) and np.allclose(la, lb, rtol=0, atol=1e-10)
+    # and moving only the query does change the result
+    c, _ = O.recon_decode_sequence(V, dims, q, n + 3, M, 0.3)
+    assert not np.allclose(a, c, rtol=0, atol=1e-6)
+
+
+def test_recon_decode_empty_and_flops():
+    dims = O.Dims(H=2, G=1, d_h=4, d_n=4, d_r=0)
+    out, lse = O.recon_decode_sequence(np.zeros((0, 1, 4)), dims, np.ones((2, 4)), 0,
+                                       np.ones((2, 4, 4)), 1.0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    # per token and head: a d_h x d_n rebuild, a d_n score and a d_h weighted sum
+    assert O.recon_decode_flops(3, 2, 4, 6) == 2 * 3 * (2 * 4 * 6 + 2 * 6 + 2 * 4)
