@@ -112,7 +112,8 @@ typedef struct gva_cache {
  * Rows p = 0 .. max_pos-1, pairs i = 0 .. d_r/2-1: (cos(p * theta_i), sin(p * theta_i)) with
  * theta_i = base^(-2i / d_r), evaluated in float64 with the C library's pow, cos and sin.
  * The positional slice is rotated by position ([review] section 关键技巧二); the frequency
- * convention is the usual RoPE one. */
+ * convention is the usual RoPE one. d_r is the rotated width: the positional slice's d_r, or
+ * d_n for the keys of gva_recon_decode; it must be even and in [2, 512]. */
 size_t gva_rope_table_bytes(int32_t max_pos, int32_t d_r);
 /* host_out: host float64 buffer of gva_rope_table_bytes(max_pos, d_r) bytes. */
 gva_status gva_rope_table_fill(double *host_out, int32_t max_pos, int32_t d_r, double base);
@@ -240,6 +241,39 @@ gva_status gva_gqa_decode(const gva_dims *dims, const gva_cache *values, const v
                           int32_t B, const int32_t *seq_len, int32_t max_len, const float *q,
                           float scale, void *workspace, size_t workspace_bytes, float *out,
                           float *lse, hipStream_t stream);
+
+/* ---- Non-absorbable comparator ([summary]: the scale-matched + query RMSNorm row applies
+ * ordinary RoPE to the reconstructed key and therefore cannot absorb the map; [review] section
+ * 第二次尝试: K_h = V_g M_h) ---------------------------------------------------------------
+ * Decodes a value-only cache whose content keys are rebuilt from the cached values at every step
+ * and rotated at their own positions, so the map cannot be folded into the query:
+ *   k_{h,j} = R_j (M_h^T v_{j,g(h)})      (d_n wide, M_h of shape d_h x d_n)
+ *   s_j     = scale * (R_p q_h) . k_{h,j},  p = q_pos[b]
+ *   out[b][h][:] = sum_{j < seq_len[b]} softmax_j(s) v_{j,g(h)},  lse as for gva_decode
+ * R_x rotates interleaved pairs (x[2i], x[2i+1]) by x * theta_i with theta_i = base^(-2i / d_n):
+ * the rows of a gva_rope_table_fill(max_pos, d_n, base) table.
+ *   dims: H, G, d_h, d_n (d_r is not used). Supported: d_h and d_n in {64, 128}, H / G <= 4.
+ *   values: a bf16 cache as for gva_decode holding the value pool; its positional-key pool and
+ *   its RoPE table are not read (they may be NULL). Strides must be multiples of 8 elements.
+ *   q: device float32 [B][H][d_n], 16-byte aligned (the query content vectors, normalised as
+ *   the model does before attention). q_pos: device int32 [B].
+ *   Mt: device, 16-byte aligned, bf16 bits [H][d_n][d_h] with Mt[h][k][i] = M_h[i][k] (the map
+ *   in the model's bf16, stored transposed).
+ *   rope: device float64 [max_pos][d_n / 2][2], 16-byte aligned; max_pos >= 32.
+ *   num_splits: chunks per sequence (0 = automatic), merged as in gva_decode.
+ *   workspace: at least gva_recon_decode_workspace_bytes(dims, B, max_len, num_splits) bytes,
+ *   256-byte aligned (none when that is 0).
+ *   out: device float32 [B][H][d_h], 16-byte aligned; lse: device float32 [B][H] or NULL.
+ * Device-detected errors (NaN rows, err_flag bits): a bad block-table entry (BLOCK); seq_len[b]
+ * negative or above max_len (LENGTH) or above the table's capacity (CAPACITY); q_pos[b] outside
+ * [0, max_pos) or seq_len[b] > max_pos (ROPE). */
+size_t gva_recon_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
+                                        int32_t num_splits);
+gva_status gva_recon_decode(const gva_dims *dims, const gva_cache *values, int32_t B,
+                            const int32_t *seq_len, int32_t max_len, const float *q,
+                            const int32_t *q_pos, const uint16_t *Mt, const double *rope,
+                            int32_t max_pos, float scale, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
 
 /* ---- Diagnostics --------------------------------------------------------------------------- */
 const char *gva_status_string(gva_status status);

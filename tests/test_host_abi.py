@@ -50,7 +50,7 @@ def test_version_and_status_strings(L):
         assert L.gva_status_string(s).decode() == name
 
 
-@pytest.mark.parametrize("max_pos,d_r", [(1, 2), (300, 16), (1025, 24), (77, 64)])
+@pytest.mark.parametrize("max_pos,d_r", [(1, 2), (300, 16), (1025, 24), (77, 64), (40, 128)])
 def test_rope_table_bit_identical_to_oracle(L, max_pos, d_r):
     lib_tab = gb.gva_rope_table_fill(max_pos, d_r, 10000.0)
     ora_tab = O.rope_table(max_pos, d_r, 10000.0)
@@ -60,11 +60,12 @@ def test_rope_table_bit_identical_to_oracle(L, max_pos, d_r):
 
 def test_rope_table_rejects_bad_arguments(L):
     buf = np.empty(64, dtype=np.float64)
-    for args in [(0, 16, 1e4), (4, 3, 1e4), (4, 0, 1e4), (4, 66, 1e4), (4, 16, -1.0),
+    for args in [(0, 16, 1e4), (4, 3, 1e4), (4, 0, 1e4), (4, 514, 1e4), (4, 16, -1.0),
                  (4, 16, float("inf"))]:
         assert L.gva_rope_table_fill(buf.ctypes.data, *args) == gb.GVA_ERR_INVALID_ARG
     assert L.gva_rope_table_fill(None, 4, 16, 1e4) == gb.GVA_ERR_INVALID_ARG
     assert gb.gva_rope_table_bytes(0, 16) == 0 and gb.gva_rope_table_bytes(4, 5) == 0
+    assert gb.gva_rope_table_bytes(4, 128) == 4 * 64 * 2 * 8     # a key-wide table (d_n = 128)
 
 
 # ---- validation, with fake (never dereferenced) device addresses ----------------------------
@@ -272,3 +273,44 @@ def test_prefill_validation(L):
     assert pf(ms=1000) == gb.GVA_ERR_INVALID_ARG           # beyond the table's capacity
     assert pf(scale=-1.0) == gb.GVA_ERR_INVALID_ARG
     assert pf(c=_cache(dtype=gb.GVA_DTYPE_F32, max_blocks=64)) == gb.GVA_ERR_UNSUPPORTED
+
+
+def test_recon_validation(L):
+    """The non-absorbable comparator's argument checks, all on the host before any launch."""
+    d, c = _dims(), _cache()
+
+    def rc(**kw):
+        return L.gva_recon_decode(ctypes.byref(kw.get("d", d)), ctypes.byref(kw.get("c", c)),
+                                  kw.get("B", 2), kw.get("sl", A), kw.get("ml", 100),
+                                  kw.get("q", A), kw.get("qp", A), kw.get("Mt", A),
+                                  kw.get("rope", A + 16384), kw.get("mp", 1024),
+                                  kw.get("scale", 0.1), kw.get("S", 0), kw.get("ws", None),
+                                  kw.get("wsb", 0), kw.get("out", A), None, None)
+    assert rc(B=0) == gb.GVA_ERR_INVALID_ARG
+    for k in ("sl", "q", "qp", "Mt", "rope", "out"):
+        assert rc(**{k: None}) == gb.GVA_ERR_INVALID_ARG, k
+    for k in ("q", "Mt", "rope", "out"):
+        assert rc(**{k: A + 8}) == gb.GVA_ERR_INVALID_ARG, k      # 16-byte alignment
+    assert rc(mp=31) == gb.GVA_ERR_INVALID_ARG                     # the in-tile angles need 32 rows
+    assert rc(ml=8 * 16 + 1) == gb.GVA_ERR_INVALID_ARG              # beyond the table's capacity
+    assert rc(ml=-1) == gb.GVA_ERR_INVALID_ARG
+    assert rc(scale=0.0) == gb.GVA_ERR_INVALID_ARG
+    assert rc(S=1025) == gb.GVA_ERR_INVALID_ARG
+    assert rc(d=_dims(d_h=96)) == gb.GVA_ERR_UNSUPPORTED
+    assert rc(d=_dims(d_n=96)) == gb.GVA_ERR_UNSUPPORTED
+    assert rc(d=_dims(H=32, G=4)) == gb.GVA_ERR_UNSUPPORTED         # eight heads per group
+    assert rc(d=_dims(H=12, G=8)) == gb.GVA_ERR_INVALID_ARG
+    assert rc(c=_cache(dtype=gb.GVA_DTYPE_F32)) == gb.GVA_ERR_UNSUPPORTED
+    assert rc(c=_cache(v_stride_token=132)) == gb.GVA_ERR_INVALID_ARG
+    assert rc(c=_cache(block_size=24)) == gb.GVA_ERR_INVALID_ARG
+    # d_r is not used: dims with d_r = 0 pass the shape checks (and then need a workspace)
+    assert rc(d=_dims(d_r=0)) == gb.GVA_ERR_WORKSPACE
+    # two sequences of up to 100 positions are split in two chunks of 64: a workspace is needed
+    wsb = gb.gva_recon_decode_workspace_bytes(d, 2, 100, 0)
+    assert wsb > 0
+    assert rc() == gb.GVA_ERR_WORKSPACE
+    assert rc(ws=A + 64, wsb=wsb) == gb.GVA_ERR_WORKSPACE          # not 256-byte aligned
+    assert rc(ws=A, wsb=wsb - 1) == gb.GVA_ERR_WORKSPACE
+    # a large batch runs one chunk per sequence and needs none
+    assert gb.gva_recon_decode_workspace_bytes(d, 256, 100, 0) == 0
+    assert gb.gva_recon_decode_workspace_bytes(d, 2, 100, 1) == 0

@@ -29,6 +29,7 @@ EXPORTED = [
     "gva_rope_table_bytes", "gva_rope_table_fill", "gva_cache_append", "gva_absorb_query",
     "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
     "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode",
+    "gva_recon_decode_workspace_bytes", "gva_recon_decode",
     "gva_status_string", "gva_last_error", "gva_version",
 ]
 
@@ -97,6 +98,11 @@ def lib() -> ctypes.CDLL:
     L.gva_gqa_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), P, c_int32, P, c_int32,
                                  P, c_float, P, c_size_t, P, P, P]
     L.gva_gqa_decode.restype = c_int32
+    L.gva_recon_decode_workspace_bytes.argtypes = [POINTER(GvaDims), c_int32, c_int32, c_int32]
+    L.gva_recon_decode_workspace_bytes.restype = c_size_t
+    L.gva_recon_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32,
+                                   P, P, P, P, c_int32, c_float, c_int32, P, c_size_t, P, P, P]
+    L.gva_recon_decode.restype = c_int32
     L.gva_status_string.argtypes = [c_int32]
     L.gva_status_string.restype = c_char_p
     L.gva_last_error.argtypes = []
@@ -220,6 +226,22 @@ def gva_gqa_decode(dims: GvaDims, values: "GvaCache", keys, B: int, seq_len, max
     _check(lib().gva_gqa_decode(ctypes.byref(dims), ctypes.byref(values.struct), _ptr(keys), B,
                                 _ptr(seq_len), max_len, _ptr(q), scale, _ptr(workspace), ws_bytes,
                                 _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def gva_recon_decode_workspace_bytes(dims: GvaDims, B: int, max_len: int, num_splits: int = 0) -> int:
+    return int(lib().gva_recon_decode_workspace_bytes(ctypes.byref(dims), B, max_len, num_splits))
+
+
+def gva_recon_decode(dims: GvaDims, values: "GvaCache", B: int, seq_len, max_len: int, q, q_pos,
+                     Mt, rope, max_pos: int, scale: float, out, lse=None, num_splits: int = 0,
+                     workspace=None, stream=None) -> None:
+    """The non-absorbable comparator: Mt is bf16 bits [H][d_n][d_h] (an int16 tensor), rope a
+    float64 table of width d_n."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gva_recon_decode(ctypes.byref(dims), ctypes.byref(values.struct), B,
+                                  _ptr(seq_len), max_len, _ptr(q), _ptr(q_pos), _ptr(Mt),
+                                  _ptr(rope), max_pos, scale, num_splits, _ptr(workspace),
+                                  ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def gva_version() -> str:

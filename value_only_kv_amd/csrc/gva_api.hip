@@ -168,6 +168,48 @@ gva_status gva_gqa_decode(const gva_dims *dims, const gva_cache *values, const v
   return GVA_OK;
 }
 
+gva_status gva_recon_decode(const gva_dims *dims, const gva_cache *values, int32_t B,
+                            const int32_t *seq_len, int32_t max_len, const float *q,
+                            const int32_t *q_pos, const uint16_t *Mt, const double *rope,
+                            int32_t max_pos, float scale, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, float *out, float *lse, hipStream_t stream) {
+  gva::DecodePlan plan{};
+  gva_status st = gva::check_recon(dims, values, B, seq_len, max_len, q, q_pos, Mt, rope, max_pos,
+                                   scale, num_splits, workspace, workspace_bytes, out, &plan);
+  if (st != GVA_OK) return st;
+  gva::ReconArgs r{};
+  r.kv = cache_args(dims, values);
+  r.kv.kr = nullptr;
+  r.kv.d_r = 0;
+  r.kv.B = B;
+  r.kv.seq_len = seq_len;
+  r.kv.max_len = max_len;
+  r.kv.qscale = scale * 1.4426950408889634f;
+  r.kv.num_splits = plan.num_splits;
+  r.kv.chunk = plan.chunk;
+  r.kv.out = out;
+  r.kv.lse = lse;
+  if (plan.num_splits > 1) {
+    char *ws = static_cast<char *>(workspace);
+    r.kv.part_o = reinterpret_cast<float *>(ws + plan.off_o);
+    r.kv.part_m = reinterpret_cast<float *>(ws + plan.off_m);
+    r.kv.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+  }
+  r.d_n = dims->d_n;
+  r.q = q;
+  r.q_pos = q_pos;
+  r.Mt = Mt;
+  r.rope = rope;
+  r.max_pos = max_pos;
+  hipError_t e = gva::launch_recon_decode(r, stream);
+  if (e != hipSuccess) return hip_status(e, "comparator decode launch");
+  if (plan.num_splits > 1) {
+    e = gva::launch_combine(r.kv, stream);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return GVA_OK;
+}
+
 gva_status gva_prefill_chunk(const gva_dims *dims, const gva_cache *cache, int32_t B,
                              const int32_t *start, int32_t max_start, int32_t chunk_len,
                              const float *q_abs, const float *v_new, const float *kr_raw,

@@ -245,6 +245,68 @@ gva_status check_step(const gva_dims *d, const gva_cache *c, int32_t B, const in
   return check_absorb(d, B, q_nope, q_rope, pos, M, c->rope, c->max_pos, q_abs);
 }
 
+bool recon_supported(const gva_dims *d, const char **why) {
+  const char *w = nullptr;
+  if (d->d_h != 64 && d->d_h != 128) w = "the comparator kernel needs d_h of 64 or 128";
+  else if (d->d_n != 64 && d->d_n != 128) w = "the comparator kernel needs d_n of 64 or 128";
+  else if (d->H / d->G > 4) w = "the comparator kernel needs H / G <= 4";
+  if (why) *why = w;
+  return w == nullptr;
+}
+
+gva_status check_recon(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *seq_len,
+                       int32_t max_len, const float *q, const int32_t *q_pos, const uint16_t *Mt,
+                       const double *rope, int32_t max_pos, float scale, int32_t num_splits,
+                       const void *workspace, size_t workspace_bytes, const float *out,
+                       DecodePlan *plan) {
+  if (!d) return fail(GVA_ERR_INVALID_ARG, "dims is NULL");
+  gva_dims dd = *d;
+  dd.d_r = 2;                              // not used by this entry point
+  gva_status st = check_dims(&dd);
+  if (st != GVA_OK) return st;
+  const char *why = nullptr;
+  if (!recon_supported(d, &why)) return fail(GVA_ERR_UNSUPPORTED, "%s", why);
+  if (!c) return fail(GVA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->dtype != GVA_DTYPE_BF16) return fail(GVA_ERR_UNSUPPORTED, "the comparator needs a bf16 cache");
+  if (!c->v || !aligned(c->v, 16)) return fail(GVA_ERR_INVALID_ARG, "cache v must be a 16-byte aligned pointer");
+  if (!c->block_table) return fail(GVA_ERR_INVALID_ARG, "block_table is NULL");
+  if (c->num_blocks < 1 || c->num_blocks > (int64_t)INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31)");
+  if (!pow2(c->block_size) || c->block_size > (1 << 30))
+    return fail(GVA_ERR_INVALID_ARG, "block_size=%d must be a power of two", c->block_size);
+  if (c->max_blocks < 1) return fail(GVA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  if ((int64_t)c->max_blocks * c->block_size > (int64_t)INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARG, "max_blocks * block_size exceeds int32 positions");
+  const int64_t vs[3] = {c->v_stride_block, c->v_stride_token, c->v_stride_group};
+  for (int i = 0; i < 3; ++i)
+    if (vs[i] < 0 || vs[i] % 8 != 0)
+      return fail(GVA_ERR_INVALID_ARG, "v strides must be >= 0 and multiples of 8 elements");
+  if (c->v_stride_group < d->d_h && d->G > 1 && c->v_stride_token < d->d_h)
+    return fail(GVA_ERR_INVALID_ARG, "v strides overlap rows");
+  if (B < 1) return fail(GVA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (!seq_len || !q || !q_pos || !Mt || !rope || !out)
+    return fail(GVA_ERR_INVALID_ARG, "comparator argument is NULL");
+  if (!aligned(q, 16) || !aligned(Mt, 16) || !aligned(rope, 16) || !aligned(out, 16))
+    return fail(GVA_ERR_INVALID_ARG, "q, Mt, rope and out must be 16-byte aligned");
+  if (max_pos < 32) return fail(GVA_ERR_INVALID_ARG, "max_pos=%d must be >= 32", max_pos);
+  if (max_len < 0) return fail(GVA_ERR_INVALID_ARG, "max_len=%d must be >= 0", max_len);
+  if ((int64_t)max_len > (int64_t)c->max_blocks * c->block_size)
+    return fail(GVA_ERR_INVALID_ARG, "max_len=%d exceeds the block table's capacity", max_len);
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(GVA_ERR_INVALID_ARG, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
+  if (!plan_decode(&dd, B, max_len, num_splits, false, plan))
+    return fail(GVA_ERR_INVALID_ARG, "cannot plan the decode split");
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+      return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan->ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  return GVA_OK;
+}
+
 gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
                          int32_t max_start, int32_t chunk_len, const float *q_abs,
                          const float *v_new, const float *kr_raw, float scale, const float *out) {
@@ -273,15 +335,16 @@ gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const
 extern "C" {
 
 size_t gva_rope_table_bytes(int32_t max_pos, int32_t d_r) {
-  if (max_pos < 1 || d_r < 2 || d_r % 2 != 0 || d_r > gva::kMaxDr) return 0;
+  if (max_pos < 1 || d_r < 2 || d_r % 2 != 0 || d_r > gva::kMaxDn) return 0;
   return (size_t)max_pos * (size_t)(d_r / 2) * 2 * sizeof(double);
 }
 
 gva_status gva_rope_table_fill(double *host_out, int32_t max_pos, int32_t d_r, double base) {
   if (!host_out) return gva::fail(GVA_ERR_INVALID_ARG, "host_out is NULL");
   if (max_pos < 1) return gva::fail(GVA_ERR_INVALID_ARG, "max_pos=%d must be >= 1", max_pos);
-  if (d_r < 2 || d_r % 2 != 0 || d_r > gva::kMaxDr)
-    return gva::fail(GVA_ERR_INVALID_ARG, "d_r=%d must be even and in [2, %d]", d_r, gva::kMaxDr);
+  // d_r is the rotated width: the positional slice's d_r, or d_n for the comparator's keys
+  if (d_r < 2 || d_r % 2 != 0 || d_r > gva::kMaxDn)
+    return gva::fail(GVA_ERR_INVALID_ARG, "width=%d must be even and in [2, %d]", d_r, gva::kMaxDn);
   if (!(base > 0.0) || !isfinite(base)) return gva::fail(GVA_ERR_INVALID_ARG, "base must be > 0");
   const int half = d_r / 2;
   for (int i = 0; i < half; ++i) {
@@ -307,6 +370,17 @@ size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_l
   if (!gva::plan_decode(dims, B, max_len, num_splits, true, &pq, false)) return 0;
   size_t ws = p.ws_bytes > pb.ws_bytes ? p.ws_bytes : pb.ws_bytes;
   return ws > pq.ws_bytes ? ws : pq.ws_bytes;
+}
+
+size_t gva_recon_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
+                                        int32_t num_splits) {
+  if (!dims) return 0;
+  gva_dims dd = *dims;
+  dd.d_r = 2;                              // not used by the comparator
+  if (gva::check_dims(&dd) != GVA_OK) return 0;
+  gva::DecodePlan p;
+  if (!gva::plan_decode(&dd, B, max_len, num_splits, false, &p)) return 0;
+  return p.ws_bytes;
 }
 
 int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,

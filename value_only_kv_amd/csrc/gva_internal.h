@@ -99,6 +99,15 @@ gva_status check_step(const gva_dims *d, const gva_cache *c, int32_t B, const in
                       const float *v_new, const float *kr_raw, const float *q_nope,
                       const float *q_rope, const float *M, const float *q_abs);
 
+// The non-absorbable comparator (gva_recon_decode): shapes it implements, and its argument
+// checks; the plan is the split grid of plan_decode.
+bool recon_supported(const gva_dims *d, const char **why);
+gva_status check_recon(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *seq_len,
+                       int32_t max_len, const float *q, const int32_t *q_pos, const uint16_t *Mt,
+                       const double *rope, int32_t max_pos, float scale, int32_t num_splits,
+                       const void *workspace, size_t workspace_bytes, const float *out,
+                       DecodePlan *plan);
+
 gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
                          int32_t max_start, int32_t chunk_len, const float *q_abs,
                          const float *v_new, const float *kr_raw, float scale, const float *out);
@@ -164,6 +173,17 @@ struct PrefillArgs {
   float *lse;           // [B][C][H] or nullptr
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+struct ReconArgs {
+  DecodeArgs kv;        // value cache, shape, split plan, partials and outputs (d_r unused)
+  int32_t d_n;
+  const float *q;       // [B][H][d_n]
+  const int32_t *q_pos; // [B]
+  const uint16_t *Mt;   // bf16 bits [H][d_n][d_h]
+  const double *rope;   // [max_pos][d_n / 2][2]
+  int32_t max_pos;
+};
+hipError_t launch_recon_decode(const ReconArgs &r, hipStream_t stream);
 
 }  // namespace gva
 

@@ -15,6 +15,7 @@ Streams (numpy PCG64 through SeedSequence):
   * [1000 + k, 1 << 20]  weights and queries of config k: M, then q_nope, q_rope
   * [1000 + k, b]        sequence b of config k: V rows, then raw positional keys
   * [1000 + k, 99999]    config k's lengths, then its block permutation
+  * [1000 + k, 1 << 22 | s] the non-absorbable comparator's maps and queries
 All values are drawn in float64 from N(0, 1) and cast to float32 once.
 """
 from __future__ import annotations
@@ -232,6 +233,24 @@ def comparator_keys(w: Workload, b: int, n_tok: int) -> np.ndarray:
     rng = np.random.default_rng(np.random.SeedSequence([1000 + w.index, b, 2]))
     x = rng.standard_normal(size=(n_tok, w.G * w.d_h), dtype=np.float64).astype(np.float32)
     return np.ascontiguousarray(x.reshape(n_tok, w.G, w.d_h))
+
+
+def recon_inputs(w: Workload, stream: int = 3):
+    """Inputs of the non-absorbable comparator on a stream of their own, [1000 + k, 1 << 22 |
+    stream]: maps M ~ N(0, 1/d_h) held in bf16 (the model's weight type) and queries
+    q ~ N(0, 1) [B, H, d_n] float32.
+
+    Returns (q, M, Mt_bits): M [H, d_h, d_n] float64 holding exactly the bf16 values, and
+    Mt_bits [H, d_n, d_h] uint16, the same values' bits transposed as the library takes them.
+    The rounding to bf16 is torch's (float32 to bfloat16, nearest-even)."""
+    import torch
+    rng = _rng(w, (1 << 22) | stream)
+    M32 = _normal_f32(rng, (w.H, w.d_h, w.d_n), 1.0 / float(np.sqrt(w.d_h)))
+    q = _normal_f32(rng, (w.B, w.H, w.d_n))
+    Mb = torch.from_numpy(M32).to(torch.bfloat16)
+    M = Mb.to(torch.float64).numpy()
+    Mt_bits = Mb.transpose(1, 2).contiguous().view(torch.int16).numpy().view(np.uint16)
+    return q, M, Mt_bits
 
 
 def decode_query_positions(w: Workload, lens: np.ndarray) -> np.ndarray:
