@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_BF16 = 2.5e15         # MI355X dense bf16 matrix-core flop/s
 METRIC = "GVA decode attention cache-read GB/s (% of HBM peak) and seq-steps/s per GPU"
 
 
@@ -45,6 +46,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     p.add_argument("--no-gqa", action="store_true", help="skip the GQA comparator measurement")
     p.add_argument("--no-small", action="store_true", help="skip the small-batch step latencies")
+    p.add_argument("--no-recon", action="store_true",
+                   help="skip the non-absorbable comparator measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -210,6 +213,53 @@ def main():
         del keys
         torch.cuda.empty_cache()
 
+    # ---------------- non-absorbable comparator on the same batch ----------------
+    # The scale-matched row's decode: the same value pool (its positional-key pool is not read),
+    # every head's content keys rebuilt from the values and rotated at their positions at every
+    # step, with the maps in bf16. Its cost is the key rebuild, H d_h d_n multiply-adds per token.
+    recon = None
+    if not args.no_recon:
+        q_r, _, mt_bits = synth.recon_inputs(w)
+        q_r_t = torch.from_numpy(q_r).cuda()
+        mt_t = torch.from_numpy(mt_bits.view(np.int16)).cuda()
+        max_pos_r = max_len + 1
+        rope_r = torch.from_numpy(gb.gva_rope_table_fill(max_pos_r, w.d_n, w.base)).cuda()
+        wsb_r = gb.gva_recon_decode_workspace_bytes(dc.dims, B, max_len, 0)
+        ws_r = torch.empty(max(wsb_r, 256) // 4, dtype=torch.float32, device="cuda")
+        scale_r = 1.0 / float(np.sqrt(w.d_n))
+
+        def recon_call():
+            gb.gva_recon_decode(dc.dims, dc.cache, B, seq_len, max_len, q_r_t, pos, mt_t, rope_r,
+                                max_pos_r, scale_r, out, lse, workspace=ws_r, stream=stream)
+
+        for _ in range(3):
+            recon_call()
+        evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        for e0, e1 in evr:
+            e0.record(stream)
+            recon_call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all().item(), "non-finite comparator output"
+        assert int(dc.cache.err_flag.item()) == 0, "device error flag raised"
+        t_rec = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evr])) / 1e3
+        toks = int((lens + 1).sum())
+        v_bytes = toks * w.G * w.d_h * elem
+        rebuild = 2 * H * toks * w.d_h * w.d_n
+        recon = {"workload": "same batch, lengths and paged value pool (positional-key pool not "
+                             "read); maps M [H][d_h][d_n] in bf16; query at the appended position",
+                 "ms": round(t_rec * 1e3, 4), "value_bytes": v_bytes,
+                 "GB_s": round(v_bytes / t_rec / 1e9, 1),
+                 "key_rebuild_flop": rebuild,
+                 "key_rebuild_TFLOP_s": round(rebuild / t_rec / 1e12, 1),
+                 "key_rebuild_frac_of_bf16_dense_peak": round(rebuild / t_rec / MFMA_PEAK_BF16, 4),
+                 "gva_speedup_over_recon": round(t_rec / t_dec, 3)}
+        log(f"non-absorbable comparator decode: {t_rec * 1e3:.3f} ms ({rebuild / t_rec / 1e12:.1f} "
+            f"TFLOP/s of key rebuild); the absorbed GVA decode is {t_rec / t_dec:.2f}x faster")
+        del rope_r, mt_t, q_r_t, ws_r
+        torch.cuda.empty_cache()
+
     result_extra = {}
     # ---------------- long context, one sequence ----------------
     if not args.no_long:
@@ -309,6 +359,7 @@ def main():
         "prefill": prefill,
         "small_batch_step": small,
         "gqa_comparator": gqa,
+        "recon_comparator": recon,
         "device": dev,
     }
     print(json.dumps(res), flush=True)
@@ -376,12 +427,12 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
     td = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)[iters // 2]
     dec_bytes = int((lens + C + 1).sum()) * (w.G * w.d_h + w.d_r) * 2
     log(f"C5 prefill: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s "
-        f"({tflops / 2500:.1%} of bf16 dense peak); mix decode step {td * 1e6:.1f} us")
+        f"({tflops * 1e12 / MFMA_PEAK_BF16:.1%} of bf16 dense peak); mix decode step {td * 1e6:.1f} us")
     assert torch.isfinite(out).all().item()
     res = {"workload": "4 sequences x (8192 cached + 512 causal queries), H=32, G=8, d_h=d_n=128, "
                        "d_r=16, bf16 cache in 16-token blocks; chunk append included",
            "us": round(t * 1e6, 2), "flop": flop, "TFLOP_s": round(tflops, 1),
-           "mfma_util_bf16_dense": round(tflops / 2500.0, 4),
+           "mfma_util_bf16_dense": round(tflops * 1e12 / MFMA_PEAK_BF16, 4),
            "decode_step_after_us": round(td * 1e6, 2),
            "decode_step_after_GB_s": round(dec_bytes / td / 1e9, 1)}
     del dc

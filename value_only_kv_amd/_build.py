@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]
+# Per-source additions. The comparator kernel keeps its matrix-core accumulators in ordinary
+# vector registers: its vector-ALU code reads every product, and the compiler's default (the
+# accumulation registers) adds a copy per value.
+HIP_FILE_FLAGS = {"k_recon.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 GXX_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",
              "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include"),
              "-I" + os.path.join(ROOT, "include")]
@@ -62,7 +66,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c",
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2) // 2), 8)
     with cf.ThreadPoolExecutor(jobs) as ex:

@@ -22,9 +22,10 @@
 //     while the query is rotated once per tile by p - j0 (one table row per tile, staged in LDS
 //     as float32);
 //   * the score is summed in float32 on the vector ALU over the lane's dims and then over the
-//     four lanes that hold one key; the softmax (base 2) and the weighted sum of the value rows
-//     (the same registers, widened to float32) follow, with per-lane partial sums that are
-//     reduced at the end of the chunk.
+//     four lanes that hold one key; the softmax (base 2) and the weighted sum follow: the lane's
+//     two probabilities (keys delta and delta + 16) as a bf16 pair against the same dim of both
+//     value rows (v_dot2_f32_bf16, float32 accumulation, the value registers of the rebuild),
+//     into per-lane partial sums that are reduced at the end of the chunk.
 // Partials (m, l, o) go to the split-grid rows the decode combine reads; a single chunk per
 // sequence writes the output directly.
 #include <hip/hip_runtime.h>
@@ -39,6 +40,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) double f64x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kTile = 32;
 
@@ -67,10 +70,15 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + row_ror<1>(v);
 }
 
-// bf16 element e (0..7) of 8 packed in a u32x4, as float32
-__device__ __forceinline__ float bf16_at(const u32x4 &w, int e) {
-  const unsigned x = w[e >> 1];
-  return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+// (x, y) rounded to bf16 (nearest-even) and packed, x in the low half
+__device__ __forceinline__ unsigned pack2(float x, float y) {
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+// a.lo * b.lo + a.hi * b.hi + c for bf16 pairs, accumulated in float32
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
 }
 
 template <int DH, int DN, int NH>
@@ -234,32 +242,45 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         vb[tb][ks] = *reinterpret_cast<const u32x4 *>(vt + (16 * tb + n) * kStride + 32 * ks + 8 * kq);
+    // (cos, sin) of (p - j0) theta for the lane's pairs 8 nb + 2 kq and + 1
+    f32x4 c4[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) c4[nb] = *reinterpret_cast<const f32x4 *>(cs + 2 * (8 * nb + 2 * kq));
+    // A operands (M_h^T rows) of one 16-dim block, read one block ahead of its products
+    u32x4 am[2][KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      am[0][ks] = *reinterpret_cast<const u32x4 *>(mh + n * kStride + 32 * ks + 8 * kq);
     float sp[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
+      if (nb + 1 < NB) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          am[(nb + 1) & 1][ks] = *reinterpret_cast<const u32x4 *>(
+              mh + (16 * (nb + 1) + n) * kStride + 32 * ks + 8 * kq);
+      }
       // K^T[16 nb + i][key] for both key blocks: lane (n, kq) gets dims 16 nb + 4 kq + 0..3
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 am = *reinterpret_cast<const u32x4 *>(mh + (16 * nb + n) * kStride + 32 * ks + 8 * kq);
-        acc[0] = mfma(am, vb[0][ks], acc[0]);
-        acc[1] = mfma(am, vb[1][ks], acc[1]);
+        acc[0] = mfma(am[nb & 1][ks], vb[0][ks], acc[0]);
+        acc[1] = mfma(am[nb & 1][ks], vb[1][ks], acc[1]);
       }
-      // (cos, sin) of (p - j0) theta for pairs 8 nb + 2 kq and + 1
-      const f32x4 c4 = *reinterpret_cast<const f32x4 *>(cs + 2 * (8 * nb + 2 * kq));
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const float c0 = c4[2 * u], s0 = c4[2 * u + 1];
+        const float c0 = c4[nb][2 * u], s0 = c4[nb][2 * u + 1];
         const float x0 = qv[nb][2 * u], x1 = qv[nb][2 * u + 1];
         const float q0 = c0 * x0 - s0 * x1;            // R_{p - j0} q
         const float q1 = s0 * x0 + c0 * x1;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
+          // q . R_delta k = cos (q0 k0 + q1 k1) + sin (q1 k0 - q0 k1)
           const float k0 = acc[tb][2 * u], k1 = acc[tb][2 * u + 1];
-          const float c = rc[tb][nb][u], sn = rsn[tb][nb][u];
-          const float r0 = c * k0 - sn * k1;           // R_delta k
-          const float r1 = sn * k0 + c * k1;
-          sp[tb] += q0 * r0 + q1 * r1;
+          const float dot = fmaf(k1, q1, k0 * q0);
+          const float crs = fmaf(-k1, q0, k0 * q1);
+          sp[tb] = fmaf(rc[tb][nb][u], dot, sp[tb]);
+          sp[tb] = fmaf(rsn[tb][nb][u], crs, sp[tb]);
         }
       }
     }
@@ -285,11 +306,17 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
     const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_run);
     const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_run);
     l_part += p0 + p1;
+    // weighted sum: the probabilities of keys n and 16 + n as a bf16 pair against the same
+    // dim of both keys' value rows (v_dot2, float32 accumulation)
+    const unsigned pp = pack2(p0, p1);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        o_part[ks][e] = fmaf(p1, bf16_at(vb[1][ks], e), fmaf(p0, bf16_at(vb[0][ks], e), o_part[ks][e]));
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const unsigned x0 = vb[0][ks][w2], x1 = vb[1][ks][w2];
+        o_part[ks][2 * w2] = dot2(pp, __builtin_amdgcn_perm(x1, x0, 0x05040100u), o_part[ks][2 * w2]);
+        o_part[ks][2 * w2 + 1] = dot2(pp, __builtin_amdgcn_perm(x1, x0, 0x07060302u), o_part[ks][2 * w2 + 1]);
+      }
   };
 
   const int ntiles = (c1 - c0 + kTile - 1) / kTile;
