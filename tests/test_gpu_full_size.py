@@ -7,7 +7,8 @@ count), on outputs the oracle computes one sequence at a time.
   permutation of the pool): append one token per sequence, absorb the queries, decode over
   len_b + 1 positions. Six sampled sequences (the longest, the shortest and four drawn at random)
   carry the seeded synthetic tokens and are checked against the oracle; the other sequences are
-  filled with device random values, which only they read.
+  filled with device random values, which only they read. The non-absorbable comparator runs on
+  the same cache and is checked on three of the sampled sequences.
 """
 import numpy as np
 import pytest
@@ -47,13 +48,15 @@ def test_long_context_full_size(name):
     assert c.err_flag() == 0
 
 
-def test_ragged_batch_full_size_sampled_sequences():
+@pytest.fixture(scope="module")
+def ragged():
+    """The full ragged batch, built once for the tests below: sampled sequences carry their
+    seeded synthetic tokens (the appended step token included), the others device random values."""
     w = synth.workload("C4")
     lens = synth.lengths(w)
     lay = synth.layout(w, lens)
     B, G, d_h, d_r, H = w.B, w.G, w.d_h, w.d_r, w.H
     cdims = gb.GvaDims(H, G, d_h, w.d_n, d_r)
-    dims = O.Dims(H, G, d_h, w.d_n, d_r)
     max_pos = int(synth.capacity(w, lens).max()) + 1
     tab_lib = torch.from_numpy(gb.gva_rope_table_fill(max_pos, d_r, w.base)).cuda()
     cache = gb.GvaCache.allocate(cdims, w.dtype, lay.num_blocks, lay.block_size,
@@ -76,7 +79,7 @@ def test_ragged_batch_full_size_sampled_sequences():
                             torch.from_numpy(poss[o:o + n]).cuda(),
                             torch.randn((n, G, d_h), generator=gen, device="cuda"),
                             torch.randn((n, d_r), generator=gen, device="cuda"))
-    # sampled sequences: their seeded tokens; position len_b is appended by the step below
+    # sampled sequences: their seeded tokens; position len_b is appended as the step's token
     toks = {}
     for b in sampled:
         n = int(lens[b])
@@ -85,7 +88,7 @@ def test_ragged_batch_full_size_sampled_sequences():
         gb.gva_cache_append(cdims, cache, B, torch.full((n,), b, dtype=torch.int32).cuda(),
                             torch.arange(n, dtype=torch.int32).cuda(),
                             torch.from_numpy(v[:n]).cuda(), torch.from_numpy(kr[:n]).cuda())
-    # the step: append one token per sequence at position len_b, absorb, decode over len_b + 1
+    # the step: append one token per sequence at position len_b
     v_step = torch.randn((B, G, d_h), generator=gen, device="cuda")
     k_step = torch.randn((B, d_r), generator=gen, device="cuda")
     for b in sampled:
@@ -94,9 +97,32 @@ def test_ragged_batch_full_size_sampled_sequences():
     pos = lens.astype(np.int32)
     gb.gva_cache_append(cdims, cache, B, torch.arange(B, dtype=torch.int32).cuda(),
                         torch.from_numpy(pos).cuda(), v_step, k_step)
+    torch.cuda.synchronize()
+    return dict(w=w, lens=lens, cdims=cdims, dims=O.Dims(H, G, d_h, w.d_n, d_r), cache=cache,
+                tab_lib=tab_lib, max_pos=max_pos, sampled=sampled, toks=toks, pos=pos)
+
+
+def _sequence_values(r, b):
+    """The oracle's own contiguous pool for sampled sequence b: V [n, G, d_h] and kr [n, d_r]."""
+    w, dims = r["w"], r["dims"]
+    G, d_h, d_r = w.G, w.d_h, w.d_r
+    n = int(r["lens"][b]) + 1
+    v, kr = r["toks"][b]
+    tab_ora = O.rope_rows(np.arange(n), d_r, w.base)
+    pool = O.Pool.empty("bf16", n * G * d_h, n * d_r, (n * G * d_h, G * d_h, d_h, n * d_r, d_r),
+                        1, 1 << int(np.ceil(np.log2(n))), np.zeros((1, 1)))
+    O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr, tab_ora)
+    return O.gather(pool, dims, 0, n)
+
+
+def test_ragged_batch_full_size_sampled_sequences(ragged):
+    """Absorb the queries and decode over len_b + 1 positions, as the bench does."""
+    r = ragged
+    w, cdims, dims, cache, pos = r["w"], r["cdims"], r["dims"], r["cache"], r["pos"]
+    B, H, d_h = w.B, w.H, w.d_h
     M = synth.weights(w)
     q_nope, q_rope = synth.queries(w, B)
-    q_dev = _device_absorb(cdims, w, q_nope, q_rope, pos, M, tab_lib, max_pos)
+    q_dev = _device_absorb(cdims, w, q_nope, q_rope, pos, M, r["tab_lib"], r["max_pos"])
     seq_len = torch.from_numpy(pos + 1).cuda()
     max_len = int(pos.max()) + 1
     out = torch.full((B, H, d_h), float("nan"), device="cuda")
@@ -110,18 +136,46 @@ def test_ragged_batch_full_size_sampled_sequences():
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     assert np.all(np.isfinite(out))
 
-    tab_ora = O.rope_rows(np.arange(max_pos), d_r, w.base)
-    for b in sampled:
-        n = int(lens[b]) + 1
-        v, kr = toks[b]
-        # the oracle's own contiguous pool for this sequence
-        pool = O.Pool.empty("bf16", n * G * d_h, n * d_r, (n * G * d_h, G * d_h, d_h, n * d_r, d_r),
-                            1, 1 << int(np.ceil(np.log2(n))), np.zeros((1, 1)))
-        O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr, tab_ora)
-        V, krc = O.gather(pool, dims, 0, n)
-        qt, r = O.absorb(q_nope[b:b + 1], q_rope[b:b + 1], pos[b:b + 1], M, tab_ora)
-        q_ref = O.q_abs_of(qt, r)[0]
+    tab_ora = O.rope_rows(np.arange(r["max_pos"]), w.d_r, w.base)
+    for b in r["sampled"]:
+        n = int(r["lens"][b]) + 1
+        V, krc = _sequence_values(r, b)
+        qt, rr = O.absorb(q_nope[b:b + 1], q_rope[b:b + 1], pos[b:b + 1], M, tab_ora)
+        q_ref = O.q_abs_of(qt, rr)[0]
         ref, ref_lse = O.decode_sequence(V, krc, dims, q_ref, w.scale)
         check_output(out[b], ref, "bf16", f"ragged batch seq {b} len {n}")
+        ok, e = lse_ok(lse[b], ref_lse, 1e-3)
+        assert ok, (b, e)
+
+
+def test_recon_comparator_full_size(ragged):
+    """The non-absorbable comparator on the same batch, in the bench's configuration (automatic
+    split count, the query at the appended position, a key-wide RoPE table): the longest, the
+    shortest and one more sampled sequence against the oracle."""
+    r = ragged
+    w, cdims, dims, cache, pos = r["w"], r["cdims"], r["dims"], r["cache"], r["pos"]
+    B, H, d_h = w.B, w.H, w.d_h
+    max_len = int(pos.max()) + 1
+    max_pos = max_len + 1
+    rope = torch.from_numpy(gb.gva_rope_table_fill(max_pos, w.d_n, w.base)).cuda()
+    q, Mv, mt_bits = synth.recon_inputs(w)
+    out = torch.full((B, H, d_h), float("nan"), device="cuda")
+    lse = torch.full((B, H), float("nan"), device="cuda")
+    wsb = gb.gva_recon_decode_workspace_bytes(cdims, B, max_len, 0)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    scale = 1.0 / float(np.sqrt(w.d_n))
+    gb.gva_recon_decode(cdims, cache, B, torch.from_numpy(pos + 1).cuda(), max_len,
+                        torch.from_numpy(q).cuda(), torch.from_numpy(pos).cuda(),
+                        torch.from_numpy(mt_bits.view(np.int16)).cuda(), rope, max_pos, scale,
+                        out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    s = r["sampled"]
+    for b in sorted({s[0], s[-1], s[len(s) // 2]}):
+        V, _ = _sequence_values(r, b)
+        ref, ref_lse = O.recon_decode_sequence(V, dims, q[b], int(pos[b]), Mv, scale, w.base)
+        check_output(out[b], ref, "bf16", f"comparator ragged batch seq {b} len {V.shape[0]}")
         ok, e = lse_ok(lse[b], ref_lse, 1e-3)
         assert ok, (b, e)
