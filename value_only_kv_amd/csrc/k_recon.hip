@@ -8,11 +8,11 @@
 //   k_{h,j} = R_j (M_h^T v_j),   s_j = scale (R_p q_h) . k_{h,j},   o_h = sum_j softmax_j(s) v_j.
 // That per-token d_h x d_n product per head is the cost absorption avoids.
 //
-// Work-group: one (sequence, chunk, group), one wave per head of the group (H / G <= 4), with
-// the group's maps M_h^T resident in LDS for the whole chunk. Keys are walked in tiles of 32
-// positions:
-//   * the tile's value rows are staged once in LDS (double-buffered; the next tile's rows are
-//     loaded from HBM into registers while the current one is computed);
+// Work-group: one (sequence, chunk, group), two waves per head of the group (H / G <= 4, two
+// waves per SIMD), with the group's maps M_h^T resident in LDS for the whole chunk. Keys are
+// walked in steps of two tiles of 32 positions, one tile for each half of the waves:
+//   * a step's value rows are staged once in LDS (the next step's rows are loaded from HBM into
+//     registers while the current one is computed; one barrier per tile);
 //   * each wave rebuilds its head's keys, K^T[dim][key] = M_h^T V^T, on
 //     v_mfma_f32_16x16x32_bf16 (A = M_h^T from LDS, B = the value rows; both operands are exact
 //     bf16 and the products accumulate in float32);
@@ -26,8 +26,9 @@
 //     two probabilities (keys delta and delta + 16) as a bf16 pair against the same dim of both
 //     value rows (v_dot2_f32_bf16, float32 accumulation, the value registers of the rebuild),
 //     into per-lane partial sums that are reduced at the end of the chunk.
-// Partials (m, l, o) go to the split-grid rows the decode combine reads; a single chunk per
-// sequence writes the output directly.
+// At the end of the chunk the two waves of a head merge their (m, l, o) through LDS. Partials go
+// to the split-grid rows the decode combine reads; a single chunk per sequence writes the output
+// directly.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -82,21 +83,24 @@ __device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
 }
 
 template <int DH, int DN, int NH>
-__global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
+__global__ __launch_bounds__(128 * NH) void k_recon_decode(gva::ReconArgs r) {
   constexpr int KSTEPS = DH / 32;          // k-steps of the key rebuild
   constexpr int NB = DN / 16;              // 16-dim blocks of a key
   constexpr int kStride = DH + 8;          // LDS row (M^T row, value row) in elements: 16 B pad
-  constexpr int kUnits = kTile * DH / 8;   // 16-byte pieces of a value tile
-  constexpr int kThreads = 64 * NH;
+  constexpr int kStep = 2 * kTile;         // positions staged per step: one tile per half
+  constexpr int kUnits = kStep * DH / 8;   // 16-byte pieces of a step's value rows
+  constexpr int kThreads = 128 * NH;
   constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) uint16_t m_lds[NH * DN * kStride];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTile * kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kStep * kStride];
   __shared__ __attribute__((aligned(16))) float cs_lds[2][DN];   // (cos, sin) of DN / 2 pairs
   __shared__ int bad_lds;
 
   const gva::DecodeArgs &a = r.kv;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head within the group
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave / NH;              // which tile of each step this wave takes
+  const int hw = wave - half * NH;         // head within the group
   const int n = lane & 15;
   const int kq = lane >> 4;
   const int S = a.num_splits;
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
   id /= a.G;
   const int s = id % S;
   const int b = id / S;
-  const int h = g * NH + wave;
+  const int h = g * NH + hw;
   const int len = a.seq_len[b];
   const int p = r.q_pos[b];
   const int cap = a.max_blocks << a.log2_bs;
@@ -121,16 +125,16 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
   const int c0 = s * a.chunk;
   if (err) {                                           // uniform per work-group
     if (threadIdx.x == 0 && s == 0 && g == 0) gvad::raise_err(a.err_flag, err);
-    if (S == 1) {
+    if (half == 0 && S == 1) {
       for (int d = lane; d < DH; d += 64) a.out[orow * DH + d] = qnan;
       if (a.lse && lane == 0) a.lse[orow] = qnan;
-    } else if (err == GVA_DEVERR_ROPE && c0 < len && lane == 0) {
+    } else if (half == 0 && err == GVA_DEVERR_ROPE && c0 < len && lane == 0) {
       a.part_m[prow] = qnan;                           // the combine reads this chunk
     }
     return;
   }
   if (c0 >= len) {                                     // uniform per work-group
-    if (S == 1) {                                      // len == 0
+    if (half == 0 && S == 1) {                         // len == 0
       for (int d = lane; d < DH; d += 64) a.out[orow * DH + d] = 0.0f;
       if (a.lse && lane == 0) a.lse[orow] = -INFINITY;
     }
@@ -175,15 +179,16 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
         rsn[tb][nb][u] = static_cast<float>(t[1]);
       }
 
-  // staging of one tile: value rows (keys past the chunk repeat its last key) and the angle row
-  // of p - j0 (a negative offset uses the row of its magnitude with the sine negated)
+  // staging of one step (two tiles, 64 positions from j0): value rows (keys past the chunk
+  // repeat its last key) and, for each tile, the angle row of p - its first position (a
+  // negative offset uses the row of its magnitude with the sine negated)
   const int32_t *bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
   const int pos_mask = (1 << a.log2_bs) - 1;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v) + static_cast<int64_t>(g) * a.v_sg;
   u32x4 stv[kPer];
   f64x2 sta = {0.0, 0.0};
   bool bad = false;
-  auto load_tile = [&](int j0) __attribute__((always_inline)) {
+  auto load_step = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int unit = threadIdx.x + kThreads * i;
@@ -199,27 +204,30 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
         stv[i] = *reinterpret_cast<const u32x4 *>(vbase + off);
       }
     }
-    if (threadIdx.x < DN / 2) {
-      const int d = p - j0;
-      const int row = d < 0 ? -d : d;
+    if (threadIdx.x < DN) {                          // thread t: tile t / (DN/2), pair t % (DN/2)
+      const int d = p - j0 - kTile * (threadIdx.x / (DN / 2));
+      // inside the table for every tile that exists (|d| < len <= max_pos); the clamp only
+      // keeps the unused row of a missing second tile in bounds
+      const int row = min(d < 0 ? -d : d, r.max_pos - 1);
       sta = *reinterpret_cast<const f64x2 *>(
-          r.rope + (static_cast<int64_t>(row) * (DN / 2) + threadIdx.x) * 2);
+          r.rope + (static_cast<int64_t>(row) * (DN / 2) + threadIdx.x % (DN / 2)) * 2);
       if (d < 0) sta[1] = -sta[1];
     }
   };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+  auto store_step = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int unit = threadIdx.x + kThreads * i;
       if (kUnits % kThreads == 0 || unit < kUnits) {
         const int key = unit / (DH / 8);
         const int col = (unit - key * (DH / 8)) * 8;
-        *reinterpret_cast<u32x4 *>(&v_lds[buf][key * kStride + col]) = stv[i];
+        *reinterpret_cast<u32x4 *>(&v_lds[key * kStride + col]) = stv[i];
       }
     }
-    if (threadIdx.x < DN / 2) {
-      cs_lds[buf][2 * threadIdx.x] = static_cast<float>(sta[0]);
-      cs_lds[buf][2 * threadIdx.x + 1] = static_cast<float>(sta[1]);
+    if (threadIdx.x < DN) {
+      float *dst = cs_lds[threadIdx.x / (DN / 2)] + 2 * (threadIdx.x % (DN / 2));
+      dst[0] = static_cast<float>(sta[0]);
+      dst[1] = static_cast<float>(sta[1]);
     }
   };
 
@@ -229,12 +237,13 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
   for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o_part[ks][e] = 0.0f;
-  const uint16_t *mh = m_lds + wave * DN * kStride;
+  const uint16_t *mh = m_lds + hw * DN * kStride;
 
-  // One tile: rebuild the keys, rotate, score, softmax, weighted sum.
-  auto compute = [&](int buf, int j0) __attribute__((always_inline)) {
-    const uint16_t *vt = v_lds[buf];
-    const float *cs = cs_lds[buf];
+  // This wave's tile of the step (first position j0): rebuild the keys, rotate, score, softmax,
+  // weighted sum.
+  auto compute = [&](int j0) __attribute__((always_inline)) {
+    const uint16_t *vt = v_lds + half * kTile * kStride;
+    const float *cs = cs_lds[half];
     // B operands: lane (n, kq) holds key 16 tb + n, dims 32 ks + 8 kq .. + 8
     u32x4 vb[2][KSTEPS];
 #pragma unroll
@@ -319,39 +328,64 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
       }
   };
 
-  const int ntiles = (c1 - c0 + kTile - 1) / kTile;
-  load_tile(c0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = c0 + t * kTile;
-    if (t + 1 < ntiles) load_tile(j0 + kTile);         // uniform per work-group
-    compute(t & 1, j0);
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
+  const int nsteps = (c1 - c0 + kStep - 1) / kStep;
+  load_step(c0);
+  for (int t = 0; t < nsteps; ++t) {
+    const int j0 = c0 + t * kStep;
+    store_step();
+    __syncthreads();
+    if (t + 1 < nsteps) load_step(j0 + kStep);         // uniform per work-group
+    const int jw = j0 + half * kTile;
+    if (jw < c1) compute(jw);                          // uniform per wave
     __syncthreads();
   }
   if (bad) {
     bad_lds = 1;
     gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
   }
-  __syncthreads();
-  const bool poisoned = bad_lds != 0;
 
   // reduce over the 16 lanes of a row (the keys); row kq holds dims 32 ks + 8 kq + e
-  const float l = row16_sum(l_part);
+  float l = row16_sum(l_part);
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o_part[ks][e] = row16_sum(o_part[ks][e]);
+  // merge the two halves of each head through LDS (the value rows are no longer needed):
+  // half 1 leaves m, l and its sums; half 0 rescales both to the larger m and adds
+  float *mo = reinterpret_cast<float *>(v_lds);        // [NH][DH]
+  float *mm = mo + NH * DH;                            // [NH]
+  float *ml = mm + NH;                                 // [NH]
+  if (half == 1) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (n != ks) continue;
+      float *dst = mo + hw * DH + 32 * ks + 8 * kq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = o_part[ks][e];
+    }
+    if (lane == 0) {
+      mm[hw] = m_run;
+      ml[hw] = l;
+    }
+  }
+  __syncthreads();
+  if (half == 1) return;
+  const bool poisoned = bad_lds != 0;
+  const float m1 = mm[hw];
+  const float mx = fmaxf(m_run, m1);                  // finite: half 0 saw the chunk's first tile
+  const float a0 = __builtin_amdgcn_exp2f(m_run - mx);
+  const float a1 = __builtin_amdgcn_exp2f(m1 - mx);   // 0 when half 1 had no tile
+  l = l * a0 + ml[hw] * a1;
   const float inv = 1.0f / l;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     if (n != ks) continue;                             // lane (ks, kq) writes dims 32 ks + 8 kq ..
+    const float *src = mo + hw * DH + 32 * ks + 8 * kq;
     f32x4 w0, w1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w0[e] = o_part[ks][e];
-      w1[e] = o_part[ks][4 + e];
+      w0[e] = o_part[ks][e] * a0 + src[e] * a1;
+      w1[e] = o_part[ks][4 + e] * a0 + src[4 + e] * a1;
     }
     if (S == 1) {
       w0 *= inv;
@@ -364,9 +398,9 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
   }
   if (lane == 0) {
     if (S == 1) {
-      if (a.lse) a.lse[orow] = poisoned ? qnan : (m_run + log2f(l)) * gvad::kLn2;
+      if (a.lse) a.lse[orow] = poisoned ? qnan : (mx + log2f(l)) * gvad::kLn2;
     } else {
-      a.part_m[prow] = poisoned ? qnan : m_run;
+      a.part_m[prow] = poisoned ? qnan : mx;
       a.part_l[prow] = l;
     }
   }
@@ -375,10 +409,10 @@ __global__ __launch_bounds__(64 * NH) void k_recon_decode(gva::ReconArgs r) {
 template <int DH, int DN>
 hipError_t launch_dn(const gva::ReconArgs &r, dim3 grid, int nh, hipStream_t stream) {
   switch (nh) {
-    case 1: hipLaunchKernelGGL((k_recon_decode<DH, DN, 1>), grid, dim3(64), 0, stream, r); break;
-    case 2: hipLaunchKernelGGL((k_recon_decode<DH, DN, 2>), grid, dim3(128), 0, stream, r); break;
-    case 3: hipLaunchKernelGGL((k_recon_decode<DH, DN, 3>), grid, dim3(192), 0, stream, r); break;
-    case 4: hipLaunchKernelGGL((k_recon_decode<DH, DN, 4>), grid, dim3(256), 0, stream, r); break;
+    case 1: hipLaunchKernelGGL((k_recon_decode<DH, DN, 1>), grid, dim3(128), 0, stream, r); break;
+    case 2: hipLaunchKernelGGL((k_recon_decode<DH, DN, 2>), grid, dim3(256), 0, stream, r); break;
+    case 3: hipLaunchKernelGGL((k_recon_decode<DH, DN, 3>), grid, dim3(384), 0, stream, r); break;
+    case 4: hipLaunchKernelGGL((k_recon_decode<DH, DN, 4>), grid, dim3(512), 0, stream, r); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
