@@ -467,6 +467,44 @@ def recon_decode_flops(len_b: int, H: int, d_h: int, d_n: int) -> int:
 
 
 # --------------------------------------------------------------------------------------
+# MLA-style latent comparator. MLA caches one joint latent of width d_c plus a shared RoPE
+# channel, T (d_c + d_r) scalars, and projects keys and values back up from the latent at
+# decode ([review] section 问题; [mla] section 3.1 for the up-projections W^UK and W^UV).
+# With the key up-projection folded into the query, q~_h = W^UK_h q_nope_h, its decode is the
+# absorbed decode above with one group whose cached "value" is the latent: decode_sequence
+# with G = 1 and d_h = d_c; the value up-projection multiplies the latent output afterwards.
+# mla_decode_materialized writes the textbook form out (every head's keys and values projected
+# up from the latents) to check that identity.
+# --------------------------------------------------------------------------------------
+
+
+def mla_cache_scalars(T: int, d_c: int, d_r: int) -> int:
+    """Scalars one layer's MLA cache holds: T (d_c + d_r)."""
+    return T * (d_c + d_r)
+
+
+def mla_decode_materialized(C: np.ndarray, kr: np.ndarray, q_nope_b, r_b, W_uk, W_uv,
+                            scale: float):
+    """One sequence; C [n, d_c] cached latents, kr [n, d_r] cached (rotated) positional keys,
+    q_nope_b [H, d_k], r_b [H, d_r] rotated positional queries, W_uk [H, d_c, d_k],
+    W_uv [H, d_c, d_v]. Keys K_h = C W_uk[h], values V_h = C W_uv[h]; returns out [H, d_v]
+    and lse [H] (float64)."""
+    C = np.asarray(C, dtype=np.float64)
+    kr = np.asarray(kr, dtype=np.float64)
+    q_nope_b = np.asarray(q_nope_b, dtype=np.float64)
+    r_b = np.asarray(r_b, dtype=np.float64)
+    H = q_nope_b.shape[0]
+    out = np.zeros((H, W_uv.shape[2]))
+    lse = np.full(H, -np.inf)
+    for h in range(H):
+        K = C @ np.asarray(W_uk[h], dtype=np.float64)
+        V = C @ np.asarray(W_uv[h], dtype=np.float64)
+        s = scale * (K @ q_nope_b[h] + kr @ r_b[h])
+        out[h], lse[h], _ = softmax_attend(s, V)
+    return out, lse
+
+
+# --------------------------------------------------------------------------------------
 # O7: chunked prefill.  The chunk's tokens are appended first (O4); query i of sequence b
 # sits at position start_b + i and attends to positions 0..start_b + i (inclusive), over
 # the cache-rounded values ([summary]: prefill is a dense, matrix-heavy pass).

@@ -656,3 +656,47 @@ def test_recon_decode_empty_and_flops():
     assert np.all(out == 0) and np.all(np.isneginf(lse))
     # per token and head: a d_h x d_n rebuild, a d_n score and a d_h weighted sum
     assert O.recon_decode_flops(3, 2, 4, 6) == 2 * 3 * (2 * 4 * 6 + 2 * 6 + 2 * 4)
+
+
+# ----------------------------------------------------------------------------------------
+# MLA-style latent comparator
+# ----------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mla_absorbed_decode_equals_textbook(seed):
+    """The textbook MLA step (keys and values projected up from the cached latents per head) equals
+    the absorbed decode with one group whose value is the latent (q~_h = W^UK_h q_nope_h),
+    followed by the value up-projection. d_c, d_k and d_v all differ, so a transposed
+    projection fails."""
+    rng = np.random.default_rng(seed)
+    H, n, d_c, d_k, d_v, d_r, scale = 6, 29, 12, 8, 10, 4, 0.3
+    C = rng.standard_normal((n, d_c))
+    kr = rng.standard_normal((n, d_r))
+    q_nope = rng.standard_normal((H, d_k))
+    r = rng.standard_normal((H, d_r))
+    W_uk = rng.standard_normal((H, d_c, d_k))
+    W_uv = rng.standard_normal((H, d_c, d_v))
+    out, lse = O.mla_decode_materialized(C, kr, q_nope, r, W_uk, W_uv, scale)
+    dims = O.Dims(H=H, G=1, d_h=d_c, d_n=d_k, d_r=d_r)
+    q_abs = np.concatenate([np.einsum("hck,hk->hc", W_uk, q_nope), r], axis=1)
+    lat, lse_a = O.decode_sequence(C[:, None, :], kr, dims, q_abs, scale)
+    assert np.allclose(np.einsum("hc,hcv->hv", lat, W_uv), out, rtol=0, atol=1e-12)
+    assert np.allclose(lse_a, lse, rtol=0, atol=1e-12)
+    # and against torch's attention on the up-projected keys and values
+    Kh = torch.from_numpy(np.einsum("nc,hck->hnk", C, W_uk))
+    Vh = torch.from_numpy(np.einsum("nc,hcv->hnv", C, W_uv))
+    qh = torch.from_numpy(q_nope)[:, None, :]
+    s = scale * (torch.einsum("hqk,hnk->hqn", qh, Kh) + torch.from_numpy(r @ kr.T)[:, None, :])
+    ref = (torch.softmax(s, dim=-1) @ Vh)[:, 0, :].numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_mla_cache_ledger_against_pages():
+    """[review] section 问题: MLA caches T (d_c + d_r) scalars; with the DeepSeek-V2 latent of
+    [mla] section 3.1 (d_c = 512) and a 64-wide shared RoPE channel that is 576 per token, and
+    the latent alone replaces h (d_k + d_v) = 128 x 256 = 32768 per token."""
+    assert O.mla_cache_scalars(1, 512, 64) == 576
+    assert O.mla_cache_scalars(1000, 512, 0) * 64 == 1000 * 128 * (128 + 128)
+    # beside the matched GVA cache of the ragged-batch shape (G = 8, d_h = 128, d_r = 24)
+    assert O.mla_cache_scalars(1, 512, 64) / O.gva_cache_scalars(1, 8, 128, 24) < 0.55
