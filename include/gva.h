@@ -275,6 +275,33 @@ gva_status gva_recon_decode(const gva_dims *dims, const gva_cache *values, int32
                             int32_t max_pos, float scale, int32_t num_splits, void *workspace,
                             size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
 
+/* ---- MLA-style latent comparator ([review] section 问题: MLA caches one joint latent of width
+ * d_c plus a shared RoPE channel, T (d_c + d_r) scalars, and projects keys and values back up at
+ * decode) -----------------------------------------------------------------------------------
+ * Decodes an MLA cache with the key up-projection folded into the query: the absorbed decode of
+ * gva_decode with one group (G = 1) whose cached value is the latent (d_h = d_c):
+ *   out[b][h][:] = sum_{j < seq_len[b]} softmax_j(scale * (q~_h . c_j + r_h . kr_j)) c_j
+ * (width d_c); the value up-projection multiplies out afterwards, outside this call, as W_O
+ * does for GVA.
+ *   dims: H in {8, 16, 32}, G = 1, d_h = d_c in {256, 512}, d_r a multiple of 8 in [8, 64]
+ *   (d_n is not used).
+ *   latent: a bf16 cache as for gva_decode, v holding the latents (v_stride_group is not used)
+ *   and kr the rotated positional keys; strides multiples of 8 elements; its RoPE table is not
+ *   read. gva_cache_append fills such a pool when each latent row is described as d_c / 256
+ *   groups of 256 (v_stride_group = 256).
+ *   q_abs: device float32 [B][H][d_c + d_r] = [q~_h ; rotated q_rope_h], 16-byte aligned.
+ *   workspace: at least gva_mla_decode_workspace_bytes(dims, B, max_len, num_splits) bytes,
+ *   256-byte aligned (none when that is 0); num_splits as for gva_recon_decode.
+ *   out: device float32 [B][H][d_c], 16-byte aligned; lse: device float32 [B][H] or NULL.
+ * Device-detected errors: a bad block-table entry (BLOCK), seq_len[b] negative or above max_len
+ * (LENGTH) or above the table's capacity (CAPACITY), each giving a NaN output row. */
+size_t gva_mla_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
+                                      int32_t num_splits);
+gva_status gva_mla_decode(const gva_dims *dims, const gva_cache *latent, int32_t B,
+                          const int32_t *seq_len, int32_t max_len, const float *q_abs,
+                          float scale, int32_t num_splits, void *workspace,
+                          size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
+
 /* ---- Diagnostics --------------------------------------------------------------------------- */
 const char *gva_status_string(gva_status status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */

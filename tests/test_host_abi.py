@@ -314,3 +314,38 @@ def test_recon_validation(L):
     # a large batch runs one chunk per sequence and needs none
     assert gb.gva_recon_decode_workspace_bytes(d, 256, 100, 0) == 0
     assert gb.gva_recon_decode_workspace_bytes(d, 2, 100, 1) == 0
+
+
+def test_mla_validation(L):
+    """The MLA-style latent comparator's argument checks, all on the host before any launch."""
+    d = _dims(H=32, G=1, d_h=256, d_n=256, d_r=64)
+    c = _cache(d=_dims(H=32, G=1, d_h=256, d_n=256, d_r=64))
+
+    def ml(**kw):
+        return L.gva_mla_decode(ctypes.byref(kw.get("d", d)), ctypes.byref(kw.get("c", c)),
+                                kw.get("B", 2), kw.get("sl", A), kw.get("ml", 100),
+                                kw.get("q", A), kw.get("scale", 0.1), kw.get("S", 0),
+                                kw.get("ws", None), kw.get("wsb", 0), kw.get("out", A), None, None)
+    assert ml(d=_dims(H=32, G=2, d_h=256, d_r=64)) == gb.GVA_ERR_INVALID_ARG     # one latent
+    assert ml(d=_dims(H=24, G=1, d_h=256, d_r=64)) == gb.GVA_ERR_UNSUPPORTED
+    assert ml(d=_dims(H=32, G=1, d_h=384, d_r=64)) == gb.GVA_ERR_UNSUPPORTED
+    assert ml(d=_dims(H=32, G=1, d_h=256, d_r=12)) == gb.GVA_ERR_UNSUPPORTED
+    assert ml(d=_dims(H=32, G=1, d_h=256, d_r=72)) == gb.GVA_ERR_UNSUPPORTED
+    assert ml(c=_cache(dtype=gb.GVA_DTYPE_F32)) == gb.GVA_ERR_UNSUPPORTED
+    assert ml(c=_cache(d=d, v_stride_token=260)) == gb.GVA_ERR_INVALID_ARG       # not 8-aligned
+    assert ml(B=0) == gb.GVA_ERR_INVALID_ARG
+    for k in ("sl", "q", "out"):
+        assert ml(**{k: None}) == gb.GVA_ERR_INVALID_ARG, k
+    assert ml(q=A + 8) == gb.GVA_ERR_INVALID_ARG
+    assert ml(ml=8 * 16 + 1) == gb.GVA_ERR_INVALID_ARG
+    assert ml(scale=0.0) == gb.GVA_ERR_INVALID_ARG
+    assert ml(S=1025) == gb.GVA_ERR_INVALID_ARG
+    # d_c = 512 is accepted (and a split plan then needs a workspace)
+    d512 = _dims(H=32, G=1, d_h=256, d_n=256, d_r=64)
+    d512.d_h = 512
+    wsb = gb.gva_mla_decode_workspace_bytes(d512, 2, 100, 0)
+    assert wsb > 0
+    assert ml(d=d512, c=_cache(d=d, v_stride_token=512, v_stride_block=16 * 512)) == gb.GVA_ERR_WORKSPACE
+    assert ml(d=d512, c=_cache(d=d, v_stride_token=512, v_stride_block=16 * 512),
+              ws=A + 64, wsb=wsb) == gb.GVA_ERR_WORKSPACE
+    assert gb.gva_mla_decode_workspace_bytes(d512, 256, 100, 0) == 0

@@ -30,6 +30,7 @@ EXPORTED = [
     "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
     "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode",
     "gva_recon_decode_workspace_bytes", "gva_recon_decode",
+    "gva_mla_decode_workspace_bytes", "gva_mla_decode",
     "gva_status_string", "gva_last_error", "gva_version",
 ]
 
@@ -103,6 +104,11 @@ def lib() -> ctypes.CDLL:
     L.gva_recon_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32,
                                    P, P, P, P, c_int32, c_float, c_int32, P, c_size_t, P, P, P]
     L.gva_recon_decode.restype = c_int32
+    L.gva_mla_decode_workspace_bytes.argtypes = [POINTER(GvaDims), c_int32, c_int32, c_int32]
+    L.gva_mla_decode_workspace_bytes.restype = c_size_t
+    L.gva_mla_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32,
+                                 P, c_float, c_int32, P, c_size_t, P, P, P]
+    L.gva_mla_decode.restype = c_int32
     L.gva_status_string.argtypes = [c_int32]
     L.gva_status_string.restype = c_char_p
     L.gva_last_error.argtypes = []
@@ -242,6 +248,21 @@ def gva_recon_decode(dims: GvaDims, values: "GvaCache", B: int, seq_len, max_len
                                   _ptr(seq_len), max_len, _ptr(q), _ptr(q_pos), _ptr(Mt),
                                   _ptr(rope), max_pos, scale, num_splits, _ptr(workspace),
                                   ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def gva_mla_decode_workspace_bytes(dims: GvaDims, B: int, max_len: int, num_splits: int = 0) -> int:
+    return int(lib().gva_mla_decode_workspace_bytes(ctypes.byref(dims), B, max_len, num_splits))
+
+
+def gva_mla_decode(dims: GvaDims, latent: "GvaCache", B: int, seq_len, max_len: int, q_abs,
+                   scale: float, out, lse=None, num_splits: int = 0, workspace=None,
+                   stream=None) -> None:
+    """The MLA-style latent comparator: dims with G = 1 and d_h = d_c; latent.v holds the
+    latents, latent.kr the rotated positional keys."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gva_mla_decode(ctypes.byref(dims), ctypes.byref(latent.struct), B, _ptr(seq_len),
+                                max_len, _ptr(q_abs), scale, num_splits, _ptr(workspace),
+                                ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def gva_version() -> str:

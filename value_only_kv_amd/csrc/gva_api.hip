@@ -210,6 +210,39 @@ gva_status gva_recon_decode(const gva_dims *dims, const gva_cache *values, int32
   return GVA_OK;
 }
 
+gva_status gva_mla_decode(const gva_dims *dims, const gva_cache *latent, int32_t B,
+                          const int32_t *seq_len, int32_t max_len, const float *q_abs,
+                          float scale, int32_t num_splits, void *workspace,
+                          size_t workspace_bytes, float *out, float *lse, hipStream_t stream) {
+  gva::DecodePlan plan{};
+  gva_status st = gva::check_latent(dims, latent, B, seq_len, max_len, q_abs, scale, num_splits,
+                                    workspace, workspace_bytes, out, &plan);
+  if (st != GVA_OK) return st;
+  gva::DecodeArgs a = cache_args(dims, latent);
+  a.B = B;
+  a.seq_len = seq_len;
+  a.max_len = max_len;
+  a.q_abs = q_abs;
+  a.qscale = scale * 1.4426950408889634f;
+  a.num_splits = plan.num_splits;
+  a.chunk = plan.chunk;
+  a.out = out;
+  a.lse = lse;
+  if (plan.num_splits > 1) {
+    char *ws = static_cast<char *>(workspace);
+    a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
+    a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
+    a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+  }
+  hipError_t e = gva::launch_latent_decode(a, stream);
+  if (e != hipSuccess) return hip_status(e, "latent comparator decode launch");
+  if (plan.num_splits > 1) {
+    e = gva::launch_combine(a, stream);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return GVA_OK;
+}
+
 gva_status gva_prefill_chunk(const gva_dims *dims, const gva_cache *cache, int32_t B,
                              const int32_t *start, int32_t max_start, int32_t chunk_len,
                              const float *q_abs, const float *v_new, const float *kr_raw,

@@ -307,6 +307,58 @@ gva_status check_recon(const gva_dims *d, const gva_cache *c, int32_t B, const i
   return GVA_OK;
 }
 
+gva_status check_latent(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *seq_len,
+                        int32_t max_len, const float *q_abs, float scale, int32_t num_splits,
+                        const void *workspace, size_t workspace_bytes, const float *out,
+                        DecodePlan *plan) {
+  if (!d) return fail(GVA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->G != 1) return fail(GVA_ERR_INVALID_ARG, "the latent comparator takes G=1 (one latent), got G=%d", d->G);
+  if (d->H != 8 && d->H != 16 && d->H != 32)
+    return fail(GVA_ERR_UNSUPPORTED, "the latent comparator supports H of 8, 16 or 32, got %d", d->H);
+  if (d->d_h != 256 && d->d_h != 512)
+    return fail(GVA_ERR_UNSUPPORTED, "the latent comparator supports d_c (d_h) of 256 or 512, got %d", d->d_h);
+  if (d->d_r < 8 || d->d_r > 64 || d->d_r % 8 != 0)
+    return fail(GVA_ERR_UNSUPPORTED, "the latent comparator needs d_r in [8, 64], a multiple of 8");
+  if (!c) return fail(GVA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->dtype != GVA_DTYPE_BF16) return fail(GVA_ERR_UNSUPPORTED, "the latent comparator needs a bf16 cache");
+  if (!c->v || !c->kr || !aligned(c->v, 16) || !aligned(c->kr, 16))
+    return fail(GVA_ERR_INVALID_ARG, "cache v and kr must be 16-byte aligned pointers");
+  if (!c->block_table) return fail(GVA_ERR_INVALID_ARG, "block_table is NULL");
+  if (c->num_blocks < 1 || c->num_blocks > (int64_t)INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31)");
+  if (!pow2(c->block_size) || c->block_size > (1 << 30))
+    return fail(GVA_ERR_INVALID_ARG, "block_size=%d must be a power of two", c->block_size);
+  if (c->max_blocks < 1) return fail(GVA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  if ((int64_t)c->max_blocks * c->block_size > (int64_t)INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARG, "max_blocks * block_size exceeds int32 positions");
+  const int64_t st[4] = {c->v_stride_block, c->v_stride_token, c->kr_stride_block, c->kr_stride_token};
+  for (int i = 0; i < 4; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0)
+      return fail(GVA_ERR_INVALID_ARG, "latent and kr strides must be >= 0 and multiples of 8 elements");
+  if (c->block_size > 1 && (c->v_stride_token < d->d_h || c->kr_stride_token < d->d_r))
+    return fail(GVA_ERR_INVALID_ARG, "latent or kr token rows overlap");
+  if (B < 1) return fail(GVA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (!seq_len || !q_abs || !out) return fail(GVA_ERR_INVALID_ARG, "latent comparator argument is NULL");
+  if (!aligned(q_abs, 16) || !aligned(out, 16))
+    return fail(GVA_ERR_INVALID_ARG, "q_abs and out must be 16-byte aligned");
+  if (max_len < 0) return fail(GVA_ERR_INVALID_ARG, "max_len=%d must be >= 0", max_len);
+  if ((int64_t)max_len > (int64_t)c->max_blocks * c->block_size)
+    return fail(GVA_ERR_INVALID_ARG, "max_len=%d exceeds the block table's capacity", max_len);
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(GVA_ERR_INVALID_ARG, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
+  if (!plan_decode(d, B, max_len, num_splits, false, plan))
+    return fail(GVA_ERR_INVALID_ARG, "cannot plan the decode split");
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+      return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan->ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  return GVA_OK;
+}
+
 gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
                          int32_t max_start, int32_t chunk_len, const float *q_abs,
                          const float *v_new, const float *kr_raw, float scale, const float *out) {
@@ -380,6 +432,14 @@ size_t gva_recon_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t
   if (gva::check_dims(&dd) != GVA_OK) return 0;
   gva::DecodePlan p;
   if (!gva::plan_decode(&dd, B, max_len, num_splits, false, &p)) return 0;
+  return p.ws_bytes;
+}
+
+size_t gva_mla_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
+                                      int32_t num_splits) {
+  if (!dims || dims->G != 1 || dims->H < 1) return 0;
+  gva::DecodePlan p;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, false, &p)) return 0;
   return p.ws_bytes;
 }
 

@@ -108,6 +108,13 @@ gva_status check_recon(const gva_dims *d, const gva_cache *c, int32_t B, const i
                        const void *workspace, size_t workspace_bytes, const float *out,
                        DecodePlan *plan);
 
+// The MLA-style latent comparator (gva_mla_decode): one group (G = 1) whose value is the
+// latent, d_h = d_c in {256, 512}, H in {8, 16, 32}; the plan is the split grid of plan_decode.
+gva_status check_latent(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *seq_len,
+                        int32_t max_len, const float *q_abs, float scale, int32_t num_splits,
+                        const void *workspace, size_t workspace_bytes, const float *out,
+                        DecodePlan *plan);
+
 gva_status check_prefill(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *start,
                          int32_t max_start, int32_t chunk_len, const float *q_abs,
                          const float *v_new, const float *kr_raw, float scale, const float *out);
@@ -184,6 +191,7 @@ struct ReconArgs {
   int32_t max_pos;
 };
 hipError_t launch_recon_decode(const ReconArgs &r, hipStream_t stream);
+hipError_t launch_latent_decode(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace gva
 

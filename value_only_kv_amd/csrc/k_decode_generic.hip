@@ -451,7 +451,7 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
   // waves grow with the partials per sequence (balanced mode: about R / B + 1 of them); with
   // few of them, one wave per (sequence, head)
   const int per_seq = a.num_ranges > 0 ? a.num_ranges / a.B + 1 : a.num_splits;
-  if (per_seq <= kCombineWaveRows) {
+  if (per_seq <= kCombineWaveRows && a.d_h <= 256) {   // the one-wave combine holds 256 dims
     const dim3 grid((a.H + 3) / 4, a.B);
     switch ((a.d_h + 63) / 64) {
       case 1: hipLaunchKernelGGL(k_combine_wave<1>, grid, dim3(256), 0, stream, a); break;

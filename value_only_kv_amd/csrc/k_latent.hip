@@ -1,0 +1,328 @@
+// k_latent.hip - decode of the MLA-style latent comparator on matrix cores (gfx950).
+//
+// MLA caches one joint latent of width d_c per token plus a shared, already rotated positional
+// key of width d_r, and projects keys and values back up from the latent at decode
+// ("GVA：KV 缓存里的 Key 其实可以不存", shibing624.github.io review of arXiv:2609.13285, section
+// 问题: T (d_c + d_r) scalars). With the key up-projection folded into the query, the step is
+// the absorbed decode of a single group whose cached value is the latent:
+//   s_j = scale (q~_h . c_j + r_h . kr_j),   out_h = sum_j softmax_j(s) c_j   (width d_c),
+// the value up-projection acting on out_h afterwards, outside this call. Unlike the GVA value
+// groups, every head reads the same latent, and d_c is wide (512 in the DeepSeek-V2 example of
+// the [mla] page), so the latent tile is staged once in LDS and shared by all the waves.
+//
+// Work-group: one (sequence, chunk) of the split plan, H / 8 waves of 8 heads each. Per tile of
+// 32 positions:
+//   * the natural rows [c (d_c) | kr (d_r, padded to a multiple of 32)] go straight from HBM
+//     into LDS (global_load_lds_dwordx4, double-buffered, one tile ahead): a unit of 16 keys x
+//     32 elements is one wave instruction that writes 1 KB, lane i's 16 bytes at 16 i, which is
+//     exactly the score product's A-operand form;
+//   * scores S^T[key][col] on v_mfma_f32_16x16x32_bf16, B = the absorbed query in its 16
+//     columns: column n < 8 the bf16 hi part of head 8 w + n, column n + 8 its lo part; a row
+//     rotation by 8 lanes (DPP) adds the two;
+//   * online softmax per head in the base-2 domain, with a lazily raised reference maximum;
+//   * weighted sum O^T[dim][col] += C^T P^T with the probabilities as a bf16 hi (columns < 8) and
+//     lo (columns >= 8) pair and C^T read from the units with the transposing LDS load, whose
+//     per-lane addresses follow each key's two 8-element pieces.
+// Partials (m, l, o) go to the split-grid rows the decode combine reads; one chunk per sequence
+// writes the output directly.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "gva_device.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+constexpr int kTile = 32;
+constexpr float kLazyRescale = 8.0f;   // the reference moves when a score passes it by more
+
+__device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ unsigned pack2(float x, float y) {
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));  // RNE, x low
+}
+__device__ __forceinline__ float low_bf16(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float high_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+// value of the lane 8 places along in its row of 16 (DPP row rotation)
+__device__ __forceinline__ float ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float max4(const f32x4 &v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+
+// LDS tile: unit (kb, ks) = keys 16 kb .. + 16, elements 32 ks .. + 32 of the natural rows,
+// 1 KB in A-operand order: key n, elements 8 q .. + 8 at 16 (n + 16 q).
+template <int KS, int RS>
+struct LatentTile {
+  static constexpr int kSteps = KS + RS;             // k-steps of a natural row
+  static constexpr int kUnits = 2 * kSteps;
+  static constexpr int kBytes = kUnits * 1024;
+};
+__device__ __forceinline__ int unit_off(int kb, int ks, int steps) { return (kb * steps + ks) * 1024; }
+
+template <int KS, int RS, int NW>
+__global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
+  using L = LatentTile<KS, RS>;
+  constexpr int kSteps = L::kSteps;
+  constexpr int kPer = (L::kUnits + NW - 1) / NW;    // units each wave stages per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][L::kBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+  const int S = a.num_splits;
+  const int s = blockIdx.x % S;
+  const int b = blockIdx.x / S;
+  const int d_c = a.d_h;
+  const int len = a.seq_len[b];
+  const int cap = a.max_blocks << a.log2_bs;
+  const float qnan = __int_as_float(0x7fc00000);
+  const int hcol = 8 * wave + (n & 7);                // the head of this lane's column
+  const bool lo_col = n >= 8;
+  const int64_t orow = static_cast<int64_t>(b) * a.H + hcol;
+  const int64_t prow = (static_cast<int64_t>(b) * S + s) * a.H + hcol;
+  const int c0 = s * a.chunk;
+  int err = 0;
+  if (len < 0 || len > a.max_len) err = GVA_DEVERR_LENGTH;
+  else if (len > cap) err = GVA_DEVERR_CAPACITY;
+  if (err) {                                           // uniform per work-group
+    if (threadIdx.x == 0 && s == 0) gvad::raise_err(a.err_flag, err);
+    if (S == 1 && !lo_col) {
+      for (int d = 4 * q; d < d_c; d += 16) *reinterpret_cast<f32x4 *>(a.out + orow * d_c + d) = f32x4{qnan, qnan, qnan, qnan};
+      if (a.lse && q == 0) a.lse[orow] = qnan;
+    }
+    return;                                            // S > 1: the combine checks the length
+  }
+  if (c0 >= len) {                                     // uniform per work-group
+    if (S == 1 && !lo_col) {                           // len == 0
+      for (int d = 4 * q; d < d_c; d += 16) *reinterpret_cast<f32x4 *>(a.out + orow * d_c + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (a.lse && q == 0) a.lse[orow] = -INFINITY;
+    }
+    return;                                            // past the end: the combine skips it
+  }
+  const int c1 = min(len, c0 + a.chunk);
+
+  // absorbed query, B-operand form: column n holds head hcol, elements 32 ks + 8 q .. + 8, as
+  // the bf16 hi part (n < 8) or lo part (n >= 8); positional padding is zero
+  u32x4 Q[kSteps];
+  {
+    const float *qp = a.q_abs + orow * (d_c + a.d_r);
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x0, x1;
+        if (ks < KS) {
+          x0 = qp[32 * ks + 8 * q + 2 * i];
+          x1 = qp[32 * ks + 8 * q + 2 * i + 1];
+        } else {
+          const int e = 32 * (ks - KS) + 8 * q + 2 * i;
+          x0 = e < a.d_r ? qp[d_c + e] : 0.0f;
+          x1 = e + 1 < a.d_r ? qp[d_c + e + 1] : 0.0f;
+        }
+        x0 *= a.qscale;
+        x1 *= a.qscale;
+        const unsigned w = pack2(x0, x1);
+        Q[ks][i] = lo_col ? pack2(x0 - low_bf16(w), x1 - high_bf16(w)) : w;
+      }
+    }
+  }
+
+  // staging: wave w loads units w, w + NW, ... of a tile (keys past the chunk repeat its last
+  // key; waves past the last unit load it again: the same bytes to the same place). The
+  // block-table entries of a tile's two key blocks are loaded one tile ahead of its staging.
+  const int32_t *bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  const int pos_mask = (1 << a.log2_bs) - 1;
+  bool bad = false;
+  int32_t pg[2];
+  auto pages = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) pg[kb] = bt[min(j0 + 16 * kb + n, c1 - 1) >> a.log2_bs];
+  };
+  auto stage = [&](int buf, int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int unit = min(wave + NW * i, L::kUnits - 1);
+      const int kb = unit / kSteps;
+      const int ks = unit - kb * kSteps;
+      const int j = min(j0 + 16 * kb + n, c1 - 1);
+      const int32_t blk = pg[kb];
+      const bool ok = blk >= 0 && static_cast<int64_t>(blk) < a.num_blocks;
+      bad = bad || !ok;
+      const int64_t bb = ok ? static_cast<int64_t>(blk) : 0;
+      const int64_t row = j & pos_mask;
+      const uint16_t *src;
+      if (ks < KS) {
+        src = static_cast<const uint16_t *>(a.v) + bb * a.v_sb + row * a.v_st + 32 * ks + 8 * q;
+      } else {
+        // positional elements past d_r read the row's last 8 (finite values, met by zeros in Q)
+        const int e = min(32 * (ks - KS) + 8 * q, a.d_r - 8);
+        src = static_cast<const uint16_t *>(a.kr) + bb * a.kr_sb + row * a.kr_st + e;
+      }
+      __builtin_amdgcn_global_load_lds((glb_void *)src,
+                                       (lds_void *)(&lds[buf][unit_off(kb, ks, kSteps)]), 16, 0, 0);
+    }
+  };
+
+  // transposing-read address of this lane within a unit: key lane / 4, and of its 16-dim
+  // block's two 8-element pieces the one of column chunk lane % 4
+  const int tr_key = lane >> 2;
+  const int tr_k = lane & 3;
+  f32x4 O[2 * KS];
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref = -INFINITY, lsum = 0.0f;
+
+  auto tile = [&](int buf, int j0) __attribute__((always_inline)) {
+    const uint8_t *base = lds[buf];
+    const float negm = (mref == -INFINITY || lo_col) ? 0.0f : -mref;
+    f32x4 Sc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      Sc[tb] = f32x4{negm, negm, negm, negm};
+#pragma unroll
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(base + unit_off(tb, ks, kSteps) + 16 * lane);
+        Sc[tb] = mfma(ka, Q[ks], Sc[tb]);
+      }
+      // hi + lo columns: every lane of the row pair (n, n + 8) holds head hcol's score
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Sc[tb][e] += ror8(Sc[tb][e]);
+        if (j0 + 16 * tb + 4 * q + e >= c1) Sc[tb][e] = -INFINITY;
+      }
+    }
+    // tile maximum relative to the reference, over the head's 32 keys (4 rows of 16 lanes)
+    const float mt = gvad::xor32_max(gvad::xor16_max(fmaxf(max4(Sc[0]), max4(Sc[1]))));
+    const bool raise = mt > kLazyRescale || (mref == -INFINITY && mt != -INFINITY);
+    if (__any(raise)) {                                // rare after the first tiles
+      const float delta = raise ? mt : 0.0f;
+      const float mnew = mref == -INFINITY ? mt : mref + delta;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;   // 0 from -inf
+      mref = raise ? mnew : mref;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) O[i] *= alpha;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) Sc[tb] -= delta;
+    }
+    float pv[8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[4 * tb + e] = __builtin_amdgcn_exp2f(Sc[tb][e]);
+        lsum += pv[4 * tb + e];
+      }
+    u32x4 PB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned w = pack2(pv[2 * i], pv[2 * i + 1]);
+      PB[i] = lo_col ? pack2(pv[2 * i] - low_bf16(w), pv[2 * i + 1] - high_bf16(w)) : w;
+    }
+    // O^T[dim][col] += C^T[dim][key] P^T[key][col]; dims 16 nb .. belong to unit step nb / 2,
+    // pieces 2 (nb % 2) and + 1; the first read gives keys 4 q .. + 3 of block 0, the second the
+    // same of block 1 (the order the lane holds its probabilities in)
+#pragma unroll
+    for (int nb = 0; nb < 2 * KS; ++nb) {
+      const int piece = 2 * (nb & 1) + (tr_k >> 1);
+      const int off = 16 * (tr_key + 16 * piece) + 8 * (tr_k & 1);
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4 *)(base + unit_off(0, nb >> 1, kSteps) + off));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4 *)(base + unit_off(1, nb >> 1, kSteps) + off));
+      const bf16x8 VT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VT, __builtin_bit_cast(bf16x8, PB), O[nb], 0, 0, 0);
+    }
+  };
+
+  const int ntiles = (c1 - c0 + kTile - 1) / kTile;
+  pages(c0);
+  stage(0, c0);
+  pages(c0 + kTile);                                   // (repeats the last key past the end)
+  __builtin_amdgcn_s_waitcnt(0);                       // the tile's units are in LDS
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    // uniform per work-group: stage tile t + 1 with the entries loaded one tile ago, then load
+    // the entries of tile t + 2
+    if (t + 1 < ntiles) stage((t + 1) & 1, c0 + (t + 1) * kTile);
+    if (t + 2 < ntiles) pages(c0 + (t + 2) * kTile);
+    tile(t & 1, c0 + t * kTile);
+    __builtin_amdgcn_s_waitcnt(0);                     // the next tile's units are in LDS
+    __syncthreads();
+  }
+  __shared__ int bad_lds;
+  if (threadIdx.x == 0) bad_lds = 0;
+  __syncthreads();
+  if (bad) {
+    bad_lds = 1;
+    gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
+  }
+  __syncthreads();
+  const bool poisoned = bad_lds != 0;
+
+  // head totals: the hi and lo columns' sums added (row rotation by 8), the probability sum
+  // taken over the four rows (lsum counts each key once per column pair: use the hi lanes')
+  // (the rotations read the lo lanes, so they run before those lanes stop)
+  const float l = gvad::xor32_sum(gvad::xor16_sum(lo_col ? 0.0f : lsum));
+  const float lt = l + ror8(l);                        // the lo lanes held 0
+#pragma unroll
+  for (int nb = 0; nb < 2 * KS; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O[nb][e] += ror8(O[nb][e]);
+  if (lo_col) return;
+  const float inv = 1.0f / lt;
+  float *dst = S == 1 ? a.out + orow * d_c : a.part_o + prow * d_c;
+#pragma unroll
+  for (int nb = 0; nb < 2 * KS; ++nb) {
+    f32x4 v = O[nb];
+    if (S == 1) v *= inv;
+    if (poisoned) v = f32x4{qnan, qnan, qnan, qnan};
+    *reinterpret_cast<f32x4 *>(dst + 16 * nb + 4 * q) = v;
+  }
+  if (q == 0) {
+    if (S == 1) {
+      if (a.lse) a.lse[orow] = poisoned ? qnan : (mref + log2f(lt)) * gvad::kLn2;
+    } else {
+      a.part_m[prow] = poisoned ? qnan : mref;
+      a.part_l[prow] = lt;
+    }
+  }
+}
+
+}  // namespace
+
+namespace gva {
+
+hipError_t launch_latent_decode(const DecodeArgs &a, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(a.B) * a.num_splits;
+  if (blocks < 1 || blocks > INT32_MAX || a.H % 8 != 0) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const int nw = a.H / 8;
+  const int rs = (a.d_r + 31) / 32;
+#define GVA_LATENT_CASE(KS, RS, NW)                                                           \
+  if (a.d_h == 32 * KS && rs == RS && nw == NW) {                                             \
+    hipLaunchKernelGGL((k_latent_decode<KS, RS, NW>), grid, dim3(64 * NW), 0, stream, a);     \
+    return hipGetLastError();                                                                 \
+  }
+  GVA_LATENT_CASE(8, 1, 1) GVA_LATENT_CASE(8, 1, 2) GVA_LATENT_CASE(8, 1, 4)
+  GVA_LATENT_CASE(8, 2, 1) GVA_LATENT_CASE(8, 2, 2) GVA_LATENT_CASE(8, 2, 4)
+  GVA_LATENT_CASE(16, 1, 1) GVA_LATENT_CASE(16, 1, 2) GVA_LATENT_CASE(16, 1, 4)
+  GVA_LATENT_CASE(16, 2, 1) GVA_LATENT_CASE(16, 2, 2) GVA_LATENT_CASE(16, 2, 4)
+#undef GVA_LATENT_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gva

@@ -16,6 +16,7 @@ Streams (numpy PCG64 through SeedSequence):
   * [1000 + k, b]        sequence b of config k: V rows, then raw positional keys
   * [1000 + k, 99999]    config k's lengths, then its block permutation
   * [1000 + k, 1 << 22 | s] the non-absorbable comparator's maps and queries
+  * [1000 + k, 1 << 23 | s] the latent comparator's absorbed queries
 All values are drawn in float64 from N(0, 1) and cast to float32 once.
 """
 from __future__ import annotations
@@ -251,6 +252,13 @@ def recon_inputs(w: Workload, stream: int = 3):
     M = Mb.to(torch.float64).numpy()
     Mt_bits = Mb.transpose(1, 2).contiguous().view(torch.int16).numpy().view(np.uint16)
     return q, M, Mt_bits
+
+
+def mla_queries(w: Workload, H: int, d_c: int, d_r: int, stream: int = 1) -> np.ndarray:
+    """Absorbed queries of the MLA-style latent comparator, [B, H, d_c + d_r] float32 N(0, 1), on
+    a stream of their own, [1000 + k, 1 << 23 | stream]."""
+    rng = _rng(w, (1 << 23) | stream)
+    return _normal_f32(rng, (w.B, H, d_c + d_r))
 
 
 def decode_query_positions(w: Workload, lens: np.ndarray) -> np.ndarray:
