@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-small", action="store_true", help="skip the small-batch step latencies")
     p.add_argument("--no-recon", action="store_true",
                    help="skip the non-absorbable comparator measurement")
+    p.add_argument("--no-mla", action="store_true",
+                   help="skip the MLA-style latent comparator measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -56,10 +58,10 @@ def parse():
 class DeviceCache:
     """A workload's cache on the device, filled through gva_cache_append with seeded data."""
 
-    def __init__(self, w, lens, fill_seed, torch, gb, synth):
+    def __init__(self, w, lens, fill_seed, torch, gb, synth, group_major=True):
         self.w = w
         self.lens = lens
-        self.lay = synth.layout(w, lens)
+        self.lay = synth.layout(w, lens, group_major)
         cap = synth.capacity(w, lens)
         self.max_pos = int(cap.max()) + 1
         self.dims = gb.GvaDims(w.H, w.G, w.d_h, w.d_n, w.d_r)
@@ -260,6 +262,56 @@ def main():
         del rope_r, mt_t, q_r_t, ws_r
         torch.cuda.empty_cache()
 
+    # ---------------- MLA-style latent comparator on the same lengths ----------------
+    # A latent cache of d_c = 512 (the DeepSeek-V2 latent width) plus a 64-wide shared RoPE key,
+    # 576 scalars per token against GVA's 1048, for the same 256 sequences of len_b + 1 tokens
+    # and 32 heads, decoded absorbed (the latent output before the value up-projection). The
+    # pool is filled through gva_cache_append, each latent row as two token-major groups of 256.
+    mla = None
+    if not args.no_mla:
+        d_c, d_r_m = 512, 64
+        wm = synth.workload("C4", G=d_c // 256, d_h=256, d_n=256, d_r=d_r_m)
+        dm = DeviceCache(wm, lens + 1, 4321, torch, gb, synth, group_major=False)
+        mdims = gb.GvaDims(H, 1, d_c, d_c, d_r_m)
+        q_m = torch.randn((B, H, d_c + d_r_m), generator=gen, device="cuda")
+        out_m = torch.empty((B, H, d_c), device="cuda")
+        lse_m = torch.empty((B, H), device="cuda")
+        wsb_m = gb.gva_mla_decode_workspace_bytes(mdims, B, max_len, 0)
+        ws_m = torch.empty(max(wsb_m, 256) // 4, dtype=torch.float32, device="cuda")
+        scale_m = 1.0 / float(np.sqrt(d_c + d_r_m))
+
+        def mla_call():
+            gb.gva_mla_decode(mdims, dm.cache, B, seq_len, max_len, q_m, scale_m, out_m, lse_m,
+                              workspace=ws_m, stream=stream)
+
+        for _ in range(3):
+            mla_call()
+        evm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(50)]
+        for e0, e1 in evm:
+            e0.record(stream)
+            mla_call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_m).all().item(), "non-finite latent comparator output"
+        assert int(dm.cache.err_flag.item()) == 0, "device error flag raised"
+        t_mla = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evm])) / 1e3
+        mla_bytes = int((lens + 1).sum()) * (d_c + d_r_m) * elem
+        mla = {"workload": "same 256 sequences and lengths (len_b + 1 tokens); latent d_c = 512 "
+                           "and shared RoPE key d_r = 64 per token, 32 heads, bf16 paged "
+                           "16-token blocks; absorbed queries, output before the value "
+                           "up-projection",
+               "ms": round(t_mla * 1e3, 4), "cache_bytes": mla_bytes,
+               "GB_s": round(mla_bytes / t_mla / 1e9, 1),
+               "frac_of_hbm_peak": round(mla_bytes / t_mla / 1e9 / HBM_PEAK_GBS, 4),
+               "mla_bytes_over_gva_bytes": round(mla_bytes / read_bytes, 4),
+               "mla_time_over_gva_time": round(t_mla / t_dec, 3)}
+        log(f"MLA-style latent comparator decode: {t_mla * 1e3:.3f} ms ({mla_bytes / t_mla / 1e9:.1f} "
+            f"GB/s of its {mla_bytes / 1e9:.2f} GB); {t_mla / t_dec:.2f}x the GVA decode's time "
+            f"for {mla_bytes / read_bytes:.2f}x its bytes")
+        del dm, q_m, out_m, ws_m
+        torch.cuda.empty_cache()
+
     result_extra = {}
     # ---------------- long context, one sequence ----------------
     if not args.no_long:
@@ -360,6 +412,7 @@ def main():
         "small_batch_step": small,
         "gqa_comparator": gqa,
         "recon_comparator": recon,
+        "mla_comparator": mla,
         "device": dev,
     }
     print(json.dumps(res), flush=True)
