@@ -286,8 +286,8 @@ gva_status gva_recon_decode(const gva_dims *dims, const gva_cache *values, int32
  *   dims: H in {8, 16, 32}, G = 1, d_h = d_c in {256, 512}, d_r a multiple of 8 in [8, 64]
  *   (d_n is not used).
  *   latent: a bf16 cache as for gva_decode, v holding the latents (v_stride_group is not used)
- *   and kr the rotated positional keys; strides multiples of 8 elements; its RoPE table is not
- *   read. gva_cache_append fills such a pool when each latent row is described as d_c / 256
+ *   and kr the rotated positional keys; strides multiples of 8 elements; block_size >= 16; its
+ *   RoPE table is not read. gva_cache_append fills such a pool when each latent row is described as d_c / 256
  *   groups of 256 (v_stride_group = 256).
  *   q_abs: device float32 [B][H][d_c + d_r] = [q~_h ; rotated q_rope_h], 16-byte aligned.
  *   workspace: at least gva_mla_decode_workspace_bytes(dims, B, max_len, num_splits) bytes,

@@ -333,6 +333,7 @@ def test_mla_validation(L):
     assert ml(d=_dims(H=32, G=1, d_h=256, d_r=72)) == gb.GVA_ERR_UNSUPPORTED
     assert ml(c=_cache(dtype=gb.GVA_DTYPE_F32)) == gb.GVA_ERR_UNSUPPORTED
     assert ml(c=_cache(d=d, v_stride_token=260)) == gb.GVA_ERR_INVALID_ARG       # not 8-aligned
+    assert ml(c=_cache(d=d, bs=8, max_blocks=16)) == gb.GVA_ERR_UNSUPPORTED     # blocks < 16
     assert ml(B=0) == gb.GVA_ERR_INVALID_ARG
     for k in ("sl", "q", "out"):
         assert ml(**{k: None}) == gb.GVA_ERR_INVALID_ARG, k

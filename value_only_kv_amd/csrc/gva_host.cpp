@@ -328,6 +328,8 @@ gva_status check_latent(const gva_dims *d, const gva_cache *c, int32_t B, const 
     return fail(GVA_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31)");
   if (!pow2(c->block_size) || c->block_size > (1 << 30))
     return fail(GVA_ERR_INVALID_ARG, "block_size=%d must be a power of two", c->block_size);
+  if (c->block_size < 16)
+    return fail(GVA_ERR_UNSUPPORTED, "the latent comparator needs block_size >= 16");
   if (c->max_blocks < 1) return fail(GVA_ERR_INVALID_ARG, "max_blocks must be >= 1");
   if ((int64_t)c->max_blocks * c->block_size > (int64_t)INT32_MAX)
     return fail(GVA_ERR_INVALID_ARG, "max_blocks * block_size exceeds int32 positions");

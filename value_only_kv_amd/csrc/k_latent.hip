@@ -13,7 +13,8 @@
 // Work-group: one (sequence, chunk) of the split plan, H / 8 waves of 8 heads each. Per tile of
 // 32 positions:
 //   * the natural rows [c (d_c) | kr (d_r, padded to a multiple of 32)] go straight from HBM
-//     into LDS (global_load_lds_dwordx4, double-buffered, one tile ahead): a unit of 16 keys x
+//     into LDS (global_load_lds_dwordx4, a ring of three or four buffers, two or three tiles
+//     ahead): a unit of 16 keys x
 //     32 elements is one wave instruction that writes 1 KB, lane i's 16 bytes at 16 i, which is
 //     exactly the score product's A-operand form;
 //   * scores S^T[key][col] on v_mfma_f32_16x16x32_bf16, B = the absorbed query in its 16
@@ -28,6 +29,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "gva_device.h"
 
@@ -61,6 +64,23 @@ __device__ __forceinline__ float ror8(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
 }
 __device__ __forceinline__ float max4(const f32x4 &v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+// s_waitcnt limiting only the vector-memory counter to N (its low 4 bits at [3:0], high 2 at
+// [15:14]; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt limiting only the LDS / scalar-memory counter to zero
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+// work-group barrier after this wave's own LDS reads; unlike a fenced barrier it does not wait
+// for the transfers into LDS still in flight (later tiles'), whose completion the caller orders
+// with wait_vmcnt. The clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // LDS tile: unit (kb, ks) = keys 16 kb .. + 16, elements 32 ks .. + 32 of the natural rows,
 // 1 KB in A-operand order: key n, elements 8 q .. + 8 at 16 (n + 16 q).
@@ -70,6 +90,17 @@ struct LatentTile {
   static constexpr int kUnits = 2 * kSteps;
   static constexpr int kBytes = kUnits * 1024;
 };
+// LDS buffers of the staging ring (tiles in flight + the one being read): up to four, as many as
+// 160 KB of LDS holds and as the 6-bit vector-memory counter can wait on ((bufs - 2) tiles of
+// transfers outstanding while the next is awaited), at least three
+template <int KS, int RS, int NW>
+constexpr int latent_bufs() {
+  constexpr int units = LatentTile<KS, RS>::kUnits, bytes = LatentTile<KS, RS>::kBytes;
+  constexpr int per = (units + NW - 1) / NW;
+  int n = 4;
+  while (n > 3 && (n * bytes > 160 * 1024 - 1024 || (n - 2) * per > 63)) --n;
+  return n;
+}
 __device__ __forceinline__ int unit_off(int kb, int ks, int steps) { return (kb * steps + ks) * 1024; }
 
 template <int KS, int RS, int NW>
@@ -77,14 +108,33 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
   using L = LatentTile<KS, RS>;
   constexpr int kSteps = L::kSteps;
   constexpr int kPer = (L::kUnits + NW - 1) / NW;    // units each wave stages per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][L::kBytes];
+  constexpr int kBufs = latent_bufs<KS, RS, NW>();
+  constexpr int kDepth = kBufs - 1;                  // tiles staged ahead of the one read
+  static_assert(kBufs >= 3 && kBufs <= 4 && kBufs * L::kBytes <= 160 * 1024 - 1024 &&
+                (kDepth - 1) * kPer < 64, "ring");
+  // one array per buffer: distinct objects, so that the compiler can tell a tile's LDS reads
+  // from the transfers into the other buffers
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[L::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[L::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[L::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[kBufs > 3 ? L::kBytes : 1024];
+  auto ring = [&](auto I) __attribute__((always_inline)) -> uint8_t * {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return lds0;
+    else if constexpr (i == 1) return lds1;
+    else if constexpr (i == 2) return lds2;
+    else return lds3;
+  };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int q = lane >> 4;
   const int S = a.num_splits;
-  const int s = blockIdx.x % S;
-  const int b = blockIdx.x / S;
+  // sequence-fastest numbering: work-groups go to the eight XCDs in turn, so a chunk-major grid
+  // would put every sequence's chunk s on XCD s % 8 (and all the first chunks on one XCD); this
+  // way each XCD holds all the chunks of every eighth sequence
+  const int b = blockIdx.x % a.B;
+  const int s = blockIdx.x / a.B;
   const int d_c = a.d_h;
   const int len = a.seq_len[b];
   const int cap = a.max_blocks << a.log2_bs;
@@ -116,49 +166,63 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
 
   // absorbed query, B-operand form: column n holds head hcol, elements 32 ks + 8 q .. + 8, as
   // the bf16 hi part (n < 8) or lo part (n >= 8); positional padding is zero
+  // (all of the row's loads are issued before any conversion; the lo part subtracts the hi
+  // part's value, zero on the hi columns, so that no lane takes a branch)
   u32x4 Q[kSteps];
   {
     const float *qp = a.q_abs + orow * (d_c + a.d_r);
+    float x[kSteps][8];
 #pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
+    for (int ks = 0; ks < kSteps; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (ks < KS) {
+          x[ks][i] = qp[32 * ks + 8 * q + i];
+        } else {
+          const int e = 32 * (ks - KS) + 8 * q + i;
+          const float v = qp[d_c + min(e, a.d_r - 1)];
+          x[ks][i] = e < a.d_r ? v : 0.0f;
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x0, x1;
-        if (ks < KS) {
-          x0 = qp[32 * ks + 8 * q + 2 * i];
-          x1 = qp[32 * ks + 8 * q + 2 * i + 1];
-        } else {
-          const int e = 32 * (ks - KS) + 8 * q + 2 * i;
-          x0 = e < a.d_r ? qp[d_c + e] : 0.0f;
-          x1 = e + 1 < a.d_r ? qp[d_c + e + 1] : 0.0f;
-        }
-        x0 *= a.qscale;
-        x1 *= a.qscale;
+        const float x0 = x[ks][2 * i] * a.qscale;
+        const float x1 = x[ks][2 * i + 1] * a.qscale;
         const unsigned w = pack2(x0, x1);
-        Q[ks][i] = lo_col ? pack2(x0 - low_bf16(w), x1 - high_bf16(w)) : w;
+        const float r0 = lo_col ? low_bf16(w) : 0.0f;
+        const float r1 = lo_col ? high_bf16(w) : 0.0f;
+        Q[ks][i] = pack2(x0 - r0, x1 - r1);
       }
-    }
   }
 
   // staging: wave w loads units w, w + NW, ... of a tile (keys past the chunk repeat its last
-  // key; waves past the last unit load it again: the same bytes to the same place). The
-  // block-table entries of a tile's two key blocks are loaded one tile ahead of its staging.
-  const int32_t *bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  // key; waves past the last unit load it again: the same bytes to the same place). Blocks hold
+  // at least 16 positions and tiles start at multiples of 16, so each of a tile's two 16-key
+  // blocks lies in one page (a clamped key stays in its block's page): the entries are uniform,
+  // loaded two tiles ahead of their staging into one of kBufs register sets.
+  // (read through the constant address space: the table does not change during the call, and
+  // its uniform loads become scalar ones, which leave the vector-memory counter to the staging)
+  typedef __attribute__((address_space(4))) const int32_t cint32;
+  cint32 *bt = (cint32 *)(a.block_table + static_cast<int64_t>(b) * a.max_blocks);
   const int pos_mask = (1 << a.log2_bs) - 1;
   bool bad = false;
-  int32_t pg[2];
-  auto pages = [&](int j0) __attribute__((always_inline)) {
+  int32_t pgs[kBufs][2];
+  auto pages = [&](int32_t (&pg)[2], int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) pg[kb] = bt[min(j0 + 16 * kb + n, c1 - 1) >> a.log2_bs];
+    for (int kb = 0; kb < 2; ++kb) pg[kb] = bt[min(j0 + 16 * kb, c1 - 1) >> a.log2_bs];
   };
-  auto stage = [&](int buf, int j0) __attribute__((always_inline)) {
-#pragma unroll
+  // (a single wave stages the whole tile: its address arithmetic is unrolled in part only)
+  constexpr int kStageUnroll = kPer <= 12 ? kPer : 6;
+  auto stage = [&](uint8_t *buf, int32_t pg0, int32_t pg1, int j0) __attribute__((always_inline)) {
+#pragma unroll kStageUnroll
     for (int i = 0; i < kPer; ++i) {
       const int unit = min(wave + NW * i, L::kUnits - 1);
       const int kb = unit / kSteps;
       const int ks = unit - kb * kSteps;
       const int j = min(j0 + 16 * kb + n, c1 - 1);
-      const int32_t blk = pg[kb];
+      const int32_t blk = kb ? pg1 : pg0;
       const bool ok = blk >= 0 && static_cast<int64_t>(blk) < a.num_blocks;
       bad = bad || !ok;
       const int64_t bb = ok ? static_cast<int64_t>(blk) : 0;
@@ -171,8 +235,8 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
         const int e = min(32 * (ks - KS) + 8 * q, a.d_r - 8);
         src = static_cast<const uint16_t *>(a.kr) + bb * a.kr_sb + row * a.kr_st + e;
       }
-      __builtin_amdgcn_global_load_lds((glb_void *)src,
-                                       (lds_void *)(&lds[buf][unit_off(kb, ks, kSteps)]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(buf + unit_off(kb, ks, kSteps)),
+                                       16, 0, 0);
     }
   };
 
@@ -185,18 +249,19 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
   for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mref = -INFINITY, lsum = 0.0f;
 
-  auto tile = [&](int buf, int j0) __attribute__((always_inline)) {
-    const uint8_t *base = lds[buf];
+  auto tile = [&](const uint8_t *base, int j0) __attribute__((always_inline)) {
     const float negm = (mref == -INFINITY || lo_col) ? 0.0f : -mref;
     f32x4 Sc[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       Sc[tb] = f32x4{negm, negm, negm, negm};
+      // all of a key block's A operands are read before its products, so one wait covers them
+      u32x4 ka[kSteps];
 #pragma unroll
-      for (int ks = 0; ks < kSteps; ++ks) {
-        const u32x4 ka = *reinterpret_cast<const u32x4 *>(base + unit_off(tb, ks, kSteps) + 16 * lane);
-        Sc[tb] = mfma(ka, Q[ks], Sc[tb]);
-      }
+      for (int ks = 0; ks < kSteps; ++ks)
+        ka[ks] = *reinterpret_cast<const u32x4 *>(base + unit_off(tb, ks, kSteps) + 16 * lane);
+#pragma unroll
+      for (int ks = 0; ks < kSteps; ++ks) Sc[tb] = mfma(ka[ks], Q[ks], Sc[tb]);
       // hi + lo columns: every lane of the row pair (n, n + 8) holds head hcol's score
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -230,39 +295,90 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const unsigned w = pack2(pv[2 * i], pv[2 * i + 1]);
-      PB[i] = lo_col ? pack2(pv[2 * i] - low_bf16(w), pv[2 * i + 1] - high_bf16(w)) : w;
+      const float r0 = lo_col ? low_bf16(w) : 0.0f;
+      const float r1 = lo_col ? high_bf16(w) : 0.0f;
+      PB[i] = pack2(pv[2 * i] - r0, pv[2 * i + 1] - r1);
     }
     // O^T[dim][col] += C^T[dim][key] P^T[key][col]; dims 16 nb .. belong to unit step nb / 2,
     // pieces 2 (nb % 2) and + 1; the first read gives keys 4 q .. + 3 of block 0, the second the
     // same of block 1 (the order the lane holds its probabilities in)
+    // (in groups of eight 16-dim blocks: their transposing reads first, then their products)
+    constexpr int kGroup = 8;
+    static_assert((2 * KS) % kGroup == 0, "whole groups of 16-dim blocks");
 #pragma unroll
-    for (int nb = 0; nb < 2 * KS; ++nb) {
-      const int piece = 2 * (nb & 1) + (tr_k >> 1);
-      const int off = 16 * (tr_key + 16 * piece) + 8 * (tr_k & 1);
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4 *)(base + unit_off(0, nb >> 1, kSteps) + off));
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4 *)(base + unit_off(1, nb >> 1, kSteps) + off));
-      const bf16x8 VT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VT, __builtin_bit_cast(bf16x8, PB), O[nb], 0, 0, 0);
+    for (int g0 = 0; g0 < 2 * KS; g0 += kGroup) {
+      i16x4 v0[kGroup], v1[kGroup];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const int nb = g0 + i;
+        const int piece = 2 * (nb & 1) + (tr_k >> 1);
+        const int off = 16 * (tr_key + 16 * piece) + 8 * (tr_k & 1);
+        v0[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(base + unit_off(0, nb >> 1, kSteps) + off));
+        v1[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(base + unit_off(1, nb >> 1, kSteps) + off));
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const bf16x8 VT = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(v0[i], v1[i], 0, 1, 2, 3, 4, 5, 6, 7));
+        O[g0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VT, __builtin_bit_cast(bf16x8, PB),
+                                                            O[g0 + i], 0, 0, 0);
+      }
     }
   };
 
+  // Ring of kBufs buffers, kDepth tiles in flight: step t loads the entries of tile t + kDepth + 2,
+  // stages tile t + kDepth into the buffer tile t - 1 was read from (every wave passed the
+  // barrier after it), reads tile t, then waits for tile t + 1. Tiles past the chunk's end are
+  // staged too (their keys repeat the last one), so every step issues the same transfers and
+  // the wait is a fixed count: each step issues at least kPer vector-memory operations, so at
+  // most (kDepth - 1) kPer may follow tile t + 1's. The buffer and entry-set indices are
+  // compile-time constants of the unrolled ring, which lets the compiler see that a tile's LDS
+  // reads do not overlap the transfers in flight.
   const int ntiles = (c1 - c0 + kTile - 1) / kTile;
-  pages(c0);
-  stage(0, c0);
-  pages(c0 + kTile);                                   // (repeats the last key past the end)
-  __builtin_amdgcn_s_waitcnt(0);                       // the tile's units are in LDS
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    // uniform per work-group: stage tile t + 1 with the entries loaded one tile ago, then load
-    // the entries of tile t + 2
-    if (t + 1 < ntiles) stage((t + 1) & 1, c0 + (t + 1) * kTile);
-    if (t + 2 < ntiles) pages(c0 + (t + 2) * kTile);
-    tile(t & 1, c0 + t * kTile);
-    __builtin_amdgcn_s_waitcnt(0);                     // the next tile's units are in LDS
-    __syncthreads();
+  using std::integral_constant;
+  auto prime = [&](auto U) __attribute__((always_inline)) {      // U < kDepth
+    constexpr int u = decltype(U)::value;
+    pages(pgs[(u + 2) % kBufs], c0 + (u + 2) * kTile);
+    stage(ring(U), pgs[u][0], pgs[u][1], c0 + u * kTile);
+  };
+  auto step = [&](auto U, int t) __attribute__((always_inline)) {  // t % kBufs == U
+    constexpr int u = decltype(U)::value;
+    constexpr int sb = (u + kDepth) % kBufs;
+    pages(pgs[(u + kDepth + 2) % kBufs], c0 + (t + kDepth + 2) * kTile);
+    stage(ring(integral_constant<int, sb>{}), pgs[sb][0], pgs[sb][1], c0 + (t + kDepth) * kTile);
+    wait_lgkm0();                                      // the entries, before the tile's LDS reads
+    tile(ring(U), c0 + t * kTile);
+    wait_vmcnt<(kDepth - 1) * kPer>();                 // tile t + 1's units are in LDS
+    ring_barrier();
+  };
+  pages(pgs[0], c0);
+  pages(pgs[1], c0 + kTile);
+  prime(integral_constant<int, 0>{});
+  prime(integral_constant<int, 1>{});
+  if constexpr (kDepth > 2) prime(integral_constant<int, 2>{});
+  wait_vmcnt<(kDepth - 1) * kPer>();                   // tile 0's units are in LDS
+  ring_barrier();
+  // whole turns of the ring, then the last ntiles % kBufs tiles (a loop without early exits:
+  // the compiler then keeps track of which buffer each transfer in flight writes)
+  int t0 = 0;
+  for (; t0 + kBufs <= ntiles; t0 += kBufs) {          // uniform per work-group
+    step(integral_constant<int, 0>{}, t0);
+    step(integral_constant<int, 1>{}, t0 + 1);
+    step(integral_constant<int, 2>{}, t0 + 2);
+    if constexpr (kBufs > 3) step(integral_constant<int, 3>{}, t0 + 3);
   }
+  if (t0 < ntiles) {
+    step(integral_constant<int, 0>{}, t0);
+    if (t0 + 1 < ntiles) {
+      step(integral_constant<int, 1>{}, t0 + 1);
+      if constexpr (kBufs > 3) {
+        if (t0 + 2 < ntiles) step(integral_constant<int, 2>{}, t0 + 2);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);                       // no transfer into LDS outlives the loop
   __shared__ int bad_lds;
   if (threadIdx.x == 0) bad_lds = 0;
   __syncthreads();
