@@ -32,7 +32,13 @@ HIPCC_FLAGS = [
 # Per-source additions. The comparator kernel keeps its matrix-core accumulators in ordinary
 # vector registers: its vector-ALU code reads every product, and the compiler's default (the
 # accumulation registers) adds a copy per value.
-HIP_FILE_FLAGS = {"k_recon.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+HIP_FILE_FLAGS = {"k_recon.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                  "k_latent.hip": ["-Rpass-analysis=kernel-resource-usage"]}
+# Sources whose kernels must not use scratch memory: the latent comparator's staging ring waits
+# for a fixed count of vector-memory operations, which holds only while its loop issues no
+# vector-memory stores (register spills would be such stores). The build reads the compiler's
+# resource report and fails when a kernel of these sources has a scratch size.
+NO_SCRATCH = {"k_latent.hip"}
 GXX_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",
              "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include"),
              "-I" + os.path.join(ROOT, "include")]
@@ -54,6 +60,18 @@ def _run(cmd):
     return out
 
 
+def scratch_users(report: str) -> list:
+    """Kernels with a nonzero scratch size in a -Rpass-analysis=kernel-resource-usage report."""
+    bad, name = [], None
+    for line in report.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line:
+            if int(line.split("ScratchSize [bytes/lane]:")[1].split()[0]) != 0:
+                bad.append(name)
+    return bad
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compiles every source and links libgva.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -70,8 +88,14 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
                      os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2) // 2), 8)
+    srcs = HOST_SOURCES + HIP_SOURCES
     with cf.ThreadPoolExecutor(jobs) as ex:
-        for out in ex.map(_run, cmds):
+        for src, out in zip(srcs, ex.map(_run, cmds)):
+            if src in NO_SCRATCH:
+                bad = scratch_users(out)
+                if bad:
+                    raise RuntimeError(f"{src}: kernels use scratch memory: {bad}")
+                out = ""
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
