@@ -57,6 +57,8 @@ SHAPES = [
     dict(H=16, d_c=256, d_r=32),
     dict(H=8, d_c=256, d_r=16),       # a positional key narrower than its 32-element step
     dict(H=32, d_c=256, d_r=64),
+    dict(H=8, d_c=512, d_r=64),       # one wave stages the whole tile: the three-buffer ring
+    dict(H=16, d_c=512, d_r=24),      # two waves; a positional key of 24 in one 32-element step
 ]
 
 
