@@ -179,3 +179,84 @@ def test_recon_comparator_full_size(ragged):
         check_output(out[b], ref, "bf16", f"comparator ragged batch seq {b} len {V.shape[0]}")
         ok, e = lse_ok(lse[b], ref_lse, 1e-3)
         assert ok, (b, e)
+
+
+@pytest.fixture(scope="module")
+def ragged_latent():
+    """The ragged batch's lengths (len_b + 1 tokens, as the bench decodes) in an MLA-style latent
+    pool: d_c = 512 described as two token-major groups of 256, a 64-wide positional key, 32
+    heads. Sampled sequences carry their seeded tokens, the others device random values."""
+    w = synth.workload("C4", G=2, d_h=256, d_n=256, d_r=64)
+    lens = synth.lengths(w) + 1
+    lay = synth.layout(w, lens, group_major=False)
+    B, G, d_h, d_r, H = w.B, w.G, w.d_h, w.d_r, w.H
+    cdims = gb.GvaDims(H, G, d_h, w.d_n, d_r)
+    max_pos = int(synth.capacity(w, lens).max()) + 1
+    tab_lib = torch.from_numpy(gb.gva_rope_table_fill(max_pos, d_r, w.base)).cuda()
+    cache = gb.GvaCache.allocate(cdims, w.dtype, lay.num_blocks, lay.block_size,
+                                 torch.from_numpy(lay.block_table).cuda(), tab_lib,
+                                 (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st))
+    rng = np.random.default_rng(29)
+    sampled = sorted({int(np.argmax(lens)), int(np.argmin(lens)),
+                      int(rng.choice(B))})
+    print(f"latent pool: sampled sequences {sampled}, lengths {[int(lens[b]) for b in sampled]}",
+          flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    others = [b for b in range(B) if b not in sampled]
+    seqs = np.repeat(np.asarray(others, np.int32), lens[others])
+    poss = np.concatenate([np.arange(lens[b], dtype=np.int32) for b in others])
+    for o in range(0, seqs.size, 1 << 16):
+        n = min(1 << 16, seqs.size - o)
+        gb.gva_cache_append(cdims, cache, B, torch.from_numpy(seqs[o:o + n]).cuda(),
+                            torch.from_numpy(poss[o:o + n]).cuda(),
+                            torch.randn((n, G, d_h), generator=gen, device="cuda"),
+                            torch.randn((n, d_r), generator=gen, device="cuda"))
+    toks = {}
+    for b in sampled:
+        n = int(lens[b])
+        v, kr = synth.sequence_tokens(w, b, n)
+        toks[b] = (v, kr)
+        gb.gva_cache_append(cdims, cache, B, torch.full((n,), b, dtype=torch.int32).cuda(),
+                            torch.arange(n, dtype=torch.int32).cuda(),
+                            torch.from_numpy(v).cuda(), torch.from_numpy(kr).cuda())
+    torch.cuda.synchronize()
+    return dict(w=w, lens=lens, cdims=cdims, dims=O.Dims(H, G, d_h, w.d_n, d_r), cache=cache,
+                sampled=sampled, toks=toks)
+
+
+def test_mla_comparator_full_size(ragged_latent):
+    """The MLA-style latent comparator in the bench's configuration (the ragged batch's lengths,
+    d_c = 512, d_r = 64, 32 heads, automatic split count): the longest, the shortest and one more
+    sampled sequence against the oracle's absorbed one-group decode."""
+    r = ragged_latent
+    w, cache, lens, dims = r["w"], r["cache"], r["lens"], r["dims"]
+    B, H, d_c, d_r = w.B, w.H, w.G * w.d_h, w.d_r
+    mdims = gb.GvaDims(H, 1, d_c, d_c, d_r)
+    odims = O.Dims(H, 1, d_c, d_c, d_r)
+    q = synth.mla_queries(w, H, d_c, d_r)
+    scale = 1.0 / float(np.sqrt(d_c + d_r))
+    max_len = int(lens.max())
+    out = torch.full((B, H, d_c), float("nan"), device="cuda")
+    lse = torch.full((B, H), float("nan"), device="cuda")
+    wsb = gb.gva_mla_decode_workspace_bytes(mdims, B, max_len, 0)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    gb.gva_mla_decode(mdims, cache, B, torch.from_numpy(lens.astype(np.int32)).cuda(), max_len,
+                      torch.from_numpy(q).cuda(), scale, out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(cache.err_flag.item()) == 0
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b in r["sampled"]:
+        n = int(lens[b])
+        v, kr = r["toks"][b]
+        tab_ora = O.rope_rows(np.arange(n), d_r, w.base)
+        pool = O.Pool.empty("bf16", n * w.G * w.d_h, n * d_r,
+                            (n * w.G * w.d_h, w.G * w.d_h, w.d_h, n * d_r, d_r),
+                            1, 1 << int(np.ceil(np.log2(n))), np.zeros((1, 1)))
+        O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr, tab_ora)
+        V, K = O.gather(pool, dims, 0, n)
+        ref, ref_lse = O.decode_sequence(V.reshape(n, 1, d_c), K, odims, q[b], scale)
+        check_output(out[b], ref, "bf16", f"latent comparator ragged batch seq {b} len {n}")
+        ok, e = lse_ok(lse[b], ref_lse, 1e-3)
+        assert ok, (b, e)
