@@ -58,3 +58,27 @@ def test_committed_traffic_profile_is_well_formed():
             kv[k] = int(v)
     assert set(kv) == {"traffic_bytes_per_call", "algorithmic_bytes_per_call"}
     assert 1.0 <= kv["traffic_bytes_per_call"] / kv["algorithmic_bytes_per_call"] < 1.5
+
+
+def test_counters_clock_and_matrix_core_busy(tmp_path):
+    """Per-dispatch means, the clock from the 8 XCDs' summed GRBM_GUI_ACTIVE and the matrix-core
+    busy share of an average SIMD, for the selected kernel and grid only."""
+    p = tmp_path / "pmc.csv"
+    cols = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value",
+            "Start_Timestamp", "End_Timestamp"]
+    # two dispatches of 10 us; 8 XCDs x 20000 cycles = 2.0 GHz; matrix cores busy 1024 x 5000
+    rows = []
+    for d in (1, 2):
+        rows += [[d, "void (anonymous namespace)::k_prefill<4>(gva::PrefillArgs)", 131072,
+                  "GRBM_GUI_ACTIVE", 8 * 20000.0, 0, 10000],
+                 [d, "void (anonymous namespace)::k_prefill<4>(gva::PrefillArgs)", 131072,
+                  "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 5000.0 * d, 0, 10000]]
+    rows += [[3, "void (anonymous namespace)::k_prefill<4>(gva::PrefillArgs)", 64,
+              "GRBM_GUI_ACTIVE", 1.0, 0, 10]]
+    _write(p, cols, rows)
+    text = ps.counters(str(p), ["k_prefill<4>:131072"], "cmd")
+    line = [l for l in text.splitlines() if l.startswith("| `k_prefill<4>`")]
+    assert len(line) == 1
+    cells = [c.strip() for c in line[0].strip("|").split("|")]
+    assert cells[1:4] == ["131072", "2", "10.00"]
+    assert cells[-2:] == ["2.00", "0.375"]                  # mean busy 7500 of 20000 cycles

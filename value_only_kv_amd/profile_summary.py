@@ -10,12 +10,19 @@ Two reports:
            the same run (the largest ``__amd_rocclr_copyBuffer`` dispatch), so the factor
            is measured, not assumed.
 
+  counters per-dispatch means of the counters of one ``--pmc`` run for selected kernels, with
+           the clock (GRBM_GUI_ACTIVE counts every XCD's cycles) and, when
+           SQ_VALU_MFMA_BUSY_CYCLES is among them, the fraction of the kernel's cycles the
+           matrix cores of an average SIMD were busy (the counter sums all SIMDs' busy cycles).
+
 The traffic report ends with machine-readable lines (``key: value``) that bench.py reads; the
 ``sources_sha256`` line ties the counters to the kernel sources they were taken with.
 
     python -m value_only_kv_amd.profile_summary stats TRACE_CSV --cmd "..." -o OUT.md
     python -m value_only_kv_amd.profile_summary traffic FETCH_CSV WRITE_CSV --copy-bytes N \
         --select NAME:GRID [--select NAME:GRID ...] --algorithmic-bytes B --cmd "..." -o OUT.md
+    python -m value_only_kv_amd.profile_summary counters PMC_CSV --select NAME:GRID [...] \
+        --cmd "..." -o OUT.md
 """
 from __future__ import annotations
 
@@ -115,6 +122,54 @@ def traffic(fetch_csv: str, write_csv: str, copy_bytes: int, selects, algorithmi
     return "\n".join(lines) + "\n"
 
 
+MI355X_XCDS = 8
+MI355X_SIMDS = 256 * 4
+
+
+def counters(pmc_csv: str, selects, cmd: str, note: str = "") -> str:
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(dict)
+    names = []
+    for r in csv.DictReader(open(pmc_csv)):
+        key = (r["Kernel_Name"], int(r["Grid_Size"]))
+        vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        durs[key][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if r["Counter_Name"] not in names:
+            names.append(r["Counter_Name"])
+    lines = ["# rocprofv3 counters per dispatch", "", "Command:", "", "```", cmd, "```", "",
+             *([note, ""] if note else []),
+             "Means per dispatch. GRBM_GUI_ACTIVE sums the cycles of the 8 XCDs, so the clock is "
+             "GRBM_GUI_ACTIVE / 8 / duration. Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(1024 SIMDs x GRBM_GUI_ACTIVE / 8): the share of the kernel's cycles an average "
+             "SIMD's matrix core was busy.", "",
+             "| kernel | grid | dispatches | avg us | " + " | ".join(names) +
+             " | clock GHz | matrix-core busy |",
+             "|---|---|---|---|" + "---|" * len(names) + "---|---|"]
+    for sel in selects:
+        name, grid = sel.rsplit(":", 1)
+        grid = int(grid)
+        keys = [k for k in vals if name in k[0] and k[1] == grid]
+        if not keys:
+            raise SystemExit(f"no dispatch of {name} with grid {grid}")
+        agg = collections.defaultdict(list)
+        ds = []
+        for k in keys:
+            for c, v in vals[k].items():
+                agg[c] += v
+            ds += list(durs[k].values())
+        mean = {c: sum(v) / len(v) for c, v in agg.items()}
+        dur_ns = sum(ds) / len(ds)
+        grbm = mean.get("GRBM_GUI_ACTIVE")
+        clock = f"{grbm / MI355X_XCDS / dur_ns:.2f}" if grbm else "-"
+        busy = "-"
+        if grbm and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            busy = f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (MI355X_SIMDS * grbm / MI355X_XCDS):.3f}"
+        cells = " | ".join(f"{mean[c]:.4g}" if c in mean else "-" for c in names)
+        lines.append(f"| `{_short(keys[0][0])}` | {grid} | {len(ds)} | {dur_ns / 1e3:.2f} | "
+                     f"{cells} | {clock} | {busy} |")
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(md_path: str, algorithmic: int):
     """Returns the stored traffic (bytes per call) if the decode sources and the workload's
     algorithmic bytes still match the ones the counters were taken with, else None."""
@@ -149,9 +204,17 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--note", default="")
     t.add_argument("-o", "--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_csv")
+    c.add_argument("--select", action="append", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--note", default="")
+    c.add_argument("-o", "--out", required=True)
     a = p.parse_args()
     if a.what == "stats":
         text = stats(a.trace_csv, a.cmd, a.note)
+    elif a.what == "counters":
+        text = counters(a.pmc_csv, a.select, a.cmd, a.note)
     else:
         text = traffic(a.fetch_csv, a.write_csv, a.copy_bytes, a.select, a.algorithmic_bytes,
                        a.cmd, a.note)
