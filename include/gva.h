@@ -290,8 +290,10 @@ gva_status gva_recon_decode(const gva_dims *dims, const gva_cache *values, int32
  *   RoPE table is not read. gva_cache_append fills such a pool when each latent row is described as d_c / 256
  *   groups of 256 (v_stride_group = 256).
  *   q_abs: device float32 [B][H][d_c + d_r] = [q~_h ; rotated q_rope_h], 16-byte aligned.
- *   workspace: at least gva_mla_decode_workspace_bytes(dims, B, max_len, num_splits) bytes,
- *   256-byte aligned (none when that is 0); num_splits as for gva_recon_decode.
+ *   workspace: device, at least gva_mla_decode_workspace_bytes(dims, B, max_len, num_splits)
+ *   bytes (never 0: besides the split partials it holds the counter of the work queue the
+ *   call's work-groups take their items from, reset by the call itself), 256-byte aligned;
+ *   calls that overlap must not share one. num_splits as for gva_recon_decode.
  *   out: device float32 [B][H][d_c], 16-byte aligned; lse: device float32 [B][H] or NULL.
  * Device-detected errors: a bad block-table entry (BLOCK), seq_len[b] negative or above max_len
  * (LENGTH) or above the table's capacity (CAPACITY), each giving a NaN output row. */

@@ -349,4 +349,7 @@ def test_mla_validation(L):
     assert ml(d=d512, c=_cache(d=d, v_stride_token=512, v_stride_block=16 * 512)) == gb.GVA_ERR_WORKSPACE
     assert ml(d=d512, c=_cache(d=d, v_stride_token=512, v_stride_block=16 * 512),
               ws=A + 64, wsb=wsb) == gb.GVA_ERR_WORKSPACE
-    assert gb.gva_mla_decode_workspace_bytes(d512, 256, 100, 0) == 0
+    # one chunk per sequence: no partials, only the work queue's counter
+    assert gb.gva_mla_decode_workspace_bytes(d512, 256, 100, 0) == 256
+    assert ml(d=d512, c=_cache(d=d, v_stride_token=512, v_stride_block=16 * 512),
+              B=256, ml=100) == gb.GVA_ERR_WORKSPACE

@@ -228,12 +228,13 @@ gva_status gva_mla_decode(const gva_dims *dims, const gva_cache *latent, int32_t
   a.chunk = plan.chunk;
   a.out = out;
   a.lse = lse;
+  char *ws = static_cast<char *>(workspace);
   if (plan.num_splits > 1) {
-    char *ws = static_cast<char *>(workspace);
     a.part_o = reinterpret_cast<float *>(ws + plan.off_o);
     a.part_m = reinterpret_cast<float *>(ws + plan.off_m);
     a.part_l = reinterpret_cast<float *>(ws + plan.off_l);
   }
+  a.work_next = reinterpret_cast<int32_t *>(ws + plan.off_queue);
   hipError_t e = gva::launch_latent_decode(a, stream);
   if (e != hipSuccess) return hip_status(e, "latent comparator decode launch");
   if (plan.num_splits > 1) {

@@ -307,6 +307,11 @@ gva_status check_recon(const gva_dims *d, const gva_cache *c, int32_t B, const i
   return GVA_OK;
 }
 
+void add_latent_queue(DecodePlan *plan) {
+  plan->off_queue = round_up(plan->ws_bytes, 256);
+  plan->ws_bytes = plan->off_queue + 256;
+}
+
 gva_status check_latent(const gva_dims *d, const gva_cache *c, int32_t B, const int32_t *seq_len,
                         int32_t max_len, const float *q_abs, float scale, int32_t num_splits,
                         const void *workspace, size_t workspace_bytes, const float *out,
@@ -352,12 +357,11 @@ gva_status check_latent(const gva_dims *d, const gva_cache *c, int32_t B, const 
     return fail(GVA_ERR_INVALID_ARG, "num_splits=%d outside [0, %d]", num_splits, kMaxSplits);
   if (!plan_decode(d, B, max_len, num_splits, false, plan))
     return fail(GVA_ERR_INVALID_ARG, "cannot plan the decode split");
-  if (plan->ws_bytes > 0) {
-    if (!workspace || workspace_bytes < plan->ws_bytes)
-      return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan->ws_bytes,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 256)) return fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  }
+  add_latent_queue(plan);
+  if (!workspace || workspace_bytes < plan->ws_bytes)
+    return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan->ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   return GVA_OK;
 }
 
@@ -442,6 +446,7 @@ size_t gva_mla_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t m
   if (!dims || dims->G != 1 || dims->H < 1) return 0;
   gva::DecodePlan p;
   if (!gva::plan_decode(dims, B, max_len, num_splits, false, &p)) return 0;
+  gva::add_latent_queue(&p);
   return p.ws_bytes;
 }
 

@@ -79,7 +79,11 @@ struct DecodePlan {
   size_t off_l;
   size_t off_o;
   size_t off_prefix;    // balanced mode: the per-sequence tile prefix, int32 [B + 1]
+  size_t off_queue;     // latent comparator: its work queue's counter (256 bytes at the end)
 };
+// The latent comparator's workspace: the split plan's partials, then one 256-byte word for the
+// counter of its work queue (so it is never empty).
+void add_latent_queue(DecodePlan *plan);
 
 // Plans the split of positions [0, max_len) into chunks (balanced == false), or the cut of all
 // sequences' 32-position tiles into equal ranges (balanced == true, the matrix-core kernel's
@@ -149,6 +153,7 @@ struct DecodeArgs {
   float *part_o;        // same rows as part_m, [d_h] each
   float *out;           // [B][H][d_h]
   float *lse;           // [B][H] or nullptr
+  int32_t *work_next;   // latent comparator: the work queue's counter (zeroed before the launch)
 };
 
 hipError_t launch_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,

@@ -125,22 +125,35 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
     else if constexpr (i == 2) return lds2;
     else return lds3;
   };
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;
-  const int q = lane >> 4;
   const int S = a.num_splits;
-  // sequence-fastest numbering: work-groups go to the eight XCDs in turn, so a chunk-major grid
-  // would put every sequence's chunk s on XCD s % 8 (and all the first chunks on one XCD); this
-  // way each XCD holds all the chunks of every eighth sequence
-  const int b = blockIdx.x % a.B;
-  const int s = blockIdx.x / a.B;
   const int d_c = a.d_h;
-  const int len = a.seq_len[b];
   const int cap = a.max_blocks << a.log2_bs;
   const float qnan = __int_as_float(0x7fc00000);
+  // Work queue: the resident work-groups take (sequence, chunk) items from a counter, chunk by
+  // chunk (every sequence's first chunk, then every second one, ...), so the work spreads over
+  // all CUs whatever the lengths, and the short last chunks come last. No work-group waits for
+  // another: each leaves when the queue is empty.
+  const int items = a.B * S;
+  __shared__ int s_item;
+  for (;;) {
+  if (threadIdx.x == 0) s_item = atomicAdd(a.work_next, 1);
+  __syncthreads();
+  const int item = s_item;
+  __syncthreads();
+  if (item >= items) break;                            // uniform per work-group
+  // (the lane's indices are derived anew for every item from a value the compiler cannot see
+  // through, so that nothing lane-dependent is kept live across the items)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
   const int hcol = 8 * wave + (n & 7);                // the head of this lane's column
   const bool lo_col = n >= 8;
+  const int b = item % a.B;
+  const int s = item / a.B;
+  const int len = a.seq_len[b];
   const int64_t orow = static_cast<int64_t>(b) * a.H + hcol;
   const int64_t prow = (static_cast<int64_t>(b) * S + s) * a.H + hcol;
   const int c0 = s * a.chunk;
@@ -153,14 +166,14 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
       for (int d = 4 * q; d < d_c; d += 16) *reinterpret_cast<f32x4 *>(a.out + orow * d_c + d) = f32x4{qnan, qnan, qnan, qnan};
       if (a.lse && q == 0) a.lse[orow] = qnan;
     }
-    return;                                            // S > 1: the combine checks the length
+    continue;                                          // S > 1: the combine checks the length
   }
   if (c0 >= len) {                                     // uniform per work-group
     if (S == 1 && !lo_col) {                           // len == 0
       for (int d = 4 * q; d < d_c; d += 16) *reinterpret_cast<f32x4 *>(a.out + orow * d_c + d) = f32x4{0.f, 0.f, 0.f, 0.f};
       if (a.lse && q == 0) a.lse[orow] = -INFINITY;
     }
-    return;                                            // past the end: the combine skips it
+    continue;                                          // past the end: the combine skips it
   }
   const int c1 = min(len, c0 + a.chunk);
 
@@ -398,24 +411,39 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
   for (int nb = 0; nb < 2 * KS; ++nb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) O[nb][e] += ror8(O[nb][e]);
-  if (lo_col) return;
-  const float inv = 1.0f / lt;
-  float *dst = S == 1 ? a.out + orow * d_c : a.part_o + prow * d_c;
+  if (!lo_col) {
+    const float inv = 1.0f / lt;
+    float *dst = S == 1 ? a.out + orow * d_c : a.part_o + prow * d_c;
 #pragma unroll
-  for (int nb = 0; nb < 2 * KS; ++nb) {
-    f32x4 v = O[nb];
-    if (S == 1) v *= inv;
-    if (poisoned) v = f32x4{qnan, qnan, qnan, qnan};
-    *reinterpret_cast<f32x4 *>(dst + 16 * nb + 4 * q) = v;
-  }
-  if (q == 0) {
-    if (S == 1) {
-      if (a.lse) a.lse[orow] = poisoned ? qnan : (mref + log2f(lt)) * gvad::kLn2;
-    } else {
-      a.part_m[prow] = poisoned ? qnan : mref;
-      a.part_l[prow] = lt;
+    for (int nb = 0; nb < 2 * KS; ++nb) {
+      f32x4 v = O[nb];
+      if (S == 1) v *= inv;
+      if (poisoned) v = f32x4{qnan, qnan, qnan, qnan};
+      *reinterpret_cast<f32x4 *>(dst + 16 * nb + 4 * q) = v;
+    }
+    if (q == 0) {
+      if (S == 1) {
+        if (a.lse) a.lse[orow] = poisoned ? qnan : (mref + log2f(lt)) * gvad::kLn2;
+      } else {
+        a.part_m[prow] = poisoned ? qnan : mref;
+        a.part_l[prow] = lt;
+      }
     }
   }
+  }  // the work queue
+}
+
+// Empties the work queue's counter before the decode launch (a kernel rather than a memset, so
+// the pair can be captured in a graph).
+__global__ void k_latent_queue_reset(int32_t *next) {
+  if (threadIdx.x == 0) *next = 0;
+}
+
+// Work-groups one CU holds by LDS (the registers allow as many for these kernels).
+template <int KS, int RS, int NW>
+constexpr int latent_groups_per_cu() {
+  constexpr int lds = latent_bufs<KS, RS, NW>() * LatentTile<KS, RS>::kBytes + 1024;
+  return (160 * 1024) / lds > 0 ? (160 * 1024) / lds : 1;
 }
 
 }  // namespace
@@ -423,13 +451,17 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
 namespace gva {
 
 hipError_t launch_latent_decode(const DecodeArgs &a, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(a.B) * a.num_splits;
-  if (blocks < 1 || blocks > INT32_MAX || a.H % 8 != 0) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks));
+  const int64_t items = static_cast<int64_t>(a.B) * a.num_splits;
+  if (items < 1 || items > INT32_MAX || a.H % 8 != 0 || !a.work_next) return hipErrorInvalidValue;
   const int nw = a.H / 8;
   const int rs = (a.d_r + 31) / 32;
+  hipLaunchKernelGGL(k_latent_queue_reset, dim3(1), dim3(64), 0, stream, a.work_next);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
 #define GVA_LATENT_CASE(KS, RS, NW)                                                           \
   if (a.d_h == 32 * KS && rs == RS && nw == NW) {                                             \
+    const int64_t resident = static_cast<int64_t>(kPlanCUs) * latent_groups_per_cu<KS, RS, NW>(); \
+    const dim3 grid(static_cast<unsigned>(items < resident ? items : resident));              \
     hipLaunchKernelGGL((k_latent_decode<KS, RS, NW>), grid, dim3(64 * NW), 0, stream, a);     \
     return hipGetLastError();                                                                 \
   }
