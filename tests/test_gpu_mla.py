@@ -105,3 +105,46 @@ def test_mla_length_error(num_splits):
     ref, ref_lse = _oracle(c, odims, lens, q, scale, seqs=[0, 2])
     check_output(out[[0, 2]], ref[[0, 2]], "bf16", f"latent beside an error S={num_splits}")
     assert c.err_flag() & gb.DEVERR_LENGTH
+
+
+def test_mla_graph_replays():
+    """The call captured in a graph (the work queue's reset kernel, the decode, the combine):
+    three replays, each after an eager call on other queries, equal the eager result bit for bit
+    (whichever work-group takes an item, its arithmetic is the same)."""
+    c, lens, dims, odims = _latent_case(H=32, d_c=512, d_r=64, B=6, lengths_uniform=(500, 5000))
+    B, H, d_c = len(lens), 32, 512
+    scale = 1.0 / float(np.sqrt(576))
+    max_len = int(lens.max())
+    q = torch.from_numpy(synth.mla_queries(c.w, H, d_c, 64)).cuda()
+    q_other = torch.from_numpy(synth.mla_queries(c.w, H, d_c, 64, stream=4)).cuda()
+    seq_len = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    wsb = gb.gva_mla_decode_workspace_bytes(dims, B, max_len, 0)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    out = torch.full((B, H, d_c), float("nan"), device="cuda")
+    lse = torch.full((B, H), float("nan"), device="cuda")
+
+    def call(qq, stream):
+        gb.gva_mla_decode(dims, c.cache, B, seq_len, max_len, qq, scale, out, lse,
+                          workspace=ws, stream=stream)
+
+    call(q, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager_out, eager_lse = out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(q, side)                                  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(q, torch.cuda.current_stream())
+    for rep in range(3):
+        call(q_other, torch.cuda.current_stream())     # eager work between the replays
+        torch.cuda.synchronize()
+        assert not torch.equal(out, eager_out)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {rep}"
+        assert torch.equal(lse, eager_lse), f"replay {rep}"
+    assert c.err_flag() == 0
