@@ -83,7 +83,10 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // LDS tile: unit (kb, ks) = keys 16 kb .. + 16, elements 32 ks .. + 32 of the natural rows,
-// 1 KB in A-operand order: key n, elements 8 q .. + 8 at 16 (n + 16 q).
+// 1 KB: key n, elements 8 q .. + 8 in slot (n ^ 8 (q & 1)) + 16 q of 16 bytes. Within each
+// group of 16 slots the keys are permuted, so the score product's operand reads stay
+// conflict-free, and the transposing reads, whose 32 lanes per cycle take two pieces of 8 keys,
+// cover all 64 banks instead of meeting two by two.
 template <int KS, int RS>
 struct LatentTile {
   static constexpr int kSteps = KS + RS;             // k-steps of a natural row
@@ -234,7 +237,8 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
       const int unit = min(wave + NW * i, L::kUnits - 1);
       const int kb = unit / kSteps;
       const int ks = unit - kb * kSteps;
-      const int j = min(j0 + 16 * kb + n, c1 - 1);
+      // (this lane's 16 bytes land in slot lane: key n ^ 8 (q & 1) of piece q)
+      const int j = min(j0 + 16 * kb + (n ^ (8 * (q & 1))), c1 - 1);
       const int32_t blk = kb ? pg1 : pg0;
       const bool ok = blk >= 0 && static_cast<int64_t>(blk) < a.num_blocks;
       bad = bad || !ok;
@@ -257,6 +261,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
   // block's two 8-element pieces the one of column chunk lane % 4
   const int tr_key = lane >> 2;
   const int tr_k = lane & 3;
+  const int sw_lane = 16 * (lane ^ (8 * ((lane >> 4) & 1)));   // slot of (key n, piece q)
   f32x4 O[2 * KS];
 #pragma unroll
   for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
       u32x4 ka[kSteps];
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4 *>(base + unit_off(tb, ks, kSteps) + 16 * lane);
+        ka[ks] = *reinterpret_cast<const u32x4 *>(base + unit_off(tb, ks, kSteps) + sw_lane);
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) Sc[tb] = mfma(ka[ks], Q[ks], Sc[tb]);
       // hi + lo columns: every lane of the row pair (n, n + 8) holds head hcol's score
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
       for (int i = 0; i < kGroup; ++i) {
         const int nb = g0 + i;
         const int piece = 2 * (nb & 1) + (tr_k >> 1);
-        const int off = 16 * (tr_key + 16 * piece) + 8 * (tr_k & 1);
+        const int off = 16 * ((tr_key ^ (8 * (tr_k >> 1))) + 16 * piece) + 8 * (tr_k & 1);
         v0[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4 *)(base + unit_off(0, nb >> 1, kSteps) + off));
         v1[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
