@@ -231,9 +231,11 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
   };
   // (a single wave stages the whole tile: its address arithmetic is unrolled in part only)
   constexpr int kStageUnroll = kPer <= 12 ? kPer : 6;
-  auto stage = [&](uint8_t *buf, int32_t pg0, int32_t pg1, int j0) __attribute__((always_inline)) {
+  // stage_part issues transfers i0 .. i1 - 1 of this wave's kPer for a tile
+  auto stage_part = [&](auto I0, auto I1, uint8_t *buf, int32_t pg0, int32_t pg1,
+                        int j0) __attribute__((always_inline)) {
 #pragma unroll kStageUnroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = decltype(I0)::value; i < decltype(I1)::value; ++i) {
       const int unit = min(wave + NW * i, L::kUnits - 1);
       const int kb = unit / kSteps;
       const int ks = unit - kb * kSteps;
@@ -256,6 +258,10 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
                                        16, 0, 0);
     }
   };
+  auto stage = [&](uint8_t *buf, int32_t pg0, int32_t pg1, int j0) __attribute__((always_inline)) {
+    stage_part(std::integral_constant<int, 0>{}, std::integral_constant<int, kPer>{}, buf, pg0,
+               pg1, j0);
+  };
 
   // transposing-read address of this lane within a unit: key lane / 4, and of its 16-dim
   // block's two 8-element pieces the one of column chunk lane % 4
@@ -267,7 +273,9 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
   for (int i = 0; i < 2 * KS; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mref = -INFINITY, lsum = 0.0f;
 
-  auto tile = [&](const uint8_t *base, int j0) __attribute__((always_inline)) {
+  // tile(base, j0, hook): hook(1) runs after the scores, hook(2) after the first half of the
+  // weighted sum (compile-time points of the unrolled code, so no branch is added)
+  auto tile = [&](const uint8_t *base, int j0, auto &&hook) __attribute__((always_inline)) {
     const float negm = (mref == -INFINITY || lo_col) ? 0.0f : -mref;
     f32x4 Sc[2];
 #pragma unroll
@@ -287,6 +295,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
         if (j0 + 16 * tb + 4 * q + e >= c1) Sc[tb][e] = -INFINITY;
       }
     }
+    hook(std::integral_constant<int, 1>{});
     // tile maximum relative to the reference, over the head's 32 keys (4 rows of 16 lanes)
     const float mt = gvad::xor32_max(gvad::xor16_max(fmaxf(max4(Sc[0]), max4(Sc[1]))));
     const bool raise = mt > kLazyRescale || (mref == -INFINITY && mt != -INFINITY);
@@ -343,6 +352,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
         O[g0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VT, __builtin_bit_cast(bf16x8, PB),
                                                             O[g0 + i], 0, 0, 0);
       }
+      if (g0 + kGroup == KS) hook(std::integral_constant<int, 2>{});
     }
   };
 
@@ -365,9 +375,22 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
     constexpr int u = decltype(U)::value;
     constexpr int sb = (u + kDepth) % kBufs;
     pages(pgs[(u + kDepth + 2) % kBufs], c0 + (t + kDepth + 2) * kTile);
-    stage(ring(integral_constant<int, sb>{}), pgs[sb][0], pgs[sb][1], c0 + (t + kDepth) * kTile);
+    // tile t + kDepth's transfers in three parts: before the tile, after its scores and halfway
+    // through its weighted sum, so that the waves of a CU do not all wait on one burst
+    uint8_t *const sbuf = ring(integral_constant<int, sb>{});
+    const int js = c0 + (t + kDepth) * kTile;
+    constexpr int k1 = kPer / 3, k2 = 2 * kPer / 3;
+    stage_part(integral_constant<int, 0>{}, integral_constant<int, k1>{}, sbuf, pgs[sb][0],
+               pgs[sb][1], js);
     wait_lgkm0();                                      // the entries, before the tile's LDS reads
-    tile(ring(U), c0 + t * kTile);
+    tile(ring(U), c0 + t * kTile, [&](auto P) __attribute__((always_inline)) {
+      if constexpr (decltype(P)::value == 1)
+        stage_part(integral_constant<int, k1>{}, integral_constant<int, k2>{}, sbuf, pgs[sb][0],
+                   pgs[sb][1], js);
+      else
+        stage_part(integral_constant<int, k2>{}, integral_constant<int, kPer>{}, sbuf,
+                   pgs[sb][0], pgs[sb][1], js);
+    });
     wait_vmcnt<(kDepth - 1) * kPer>();                 // tile t + 1's units are in LDS
     ring_barrier();
   };
