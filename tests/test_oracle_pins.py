@@ -700,3 +700,171 @@ def test_mla_cache_ledger_against_pages():
     assert O.mla_cache_scalars(1000, 512, 0) * 64 == 1000 * 128 * (128 + 128)
     # beside the matched GVA cache of the ragged-batch shape (G = 8, d_h = 128, d_r = 24)
     assert O.mla_cache_scalars(1, 512, 64) / O.gva_cache_scalars(1, 8, 128, 24) < 0.55
+
+
+# ----------------------------------------------------------------------------------------
+# The GVA path's positional term, end to end through append -> absorb -> decode_sequence
+# ([review] section 关键技巧二: the shared key is cached rotated at its own position j, the
+# query's slice is rotated at the query position p, so their product depends on j - p only)
+# ----------------------------------------------------------------------------------------
+
+
+def _f32_pool_pipeline(V, kr_raw, q_nope, q_rope, M, dims, scale, key_pos, q_pos):
+    """Appends the n keys at positions key_pos (one contiguous float32 sequence), absorbs the
+    query at q_pos and decodes over those keys. Returns (out, lse, kr as cached, r)."""
+    n = len(V)
+    top = int(max(int(np.max(key_pos)), q_pos)) + 1
+    bs = 1 << int(math.ceil(math.log2(top)))
+    pool = O.Pool.empty("f32", bs * dims.G * dims.d_h, bs * dims.d_r,
+                        (bs * dims.G * dims.d_h, dims.G * dims.d_h, dims.d_h, bs * dims.d_r,
+                         dims.d_r), 1, bs, np.zeros((1, 1), np.int64))
+    tab = O.rope_table(top, dims.d_r)
+    assert O.append(pool, dims, np.zeros(n, np.int64), key_pos, V, kr_raw, tab) == 0
+    Vg, krg = O.gather(pool, dims, 0, top)
+    Vg, krg = Vg[key_pos], krg[key_pos]
+    qt, r = O.absorb(q_nope[None], q_rope[None], [q_pos], M, tab)
+    out, lse = O.decode_sequence(Vg, krg, dims, O.q_abs_of(qt, r)[0], scale)
+    return out, lse, krg, r[0]
+
+
+def _positional_pin_failures():
+    """Runs the positional-term pins of the GVA path and returns the names of those that fail
+    (an empty list when the oracle is right). Tolerances: the float32 cache rounds each rotated
+    key element once (relative 2^-24), which moves a score by at most
+    scale * sum_i |r_i| |kr_i| 2^-24 < 1e-5 at these sizes; everything else is float64."""
+    fails = []
+    rng = np.random.default_rng(41)
+    H, G, n, d_h, d_n, d_r, scale = 4, 2, 23, 6, 5, 8, 0.5
+    dims = O.Dims(H=H, G=G, d_h=d_h, d_n=d_n, d_r=d_r)
+    V = rng.standard_normal((n, G, d_h)).astype(np.float32)
+    kr_raw = (3.0 * rng.standard_normal((n, d_r))).astype(np.float32)
+    q_nope = rng.standard_normal((H, d_n)).astype(np.float32)
+    q_rope = (3.0 * rng.standard_normal((H, d_r))).astype(np.float32)
+    M = rng.standard_normal((H, d_h, d_n)) / math.sqrt(d_h)
+    p, delta = 40, 977
+    j = np.arange(n)
+    a_out, a_lse, kr_a, r_a = _f32_pool_pipeline(V, kr_raw, q_nope, q_rope, M, dims, scale, j, p)
+    # 1. shifting the query and every key by the same offset changes nothing
+    b_out, b_lse, _, _ = _f32_pool_pipeline(V, kr_raw, q_nope, q_rope, M, dims, scale,
+                                            j + delta, p + delta)
+    if not (np.max(np.abs(a_out - b_out)) < 1e-5 and np.max(np.abs(a_lse - b_lse)) < 1e-5):
+        fails.append("shift invariance")
+    # 2. moving only the query does change the result
+    c_out, c_lse, _, _ = _f32_pool_pipeline(V, kr_raw, q_nope, q_rope, M, dims, scale, j, p + 3)
+    if not np.max(np.abs(c_lse - a_lse)) > 1e-3:
+        fails.append("query position matters")
+    # 3. each positional product r_h . kr_j equals Re(sum_i conj(q_i) k_i e^{i (j - p) theta_i})
+    #    of the raw pairs taken as complex numbers (theta_i from math.pow, not the oracle)
+    theta = np.array([math.pow(10000.0, -2.0 * i / d_r) for i in range(d_r // 2)])
+    kc = kr_raw[:, 0::2].astype(np.float64) + 1j * kr_raw[:, 1::2].astype(np.float64)
+    qc = q_rope[:, 0::2].astype(np.float64) + 1j * q_rope[:, 1::2].astype(np.float64)
+    rel = np.exp(1j * (j[:, None] - p) * theta[None, :])                      # [n, d_r/2]
+    want = np.real(np.einsum("hi,ni,ni->hn", np.conj(qc), kc, rel))          # [H, n]
+    got = r_a @ kr_a.T
+    if not np.max(np.abs(got - want)) < 1e-5 * max(1.0, np.max(np.abs(want))):
+        fails.append("complex relative angle")
+    # 4. the full score and softmax against the materialised form with that positional term
+    for h in range(H):
+        g = h // (H // G)
+        K = V[:, g, :].astype(np.float64) @ M[h]
+        s = scale * (K @ q_nope[h].astype(np.float64) + want[h])
+        ls = logsumexp(s)
+        if not (abs(a_lse[h] - ls) < 1e-5 and
+                np.max(np.abs(a_out[h] - np.exp(s - ls) @ V[:, g, :].astype(np.float64))) < 1e-5):
+            fails.append(f"score of head {h}")
+            break
+    return fails
+
+
+def test_gva_positional_term_pins():
+    assert _positional_pin_failures() == []
+
+
+def _rotate_sine_flipped(x, cs):
+    """A planted mistake: the rotation with the sine's sign flipped (a rotation by -angle)."""
+    x = np.asarray(x, dtype=np.float64)
+    c, s = cs[..., 0], cs[..., 1]
+    y = np.empty(np.broadcast(x[..., 0::2], c).shape[:-1] + (x.shape[-1],))
+    y[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s
+    y[..., 1::2] = -x[..., 0::2] * s + x[..., 1::2] * c
+    return y
+
+
+@pytest.mark.parametrize("mistake", ["query_unrotated", "query_at_p_minus_1", "sine_flipped"])
+def test_planted_positional_mistakes_fail_a_pin(mistake, monkeypatch):
+    """Each plausible mistake in the oracle's positional path, planted in the oracle on the CPU,
+    fails at least one of the pins above."""
+    real_absorb = O.absorb
+    if mistake == "query_unrotated":
+        def bad(q_nope, q_rope, q_pos, M, table):
+            qt, _ = real_absorb(q_nope, q_rope, q_pos, M, table)
+            return qt, np.asarray(q_rope, dtype=np.float64)
+        monkeypatch.setattr(O, "absorb", bad)
+    elif mistake == "query_at_p_minus_1":
+        def bad(q_nope, q_rope, q_pos, M, table):
+            return real_absorb(q_nope, q_rope, np.asarray(q_pos) - 1, M, table)
+        monkeypatch.setattr(O, "absorb", bad)
+    else:
+        monkeypatch.setattr(O, "rotate", _rotate_sine_flipped)
+    assert _positional_pin_failures() != []
+
+
+# ----------------------------------------------------------------------------------------
+# decode(): every sequence of a paged pool, against pure-Python loops over the raw pool
+# ----------------------------------------------------------------------------------------
+
+
+def _brute_force_pool_decode(pool, dims, seq_len, q_abs, scale, group_of):
+    """Reads the pool's float32 bits element by element through the block table and decodes
+    each (b, h) with Python loops; group_of(h) names the head's value group."""
+    B = len(seq_len)
+    out = np.zeros((B, dims.H, dims.d_h))
+    lse = np.full((B, dims.H), -np.inf)
+    f32 = lambda bits: float(np.array(bits, dtype=np.uint32).view(np.float32))
+    for b in range(B):
+        n = int(seq_len[b])
+        rows_v, rows_k = [], []
+        for p in range(n):
+            blk = int(pool.block_table[b][p // pool.block_size])
+            off = p % pool.block_size
+            rows_v.append([[f32(pool.v[blk * pool.v_sb + off * pool.v_st + g * pool.v_sg + i])
+                            for i in range(dims.d_h)] for g in range(dims.G)])
+            rows_k.append([f32(pool.kr[blk * pool.kr_sb + off * pool.kr_st + i])
+                           for i in range(dims.d_r)])
+        for h in range(dims.H):
+            if n == 0:
+                continue
+            g = group_of(h)
+            qt = q_abs[b][h][:dims.d_h]
+            r = q_abs[b][h][dims.d_h:]
+            s = [scale * (sum(qt[i] * rows_v[p][g][i] for i in range(dims.d_h)) +
+                          sum(r[i] * rows_k[p][i] for i in range(dims.d_r))) for p in range(n)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            lse[b, h] = mx + math.log(z)
+            for i in range(dims.d_h):
+                out[b, h, i] = sum(e[p] / z * rows_v[p][g][i] for p in range(n))
+    return out, lse
+
+
+def test_pool_decode_against_brute_force():
+    w, lens, lay = _small_paged(dtype="f32")
+    dims = O.Dims(w.H, w.G, w.d_h, w.d_n, w.d_r)
+    pool = O.Pool.empty("f32", lay.v_elems, lay.kr_elems,
+                        (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st),
+                        lay.num_blocks, lay.block_size, lay.block_table)
+    tab = O.rope_table(64, w.d_r)
+    for b in range(w.B):
+        v, kr_raw = synth.sequence_tokens(w, b, int(lens[b]))
+        assert O.append(pool, dims, np.full(int(lens[b]), b), np.arange(int(lens[b])), v,
+                        kr_raw, tab) == 0
+    seq_len = lens.copy()
+    seq_len[1] = 0                                   # an empty history
+    q_abs = np.random.default_rng(3).standard_normal((w.B, w.H, w.d_h + w.d_r))
+    out, lse = O.decode(pool, dims, seq_len, q_abs, 0.6)
+    ref, ref_lse = _brute_force_pool_decode(pool, dims, seq_len, q_abs, 0.6,
+                                            lambda h: h // (w.H // w.G))
+    assert np.max(np.abs(out - ref)) < 1e-12 and np.all(out[1] == 0)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - ref_lse[fin])) < 1e-12
