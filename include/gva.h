@@ -30,7 +30,8 @@
  *     cache or the RoPE table, a length above the stated bound) set bits in *err_flag when
  *     err_flag is not NULL; the affected token is not written (append) or the affected
  *     output row is filled with NaN (decode, prefill).
- *   - Grouping is contiguous: g(h) = h / (H / G), with H a multiple of G.
+ *   - Grouping: g(h) = h / (H / G) (contiguous) unless gva_dims.g_of_h names another map in
+ *     which every group holds exactly H / G heads.
  *   - RoPE pairs are interleaved: (x[2i], x[2i+1]) is rotated by p * theta_i.
  */
 #ifndef GVA_H_
@@ -75,13 +76,20 @@ typedef enum gva_decode_kernel {
 } gva_decode_kernel;
 
 /* Model shape in the pages' notation. Limits: 1 <= G <= H, H % G == 0, H <= 256,
- * 2 <= d_h <= 256 and even, 1 <= d_n <= 512, 2 <= d_r <= 64 and even. */
+ * 2 <= d_h <= 256 and even, 1 <= d_n <= 512, 2 <= d_r <= 64 and even.
+ * g_of_h: host int32 [H] or NULL. g_of_h[h] is the value group g(h) that query head h reads
+ * ("GVA：KV 缓存里的 Key 其实可以不存", section 第二次尝试: head h's key is built from the values of
+ * its group g(h); [kvcache] section 4: query heads are partitioned into groups that share one
+ * cached stream). Every entry must lie in [0, G) and every group must hold exactly H / G heads
+ * (GVA_ERR_INVALID_ARG otherwise). NULL means the contiguous map g(h) = h / (H / G). The array
+ * is read during the call only; the caller keeps ownership. */
 typedef struct gva_dims {
   int32_t H;
   int32_t G;
   int32_t d_h;
   int32_t d_n;
   int32_t d_r;
+  const int32_t *g_of_h;
 } gva_dims;
 
 /* One layer's cache, paged or contiguous, described by element strides.

@@ -30,7 +30,7 @@ Readings where the pages are silent:
   * RoPE pairs are interleaved (x_{2i}, x_{2i+1}); theta_i = base^(-2i/d_r), base 10000.
   * Rotation is done in float64 with each product and sum rounded separately, and the
     cache stores one round-to-nearest-even of that float64 value.
-  * g(h) = h // (H/G).
+  * g(h) = h // (H/G) unless a map is given (Dims.g_of_h).
   * Decode attends to every cached entry j < len_b; prefill query i at position
     start_b + i attends to positions 0..start_b + i inclusive.
   * len_b = 0 gives output 0 and lse = -inf.
@@ -181,8 +181,14 @@ class Dims:
     d_h: int
     d_n: int
     d_r: int
+    # g(h) for every head h, or None for the contiguous map h // (H/G). Heads are partitioned into
+    # groups that share one cached value stream ([kvcache] section 4; [review] section 第二次尝试);
+    # the pages draw the groups contiguous but nothing in the method depends on it.
+    g_of_h: Optional[tuple] = None
 
     def group_of(self, h: int) -> int:
+        if self.g_of_h is not None:
+            return int(self.g_of_h[h])
         return h // (self.H // self.G)
 
 

@@ -48,12 +48,13 @@ class Case:
     """One workload: device cache + oracle pool built from the same synthetic inputs."""
 
     def __init__(self, w: synth.Workload, lens=None, group_major=True, device="cuda",
-                 max_pos=None, sentinel=True):
+                 max_pos=None, sentinel=True, g_of_h=None):
         self.w = w
         self.lens = np.asarray(lens if lens is not None else synth.lengths(w), dtype=np.int64)
         self.lay = synth.layout(w, self.lens, group_major)
-        self.dims = O.Dims(w.H, w.G, w.d_h, w.d_n, w.d_r)
-        self.cdims = gb.GvaDims(w.H, w.G, w.d_h, w.d_n, w.d_r)
+        gmap = None if g_of_h is None else tuple(int(g) for g in g_of_h)
+        self.dims = O.Dims(w.H, w.G, w.d_h, w.d_n, w.d_r, gmap)
+        self.cdims = gb.dims_struct(w.H, w.G, w.d_h, w.d_n, w.d_r, gmap)
         cap = synth.capacity(w, self.lens)
         self.max_pos = int(max_pos if max_pos is not None else int(cap.max()) + 1)
         self.device = device

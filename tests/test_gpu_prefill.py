@@ -129,3 +129,97 @@ def test_prefill_bad_start_poisons_rows():
     out, lse = _run_prefill(c, bad, 40, q_abs, v_new, kr_new)
     assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1]))
     assert c.err_flag() & gb.DEVERR_LENGTH
+
+
+def _oracle_rows(c, b, start, C, q_abs, upto):
+    """Oracle outputs of sequence b's queries i with start + i < upto (their windows end before
+    position upto), from the oracle's pool: out [n, H, d_h], lse [n, H]."""
+    w = c.w
+    n = max(0, min(C, upto - start))
+    V, kr = O.gather(c.pool, c.dims, b, start + n)
+    out = np.zeros((n, w.H, w.d_h))
+    lse = np.zeros((n, w.H))
+    for i in range(n):
+        L = start + i + 1
+        out[i], lse[i] = O.decode_sequence(V[:L], kr[:L], c.dims, q_abs[b, i].astype(np.float64),
+                                           w.scale)
+    return out, lse
+
+
+def _error_case(starts, C=40, max_pos=None):
+    w = synth.workload("C5", B=len(starts), T=0, chunk=C, append_one=False, lengths_uniform=None,
+                       H=8, G=2, d_h=64, d_n=64, d_r=16)
+    starts = np.asarray(starts, np.int64)
+    c = Case(w, lens=starts, max_pos=max_pos)
+    c.append_prefix()
+    return c, starts
+
+
+def test_prefill_corrupt_prefix_block_poisons_the_sequence():
+    """A block-table entry outside the pool in the cached prefix of sequence 0: every query of
+    that sequence sees it, so all its rows are NaN and the BLOCK bit is raised; sequence 1 is
+    untouched and matches the oracle. The kernel reads block 0 in its place and exits normally."""
+    c, starts = _error_case([100, 64])
+    C = c.w.chunk
+    q_abs, v_new, kr_new = _chunk_inputs(c.w, starts, C)
+    c.block_table[0, 3] = c.lay.num_blocks + 7          # positions 48 .. 63 of sequence 0
+    out, lse = _run_prefill(c, starts, C, q_abs, v_new, kr_new)
+    assert c.err_flag() & gb.DEVERR_BLOCK
+    assert np.all(np.isnan(out[0])) and np.all(np.isnan(lse[0]))
+    # the chunk itself was appended (its blocks are valid): the pools agree bit for bit
+    O.append(c.pool, c.dims, np.repeat(np.arange(2), C),
+             (starts[:, None] + np.arange(C)[None, :]).reshape(-1),
+             v_new.reshape(-1, c.w.G, c.w.d_h), kr_new.reshape(-1, c.w.d_r), c.tab_ora)
+    v_bits, kr_bits = c.device_bits()
+    assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
+    ref, ref_lse = _oracle_rows(c, 1, int(starts[1]), C, q_abs, 1 << 30)
+    check_output(out[1], ref, "bf16", "prefill, other sequence beside a corrupt block")
+    ok, e = lse_ok(lse[1], ref_lse, 2e-2)
+    assert ok, e
+
+
+def test_prefill_corrupt_block_inside_the_chunk_poisons_later_rows_only():
+    """The entry of the block holding chunk positions 112 .. 127 of sequence 0 is corrupt: the
+    chunk append skips those tokens (BLOCK), queries at positions below 112 never see them and
+    match the oracle, and every query at 112 or later is NaN."""
+    c, starts = _error_case([100, 64])
+    C = c.w.chunk
+    q_abs, v_new, kr_new = _chunk_inputs(c.w, starts, C)
+    bad = c.lay.num_blocks + 3
+    c.block_table[0, 7] = bad
+    c.pool.block_table[0, 7] = bad                      # the oracle's append skips them too
+    out, lse = _run_prefill(c, starts, C, q_abs, v_new, kr_new)
+    assert c.err_flag() & gb.DEVERR_BLOCK
+    err = O.append(c.pool, c.dims, np.repeat(np.arange(2), C),
+                   (starts[:, None] + np.arange(C)[None, :]).reshape(-1),
+                   v_new.reshape(-1, c.w.G, c.w.d_h), kr_new.reshape(-1, c.w.d_r), c.tab_ora)
+    assert err & O.ERR_BLOCK
+    v_bits, kr_bits = c.device_bits()
+    assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
+    n_ok = 112 - int(starts[0])
+    assert np.all(np.isnan(out[0, n_ok:])) and np.all(np.isnan(lse[0, n_ok:]))
+    ref, ref_lse = _oracle_rows(c, 0, int(starts[0]), C, q_abs, 112)
+    check_output(out[0, :n_ok], ref, "bf16", "prefill rows before a corrupt chunk block")
+    ok, e = lse_ok(lse[0, :n_ok], ref_lse, 2e-2)
+    assert ok, e
+    assert np.all(np.isfinite(out[1]))
+
+
+def test_prefill_chunk_past_the_rope_table():
+    """The RoPE table has 120 rows: sequence 0's chunk (positions 100 .. 139) does not fit, so its
+    tokens from 120 on are not appended, the ROPE bit is raised and all its rows are NaN;
+    sequence 1 (positions 20 .. 59) is unaffected."""
+    c, starts = _error_case([100, 20], max_pos=120)
+    C = c.w.chunk
+    q_abs, v_new, kr_new = _chunk_inputs(c.w, starts, C)
+    out, lse = _run_prefill(c, starts, C, q_abs, v_new, kr_new)
+    assert c.err_flag() & gb.DEVERR_ROPE
+    assert np.all(np.isnan(out[0])) and np.all(np.isnan(lse[0]))
+    err = O.append(c.pool, c.dims, np.repeat(np.arange(2), C),
+                   (starts[:, None] + np.arange(C)[None, :]).reshape(-1),
+                   v_new.reshape(-1, c.w.G, c.w.d_h), kr_new.reshape(-1, c.w.d_r), c.tab_ora)
+    assert err & O.ERR_ROPE
+    v_bits, kr_bits = c.device_bits()
+    assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
+    ref, ref_lse = _oracle_rows(c, 1, int(starts[1]), C, q_abs, 1 << 30)
+    check_output(out[1], ref, "bf16", "prefill, other sequence beside a short RoPE table")

@@ -353,3 +353,31 @@ def test_mla_validation(L):
     assert gb.gva_mla_decode_workspace_bytes(d512, 256, 100, 0) == 256
     assert ml(d=d512, c=_cache(d=d, v_stride_token=512, v_stride_block=16 * 512),
               B=256, ml=100) == gb.GVA_ERR_WORKSPACE
+
+
+# ---- the head -> group map (gva_dims.g_of_h) ----------------------------------------------------
+
+
+def _absorb_empty(L, d):
+    """gva_absorb_query with no tokens: validates the dims and launches nothing."""
+    return L.gva_absorb_query(ctypes.byref(d), 0, A, A, A, A, A, 16, A, None, None)
+
+
+@pytest.mark.parametrize("gmap,ok", [
+    (None, True),
+    ([0, 0, 1, 1, 2, 2, 3, 3], True),                 # the contiguous map written out
+    ([3, 1, 0, 2, 1, 3, 2, 0], True),                 # a balanced permutation
+    ([0, 0, 1, 1, 2, 2, 3, 4], False),                # a group outside [0, G)
+    ([0, 0, 1, 1, 2, 2, 3, -1], False),               # a negative group
+    ([0, 0, 0, 1, 2, 2, 3, 3], False),                # group 0 holds 3 heads, group 1 one
+])
+def test_group_map_validation(L, gmap, ok):
+    d = gb.dims_struct(8, 4, 64, 64, 16, gmap)
+    st = _absorb_empty(L, d)
+    assert st == (gb.GVA_OK if ok else gb.GVA_ERR_INVALID_ARG), L.gva_last_error().decode()
+    # every entry point that takes dims rejects the same map before any launch
+    ws = gb.gva_decode_workspace_bytes(d, 2, 100, 0)
+    assert (ws > 0) == ok
+    if not ok:
+        assert _decode(L, d, _cache(d=d)) == gb.GVA_ERR_INVALID_ARG
+        assert "g_of_h" in L.gva_last_error().decode()

@@ -868,3 +868,30 @@ def test_pool_decode_against_brute_force():
     assert np.max(np.abs(out - ref)) < 1e-12 and np.all(out[1] == 0)
     fin = np.isfinite(ref_lse)
     assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - ref_lse[fin])) < 1e-12
+
+
+def test_pool_decode_with_a_permuted_group_map():
+    """With a non-contiguous head -> group map every head reads the values of its own group:
+    decode() equals the brute force that looks the group up in the same map, and differs from the
+    contiguous map's result."""
+    w, lens, lay = _small_paged(dtype="f32")
+    gmap = (1, 0, 0, 1)                              # H = 4, G = 2: two heads per group
+    dims = O.Dims(w.H, w.G, w.d_h, w.d_n, w.d_r, gmap)
+    pool = O.Pool.empty("f32", lay.v_elems, lay.kr_elems,
+                        (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st),
+                        lay.num_blocks, lay.block_size, lay.block_table)
+    tab = O.rope_table(64, w.d_r)
+    for b in range(w.B):
+        v, kr_raw = synth.sequence_tokens(w, b, int(lens[b]))
+        O.append(pool, dims, np.full(int(lens[b]), b), np.arange(int(lens[b])), v, kr_raw, tab)
+    q_abs = np.random.default_rng(4).standard_normal((w.B, w.H, w.d_h + w.d_r))
+    out, lse = O.decode(pool, dims, lens, q_abs, 0.6)
+    ref, ref_lse = _brute_force_pool_decode(pool, dims, lens, q_abs, 0.6, lambda h: gmap[h])
+    assert np.max(np.abs(out - ref)) < 1e-12 and np.max(np.abs(lse - ref_lse)) < 1e-12
+    contiguous, _ = O.decode(pool, O.Dims(w.H, w.G, w.d_h, w.d_n, w.d_r), lens, q_abs, 0.6)
+    assert np.max(np.abs(contiguous - out)) > 1e-3
+    # decode_sequence (used by the parity tests) agrees with decode() under the map
+    for b in range(w.B):
+        V, kr = O.gather(pool, dims, b, int(lens[b]))
+        o2, l2 = O.decode_sequence(V, kr, dims, q_abs[b], 0.6)
+        assert np.max(np.abs(o2 - out[b])) < 1e-12

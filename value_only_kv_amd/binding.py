@@ -37,7 +37,7 @@ EXPORTED = [
 
 class GvaDims(ctypes.Structure):
     _fields_ = [("H", c_int32), ("G", c_int32), ("d_h", c_int32), ("d_n", c_int32),
-                ("d_r", c_int32)]
+                ("d_r", c_int32), ("g_of_h", c_void_p)]
 
 
 class GvaCacheStruct(ctypes.Structure):
@@ -149,8 +149,15 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def dims_struct(H: int, G: int, d_h: int, d_n: int, d_r: int) -> GvaDims:
-    return GvaDims(H, G, d_h, d_n, d_r)
+def dims_struct(H: int, G: int, d_h: int, d_n: int, d_r: int, g_of_h=None) -> GvaDims:
+    """The C struct; g_of_h (a sequence of H group indices, or None for the contiguous map) is
+    kept alive as a host int32 array referenced by the struct."""
+    d = GvaDims(H, G, d_h, d_n, d_r, None)
+    if g_of_h is not None:
+        arr = np.ascontiguousarray(np.asarray(g_of_h, dtype=np.int32))
+        d._g_of_h_keep = arr
+        d.g_of_h = arr.ctypes.data
+    return d
 
 
 # ---- entry points (same names as the C ABI) -------------------------------------------------

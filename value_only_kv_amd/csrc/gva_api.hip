@@ -26,6 +26,7 @@ gva::DecodeArgs cache_args(const gva_dims *d, const gva_cache *c) {
   a.G = d->G;
   a.d_h = d->d_h;
   a.d_r = d->d_r;
+  gva::group_order(d, a.head_of);
   return a;
 }
 

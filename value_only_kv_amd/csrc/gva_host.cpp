@@ -49,7 +49,33 @@ gva_status check_dims(const gva_dims *d) {
     return fail(GVA_ERR_INVALID_ARG, "d_n=%d outside [1, %d]", d->d_n, kMaxDn);
   if (d->d_r < 2 || d->d_r > kMaxDr || d->d_r % 2 != 0)
     return fail(GVA_ERR_INVALID_ARG, "d_r=%d must be even and in [2, %d]", d->d_r, kMaxDr);
+  if (d->g_of_h) {
+    int count[kMaxH] = {0};
+    for (int h = 0; h < d->H; ++h) {
+      const int32_t g = d->g_of_h[h];
+      if (g < 0 || g >= d->G)
+        return fail(GVA_ERR_INVALID_ARG, "g_of_h[%d]=%d outside [0, G=%d)", h, g, d->G);
+      ++count[g];
+    }
+    for (int g = 0; g < d->G; ++g)
+      if (count[g] != d->H / d->G)
+        return fail(GVA_ERR_INVALID_ARG, "g_of_h gives group %d %d heads, not H/G=%d", g, count[g],
+                    d->H / d->G);
+  }
   return GVA_OK;
+}
+
+void group_order(const gva_dims *d, uint8_t *head_of) {
+  const int per = d->H / d->G;
+  if (!d->g_of_h) {
+    for (int h = 0; h < d->H; ++h) head_of[h] = static_cast<uint8_t>(h);
+    return;
+  }
+  int next[kMaxH] = {0};
+  for (int h = 0; h < d->H; ++h) {
+    const int g = d->g_of_h[h];
+    head_of[g * per + next[g]++] = static_cast<uint8_t>(h);
+  }
 }
 
 gva_status check_cache(const gva_dims *d, const gva_cache *c) {

@@ -59,6 +59,8 @@ gva_status fail(gva_status status, const char *fmt, ...);
 
 // Argument checks. None of them touches HIP, so they run (and are tested) without a GPU.
 gva_status check_dims(const gva_dims *d);
+// Fills head_of[0 .. H) with the heads in group order (see DecodeArgs::head_of) for checked dims.
+void group_order(const gva_dims *d, uint8_t *head_of);
 gva_status check_cache(const gva_dims *d, const gva_cache *c);
 gva_status check_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,
                         const int32_t *seq, const int32_t *pos, const float *v_new,
@@ -154,6 +156,9 @@ struct DecodeArgs {
   float *out;           // [B][H][d_h]
   float *lse;           // [B][H] or nullptr
   int32_t *work_next;   // latent comparator: the work queue's counter (zeroed before the launch)
+  // Heads in group order: slot g * (H / G) + c holds the c-th head (in ascending order) of value
+  // group g, so a kernel that serves group g reads the heads of slots g * (H / G) ...
+  uint8_t head_of[kMaxH];
 };
 
 hipError_t launch_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,

@@ -48,7 +48,7 @@ __device__ __forceinline__ void store_rows(const gva::DecodeArgs &a, int b, int 
   const int lane = threadIdx.x;
   const float qnan = __int_as_float(0x7fc00000);
   for (int hh = 0; hh < nh; ++hh) {
-    const int h = h0 + hh;
+    const int h = a.head_of[h0 + hh];
     if (a.num_splits == 1) {
       const float inv = l[hh] > 0.0f ? 1.0f / l[hh] : 0.0f;
       float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
   const int g = blockIdx.z / head_passes;
   const int hp = blockIdx.z - g * head_passes;
   const int hpg = a.H / a.G;
-  const int h0 = g * hpg + hp * kHeadsPerPass;
+  const int h0 = g * hpg + hp * kHeadsPerPass;     // first slot of this pass in a.head_of
   const int nh = min(kHeadsPerPass, hpg - hp * kHeadsPerPass);
   const int lane = threadIdx.x;
   const int d_h = a.d_h, d_r = a.d_r, row = d_h + d_r;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
   for (int idx = lane; idx < NHP * row; idx += 64) {
     const int hh = idx / row;
     const int e = idx - hh * row;
-    q_s[hh][e] = hh < nh ? a.q_abs[(static_cast<int64_t>(b) * a.H + h0 + hh) * row + e] * a.qscale
+    q_s[hh][e] = hh < nh ? a.q_abs[(static_cast<int64_t>(b) * a.H + a.head_of[h0 + hh]) * row + e] * a.qscale
                          : 0.0f;
   }
   __syncthreads();

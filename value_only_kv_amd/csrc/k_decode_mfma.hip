@@ -327,7 +327,7 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
   const int n = lane & 15;
   const int q = lane >> 4;
   const int nhg = a.H / a.G;
-  const int h0 = g * nhg;
+  const int h0 = g * nhg;                  // the group's first slot in a.head_of
   // the query column of this lane: head c (hi or, with merged columns, lo part)
   const int c = NH > 0 ? (n < NH ? n : n - NH) : n;
   const bool col_ok = NH > 0 ? (n < 2 * NH) : (n < nhg);
@@ -348,7 +348,7 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
     // ---- query operands (B layout: column n, K group q) ----
     bf16x8 QX[KS], QY[KS], RX, RY;
     const float *qp =
-        a.q_abs + (static_cast<int64_t>(b) * a.H + h0 + (col_ok ? c : 0)) * row_len;
+        a.q_abs + (static_cast<int64_t>(b) * a.H + a.head_of[h0 + (col_ok ? c : 0)]) * row_len;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float x[8];
@@ -448,7 +448,7 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
   // empty chunks (past the end of a sequence, or of a sequence with a bad length) are never
   // read by the combine
   if (!direct && c0 >= c1) return;
-  const int h = h0 + c;
+  const int h = a.head_of[h0 + c];
   if (direct) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h + 4 * q;

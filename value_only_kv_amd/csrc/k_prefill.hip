@@ -226,17 +226,22 @@ __device__ __forceinline__ StageSrc<KS, W> stage_src(const gva::DecodeArgs &a, i
   return src;
 }
 
+// A block-table entry outside the pool is read as block 0 (so the load stays in bounds) and the
+// lowest such key is kept in bad_key: the rows whose causal window reaches it become NaN.
 template <int KS, int W>
 __device__ __forceinline__ void stage_load(const gva::DecodeArgs &a, const StageSrc<KS, W> &src,
                                            const StagePages<KS, W> &pg, int kt0, int kend,
-                                           int wave, int n, Stage<KS, W> &st) {
+                                           int wave, int n, Stage<KS, W> &st, int &bad_key) {
   const int mask = (1 << a.log2_bs) - 1;
 #pragma unroll
   for (int i = 0; i < Stage<KS, W>::kPerWave; ++i) {
     const int32_t pb = pg.pb[i];
     // block ids are below 2^31 (checked on the host): one unsigned compare covers both ends
-    const int64_t blk = static_cast<uint32_t>(pb) < static_cast<uint32_t>(a.num_blocks) ? pb : 0;
-    const int64_t row = stage_key(kt0, stage_unit<KS, W>(wave, i), n, kend) & mask;
+    const bool ok = static_cast<uint32_t>(pb) < static_cast<uint32_t>(a.num_blocks);
+    const int64_t blk = ok ? pb : 0;
+    const int key = stage_key(kt0, stage_unit<KS, W>(wave, i), n, kend);
+    bad_key = ok ? bad_key : min(bad_key, key);
+    const int64_t row = key & mask;
     st.u[i] = *reinterpret_cast<const u32x4 *>(src.base[i] + blk * src.sb[i] + row * src.st[i]);
   }
 }
@@ -264,7 +269,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   constexpr int RT = row_tiles<KS>();
   constexpr int kRows = rows_per_group<KS>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][L::kElems];
+  __shared__ int s_bad_key;                // lowest key read from a bad block (INT_MAX: none)
   const gva::DecodeArgs &a = p.kv;
+  if (threadIdx.x == 0) s_bad_key = INT_MAX;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int n = lane & 15;
@@ -296,7 +303,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   const int row_len = a.d_h + a.d_r;
   const float qnan = __int_as_float(0x7fc00000);
   const int cap = a.max_blocks << a.log2_bs;
-  const bool seq_bad = P0 < 0 || P0 > p.max_start || P0 + C > cap;
+  // A bad start, or a chunk that does not fit the block table or the RoPE table (the chunk
+  // append skipped those tokens), makes every row of the sequence NaN.
+  int32_t seq_err = 0;
+  if (P0 < 0 || P0 > p.max_start) seq_err = GVA_DEVERR_LENGTH;
+  else if (P0 + C > cap) seq_err = GVA_DEVERR_CAPACITY;
+  else if (P0 + C > p.max_pos) seq_err = GVA_DEVERR_ROPE;
+  const bool seq_bad = seq_err != 0;
 
   // Row tile rt of this wave: rows row0 + 16 (RT wave + rt) + 0..15; this lane's row (the B
   // column) is n of each.
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     const int r = row0 + 16 * (RT * wave + rt) + n;
     const int rc = r < nrows ? r : nrows - 1;
     const int qi = rc / nhg;
-    const int h = g * nhg + (rc - qi * nhg);
+    const int h = a.head_of[g * nhg + (rc - qi * nhg)];
     qpos[rt] = P0 + qi;
     const float *qp = p.q_abs + ((static_cast<int64_t>(b) * C + qi) * a.H + h) * row_len;
 #pragma unroll
@@ -359,6 +372,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   // transposing-read address of this lane: row lane / 4, columns 4 (lane % 4) ..
   const int tr_off = (lane >> 2) * L::kNatStride + 4 * (lane & 3);
 
+  int bad_key = INT_MAX;                   // this lane's lowest key read from a bad block
   f32x4 S[RT][2];   // scores of the current tile, from its products to its softmax
   u32x4 PB[RT];     // its probabilities (bf16 pairs), from its softmax to its weighted sum
 
@@ -463,9 +477,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     StagePages<KS, W> p0, p1;
     stage_pages<KS, W>(a, bt, 0, kend, wave, n, p0);
     stage_pages<KS, W>(a, bt, kKeyTile, kend, wave, n, p1);
-    stage_load<KS, W>(a, src, p0, 0, kend, wave, n, s0);
+    stage_load<KS, W>(a, src, p0, 0, kend, wave, n, s0, bad_key);
     stage_pages<KS, W>(a, bt, 2 * kKeyTile, kend, wave, n, p0);
-    stage_load<KS, W>(a, src, p1, kKeyTile, kend, wave, n, s1);
+    stage_load<KS, W>(a, src, p1, kKeyTile, kend, wave, n, s1, bad_key);
     stage_pages<KS, W>(a, bt, 3 * kKeyTile, kend, wave, n, p1);
     stage_store<KS, W>(lds[0], wave, n, q, a.d_r, s0);
     __syncthreads();
@@ -473,13 +487,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     for (; t + 2 < ntiles; t += 2) {
       const int kt0 = t * kKeyTile;
       // tile t in lds[0]; tile t + 1 in s1; s0 free; p0 holds the pages of tile t + 2
-      stage_load<KS, W>(a, src, p0, kt0 + 2 * kKeyTile, kend, wave, n, s0);
+      stage_load<KS, W>(a, src, p0, kt0 + 2 * kKeyTile, kend, wave, n, s0, bad_key);
       stage_pages<KS, W>(a, bt, kt0 + 4 * kKeyTile, kend, wave, n, p0);
       tile(lds[0], kt0);
       stage_store<KS, W>(lds[1], wave, n, q, a.d_r, s1);
       __syncthreads();
       // tile t + 1 in lds[1]; tile t + 2 in s0; s1 free; p1 holds the pages of tile t + 3
-      stage_load<KS, W>(a, src, p1, kt0 + 3 * kKeyTile, kend, wave, n, s1);
+      stage_load<KS, W>(a, src, p1, kt0 + 3 * kKeyTile, kend, wave, n, s1, bad_key);
       stage_pages<KS, W>(a, bt, kt0 + 5 * kKeyTile, kend, wave, n, p1);
       tile(lds[1], kt0 + kKeyTile);
       stage_store<KS, W>(lds[0], wave, n, q, a.d_r, s0);
@@ -494,6 +508,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     }
   }
 
+  // the work-group's lowest bad key (every wave has passed the barrier after s_bad_key's
+  // initialisation when any lane holds one: loads happen only when kend > 0, whose loop has one)
+  {
+    int m = bad_key;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = min(m, __shfl_xor(m, o, 64));
+    if (lane == 0 && m != INT_MAX) atomicMin(&s_bad_key, m);
+    __syncthreads();
+  }
+  const int wg_bad_key = s_bad_key;
+  if (wg_bad_key != INT_MAX && threadIdx.x == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
+
   // ---- epilogue: lane (n, q) holds row n of each row tile, dims 16 nb + 4 q + e ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -501,21 +527,23 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     const int r = row0 + 16 * (RT * wave + rt) + n;
     if (r < nrows) {
       const int qi = r / nhg;
-      const int h = g * nhg + (r - qi * nhg);
+      const int h = a.head_of[g * nhg + (r - qi * nhg)];
       const int64_t orow = (static_cast<int64_t>(b) * C + qi) * a.H + h;
       float *dst = p.out + orow * a.d_h + 4 * q;
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      // the row sees keys 0 .. P0 + qi: a bad block among them poisons it
+      const bool poison = seq_bad || wg_bad_key <= P0 + qi;
 #pragma unroll
       for (int nb = 0; nb < 2 * KS; ++nb) {
         f32x4 v = O[rt][nb] * inv;
-        if (seq_bad) v = f32x4{qnan, qnan, qnan, qnan};
+        if (poison) v = f32x4{qnan, qnan, qnan, qnan};
         *reinterpret_cast<f32x4 *>(dst + 16 * nb) = v;
       }
       if (p.lse && q == 0)
-        p.lse[orow] = seq_bad ? qnan : (lt > 0.0f ? (mref[rt] + log2f(lt)) * gvad::kLn2 : -INFINITY);
+        p.lse[orow] = poison ? qnan : (lt > 0.0f ? (mref[rt] + log2f(lt)) * gvad::kLn2 : -INFINITY);
     }
   }
-  if (seq_bad && threadIdx.x == 0 && rb == 0 && g == 0) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+  if (seq_bad && threadIdx.x == 0 && rb == 0 && g == 0) gvad::raise_err(a.err_flag, seq_err);
 }
 
 }  // namespace

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(128 * NH) void k_recon_decode(gva::ReconArgs r) {
   id /= a.G;
   const int s = id % S;
   const int b = id / S;
-  const int h = g * NH + hw;
+  const int h = a.head_of[g * NH + hw];
   const int len = a.seq_len[b];
   const int p = r.q_pos[b];
   const int cap = a.max_blocks << a.log2_bs;
@@ -142,14 +142,16 @@ __global__ __launch_bounds__(128 * NH) void k_recon_decode(gva::ReconArgs r) {
   }
   const int c1 = min(len, c0 + a.chunk);
 
-  // the maps of the group's heads: LDS row (head, k) = Mt[g NH + head][k][0 .. DH)
+  // the maps of the group's heads: LDS row (head, k) = Mt[a.head_of[g NH + head]][k][0 .. DH)
   {
-    const uint16_t *msrc = r.Mt + static_cast<int64_t>(g) * NH * DN * DH;
     for (int c = threadIdx.x; c < NH * DN * (DH / 8); c += kThreads) {
       const int row = c / (DH / 8);
       const int col = (c - row * (DH / 8)) * 8;
+      const int hh = row / DN;
+      const uint16_t *msrc =
+          r.Mt + (static_cast<int64_t>(a.head_of[g * NH + hh]) * DN + (row - hh * DN)) * DH;
       *reinterpret_cast<u32x4 *>(m_lds + row * kStride + col) =
-          *reinterpret_cast<const u32x4 *>(msrc + static_cast<int64_t>(row) * DH + col);
+          *reinterpret_cast<const u32x4 *>(msrc + col);
     }
   }
   if (threadIdx.x == 0) bad_lds = 0;
