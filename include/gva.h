@@ -192,6 +192,26 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
                       int32_t num_splits, int32_t kernel, void *workspace,
                       size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
 
+/* ---- Decode without allocation --------------------------------------------------------------
+ * For callers that cannot allocate device memory or hand in a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Computes exactly what
+ * gva_decode computes for the same arguments (same plan, same kernels, bit-identical results),
+ * with the split partials kept in a static device array of GVA_NOALLOC_SCRATCH_BYTES instead of
+ * a caller workspace. That array is part of the library: each device the library runs on holds
+ * one copy until the process ends; its address is looked up on the first call made with that
+ * device current. The call allocates nothing (no hipMalloc, no allocating library routine).
+ *   Arguments: as for gva_decode, without workspace and workspace_bytes.
+ *   Returns GVA_ERR_WORKSPACE, before any launch, when the plan's partials need more than
+ *   GVA_NOALLOC_SCRATCH_BYTES (gva_decode_workspace_bytes gives the need); nothing in the array
+ *   has to start at zero, so no call clears it.
+ *   All calls on one device share its array: calls that overlap on one device (other streams,
+ *   other threads) race and must be serialised by the caller. */
+#define GVA_NOALLOC_SCRATCH_BYTES (32u << 20)
+gva_status gva_decode_noalloc(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                              const int32_t *seq_len, int32_t max_len, const float *q_abs,
+                              float scale, int32_t num_splits, int32_t kernel, float *out,
+                              float *lse, hipStream_t stream);
+
 /* ---- One decode step ([kvcache] section 1: each step appends the new token's state, then the
  * query reads the whole history; [review] sections 关键技巧一 and 关键技巧二) ------------------
  * For B sequences that each receive one token, does what gva_cache_append (token b to

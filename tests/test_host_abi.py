@@ -14,6 +14,7 @@ from value_only_kv_amd import binding as gb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gva.h")
+HEADERS = [HEADER]
 
 
 @pytest.fixture(scope="module")
@@ -25,9 +26,11 @@ def L():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gva_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gva_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
@@ -381,3 +384,26 @@ def test_group_map_validation(L, gmap, ok):
     if not ok:
         assert _decode(L, d, _cache(d=d)) == gb.GVA_ERR_INVALID_ARG
         assert "g_of_h" in L.gva_last_error().decode()
+
+
+# ---- the allocation-free decode -----------------------------------------------------------
+
+
+def test_noalloc_rejects_a_plan_above_the_static_scratch(L):
+    """A plan whose partials exceed GVA_NOALLOC_SCRATCH_BYTES (32 MiB) is refused before any HIP
+    call, with the need and the limit in the message; bad arguments are refused as gva_decode
+    refuses them."""
+    d = _dims(H=256, G=1, d_h=256, d_n=256, d_r=16)
+    c = _cache(d=d, bs=16, max_blocks=4096, num_blocks=1 << 16)
+    need = gb.gva_decode_workspace_bytes(d, 64, 60000, 1024)
+    assert need > 32 << 20
+    st = L.gva_decode_noalloc(ctypes.byref(d), ctypes.byref(c), 64, A, 60000, A, 0.1, 1024,
+                              gb.GVA_KERNEL_GENERIC, A, None, None)
+    assert st == gb.GVA_ERR_WORKSPACE
+    msg = L.gva_last_error().decode()
+    assert "static scratch" in msg and str(32 << 20) in msg
+    bad = gb.GvaDims(32, 5, 128, 128, 16)
+    assert L.gva_decode_noalloc(ctypes.byref(bad), ctypes.byref(_cache()), 2, A, 100, A, 0.1, 0,
+                                0, A, None, None) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_decode_noalloc(ctypes.byref(_dims()), ctypes.byref(_cache()), 2, A, 100, A + 4,
+                                0.1, 0, 0, A, None, None) == gb.GVA_ERR_INVALID_ARG

@@ -28,7 +28,7 @@ DEVERR_BLOCK, DEVERR_CAPACITY, DEVERR_ROPE, DEVERR_SEQ, DEVERR_LENGTH = 1, 2, 4,
 EXPORTED = [
     "gva_rope_table_bytes", "gva_rope_table_fill", "gva_cache_append", "gva_absorb_query",
     "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
-    "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode",
+    "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode", "gva_decode_noalloc",
     "gva_recon_decode_workspace_bytes", "gva_recon_decode",
     "gva_mla_decode_workspace_bytes", "gva_mla_decode",
     "gva_status_string", "gva_last_error", "gva_version",
@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.gva_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32, P,
                              c_float, c_int32, c_int32, P, c_size_t, P, P, P]
     L.gva_decode.restype = c_int32
+    L.gva_decode_noalloc.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P,
+                                     c_int32, P, c_float, c_int32, c_int32, P, P, P]
+    L.gva_decode_noalloc.restype = c_int32
     L.gva_decode_step.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, P, P, P,
                                   P, P, P, c_int32, c_float, c_int32, c_int32, P, P, c_size_t, P,
                                   P, P]
@@ -209,6 +212,15 @@ def gva_decode(dims: GvaDims, cache: "GvaCache", B: int, seq_len, max_len: int, 
     _check(lib().gva_decode(ctypes.byref(dims), ctypes.byref(cache.struct), B, _ptr(seq_len),
                             max_len, _ptr(q_abs), scale, num_splits, kernel, _ptr(workspace),
                             ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def gva_decode_noalloc(dims: GvaDims, cache: "GvaCache", B: int, seq_len, max_len: int, q_abs,
+                       scale: float, out, lse=None, num_splits: int = 0,
+                       kernel: int = GVA_KERNEL_AUTO, stream=None) -> None:
+    """gva_decode with its partials in the library's static device scratch (no workspace)."""
+    _check(lib().gva_decode_noalloc(ctypes.byref(dims), ctypes.byref(cache.struct), B,
+                                    _ptr(seq_len), max_len, _ptr(q_abs), scale, num_splits,
+                                    kernel, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def gva_decode_step(dims: GvaDims, cache: "GvaCache", B: int, pos, v_new, kr_raw, q_nope, q_rope,

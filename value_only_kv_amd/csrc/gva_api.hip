@@ -4,9 +4,23 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "gva_internal.h"
 
+// Scratch of the allocation-free decode (gva_decode_noalloc): its split partials. Each device
+// that runs the library holds its own copy until the process ends. In host code this name is
+// only a stand-in for the symbol; the device address comes from hipGetSymbolAddress (below).
+static __device__ __align__(256) uint8_t scratch[GVA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// The address of `scratch` on each device, looked up once per device on the first
+// gva_decode_noalloc call made with that device current.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
 
 gva::DecodeArgs cache_args(const gva_dims *d, const gva_cache *c) {
   gva::DecodeArgs a{};
@@ -33,6 +47,29 @@ gva::DecodeArgs cache_args(const gva_dims *d, const gva_cache *c) {
 gva_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return GVA_OK;
   return gva::fail(GVA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Device address of this device's `scratch` (looked up on first use, then cached).
+gva_status device_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return gva::fail(GVA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev,
+                     kMaxDevices);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return gva::fail(GVA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GVA_OK;
 }
 
 // Decode + combine launches for a checked call and its plan.
@@ -104,6 +141,32 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
   if (st != GVA_OK) return st;
   return launch_decode(dims, cache, B, seq_len, max_len, q_abs, scale, plan, use_mfma, workspace,
                        out, lse, stream);
+}
+
+gva_status gva_decode_noalloc(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                              const int32_t *seq_len, int32_t max_len, const float *q_abs,
+                              float scale, int32_t num_splits, int32_t kernel, float *out,
+                              float *lse, hipStream_t stream) {
+  // Validate against a stand-in workspace of unlimited size (never dereferenced), then check
+  // the plan's partials against the static scratch; both before any HIP call.
+  gva::DecodePlan plan{};
+  bool use_mfma = false;
+  void *const stand_in = reinterpret_cast<void *>(uintptr_t{256});
+  gva_status st = gva::check_decode(dims, cache, B, seq_len, max_len, q_abs, scale, num_splits,
+                                    kernel, stand_in, SIZE_MAX, out, &plan, &use_mfma);
+  if (st != GVA_OK) return st;
+  if (plan.ws_bytes > GVA_NOALLOC_SCRATCH_BYTES)
+    return gva::fail(GVA_ERR_WORKSPACE,
+                     "gva_decode_noalloc: this plan needs %zu bytes of partials, above the %zu "
+                     "bytes of static scratch; call gva_decode with a workspace instead",
+                     plan.ws_bytes, static_cast<size_t>(GVA_NOALLOC_SCRATCH_BYTES));
+  void *ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    st = device_scratch(&ws);
+    if (st != GVA_OK) return st;
+  }
+  return launch_decode(dims, cache, B, seq_len, max_len, q_abs, scale, plan, use_mfma, ws, out,
+                       lse, stream);
 }
 
 gva_status gva_decode_step(const gva_dims *dims, const gva_cache *cache, int32_t B,
