@@ -17,7 +17,7 @@ import torch
 from oracle import gva_oracle as O
 from value_only_kv_amd import binding as gb
 from value_only_kv_amd import synth
-from tests.gpu_cases import Case, absorbed_queries, check_output, lse_ok
+from tests.gpu_cases import SENTINEL, Case, absorbed_queries, check_output, lse_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +59,11 @@ def ragged():
     cdims = gb.GvaDims(H, G, d_h, w.d_n, d_r)
     max_pos = int(synth.capacity(w, lens).max()) + 1
     tab_lib = torch.from_numpy(gb.gva_rope_table_fill(max_pos, d_r, w.base)).cuda()
+    # every element starts as a NaN sentinel that no append of finite data can produce
     cache = gb.GvaCache.allocate(cdims, w.dtype, lay.num_blocks, lay.block_size,
                                  torch.from_numpy(lay.block_table).cuda(), tab_lib,
-                                 (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st))
+                                 (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st),
+                                 fill_bits=SENTINEL["bf16"])
     rng = np.random.default_rng(17)
     sampled = sorted({int(np.argmax(lens)), int(np.argmin(lens)),
                       *(int(x) for x in rng.choice(B, 4, replace=False))})
@@ -98,8 +100,9 @@ def ragged():
     gb.gva_cache_append(cdims, cache, B, torch.arange(B, dtype=torch.int32).cuda(),
                         torch.from_numpy(pos).cuda(), v_step, k_step)
     torch.cuda.synchronize()
-    return dict(w=w, lens=lens, cdims=cdims, dims=O.Dims(H, G, d_h, w.d_n, d_r), cache=cache,
-                tab_lib=tab_lib, max_pos=max_pos, sampled=sampled, toks=toks, pos=pos)
+    return dict(w=w, lens=lens, lay=lay, cdims=cdims, dims=O.Dims(H, G, d_h, w.d_n, d_r),
+                cache=cache, tab_lib=tab_lib, max_pos=max_pos, sampled=sampled, toks=toks,
+                pos=pos, v_step=v_step.cpu().numpy(), k_step=k_step.cpu().numpy())
 
 
 def _sequence_values(r, b):
@@ -113,6 +116,59 @@ def _sequence_values(r, b):
                         1, 1 << int(np.ceil(np.log2(n))), np.zeros((1, 1)))
     O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr, tab_ora)
     return O.gather(pool, dims, 0, n)
+
+
+def _device_blocks(cache, lay, ids):
+    """Raw bits (uint16) of whole blocks `ids` of the device pool: V [n, v_sb], kr [n, kr_sb]."""
+    idx = torch.from_numpy(np.asarray(ids, np.int64)).cuda()
+    v = cache.v.view(torch.int16).view(lay.num_blocks, lay.v_sb)[idx]
+    kr = cache.kr.view(torch.int16).view(lay.num_blocks, lay.kr_sb)[idx]
+    torch.cuda.synchronize()
+    return v.cpu().numpy().view(np.uint16), kr.cpu().numpy().view(np.uint16)
+
+
+def test_ragged_batch_full_size_cache_bits(ragged):
+    """The cache append at full size, bit for bit. (1) Every block a sampled sequence owns
+    (its whole history and its step token, and the sentinel in the slots past its end) equals the
+    block the oracle's own append writes from the same tokens into a pool of the same layout.
+    (2) The step token of every one of the 256 sequences, at position len_b in the seeded
+    permutation of the pool, equals the oracle's rounding of that token (rotated at len_b)."""
+    r = ragged
+    w, lay, dims, cache, lens, pos = r["w"], r["lay"], r["dims"], r["cache"], r["lens"], r["pos"]
+    strides = (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st)
+    tab = O.rope_table(r["max_pos"], w.d_r, w.base)
+    for b in r["sampled"]:
+        n = int(lens[b]) + 1
+        nblk = -(-n // lay.block_size)
+        ids = lay.block_table[b, :nblk]
+        pool = O.Pool.empty("bf16", nblk * lay.v_sb, nblk * lay.kr_sb, strides, nblk,
+                            lay.block_size, np.arange(nblk)[None, :], sentinel=SENTINEL["bf16"])
+        v, kr = r["toks"][b]
+        assert O.append(pool, dims, np.zeros(n, np.int64), np.arange(n), v, kr, tab) == 0
+        dv, dk = _device_blocks(cache, lay, ids)
+        assert np.array_equal(dv.reshape(-1), pool.v), f"value blocks of sequence {b}"
+        assert np.array_equal(dk.reshape(-1), pool.kr), f"positional-key blocks of sequence {b}"
+    # the step tokens of all sequences: one block per sequence in the oracle's pool
+    B = w.B
+    table = np.full((B, lay.max_blocks), -1, np.int64)
+    table[np.arange(B), pos // lay.block_size] = np.arange(B)
+    pool = O.Pool.empty("bf16", B * lay.v_sb, B * lay.kr_sb, strides, B, lay.block_size, table,
+                        sentinel=SENTINEL["bf16"])
+    assert O.append(pool, dims, np.arange(B), pos, r["v_step"], r["k_step"], tab) == 0
+    ids = lay.block_table[np.arange(B), pos // lay.block_size]
+    dv, dk = _device_blocks(cache, lay, ids)
+    off = pos % lay.block_size
+    g = np.arange(w.G)[None, :, None]
+    i = np.arange(w.d_h)[None, None, :]
+    vo = g * lay.v_sg + off[:, None, None] * lay.v_st + i                       # [B, G, d_h]
+    ko = off[:, None] * lay.kr_st + np.arange(w.d_r)[None, :]                   # [B, d_r]
+    bsel = np.arange(B)
+    got_v = dv[bsel[:, None, None], vo]
+    want_v = pool.v.reshape(B, lay.v_sb)[bsel[:, None, None], vo]
+    got_k = dk[bsel[:, None], ko]
+    want_k = pool.kr.reshape(B, lay.kr_sb)[bsel[:, None], ko]
+    assert np.array_equal(got_v, want_v) and np.array_equal(got_k, want_k)
+    assert int(cache.err_flag.item()) == 0
 
 
 def test_ragged_batch_full_size_sampled_sequences(ragged):
@@ -193,9 +249,11 @@ def ragged_latent():
     cdims = gb.GvaDims(H, G, d_h, w.d_n, d_r)
     max_pos = int(synth.capacity(w, lens).max()) + 1
     tab_lib = torch.from_numpy(gb.gva_rope_table_fill(max_pos, d_r, w.base)).cuda()
+    # every element starts as a NaN sentinel that no append of finite data can produce
     cache = gb.GvaCache.allocate(cdims, w.dtype, lay.num_blocks, lay.block_size,
                                  torch.from_numpy(lay.block_table).cuda(), tab_lib,
-                                 (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st))
+                                 (lay.v_sb, lay.v_st, lay.v_sg, lay.kr_sb, lay.kr_st),
+                                 fill_bits=SENTINEL["bf16"])
     rng = np.random.default_rng(29)
     sampled = sorted({int(np.argmax(lens)), int(np.argmin(lens)),
                       int(rng.choice(B))})

@@ -7,9 +7,23 @@ import torch
 from oracle import gva_oracle as O
 from value_only_kv_amd import binding as gb
 from value_only_kv_amd import synth
-from tests.gpu_cases import Case, check_output, lse_ok
+from tests.gpu_cases import ERRORS, Case, check_output, lse_ok
 
 pytestmark = pytest.mark.gpu
+
+# The lse of a row depends on its scores only, and moves by at most max_j |error of s_j| (the
+# log-sum-exp is 1-Lipschitz in the largest score error). The scores use the absorbed query as a
+# bf16 hi + lo pair (relative error 2^-16 per element) against exact bf16 keys with float32
+# accumulation, so |error of s_j| <= scale sum_i |q_i| |k_i| (2^-16 + (d_h + d_r) 2^-24): about
+# 2e-4 for unit-normal queries and keys at these widths. The probabilities' bf16 rounding enters
+# only the weighted sum, not the sum of exponentials. The bar is that of the decode, 1e-3.
+LSE_TOL = 1e-3
+
+
+def _lse_check(got, ref, what):
+    ok, e = lse_ok(got, ref, LSE_TOL)
+    ERRORS.append((what + " lse", "bf16", e, 0.0))
+    assert ok, (what, e)
 
 
 def _run_prefill(c, start, C, q_abs, v_new, kr_new):
@@ -60,8 +74,7 @@ def test_prefill_small_against_oracle(shape, starts, C):
     v_bits, kr_bits = c.device_bits()
     assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
     check_output(out, ref, "bf16", f"prefill {shape} starts={starts} C={C}")
-    ok, e = lse_ok(lse, ref_lse, 2e-2)
-    assert ok, e
+    _lse_check(lse, ref_lse, f"prefill {shape} starts={starts} C={C}")
 
 
 def test_prefill_end_to_end_through_absorb():
@@ -112,11 +125,10 @@ def test_prefill_c5_full_size_sampled_rows():
             o, l = O.decode_sequence(V[:L], krc[:L], c.dims, q_abs[b, i].astype(np.float64), w.scale)
             got.append(out[b, i])
             ref.append(o)
-            ok, e = lse_ok(lse[b, i], l, 2e-2)
-            assert ok, (b, i, e)
+            _lse_check(lse[b, i], l, f"C5 seq {b} query {i}")
         check_output(np.array(got), np.array(ref), "bf16", f"C5 seq {b}")
-    v_bits, _ = c.device_bits()
-    assert np.array_equal(v_bits, c.pool.v)
+    v_bits, kr_bits = c.device_bits()
+    assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
 
 
 def test_prefill_bad_start_poisons_rows():
@@ -174,8 +186,7 @@ def test_prefill_corrupt_prefix_block_poisons_the_sequence():
     assert np.array_equal(v_bits, c.pool.v) and np.array_equal(kr_bits, c.pool.kr)
     ref, ref_lse = _oracle_rows(c, 1, int(starts[1]), C, q_abs, 1 << 30)
     check_output(out[1], ref, "bf16", "prefill, other sequence beside a corrupt block")
-    ok, e = lse_ok(lse[1], ref_lse, 2e-2)
-    assert ok, e
+    _lse_check(lse[1], ref_lse, "prefill beside a corrupt block")
 
 
 def test_prefill_corrupt_block_inside_the_chunk_poisons_later_rows_only():
@@ -200,8 +211,7 @@ def test_prefill_corrupt_block_inside_the_chunk_poisons_later_rows_only():
     assert np.all(np.isnan(out[0, n_ok:])) and np.all(np.isnan(lse[0, n_ok:]))
     ref, ref_lse = _oracle_rows(c, 0, int(starts[0]), C, q_abs, 112)
     check_output(out[0, :n_ok], ref, "bf16", "prefill rows before a corrupt chunk block")
-    ok, e = lse_ok(lse[0, :n_ok], ref_lse, 2e-2)
-    assert ok, e
+    _lse_check(lse[0, :n_ok], ref_lse, "prefill before a corrupt chunk block")
     assert np.all(np.isfinite(out[1]))
 
 
