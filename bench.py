@@ -50,6 +50,8 @@ def parse():
                    help="skip the non-absorbable comparator measurement")
     p.add_argument("--no-mla", action="store_true",
                    help="skip the MLA-style latent comparator measurement")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the streaming-read ceiling measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -305,7 +307,11 @@ def main():
                "GB_s": round(mla_bytes / t_mla / 1e9, 1),
                "frac_of_hbm_peak": round(mla_bytes / t_mla / 1e9 / HBM_PEAK_GBS, 4),
                "mla_bytes_over_gva_bytes": round(mla_bytes / read_bytes, 4),
-               "mla_time_over_gva_time": round(t_mla / t_dec, 3)}
+               "mla_time_over_gva_time": round(t_mla / t_dec, 3),
+               # what its bytes alone would take: at the data-sheet peak, and at the GVA
+               # decode's own measured rate (the rate the MLA kernel would need to match)
+               "mla_floor_ms_at_hbm_peak": round(mla_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+               "mla_ms_at_gva_rate": round(mla_bytes / (read_bytes / t_dec) * 1e3, 4)}
         log(f"MLA-style latent comparator decode: {t_mla * 1e3:.3f} ms ({mla_bytes / t_mla / 1e9:.1f} "
             f"GB/s of its {mla_bytes / 1e9:.2f} GB); {t_mla / t_dec:.2f}x the GVA decode's time "
             f"for {mla_bytes / read_bytes:.2f}x its bytes")
@@ -325,7 +331,7 @@ def main():
             o1 = torch.empty((1, wl.H, wl.d_h), device="cuda")
             rb = int(lens_l.sum()) * (wl.G * wl.d_h + wl.d_r) * 2
             per_s = {}
-            for S_l in (64, 128, 256):
+            for S_l in (64, 128, 256, 0):
                 wsb_l = gb.gva_decode_workspace_bytes(reps[0].dims, 1, ml, S_l)
                 ws_l = torch.empty(max(wsb_l, 256) // 4, dtype=torch.float32, device="cuda")
                 for k in range(6):
@@ -343,11 +349,11 @@ def main():
                 torch.cuda.synchronize()
                 ts = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)
                 t_med = ts[len(ts) // 2]
-                per_s[str(S_l)] = {"us": round(t_med * 1e6, 2),
+                per_s[str(S_l) if S_l else "auto"] = {"us": round(t_med * 1e6, 2),
                                    "GB_s": round(rb / t_med / 1e9, 1),
                                    "frac_of_hbm_peak": round(rb / t_med / 1e9 / HBM_PEAK_GBS, 4),
                                    "seq_steps_per_s": round(1.0 / t_med, 1)}
-                log(f"{name} T={ml} S={S_l}: {t_med * 1e6:.1f} us, {rb / t_med / 1e9:.1f} GB/s")
+                log(f"{name} T={ml} S={S_l or 'auto'}: {t_med * 1e6:.1f} us, {rb / t_med / 1e9:.1f} GB/s")
             result_extra[name] = {"T": ml, "d_r": d_r, "cache_bytes": rb,
                                   "replicas_rotated": 3, "by_splits": per_s}
             del reps
@@ -370,6 +376,12 @@ def main():
             bcopy.copy_(a)
         torch.cuda.synchronize()
         log("copy calibration: 1 GiB read + 1 GiB write, 3 launches")
+
+    # ---------------- the streaming-read ceiling ----------------
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = bench_ceiling(torch, gb, stream, read_bytes,
+                                long_bytes=272629760)
 
     # ---------------- CPU oracle on a bounded sample ----------------
     cpu = None
@@ -413,9 +425,59 @@ def main():
         "gqa_comparator": gqa,
         "recon_comparator": recon,
         "mla_comparator": mla,
+        "streaming_ceiling": ceiling,
         "device": dev,
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_ceiling(torch, gb, stream, big_bytes, long_bytes, iters=10):
+    """The rate at which plain 16-byte streaming reads leave HBM (gva_diag_stream_read), at the
+    ragged batch's cache size (one buffer, far above the 256 MB last-level cache) and at the
+    T = 131072 cache size (three buffers rotated, as the long-context decode is timed), over a
+    small sweep of grid sizes and loads in flight; and a plain device copy of 1 GiB (read and
+    write) for reference. Median of HIP-event times on the launch stream."""
+    res = {}
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn(0)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for k, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            fn(k)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)[n // 2]
+
+    for label, nbytes, nbuf in (("ragged_batch_size", big_bytes, 1),
+                                ("long_context_size", long_bytes, 3)):
+        nb = (nbytes + 255) // 256 * 256
+        bufs = [torch.empty(nb // 2, dtype=torch.int16, device="cuda").fill_(k + 1)
+                for k in range(nbuf)]
+        sweep = {}
+        for wg in (1024, 2048, 4096, 8192):
+            for f in (2, 4, 8):
+                t = timed(lambda k: gb.gva_diag_stream_read(bufs[k % nbuf], nb, wg, f, sink,
+                                                            stream=stream), iters)
+                sweep[f"{wg}x{f}"] = round(nb / t / 1e9, 1)
+        best = max(sweep, key=sweep.get)
+        res[label] = {"bytes": nb, "buffers_rotated": nbuf, "best_GB_s": sweep[best],
+                      "best_frac_of_hbm_peak": round(sweep[best] / HBM_PEAK_GBS, 4),
+                      "best_config": best, "GB_s_by_workgroups_x_loads_in_flight": sweep}
+        log(f"streaming ceiling at {nb / 1e9:.3f} GB: {sweep[best]:.1f} GB/s ({best})")
+        del bufs
+        torch.cuda.empty_cache()
+    a = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    t = timed(lambda k: b.copy_(a), iters)
+    res["copy_1GiB"] = {"GB_s_read_plus_write": round(2 * a.numel() * 2 / t / 1e9, 1)}
+    log(f"1 GiB device copy: {2 * a.numel() * 2 / t / 1e9:.1f} GB/s read + write")
+    del a, b
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_prefill(torch, gb, synth, gen, stream, iters=20):
@@ -534,6 +596,28 @@ def bench_small(torch, gb, synth, gen, stream, iters=50):
                                out, lse, workspace=ws, stream=stream)
 
         r = {"workload": desc}
+        if name == "C2":
+            # the decode alone with the cache warm in the 256 MB last-level cache, and with 32
+            # replicas rotated (570 MB) so that each call reads its cache from HBM
+            reps = [dc] + [DeviceCache(w, lens, 100 + k, torch, gb, synth) for k in range(31)]
+            fused()                                      # the absorbed queries the decode reads
+
+            def dec(k):
+                rc = reps[k % len(reps)]
+                gb.gva_decode(rc.dims, rc.cache, B, sl, ml, qa, w.scale, out, lse, workspace=ws,
+                              stream=stream)
+            for label, rot in (("decode_mall_warm_us", False), ("decode_mall_defeated_us", True)):
+                for k in range(5):
+                    dec(k if rot else 0)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(iters)]
+                for k, (e0, e1) in enumerate(evs):
+                    e0.record(stream)
+                    dec(k if rot else 0)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                r[label] = round(sorted(e0.elapsed_time(e1) for e0, e1 in evs)[iters // 2] * 1e3, 1)
+            del reps
         for label, fn in (("three_calls_us", three_calls), ("decode_step_us", fused)):
             for _ in range(5):
                 fn()

@@ -1,5 +1,5 @@
 """The C-ABI library on the host, without a GPU: it loads, exports every entry point that
-include/gva.h declares, rejects bad arguments before any launch, plans splits, and fills a RoPE
+include/gva.h (and the measurement aid in include/gva_diag.h) declares, rejects bad arguments before any launch, plans splits, and fills a RoPE
 table bit-identical to the oracle's. None of these tests launches a kernel."""
 import ctypes
 import os
@@ -14,7 +14,7 @@ from value_only_kv_amd import binding as gb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gva.h")
-HEADERS = [HEADER]
+HEADERS = [HEADER, os.path.join(ROOT, "include", "gva_diag.h")]
 
 
 @pytest.fixture(scope="module")
@@ -407,3 +407,12 @@ def test_noalloc_rejects_a_plan_above_the_static_scratch(L):
                                 0, A, None, None) == gb.GVA_ERR_INVALID_ARG
     assert L.gva_decode_noalloc(ctypes.byref(_dims()), ctypes.byref(_cache()), 2, A, 100, A + 4,
                                 0.1, 0, 0, A, None, None) == gb.GVA_ERR_INVALID_ARG
+
+
+def test_stream_read_rejects_bad_arguments(L):
+    P = ctypes.c_void_p
+    assert L.gva_diag_stream_read(A + 8, 1024, 16, 4, A, None) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_diag_stream_read(A, 1000, 16, 4, A, None) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_diag_stream_read(A, 1024, 0, 4, A, None) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_diag_stream_read(A, 1024, 16, 3, A, None) == gb.GVA_ERR_INVALID_ARG
+    assert L.gva_diag_stream_read(None, 1024, 16, 4, A, None) == gb.GVA_ERR_INVALID_ARG

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libgva.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["gva_api.hip", "k_append_absorb.hip", "k_decode_generic.hip", "k_decode_mfma.hip",
-               "k_prefill.hip", "k_recon.hip", "k_latent.hip"]
+               "k_prefill.hip", "k_recon.hip", "k_latent.hip", "k_diag.hip"]
 HOST_SOURCES = ["gva_host.cpp"]
 
 HIPCC_FLAGS = [

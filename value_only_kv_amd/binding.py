@@ -31,7 +31,7 @@ EXPORTED = [
     "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode", "gva_decode_noalloc",
     "gva_recon_decode_workspace_bytes", "gva_recon_decode",
     "gva_mla_decode_workspace_bytes", "gva_mla_decode",
-    "gva_status_string", "gva_last_error", "gva_version",
+    "gva_status_string", "gva_last_error", "gva_version", "gva_diag_stream_read",
 ]
 
 
@@ -112,6 +112,8 @@ def lib() -> ctypes.CDLL:
     L.gva_mla_decode.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, c_int32,
                                  P, c_float, c_int32, P, c_size_t, P, P, P]
     L.gva_mla_decode.restype = c_int32
+    L.gva_diag_stream_read.argtypes = [P, c_size_t, c_int32, c_int32, P, P]
+    L.gva_diag_stream_read.restype = c_int32
     L.gva_status_string.argtypes = [c_int32]
     L.gva_status_string.restype = c_char_p
     L.gva_last_error.argtypes = []
@@ -282,6 +284,13 @@ def gva_mla_decode(dims: GvaDims, latent: "GvaCache", B: int, seq_len, max_len: 
     _check(lib().gva_mla_decode(ctypes.byref(dims), ctypes.byref(latent.struct), B, _ptr(seq_len),
                                 max_len, _ptr(q_abs), scale, num_splits, _ptr(workspace),
                                 ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def gva_diag_stream_read(src, nbytes: int, work_groups: int, in_flight: int, sink,
+                         stream=None) -> None:
+    """The read-only streaming kernel of gva_diag.h (a measurement aid): reads nbytes at src."""
+    _check(lib().gva_diag_stream_read(_ptr(src), nbytes, work_groups, in_flight, _ptr(sink),
+                                      _stream(stream)))
 
 
 def gva_version() -> str:
