@@ -133,7 +133,7 @@ def main():
     plan = (f"balanced: {R} equal tile ranges over all sequences" if R > 0
             else f"split: {S} chunks per sequence")
     wsb = gb.gva_decode_workspace_bytes(dc.dims, B, max_len, args.splits)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
@@ -229,7 +229,7 @@ def main():
         max_pos_r = max_len + 1
         rope_r = torch.from_numpy(gb.gva_rope_table_fill(max_pos_r, w.d_n, w.base)).cuda()
         wsb_r = gb.gva_recon_decode_workspace_bytes(dc.dims, B, max_len, 0)
-        ws_r = torch.empty(max(wsb_r, 256) // 4, dtype=torch.float32, device="cuda")
+        ws_r = torch.zeros(max(wsb_r, 256) // 4, dtype=torch.float32, device="cuda")
         scale_r = 1.0 / float(np.sqrt(w.d_n))
 
         def recon_call():
@@ -279,7 +279,7 @@ def main():
         out_m = torch.empty((B, H, d_c), device="cuda")
         lse_m = torch.empty((B, H), device="cuda")
         wsb_m = gb.gva_mla_decode_workspace_bytes(mdims, B, max_len, 0)
-        ws_m = torch.empty(max(wsb_m, 256) // 4, dtype=torch.float32, device="cuda")
+        ws_m = torch.zeros(max(wsb_m, 256) // 4, dtype=torch.float32, device="cuda")
         scale_m = 1.0 / float(np.sqrt(d_c + d_r_m))
 
         def mla_call():
@@ -333,7 +333,7 @@ def main():
             per_s = {}
             for S_l in (64, 128, 256, 0):
                 wsb_l = gb.gva_decode_workspace_bytes(reps[0].dims, 1, ml, S_l)
-                ws_l = torch.empty(max(wsb_l, 256) // 4, dtype=torch.float32, device="cuda")
+                ws_l = torch.zeros(max(wsb_l, 256) // 4, dtype=torch.float32, device="cuda")
                 for k in range(6):
                     r = reps[k % 3]
                     gb.gva_decode(r.dims, r.cache, 1, sl, ml, qa, wl.scale, o1, None,
@@ -513,22 +513,25 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
     n_pairs = sum(int(lens[b]) * C + C * (C + 1) // 2 for b in range(B))
     flop = n_pairs * H * (2 * (w.d_h + w.d_r) + 2 * w.d_h)
     tflops = flop / t / 1e12
-    # the decode step that follows: append one token at start + C, decode over start + C + 1
+    # the decode step that follows (gva_decode_step): append one token at start + C, absorb its
+    # query, decode over start + C + 1
     pos = start + C
     sl = pos + 1
-    seq = torch.arange(B, dtype=torch.int32, device="cuda")
     v1 = torch.randn((B, w.G, w.d_h), generator=gen, device="cuda")
     k1 = torch.randn((B, w.d_r), generator=gen, device="cuda")
-    q1 = torch.randn((B, H, row), generator=gen, device="cuda")
+    qn1 = torch.randn((B, H, w.d_n), generator=gen, device="cuda")
+    qr1 = torch.randn((B, H, w.d_r), generator=gen, device="cuda")
+    M1 = torch.randn((H, w.d_h, w.d_n), generator=gen, device="cuda") * w.m_sigma
+    q1 = torch.empty((B, H, row), device="cuda")
     o1 = torch.empty((B, H, w.d_h), device="cuda")
     ml = int(lens.max()) + C + 1
     wsb = gb.gva_decode_workspace_bytes(dc.dims, B, ml, 0)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    launches = gb.gva_decode_step_launches(dc.dims, dc.cache, B, ml, 0)
 
     def step():
-        gb.gva_cache_append(dc.dims, dc.cache, B, seq, pos, v1, k1, stream=stream)
-        gb.gva_decode(dc.dims, dc.cache, B, sl, ml, q1, w.scale, o1, None, workspace=ws,
-                      stream=stream)
+        gb.gva_decode_step(dc.dims, dc.cache, B, pos, v1, k1, qn1, qr1, M1, sl, ml, w.scale, q1,
+                           o1, None, workspace=ws, stream=stream)
 
     for _ in range(3):
         step()
@@ -542,13 +545,15 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
     td = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)[iters // 2]
     dec_bytes = int((lens + C + 1).sum()) * (w.G * w.d_h + w.d_r) * 2
     log(f"C5 prefill: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s "
-        f"({tflops * 1e12 / MFMA_PEAK_BF16:.1%} of bf16 dense peak); mix decode step {td * 1e6:.1f} us")
+        f"({tflops * 1e12 / MFMA_PEAK_BF16:.1%} of bf16 dense peak); mix decode step {td * 1e6:.1f} us "
+        f"({launches} launches)")
     assert torch.isfinite(out).all().item()
     res = {"workload": "4 sequences x (8192 cached + 512 causal queries), H=32, G=8, d_h=d_n=128, "
                        "d_r=16, bf16 cache in 16-token blocks; chunk append included",
            "us": round(t * 1e6, 2), "flop": flop, "TFLOP_s": round(tflops, 1),
            "mfma_util_bf16_dense": round(tflops * 1e12 / MFMA_PEAK_BF16, 4),
            "decode_step_after_us": round(td * 1e6, 2),
+           "decode_step_after_launches": launches,
            "decode_step_after_GB_s": round(dec_bytes / td / 1e9, 1)}
     del dc
     torch.cuda.empty_cache()
@@ -582,7 +587,7 @@ def bench_small(torch, gb, synth, gen, stream, iters=50):
         out = torch.empty((B, H, w.d_h), device="cuda")
         lse = torch.empty((B, H), device="cuda")
         wsb = gb.gva_decode_workspace_bytes(dc.dims, B, ml, 0)
-        ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
 
         def three_calls():
             gb.gva_cache_append(dc.dims, dc.cache, B, seq, pos, v, kr, stream=stream)
@@ -595,7 +600,8 @@ def bench_small(torch, gb, synth, gen, stream, iters=50):
             gb.gva_decode_step(dc.dims, dc.cache, B, pos, v, kr, qn, qr, M, sl, ml, w.scale, qa,
                                out, lse, workspace=ws, stream=stream)
 
-        r = {"workload": desc}
+        r = {"workload": desc,
+             "decode_step_launches": gb.gva_decode_step_launches(dc.dims, dc.cache, B, ml, 0)}
         if name == "C2":
             # the decode alone with the cache warm in the 256 MB last-level cache, and with 32
             # replicas rotated (570 MB) so that each call reads its cache from HBM
@@ -631,7 +637,7 @@ def bench_small(torch, gb, synth, gen, stream, iters=50):
             r[label] = round(sorted(e0.elapsed_time(e1) for e0, e1 in evs)[iters // 2] * 1e3, 1)
         assert torch.isfinite(out).all().item() and int(dc.cache.err_flag.item()) == 0
         log(f"{name} step ({desc}): three calls {r['three_calls_us']} us, "
-            f"gva_decode_step {r['decode_step_us']} us")
+            f"gva_decode_step {r['decode_step_us']} us ({r['decode_step_launches']} launches)")
         res[name] = r
         del dc
         torch.cuda.empty_cache()

@@ -148,8 +148,9 @@ gva_status gva_cache_append(const gva_dims *dims, const gva_cache *cache, int32_
  *   q_abs[k][h][d_h .. d_h + d_r) = float32(rotate(q_rope[k][h][:], q_pos[k]))
  * The q~ part accumulates in float32 (error within d_n * 2^-24 * sum_j |M q|); the rotated
  * part is one rounding of the float64 rotation.
- *   q_nope: device float32 [n_q][H][d_n]. q_rope: device float32 [n_q][H][d_r].
- *   q_pos: device int32 [n_q]. M: device float32 [H][d_h][d_n].
+ *   q_nope: device float32 [n_q][H][d_n], 16-byte aligned (d_n a multiple of 4).
+ *   q_rope: device float32 [n_q][H][d_r], 8-byte aligned. q_pos: device int32 [n_q].
+ *   M: device float32 [H][d_h][d_n], 16-byte aligned.
  *   rope/max_pos: the device RoPE table. q_abs: device float32 [n_q][H][d_h + d_r] (output).
  * A position outside [0, max_pos) writes NaN into that token's q_abs and raises
  * GVA_DEVERR_ROPE in *err_flag (nullable). */
@@ -177,7 +178,11 @@ gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_no
  *   kernel: GVA_KERNEL_* ; the MFMA kernel needs a bf16 cache, d_h % 32 == 0, d_h <= 256,
  *   d_r % 8 == 0, d_r <= 32, H / G <= 16, G <= 16, block_size >= 16, every stride a multiple
  *   of 8 elements (returns GVA_ERR_UNSUPPORTED otherwise).
- *   workspace: device, 256-byte aligned, at least gva_decode_workspace_bytes(...) bytes. */
+ *   workspace: device, 256-byte aligned, at least gva_decode_workspace_bytes(...) bytes,
+ *   zero-filled before its first use (e.g. with hipMemsetAsync once after allocating it). Its
+ *   first 1024 bytes hold the tickets of the one-launch decode step (gva_decode_step); no call
+ *   writes partials there and every call leaves them at zero, so one fill serves every later
+ *   call of any of these entry points. Calls that overlap must not share a workspace. */
 size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
                                   int32_t num_splits);
 /* The split count gva_decode will use for these arguments with per-sequence chunks (an
@@ -216,10 +221,18 @@ gva_status gva_decode_noalloc(const gva_dims *dims, const gva_cache *cache, int3
  * query reads the whole history; [review] sections 关键技巧一 and 关键技巧二) ------------------
  * For B sequences that each receive one token, does what gva_cache_append (token b to
  * sequence b at pos[b]), gva_absorb_query (query b at pos[b], with the cache's RoPE table and
- * err_flag) and gva_decode would do in that order, with the same arithmetic and bit-identical
- * results. The append and the absorption touch disjoint data and run as one launch, so a step
- * takes one launch fewer than the three calls; that is what counts for small batches, whose
- * step is a few microseconds of work.
+ * err_flag) and gva_decode would do in that order. The cache bytes and q_abs are bit-identical
+ * to those of the three calls. Small batches (the matrix-core kernel, d_h of 32 or 64,
+ * H / G of 1, 2, 4 or 8, B G <= 256 sequence-groups, at most 4 MiB of values per group, the
+ * automatic split count) run the whole step as ONE launch: K work-groups per (sequence, group)
+ * each append the token (one of them writes it), absorb the group's queries, decode a share
+ * of the positions (a wave that reads the new position takes the token it has just rounded,
+ * not the cache) and merge their waves' partials; the last of the K to finish merges the K
+ * partials (through the workspace and a ticket in its first 1024 bytes). Its outputs equal
+ * gva_decode's to rounding (the positions are split differently), not bit for bit. Other arguments take one
+ * launch for the append and the absorption, then the decode (and its combine), with outputs
+ * bit-identical to the three calls. gva_decode_step_launches tells which. Within one call the
+ * block that receives sequence b's token must not be read by another sequence.
  *   pos: device int32 [B], the new token's position (its sequence's length before the step).
  *   v_new: device float32 [B][G][d_h]; kr_raw: device float32 [B][d_r].
  *   q_nope: device float32 [B][H][d_n]; q_rope: device float32 [B][H][d_r];
@@ -236,6 +249,11 @@ gva_status gva_decode_step(const gva_dims *dims, const gva_cache *cache, int32_t
                            const int32_t *seq_len, int32_t max_len, float scale,
                            int32_t num_splits, int32_t kernel, float *q_abs, void *workspace,
                            size_t workspace_bytes, float *out, float *lse, hipStream_t stream);
+/* How many launches gva_decode_step makes for these arguments: 1 when the whole step runs as
+ * one launch (above), 2 or 3 otherwise (append and absorption, the decode, and its combine when
+ * the decode splits); 0 on bad arguments. */
+int32_t gva_decode_step_launches(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                                 int32_t max_len, int32_t num_splits, int32_t kernel);
 
 /* ---- Chunked prefill ([summary]: prefill stays a dense, matrix-heavy pass) -----------------
  * Appends chunk_len new tokens per sequence at positions start[b] .. start[b] + chunk_len - 1

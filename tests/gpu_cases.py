@@ -121,7 +121,7 @@ class Case:
         out = torch.full((B, H, self.w.d_h), float("nan"), device=d)
         lse = torch.full((B, H), float("nan"), device=d) if with_lse else None
         wsb = gb.gva_decode_workspace_bytes(self.cdims, B, max_len, num_splits)
-        ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=d) if wsb else None
+        ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device=d) if wsb else None
         gb.gva_decode(self.cdims, self.cache, B, sl, max_len, q, self.w.scale, out, lse,
                       num_splits=num_splits, kernel=kernel, workspace=ws)
         torch.cuda.synchronize()

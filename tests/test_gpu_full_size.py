@@ -184,7 +184,7 @@ def test_ragged_batch_full_size_sampled_sequences(ragged):
     out = torch.full((B, H, d_h), float("nan"), device="cuda")
     lse = torch.full((B, H), float("nan"), device="cuda")
     wsb = gb.gva_decode_workspace_bytes(cdims, B, max_len, 0)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     gb.gva_decode(cdims, cache, B, seq_len, max_len, torch.from_numpy(q_dev).cuda(), w.scale,
                   out, lse, workspace=ws)
     torch.cuda.synchronize()
@@ -218,7 +218,7 @@ def test_recon_comparator_full_size(ragged):
     out = torch.full((B, H, d_h), float("nan"), device="cuda")
     lse = torch.full((B, H), float("nan"), device="cuda")
     wsb = gb.gva_recon_decode_workspace_bytes(cdims, B, max_len, 0)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     scale = 1.0 / float(np.sqrt(w.d_n))
     gb.gva_recon_decode(cdims, cache, B, torch.from_numpy(pos + 1).cuda(), max_len,
                         torch.from_numpy(q).cuda(), torch.from_numpy(pos).cuda(),
@@ -298,7 +298,7 @@ def test_mla_comparator_full_size(ragged_latent):
     out = torch.full((B, H, d_c), float("nan"), device="cuda")
     lse = torch.full((B, H), float("nan"), device="cuda")
     wsb = gb.gva_mla_decode_workspace_bytes(mdims, B, max_len, 0)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     gb.gva_mla_decode(mdims, cache, B, torch.from_numpy(lens.astype(np.int32)).cuda(), max_len,
                       torch.from_numpy(q).cuda(), scale, out, lse, workspace=ws)
     torch.cuda.synchronize()

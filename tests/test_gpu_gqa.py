@@ -35,7 +35,7 @@ def _run(cv, ck, lens, q, max_len=None):
     out = torch.full((w.B, w.H, w.d_h), float("nan"), device="cuda")
     lse = torch.full((w.B, w.H), float("nan"), device="cuda")
     wsb = gb.gva_decode_workspace_bytes(cv.cdims, w.B, max_len, 0)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     gb.gva_gqa_decode(cv.cdims, cv.cache, ck.cache.v, w.B,
                       torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max_len,
                       torch.from_numpy(np.ascontiguousarray(q, np.float32)).cuda(), w.scale, out,

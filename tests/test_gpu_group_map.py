@@ -72,7 +72,7 @@ def test_step_with_group_map():
     out = torch.full((w.B, w.H, w.d_h), float("nan"), device="cuda")
     lse = torch.full((w.B, w.H), float("nan"), device="cuda")
     wsb = gb.gva_decode_workspace_bytes(c.cdims, w.B, ml, 0)
-    ws = torch.empty(max(wsb, 256) // 4, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, device="cuda")
     gb.gva_decode_step(c.cdims, c.cache, w.B, t(pos, np.int32), t(v_new, np.float32),
                        t(kr_raw, np.float32), t(q_nope, np.float32), t(q_rope, np.float32),
                        t(M, np.float32), t(sl, np.int32), ml, w.scale, qa, out, lse, workspace=ws)
@@ -131,7 +131,7 @@ def test_gqa_comparator_with_group_map():
     out = torch.full((w.B, w.H, w.d_h), float("nan"), device="cuda")
     lse = torch.full((w.B, w.H), float("nan"), device="cuda")
     wsb = gb.gva_decode_workspace_bytes(cv.cdims, w.B, ml, 0)
-    ws = torch.empty(max(wsb, 256) // 4, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, device="cuda")
     gb.gva_gqa_decode(cv.cdims, cv.cache, ck.cache.v, w.B,
                       torch.from_numpy(lens.astype(np.int32)).cuda(), ml,
                       torch.from_numpy(q.astype(np.float32)).cuda(), w.scale, out, lse, workspace=ws)
@@ -155,7 +155,7 @@ def test_recon_comparator_with_group_map():
     rope = torch.from_numpy(gb.gva_rope_table_fill(max_pos, w.d_n, w.base)).cuda()
     out = torch.full((w.B, w.H, w.d_h), float("nan"), device="cuda")
     wsb = gb.gva_recon_decode_workspace_bytes(c.cdims, w.B, ml, 0)
-    ws = torch.empty(max(wsb, 256) // 4, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, device="cuda")
     scale = 1.0 / float(np.sqrt(w.d_n))
     gb.gva_recon_decode(c.cdims, c.cache, w.B, torch.from_numpy(lens.astype(np.int32)).cuda(), ml,
                         torch.from_numpy(q.astype(np.float32)).cuda(),

@@ -33,7 +33,7 @@ def _run(c, dims, lens, q_abs, scale, num_splits=0, max_len=None):
     out = torch.full((B, dims.H, dims.d_h), float("nan"), device="cuda")
     lse = torch.full((B, dims.H), float("nan"), device="cuda")
     wsb = gb.gva_mla_decode_workspace_bytes(dims, B, max_len, num_splits)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     gb.gva_mla_decode(dims, c.cache, B, torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
                       max_len, torch.from_numpy(np.ascontiguousarray(q_abs, np.float32)).cuda(),
                       scale, out, lse, num_splits=num_splits, workspace=ws)
@@ -119,7 +119,7 @@ def test_mla_graph_replays():
     q_other = torch.from_numpy(synth.mla_queries(c.w, H, d_c, 64, stream=4)).cuda()
     seq_len = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
     wsb = gb.gva_mla_decode_workspace_bytes(dims, B, max_len, 0)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     out = torch.full((B, H, d_c), float("nan"), device="cuda")
     lse = torch.full((B, H), float("nan"), device="cuda")
 

@@ -21,7 +21,7 @@ def _run(c, q, q_pos, Mt_bits, max_pos, max_len=None, num_splits=0, lens=None):
     out = torch.full((w.B, w.H, w.d_h), float("nan"), device="cuda")
     lse = torch.full((w.B, w.H), float("nan"), device="cuda")
     wsb = gb.gva_recon_decode_workspace_bytes(c.cdims, w.B, max_len, num_splits)
-    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device="cuda")
     gb.gva_recon_decode(c.cdims, c.cache, w.B,
                         torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max_len,
                         torch.from_numpy(np.ascontiguousarray(q, np.float32)).cuda(),

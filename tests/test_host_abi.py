@@ -416,3 +416,36 @@ def test_stream_read_rejects_bad_arguments(L):
     assert L.gva_diag_stream_read(A, 1024, 0, 4, A, None) == gb.GVA_ERR_INVALID_ARG
     assert L.gva_diag_stream_read(A, 1024, 16, 3, A, None) == gb.GVA_ERR_INVALID_ARG
     assert L.gva_diag_stream_read(None, 1024, 16, 4, A, None) == gb.GVA_ERR_INVALID_ARG
+
+
+def test_absorb_requires_aligned_query_rows(L):
+    """q_nope and M are read 16 bytes at a time: a q_nope only 4- or 8-byte aligned is refused
+    before any launch (as are M, q_rope and q_abs off their alignment)."""
+    d = _dims()
+    for qn, qr, m, qa in ((A + 4, A, A, A), (A + 8, A, A, A), (A, A + 4, A, A), (A, A, A + 8, A),
+                          (A, A, A, A + 4)):
+        st = L.gva_absorb_query(ctypes.byref(d), 1, qn, qr, A, m, A, 16, qa, None, None)
+        assert st == gb.GVA_ERR_INVALID_ARG, (qn, qr, m, qa)
+        assert "misaligned" in L.gva_last_error().decode()
+
+
+def test_decode_step_launches_plan(L):
+    """The one-launch step serves small batches of the matrix-core shapes with d_h <= 128, the
+    automatic split count and sequences of at most 4 MiB of values per group."""
+    d = _dims(H=16, G=4, d_h=64, d_n=64)             # the 350M-class layer
+    c = _cache(d=d, max_blocks=4096)
+    n = lambda *a: L.gva_decode_step_launches(ctypes.byref(d), ctypes.byref(c), *a)
+    assert n(8, 4097, 0, 0) == 1                     # B = 8, T = 4096 + 1
+    assert n(64, 4097, 0, 0) == 1                    # 256 sequence-groups
+    assert n(65, 4097, 0, 0) == 3                    # 260: the balanced plan and its combine
+    assert n(8, 4097, 3, 0) == 3                     # an explicit split count
+    assert n(8, 32769, 0, 0) == 3                    # more than 4 MiB of values per group
+    assert n(8, 4097, 0, gb.GVA_KERNEL_GENERIC) == 3
+    assert n(0, 100, 0, 0) == 0 and n(4, 100, 0, 9) == 0
+    d128 = _dims()                                   # d_h = 128: two launches
+    assert L.gva_decode_step_launches(ctypes.byref(d128), ctypes.byref(_cache(max_blocks=2048)),
+                                      4, 8705, 0, 0) == 3
+    c32 = _cache(dtype=gb.GVA_DTYPE_F32, max_blocks=2048)
+    assert L.gva_decode_step_launches(ctypes.byref(d), ctypes.byref(c32), 1, 256, 1, 0) == 2
+    d256 = _dims(H=8, G=2, d_h=256, d_n=256)
+    assert L.gva_decode_step_launches(ctypes.byref(d256), ctypes.byref(_cache(d=d256)), 2, 100, 0, 0) == 3

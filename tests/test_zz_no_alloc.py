@@ -29,7 +29,7 @@ def _both(c, lens, q, num_splits=0, kernel=gb.GVA_KERNEL_AUTO):
                                   num_splits=num_splits, kernel=kernel)
         else:
             wsb = gb.gva_decode_workspace_bytes(c.cdims, B, ml, num_splits)
-            ws = torch.empty(max(wsb, 256) // 4, device="cuda")
+            ws = torch.zeros(max(wsb, 256) // 4, device="cuda")
             gb.gva_decode(c.cdims, c.cache, B, sl, ml, qa, w.scale, out, lse,
                           num_splits=num_splits, kernel=kernel, workspace=ws)
         torch.cuda.synchronize()

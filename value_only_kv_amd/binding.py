@@ -28,7 +28,7 @@ DEVERR_BLOCK, DEVERR_CAPACITY, DEVERR_ROPE, DEVERR_SEQ, DEVERR_LENGTH = 1, 2, 4,
 EXPORTED = [
     "gva_rope_table_bytes", "gva_rope_table_fill", "gva_cache_append", "gva_absorb_query",
     "gva_decode_workspace_bytes", "gva_decode_num_splits", "gva_decode_num_ranges", "gva_decode",
-    "gva_decode_step", "gva_prefill_chunk", "gva_gqa_decode", "gva_decode_noalloc",
+    "gva_decode_step", "gva_decode_step_launches", "gva_prefill_chunk", "gva_gqa_decode", "gva_decode_noalloc",
     "gva_recon_decode_workspace_bytes", "gva_recon_decode",
     "gva_mla_decode_workspace_bytes", "gva_mla_decode",
     "gva_status_string", "gva_last_error", "gva_version", "gva_diag_stream_read",
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.gva_decode_noalloc.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P,
                                      c_int32, P, c_float, c_int32, c_int32, P, P, P]
     L.gva_decode_noalloc.restype = c_int32
+    L.gva_decode_step_launches.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32,
+                                           c_int32, c_int32, c_int32]
+    L.gva_decode_step_launches.restype = c_int32
     L.gva_decode_step.argtypes = [POINTER(GvaDims), POINTER(GvaCacheStruct), c_int32, P, P, P, P,
                                   P, P, P, c_int32, c_float, c_int32, c_int32, P, P, c_size_t, P,
                                   P, P]
@@ -236,6 +239,12 @@ def gva_decode_step(dims: GvaDims, cache: "GvaCache", B: int, pos, v_new, kr_raw
                                  _ptr(seq_len), max_len, scale, num_splits, kernel, _ptr(q_abs),
                                  _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
                                  _stream(stream)))
+
+
+def gva_decode_step_launches(dims: GvaDims, cache: "GvaCache", B: int, max_len: int,
+                             num_splits: int = 0, kernel: int = GVA_KERNEL_AUTO) -> int:
+    return int(lib().gva_decode_step_launches(ctypes.byref(dims), ctypes.byref(cache.struct), B,
+                                              max_len, num_splits, kernel))
 
 
 def gva_prefill_chunk(dims: GvaDims, cache: "GvaCache", B: int, start, max_start: int,

@@ -182,6 +182,50 @@ gva_status gva_decode_step(const gva_dims *dims, const gva_cache *cache, int32_t
   st = gva::check_decode(dims, cache, B, seq_len, max_len, q_abs, scale, num_splits, kernel,
                          workspace, workspace_bytes, out, &plan, &use_mfma);
   if (st != GVA_OK) return st;
+  gva::StepPlan sp{};
+  if (gva::step_fused_supported(dims, cache, B, max_len, num_splits, use_mfma) &&
+      gva::plan_step(dims, B, max_len, &sp)) {
+    // small batch: the whole step in one launch, K work-groups per (sequence, group)
+    if (sp.ws_bytes > 0) {
+      if (!workspace || workspace_bytes < sp.ws_bytes)
+        return gva::fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", sp.ws_bytes,
+                         workspace ? workspace_bytes : (size_t)0);
+      if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return gva::fail(GVA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    gva::StepArgs sa{};
+    sa.a = cache_args(dims, cache);
+    sa.a.B = B;
+    sa.a.seq_len = seq_len;
+    sa.a.max_len = max_len;
+    sa.a.qscale = scale * 1.4426950408889634f;
+    sa.a.out = out;
+    sa.a.lse = lse;
+    sa.pos = pos;
+    sa.v_new = v_new;
+    sa.kr_raw = kr_raw;
+    sa.q_nope = q_nope;
+    sa.q_rope = q_rope;
+    sa.M = M;
+    sa.rope = cache->rope;
+    sa.max_pos = cache->max_pos;
+    sa.d_n = dims->d_n;
+    sa.q_abs = q_abs;
+    sa.K = sp.K;
+    {
+      const int64_t kw = static_cast<int64_t>(sp.K) * gva::step_waves_of(dims->d_h);
+      const int64_t tiles = (static_cast<int64_t>(max_len) + gva::kTilePositions - 1) / gva::kTilePositions;
+      sa.tiles_per_wave = static_cast<int32_t>((tiles + kw - 1) / kw);
+    }
+    if (sp.K > 1) {
+      char *ws = static_cast<char *>(workspace);
+      sa.ticket = reinterpret_cast<int32_t *>(ws);
+      sa.part_o = reinterpret_cast<float *>(ws + sp.off_po);
+      sa.part_m = reinterpret_cast<float *>(ws + sp.off_pm);
+      sa.part_l = reinterpret_cast<float *>(ws + sp.off_pl);
+    }
+    return hip_status(gva::launch_step_fused(sa, stream), "one-launch decode step");
+  }
   hipError_t e = gva::launch_step_prep(cache_args(dims, cache), cache->dtype == GVA_DTYPE_BF16, B,
                                        pos, v_new, kr_raw, cache->rope, cache->max_pos, dims->d_n,
                                        q_nope, q_rope, M, q_abs, stream);

@@ -139,9 +139,10 @@ gva_status check_absorb(const gva_dims *d, int32_t n_q, const float *q_nope, con
   if (!q_nope || !q_rope || !q_pos || !M || !rope || !q_abs)
     return fail(GVA_ERR_INVALID_ARG, "absorb argument is NULL");
   if (max_pos < 1) return fail(GVA_ERR_INVALID_ARG, "max_pos=%d must be >= 1", max_pos);
-  if (!aligned(q_nope, 4) || !aligned(q_rope, 8) || !aligned(M, 16) || !aligned(q_abs, 8) ||
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 8) || !aligned(M, 16) || !aligned(q_abs, 8) ||
       !aligned(rope, 16))
-    return fail(GVA_ERR_INVALID_ARG, "absorb buffers misaligned (M needs 16 bytes)");
+    return fail(GVA_ERR_INVALID_ARG,
+                "absorb buffers misaligned (q_nope and M need 16 bytes, q_rope and q_abs 8)");
   if (d->d_n % 4 != 0) return fail(GVA_ERR_UNSUPPORTED, "absorb needs d_n %% 4 == 0 (d_n=%d)", d->d_n);
   return GVA_OK;
 }
@@ -186,8 +187,8 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
     if (R < 1) R = 1;
     plan->num_ranges = (int32_t)R;
     const size_t rows = (size_t)(R + B) * (size_t)d->H;
-    plan->off_o = 0;
-    plan->off_m = round_up(rows * (size_t)d->d_h * 4, 256);
+    plan->off_o = kWsHeader;
+    plan->off_m = plan->off_o + round_up(rows * (size_t)d->d_h * 4, 256);
     plan->off_l = plan->off_m + round_up(rows * 4, 256);
     plan->off_prefix = plan->off_l + round_up(rows * 4, 256);
     plan->ws_bytes = plan->off_prefix + round_up((size_t)(B + 1) * 4, 256);
@@ -215,8 +216,8 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
   plan->chunk = (int32_t)chunk;
   if (S == 1) return true;
   const size_t rows = (size_t)B * (size_t)S * (size_t)d->H;
-  plan->off_o = 0;
-  plan->off_m = round_up(rows * (size_t)d->d_h * 4, 256);
+  plan->off_o = kWsHeader;
+  plan->off_m = plan->off_o + round_up(rows * (size_t)d->d_h * 4, 256);
   plan->off_l = plan->off_m + round_up(rows * 4, 256);
   plan->ws_bytes = plan->off_l + round_up(rows * 4, 256);
   return true;
@@ -269,6 +270,47 @@ gva_status check_step(const gva_dims *d, const gva_cache *c, int32_t B, const in
   if (!aligned(v_new, 8) || !aligned(kr_raw, 8))
     return fail(GVA_ERR_INVALID_ARG, "v_new and kr_raw must be 8-byte aligned");
   return check_absorb(d, B, q_nope, q_rope, pos, M, c->rope, c->max_pos, q_abs);
+}
+
+bool step_fused_supported(const gva_dims *d, const gva_cache *c, int32_t B, int32_t max_len,
+                          int32_t num_splits, bool use_mfma) {
+  // One work-group per (sequence, group) holds a whole sequence, so the batch must fill at most
+  // one work-group per compute unit and each sequence must be short enough for one unit
+  // (at most 4 MiB of values per group).
+  const int hpg = d->H / d->G;
+  if (!use_mfma || num_splits != 0) return false;
+  // d_h <= 64: every work-group forms its group's q~ itself, reading H / G rows of d_h x d_n
+  // map; at d_h = 128 that redundant read (256 KiB per work-group) costs more than the launches
+  // it saves (a B = 4, 8705-position step: 40 us in one launch against 31 us in two)
+  if (d->d_h != 32 && d->d_h != 64) return false;
+  if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8) return false;
+  if (d->d_n % 4 != 0) return false;
+  if (static_cast<int64_t>(B) * d->G > kPlanCUs) return false;
+  if (static_cast<int64_t>(max_len) * d->d_h * 2 > (int64_t{4} << 20)) return false;
+  (void)c;
+  return true;
+}
+
+bool plan_step(const gva_dims *d, int32_t B, int32_t max_len, StepPlan *plan) {
+  if (!d || B < 1 || max_len < 0 || d->G < 1) return false;
+  *plan = StepPlan{};
+  const int64_t pairs = static_cast<int64_t>(B) * d->G;
+  if (pairs > kPlanCUs) return false;
+  const int64_t waves = step_waves_of(d->d_h);
+  const int64_t tiles = (max_len + kTilePositions - 1) / kTilePositions;
+  int64_t K = kPlanCUs / pairs;
+  const int64_t by_tiles = (tiles + waves - 1) / waves;        // at least one tile per wave
+  if (K > by_tiles) K = by_tiles;
+  if (K > 32) K = 32;
+  if (K < 1) K = 1;
+  plan->K = static_cast<int32_t>(K);
+  if (K == 1) return true;
+  const size_t rows = static_cast<size_t>(pairs * K) * static_cast<size_t>(d->H / d->G);
+  plan->off_po = kWsHeader;
+  plan->off_pm = plan->off_po + round_up(rows * static_cast<size_t>(d->d_h) * 4, 256);
+  plan->off_pl = plan->off_pm + round_up(rows * 4, 256);
+  plan->ws_bytes = plan->off_pl + round_up(rows * 4, 256);
+  return true;
 }
 
 bool recon_supported(const gva_dims *d, const char **why) {
@@ -453,7 +495,11 @@ size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_l
   if (!gva::plan_decode(dims, B, max_len, num_splits, true, &pb)) return 0;
   if (!gva::plan_decode(dims, B, max_len, num_splits, true, &pq, false)) return 0;
   size_t ws = p.ws_bytes > pb.ws_bytes ? p.ws_bytes : pb.ws_bytes;
-  return ws > pq.ws_bytes ? ws : pq.ws_bytes;
+  ws = ws > pq.ws_bytes ? ws : pq.ws_bytes;
+  // the one-launch decode step's partials and tickets
+  gva::StepPlan sp;
+  if (num_splits == 0 && gva::plan_step(dims, B, max_len, &sp) && sp.ws_bytes > ws) ws = sp.ws_bytes;
+  return ws;
 }
 
 size_t gva_recon_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
@@ -482,6 +528,20 @@ int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,
   gva::DecodePlan p;
   if (!gva::plan_decode(dims, B, max_len, num_splits, false, &p)) return 0;
   return p.num_splits;
+}
+
+int32_t gva_decode_step_launches(const gva_dims *dims, const gva_cache *cache, int32_t B,
+                                 int32_t max_len, int32_t num_splits, int32_t kernel) {
+  if (gva::check_dims(dims) != GVA_OK || gva::check_cache(dims, cache) != GVA_OK) return 0;
+  if (B < 1 || max_len < 0 || num_splits < 0 || num_splits > gva::kMaxSplits) return 0;
+  if (kernel < GVA_KERNEL_AUTO || kernel > GVA_KERNEL_MFMA) return 0;
+  const bool can = gva::mfma_supported(dims, cache, nullptr);
+  if (kernel == GVA_KERNEL_MFMA && !can) return 0;
+  const bool use_mfma = kernel == GVA_KERNEL_MFMA || (kernel == GVA_KERNEL_AUTO && can);
+  if (gva::step_fused_supported(dims, cache, B, max_len, num_splits, use_mfma)) return 1;
+  gva::DecodePlan plan;
+  if (!gva::plan_decode(dims, B, max_len, num_splits, use_mfma, &plan)) return 0;
+  return (plan.num_splits > 1 || plan.num_ranges > 0) ? 3 : 2;
 }
 
 int32_t gva_decode_num_ranges(const gva_dims *dims, int32_t B, int32_t max_len) {

@@ -172,6 +172,49 @@ hipError_t launch_step_prep(const DecodeArgs &a, bool bf16, int32_t B, const int
                             const float *v_new, const float *kr_raw, const double *rope,
                             int32_t max_pos, int32_t d_n, const float *q_nope, const float *q_rope,
                             const float *M, float *q_abs, hipStream_t stream);
+// The decode step in one launch (small batches): one work-group per (sequence, value group)
+// appends the sequence's token for its group, forms the absorbed queries of its group's heads,
+// decodes with its waves splitting the positions, and merges their partials itself.
+struct StepArgs {
+  DecodeArgs a;           // cache, shape, seq_len, max_len, qscale, out, lse, head_of
+  const int32_t *pos;     // [B]: position of the new token
+  const float *v_new;     // [B][G][d_h]
+  const float *kr_raw;    // [B][d_r]
+  const float *q_nope;    // [B][H][d_n]
+  const float *q_rope;    // [B][H][d_r]
+  const float *M;         // [H][d_h][d_n]
+  const double *rope;     // [max_pos][d_r / 2][2]
+  int32_t max_pos;
+  int32_t d_n;
+  float *q_abs;           // [B][H][d_h + d_r], written
+  int32_t K;              // work-groups per (sequence, group)
+  int32_t tiles_per_wave; // runs of this many 32-position tiles, cut from max_len
+  float *part_o;          // K > 1: per work-group partials (device scope, write-through)
+  float *part_m;
+  float *part_l;
+  int32_t *ticket;        // K > 1: [B][G], zero between calls
+};
+// Whether the one-launch step serves these arguments: the matrix-core kernel's shapes with
+// d_h of 32 or 64 and H / G of 1, 2, 4 or 8, at most kPlanCUs (sequence, group) pairs, at most
+// 4 MiB of values per group, and the automatic split count.
+bool step_fused_supported(const gva_dims *d, const gva_cache *c, int32_t B, int32_t max_len,
+                          int32_t num_splits, bool use_mfma);
+// Waves per work-group of the one-launch step (two per SIMD, so up to 256 registers each).
+inline int step_waves_of(int d_h) { (void)d_h; return 8; }
+// The first kWsHeader bytes of a decode workspace hold the one-launch step's tickets, one int32
+// per (sequence, group); they must be zero before a workspace's first use, each call leaves them
+// at zero, and no plan writes partials there.
+constexpr size_t kWsHeader = 1024;
+// The one-launch step splits each (sequence, group) over K work-groups (K * B * G <= kPlanCUs,
+// at least one tile per wave); with K > 1 they meet through partials at off_part and the
+// tickets of the header.
+struct StepPlan {
+  int32_t K;
+  size_t off_po, off_pm, off_pl;  // partial o [slot][NH][d_h], m and l [slot][NH]
+  size_t ws_bytes;                // 0 when K == 1 (no workspace touched)
+};
+bool plan_step(const gva_dims *d, int32_t B, int32_t max_len, StepPlan *plan);
+hipError_t launch_step_fused(const StepArgs &s, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);

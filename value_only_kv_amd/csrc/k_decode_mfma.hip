@@ -655,9 +655,563 @@ hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_
              : launch_mode<NH, true, false, kGroupWaves>(a, grid, block, stream);
 }
 
+// ---- the decode step in one launch (small batches) -------------------------------------------
+//
+// K work-groups per (sequence b, value group g), W waves each. In one launch they do what the
+// append, the absorption and the decode of a step do for the group:
+//   1. absorption: q~ of the group's heads with float32 multiply-adds in the same order as
+//      gva_absorb_query (so q_abs is bit-identical), the rows of M staged through LDS with
+//      coalesced loads; the positional slice rotated in float64 at the token's position;
+//   2. append: the token's values for group g (and, in group 0's work-group, its rotated
+//      positional key) rounded once and written to the cache, as gva_cache_append writes them,
+//      and kept in LDS: a wave whose tile holds position pos[b] takes the token from there
+//      instead of the cache, which this launch is writing (every work-group of the sequence
+//      rounds the positional key itself);
+//   3. decode: the K W waves split the sequence's tiles into contiguous chunks and stream them
+//      as the split decode does (scores, online softmax, weighted sum on the matrix cores);
+//   4. merge: each wave leaves its (m, l, o) per head in LDS and the work-group merges them
+//      through their log-sum-exp. With K = 1 that is the output. With K > 1 each work-group
+//      writes its merged partial with device-scope stores (they write through to memory, so no
+//      cache write-back is needed), waits for them to complete, and takes a ticket (a relaxed
+//      device-scope atomic); the work-group that draws the last ticket reads the K partials with
+//      device-scope loads, merges them into the output rows and puts the ticket back to zero.
+// No work-group waits on another, and nothing is left for a second launch. (Ordering the merge
+// with release/acquire fences instead writes back and invalidates whole L2 caches: measured
+// 18 to 270 microseconds per launch here, against under 2 for the write-through pattern.)
+template <int KS>
+constexpr int step_waves() { return 8; }   // gva::step_waves_of(32 KS)
+constexpr int kStepRegionBytes = 144 * 1024;   // staging of M, then tile copies, then the merge
+
+// Loads the tile at t0 of a run ending at c1 as load_tile does, for block-table entries P read
+// at positions clamped to the run's end at max_len instead of c1 (they were fetched before the
+// sequence length was known). A 16-position block that starts at or past c1 was then looked up
+// at a position that may lie in another block: it is not checked, and fix_tile zeroes its data
+// before use, so only blocks holding positions of the run can raise the bad flag.
+template <int KS>
+__device__ __forceinline__ void load_tile_run(const gva::DecodeArgs &a, int32_t pb0, int32_t pb1,
+                                              int t0, int c1, int n, int64_t vlane, int klane,
+                                              Tile<KS, false> &T, bool &bad) {
+  const int mask = (1 << a.log2_bs) - 1;
+  const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
+  const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int32_t pb = tb == 0 ? pb0 : pb1;
+    const bool ok = pb >= 0 && static_cast<int64_t>(pb) < a.num_blocks;
+    bad |= !ok && t0 + 16 * tb < c1;
+    const int64_t blk = ok ? pb : 0;
+    const int f = min(t0 + 16 * tb, c1 - 1);
+    const int rn = min(n, c1 - 1 - f);
+    const int64_t row = static_cast<int64_t>((f & mask) + rn);
+    const uint16_t *vp = vbase + blk * a.v_sb + row * a.v_st + vlane;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = *reinterpret_cast<const u32x4 *>(vp + 32 * ks);
+    T.x[tb][0] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + klane);
+  }
+}
+
+template <int KS, int NH, int W>
+__global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
+  constexpr int DH = 32 * KS;
+  using L = TileLds<KS>;
+  static_assert(W * L::kWave <= kStepRegionBytes, "tile copies exceed the region");
+  static_assert(W * NH * (DH + 2) * 4 <= kStepRegionBytes, "merge area exceeds the region");
+  static_assert(32 * NH * (DH + 2) * 4 <= kStepRegionBytes, "K <= 32 partials exceed the region");
+  __shared__ __align__(16) uint8_t region[kStepRegionBytes];
+  __shared__ __align__(16) float q_lds[NH][DH + 32];     // q~ (DH), then r (d_r <= 32)
+  __shared__ __align__(16) uint16_t tok_v[DH];           // the new token's values, group g
+  __shared__ __align__(16) uint16_t tok_kr[32];          // its rotated positional key (padded)
+  __shared__ int s_bad;
+  __shared__ int s_last;
+  const gva::DecodeArgs &a = s.a;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+  // work-group -> (item, group) with item = (sequence b, part kk of K): items are dealt to the 8
+  // XCDs in turn and the G work-groups of an item take ids 8 apart, so they run on one XCD at
+  // about the same time and its L2 serves the positional keys they all read
+  const int id = blockIdx.x;
+  const int r8 = id >> 3;
+  const int g = r8 % a.G;
+  const int item = (r8 / a.G) * 8 + (id & 7);
+  const int K = s.K;
+  const int b = item / K;
+  const int kk = item - b * K;
+  if (b >= a.B) return;                                  // uniform per work-group
+  if (tid == 0) s_bad = 0;
+  // the group's heads, read once with uniform (scalar) loads; head(c) selects among them (a
+  // per-lane index into the kernel arguments would be a memory round trip at every use)
+  const int gh = g * NH;
+  const int hd0 = a.head_of[gh];
+  const int hd1 = NH > 1 ? a.head_of[gh + 1] : 0;
+  const int hd2 = NH > 2 ? a.head_of[gh + 2] : 0;
+  const int hd3 = NH > 2 ? a.head_of[gh + 3] : 0;
+  const int hd4 = NH > 4 ? a.head_of[gh + 4] : 0;
+  const int hd5 = NH > 4 ? a.head_of[gh + 5] : 0;
+  const int hd6 = NH > 4 ? a.head_of[gh + 6] : 0;
+  const int hd7 = NH > 4 ? a.head_of[gh + 7] : 0;
+  auto head = [&](int c) {
+    const int lo = (c & 1) ? hd1 : hd0;
+    if (NH <= 2) return lo;
+    const int l2 = (c & 2) ? ((c & 1) ? hd3 : hd2) : lo;
+    if (NH <= 4) return l2;
+    const int hi = (c & 2) ? ((c & 1) ? hd7 : hd6) : ((c & 1) ? hd5 : hd4);
+    return (c & 4) ? hi : l2;
+  };
+  const int d_r = a.d_r;
+  const int d_n = s.d_n;
+  const int row_len = DH + d_r;
+  const float qnan = __int_as_float(0x7fc00000);
+  const int p = s.pos[b];
+  const int len = a.seq_len[b];
+  const int cap = a.max_blocks << a.log2_bs;
+
+  // This wave's run: runs of tiles_per_wave tiles are cut from max_len, so the run's first
+  // position, and the block-table entries of its first two tiles, are known before the
+  // sequence's length arrives; the run ends at c1 = min(its end, len).
+  const int c0 = (kk * W + wave) * s.tiles_per_wave * kTile;
+  const int cend = min(c0 + s.tiles_per_wave * kTile, a.max_len);
+  const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  const int lb = a.log2_bs;
+  // the first two tiles' entries, one per 16-position block, as scalar loads: they do not
+  // queue behind the vector loads that stage M
+  int32_t pa0 = 0, pa1 = 0, pb0 = 0, pb1 = 0;
+  if (c0 < cend) {                                       // uniform per wave
+    pa0 = bt[c0 >> lb];
+    pa1 = bt[min(c0 + 16, cend - 1) >> lb];
+    pb0 = bt[min(c0 + kTile, cend - 1) >> lb];
+    pb1 = bt[min(c0 + kTile + 16, cend - 1) >> lb];
+  }
+  int32_t PA = 0, PB = 0;                                // later tiles' entries (vector loads)
+  const bool len_bad = len < 0 || len > a.max_len || len > cap;
+  const bool rope_bad = p < 0 || p >= s.max_pos;         // the absorbed query is NaN
+  // the append's inputs go out now too: the token's block-table entry, its values (one pair per
+  // lane below d_h / 2) and its positional key pairs with their (cos, sin)
+  int32_t aerr = 0;
+  if (p < 0) aerr = GVA_DEVERR_LENGTH;
+  else if (p >= cap) aerr = GVA_DEVERR_CAPACITY;
+  else if (p >= s.max_pos) aerr = GVA_DEVERR_ROPE;
+  const int32_t pblk = aerr ? 0 : bt[p >> lb];
+  const int half_r = d_r >> 1;
+  float2 tok_x = {0.f, 0.f}, tok_k = {0.f, 0.f};
+  double2 tok_cs = {1.0, 0.0};
+  if (!aerr) {
+    if (tid < DH / 2)
+      tok_x = reinterpret_cast<const float2 *>(s.v_new + (static_cast<int64_t>(b) * a.G + g) * DH)[tid];
+    if (tid < half_r) {
+      tok_k = reinterpret_cast<const float2 *>(s.kr_raw + static_cast<int64_t>(b) * d_r)[tid];
+      tok_cs = reinterpret_cast<const double2 *>(s.rope)[static_cast<int64_t>(p) * half_r + tid];
+    }
+  }
+  // and so do the positional query pairs of the group's heads with their (cos, sin) at p
+  // (lane t < NH d_r / 2 rotates pair t % (d_r / 2) of head t / (d_r / 2))
+  float2 rq = {0.f, 0.f};
+  double2 rq_cs = {1.0, 0.0};
+  if (!rope_bad && tid < NH * half_r) {
+    const int c = tid / half_r;
+    const int k = tid - c * half_r;
+    rq = reinterpret_cast<const float2 *>(s.q_rope + (static_cast<int64_t>(b) * a.H + head(c)) * d_r)[k];
+    rq_cs = reinterpret_cast<const double2 *>(s.rope)[static_cast<int64_t>(p) * half_r + k];
+  }
+  const int c1 = len_bad ? c0 : min(cend, len);
+  const int64_t vlane = static_cast<int64_t>(g) * a.v_sg + 8 * q;
+  const int klane = min(8 * q, d_r - 8);
+  bool bad = false;
+  Tile<KS, false> A, Bt;
+  bool tile_a_issued = false;
+  // the run's first tile, issued between the first staging loads and their LDS stores so that
+  // waiting for the staged rows does not wait for it
+  auto issue_tile_a = [&]() {
+    if (c0 < c1) load_tile_run<KS>(a, pa0, pa1, c0, c1, n, vlane, klane, A, bad);
+    if (c0 + kTile < c1) {
+      load_tile_run<KS>(a, pb0, pb1, c0 + kTile, c1, n, vlane, klane, Bt, bad);
+      if (c0 + 2 * kTile < c1) PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
+    }
+    tile_a_issued = true;
+  };
+
+  // ---- 1. absorption (q~ in the order of gva_absorb_query, so q_abs is bit-identical) ----
+  {
+    float *mst = reinterpret_cast<float *>(region);
+    const int d4 = d_n >> 2;
+    const int stride4 = d4 + 1;                          // rows padded by 16 bytes
+    const int qn_off = kStepRegionBytes / 4 - NH * d_n;  // q_nope of the group's heads
+    const int rows_per_pass = qn_off / (4 * stride4);
+    constexpr int kBatch = 8;                            // 16-byte loads in flight per lane
+    for (int o0 = 0; o0 < NH * DH; o0 += rows_per_pass) {
+      const int rows = min(rows_per_pass, NH * DH - o0);
+      // pass 0 also stages q_nope: its float4 follow the rows' in the index space
+      const int n_rows4 = rows * d4;
+      const int n4 = n_rows4 + (o0 == 0 ? NH * d4 : 0);
+      if (o0 > 0) __syncthreads();                       // the previous pass's rows are used
+      for (int e0 = tid; e0 < n4; e0 += kBatch * 64 * W) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e = e0 + u * 64 * W;
+          v[u] = float4{0.f, 0.f, 0.f, 0.f};
+          if (e < n_rows4) {
+            const int rr = e / d4;
+            const int o = o0 + rr;
+            const int c = o / DH;
+            v[u] = reinterpret_cast<const float4 *>(
+                s.M + (static_cast<int64_t>(head(c)) * DH + (o - c * DH)) * d_n)[e - rr * d4];
+          } else if (e < n4) {
+            const int f = e - n_rows4;
+            const int c = f / d4;
+            v[u] = reinterpret_cast<const float4 *>(
+                s.q_nope + (static_cast<int64_t>(b) * a.H + head(c)) * d_n)[f - c * d4];
+          }
+        }
+        if (!tile_a_issued) issue_tile_a();              // uniform
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e = e0 + u * 64 * W;
+          if (e < n_rows4) {
+            const int rr = e / d4;
+            reinterpret_cast<float4 *>(mst)[rr * stride4 + (e - rr * d4)] = v[u];
+          } else if (e < n4) {
+            reinterpret_cast<float4 *>(mst + qn_off)[e - n_rows4] = v[u];
+          }
+        }
+      }
+      __syncthreads();
+      for (int o = o0 + tid; o < o0 + rows; o += 64 * W) {
+        const int c = o / DH;
+        const int i = o - c * DH;
+        const float4 *mr = reinterpret_cast<const float4 *>(mst) + (o - o0) * stride4;
+        const float4 *qr = reinterpret_cast<const float4 *>(mst + qn_off) + c * d4;
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int j4 = 0; j4 < d4; ++j4) {
+          const float4 m4 = mr[j4];
+          const float4 q4 = qr[j4];
+          acc = fmaf(m4.x, q4.x, acc);
+          acc = fmaf(m4.y, q4.y, acc);
+          acc = fmaf(m4.z, q4.z, acc);
+          acc = fmaf(m4.w, q4.w, acc);
+        }
+        const float v = rope_bad ? qnan : acc;
+        q_lds[c][i] = v;
+        if (kk == 0) s.q_abs[(static_cast<int64_t>(b) * a.H + head(c)) * row_len + i] = v;
+      }
+    }
+    if (!tile_a_issued) issue_tile_a();
+    if (tid < NH * half_r) {                             // NH d_r / 2 <= 128 < 64 W
+      const int c = tid / half_r;
+      const int k = tid - c * half_r;
+      const int h = head(c);
+      float y0f = qnan, y1f = qnan;
+      if (!rope_bad) {
+        double y0, y1;
+        gvad::rotate_pair_f64(static_cast<double>(rq.x), static_cast<double>(rq.y), rq_cs.x, rq_cs.y,
+                              &y0, &y1);
+        y0f = gvad::f64_to_f32(y0);
+        y1f = gvad::f64_to_f32(y1);
+      }
+      q_lds[c][DH + 2 * k] = y0f;
+      q_lds[c][DH + 2 * k + 1] = y1f;
+      if (kk == 0) {
+        float *dst = s.q_abs + (static_cast<int64_t>(b) * a.H + h) * row_len + DH + 2 * k;
+        dst[0] = y0f;
+        dst[1] = y1f;
+      }
+    }
+  }
+
+  // ---- 2. append (the checks and arithmetic of gva_cache_append) ----
+  int64_t blk = -1;
+  if (!aerr) {
+    if (pblk < 0 || static_cast<int64_t>(pblk) >= a.num_blocks) aerr = GVA_DEVERR_BLOCK;
+    else blk = pblk;
+  }
+  const bool tok_ok = aerr == 0;
+  if (g == 0 && kk == 0 && tid == 0) {
+    if (aerr) gvad::raise_err(a.err_flag, aerr);
+    if (rope_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_ROPE);
+    if (len_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+  }
+  if (tok_ok) {
+    const int64_t off = p & ((1 << a.log2_bs) - 1);
+    uint32_t *v32 = reinterpret_cast<uint32_t *>(const_cast<void *>(a.v));
+    if (tid < DH / 2) {                                  // 64 W > DH / 2
+      const uint32_t w = gvad::f64_to_bf16_bits(static_cast<double>(tok_x.x)) |
+                         (static_cast<uint32_t>(gvad::f64_to_bf16_bits(static_cast<double>(tok_x.y))) << 16);
+      if (kk == 0) v32[(blk * a.v_sb + off * a.v_st + static_cast<int64_t>(g) * a.v_sg + 2 * tid) >> 1] = w;
+      reinterpret_cast<uint32_t *>(tok_v)[tid] = w;
+    }
+    uint32_t *k32 = reinterpret_cast<uint32_t *>(const_cast<void *>(a.kr));
+    if (tid < 16) {
+      uint32_t w = 0;
+      if (tid < half_r) {
+        double y0, y1;
+        gvad::rotate_pair_f64(static_cast<double>(tok_k.x), static_cast<double>(tok_k.y), tok_cs.x,
+                              tok_cs.y, &y0, &y1);
+        w = gvad::f64_to_bf16_bits(y0) | (static_cast<uint32_t>(gvad::f64_to_bf16_bits(y1)) << 16);
+        if (g == 0 && kk == 0) k32[(blk * a.kr_sb + off * a.kr_st + 2 * tid) >> 1] = w;
+      }
+      reinterpret_cast<uint32_t *>(tok_kr)[tid] = w;
+    }
+  }
+  __syncthreads();                                       // q~, r and the token are in LDS
+
+  // ---- 3. decode the wave's run of tiles ----
+  constexpr int SH = NH;
+  const int c = n < NH ? n : n - NH;                     // the query column's head
+  const bool col_ok = n < 2 * NH;
+  const bool use_lo = n >= NH;
+  const bool owner = n >= NH && n < 2 * NH;
+  Acc<KS> acc;
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i) acc.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc.m = -INFINITY;
+  acc.lsum = 0.0f;
+  if (c0 < c1) {                                         // uniform per wave
+    bf16x8 QX[KS], QY[KS], RX, RY;
+    const float *qp = q_lds[col_ok ? c : 0];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
+      const float4 x0 = *reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q);
+      const float4 x1 = *reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q + 4);
+      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = col_ok ? x[e] * a.qscale : 0.0f;
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      QX[ks] = as_bf16(use_lo ? lo : hi);
+      QY[ks] = as_bf16(lo);
+    }
+    {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * q + e;
+        x[e] = (col_ok && i < d_r) ? qp[DH + i] * a.qscale : 0.0f;
+      }
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      RX = as_bf16(use_lo ? lo : hi);
+      RY = as_bf16(lo);
+    }
+    uint8_t *lw_wr = region + wave * L::kWave + n * L::kRow + 16 * q;
+    const uint8_t *lw_rd = region + wave * L::kWave + (lane >> 2) * L::kRow + 8 * (lane & 3);
+    const u32x4 *tv = reinterpret_cast<const u32x4 *>(tok_v + 8 * q);
+    const u32x4 tk = *reinterpret_cast<const u32x4 *>(tok_kr + klane);
+    // Before a tile is used: the lanes that read position p take the new token from LDS (this
+    // launch is writing it to the cache), and a block lying wholly past c1 is zeroed (it may
+    // have been read from another block; its scores are masked, and its values must be finite).
+    auto fix_tile = [&](Tile<KS, false> &T, int t0) {
+      if (t0 + kTile > c1) {                             // the run's last tile; uniform
+        const bool past = t0 + 16 >= c1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) T.v[1][ks] = past ? u32x4{0u, 0u, 0u, 0u} : T.v[1][ks];
+        T.x[1][0] = past ? u32x4{0u, 0u, 0u, 0u} : T.x[1][0];
+      }
+      if (!tok_ok || p < t0 || p >= t0 + kTile) return;  // uniform
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int f = min(t0 + 16 * tb, c1 - 1);
+        const bool at_p = t0 + 16 * tb < c1 && f + min(n, c1 - 1 - f) == p;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = at_p ? tv[4 * ks] : T.v[tb][ks];
+        T.x[tb][0] = at_p ? tk : T.x[tb][0];
+      }
+    };
+    // two tile buffers in ping-pong, the first two tiles already in flight; nothing is loaded
+    // past c1 (the page entries of a tile go out with the data of the tile before it)
+    int t0 = c0;
+    bool first = true;
+    while (true) {
+      const int t1 = t0 + kTile;
+      if (!first && t1 < c1) {                           // uniform
+        load_tile_run<KS>(a, __builtin_amdgcn_readlane(PB, 0), __builtin_amdgcn_readlane(PB, 1), t1,
+                          c1, n, vlane, klane, Bt, bad);
+        if (t1 + kTile < c1) PA = load_pages(bt, lb, t1 + kTile, c1, lane);
+      }
+      first = false;
+      fix_tile(A, t0);
+      tile_step<KS, NH, false, false>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc, nullptr);
+      if (t1 >= c1) break;
+      const int t2 = t1 + kTile;
+      if (t2 < c1) {
+        load_tile_run<KS>(a, __builtin_amdgcn_readlane(PA, 0), __builtin_amdgcn_readlane(PA, 1), t2,
+                          c1, n, vlane, klane, A, bad);
+        if (t2 + kTile < c1) PB = load_pages(bt, lb, t2 + kTile, c1, lane);
+      }
+      fix_tile(Bt, t1);
+      tile_step<KS, NH, false, false>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc, nullptr);
+      if (t2 >= c1) break;
+      t0 = t2;
+    }
+  }
+
+  // ---- 4. merge the waves' partials in LDS ----
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc.O[i][r] += row_shr_f<SH>(acc.O[i][r]);
+  float ltot = acc.lsum + __shfl_xor(acc.lsum, 16, 64);
+  ltot += __shfl_xor(ltot, 32, 64);
+  if (__any(bad) && lane == 0) {
+    s_bad = 1;
+    gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
+  }
+  __syncthreads();                                       // every wave is done with its tile copy
+  float *pm = reinterpret_cast<float *>(region);         // [W][NH]
+  float *pl = pm + W * NH;                               // [W][NH]
+  float *po = pl + W * NH;                               // [W][NH][DH]
+  if (owner) {
+#pragma unroll
+    for (int nb = 0; nb < 2 * KS; ++nb)
+      *reinterpret_cast<f32x4 *>(po + (wave * NH + c) * DH + 16 * nb + 4 * q) = acc.O[nb];
+    if (q == 0) {
+      pm[wave * NH + c] = acc.m;
+      pl[wave * NH + c] = ltot;
+    }
+  }
+  __syncthreads();
+  // a NaN query (a position outside the RoPE table) or a NaN partial makes the row NaN, as in
+  // the separate calls
+  const bool poison = len_bad || rope_bad || s_bad != 0;
+  for (int o = tid; o < NH * DH; o += 64 * W) {
+    const int ch = o / DH;
+    const int d = o - ch * DH;
+    float ms = -INFINITY;
+    bool nan_in = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      ms = fmaxf(ms, pm[w * NH + ch]);
+      nan_in = nan_in || pl[w * NH + ch] != pl[w * NH + ch];
+    }
+    float lt = 0.0f, ov = 0.0f;
+    if (ms != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float f = __builtin_amdgcn_exp2f(pm[w * NH + ch] - ms);
+        lt += pl[w * NH + ch] * f;
+        ov += po[(w * NH + ch) * DH + d] * f;
+      }
+    }
+    const bool nan_row = poison || nan_in;
+    if (K == 1) {
+      const int64_t orow = static_cast<int64_t>(b) * a.H + head(ch);
+      a.out[orow * DH + d] = nan_row ? qnan : (lt > 0.0f ? ov / lt : 0.0f);
+      if (d == 0 && a.lse)
+        a.lse[orow] = nan_row ? qnan : (lt > 0.0f ? (ms + log2f(lt)) * gvad::kLn2 : -INFINITY);
+    } else {
+      // this work-group's partial: unnormalised o, m (NaN when poisoned) and l
+      const int64_t prow = (static_cast<int64_t>(b * a.G + g) * K + kk) * NH + ch;
+      __hip_atomic_store(s.part_o + prow * DH + d, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(s.part_m + prow, nan_row ? qnan : ms, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(s.part_l + prow, lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (K == 1) return;
+  // every lane's partial stores have completed at device scope before the ticket is taken
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t *ticket = s.ticket + b * a.G + g;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K - 1;
+  __syncthreads();
+  if (!s_last) return;                                   // uniform per work-group
+  // the last work-group merges the K partials of (b, g): one round of device-scope loads stages
+  // them in LDS (rows prow0 .. prow0 + K NH - 1 are contiguous), then the merge reads LDS
+  const int64_t prow0 = static_cast<int64_t>(b * a.G + g) * K * NH;
+  float *gm = reinterpret_cast<float *>(region);         // [K][NH]
+  float *gl = gm + K * NH;                               // [K][NH]
+  float *go = gl + K * NH;                               // [K][NH][DH]
+  {
+    // buffer loads with the device-scope cache policy (sc1): they read past this XCD's L2 like
+    // the atomic loads would, but several can be in flight; the ranges end at this pair's rows
+    constexpr int kSc1 = 16;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        s.part_o + prow0 * DH, 0, static_cast<int>(K * NH * DH * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        s.part_m + prow0, 0, static_cast<int>(K * NH * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        s.part_l + prow0, 0, static_cast<int>(K * NH * 4), 0x00020000);
+    // K NH <= 256 < 64 W: one m and one l per thread, issued before the o rows
+    const bool has_ml = tid < K * NH;
+    uint32_t mv = 0, lv = 0;
+    if (has_ml) {
+      mv = __builtin_amdgcn_raw_buffer_load_b32(rm, 4 * tid, 0, kSc1);
+      lv = __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * tid, 0, kSc1);
+    }
+    const int n4 = K * NH * DH / 4;
+#pragma unroll 4
+    for (int e = tid; e < n4; e += 64 * W)
+      reinterpret_cast<u32x4 *>(go)[e] = __builtin_amdgcn_raw_buffer_load_b128(ro, 16 * e, 0, kSc1);
+    if (has_ml) {
+      gm[tid] = __uint_as_float(mv);
+      gl[tid] = __uint_as_float(lv);
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < NH * DH; o += 64 * W) {
+    const int ch = o / DH;
+    const int d = o - ch * DH;
+    float ms = -INFINITY;
+    bool nan_in = false;
+    for (int k = 0; k < K; ++k) {
+      const float mk = gm[k * NH + ch];
+      nan_in = nan_in || mk != mk;
+      ms = fmaxf(ms, mk);
+    }
+    float lt = 0.0f, ov = 0.0f;
+    if (ms != -INFINITY && !nan_in) {
+      for (int k = 0; k < K; ++k) {
+        const float f = __builtin_amdgcn_exp2f(gm[k * NH + ch] - ms);
+        lt += gl[k * NH + ch] * f;
+        ov += go[(k * NH + ch) * DH + d] * f;
+      }
+    }
+    const int64_t orow = static_cast<int64_t>(b) * a.H + head(ch);
+    a.out[orow * DH + d] = nan_in ? qnan : (lt > 0.0f ? ov / lt : 0.0f);
+    if (d == 0 && a.lse)
+      a.lse[orow] = nan_in ? qnan : (lt > 0.0f ? (ms + log2f(lt)) * gvad::kLn2 : -INFINITY);
+  }
+  if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int KS, int NH>
+hipError_t launch_step_ks(const gva::StepArgs &s, hipStream_t stream) {
+  constexpr int W = step_waves<KS>();
+  const int64_t items = static_cast<int64_t>(s.a.B) * s.K;
+  const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8 * s.a.G));
+  hipLaunchKernelGGL((k_step_fused<KS, NH, W>), grid, dim3(64 * W), 0, stream, s);
+  return hipGetLastError();
+}
+
+template <int NH>
+hipError_t launch_step_nh(const gva::StepArgs &s, hipStream_t stream) {
+  switch (s.a.d_h / 32) {
+    case 1: return launch_step_ks<1, NH>(s, stream);
+    case 2: return launch_step_ks<2, NH>(s, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 namespace gva {
+
+hipError_t launch_step_fused(const StepArgs &s, hipStream_t stream) {
+  switch (s.a.H / s.a.G) {
+    case 1: return launch_step_nh<1>(s, stream);
+    case 2: return launch_step_nh<2>(s, stream);
+    case 4: return launch_step_nh<4>(s, stream);
+    case 8: return launch_step_nh<8>(s, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
   // the GVA balanced plan's layout (as plan_decode chose it), else four-wave work-groups
