@@ -158,7 +158,8 @@ struct DecodeArgs {
   int32_t *work_next;   // latent comparator: the work queue's counter (zeroed before the launch)
   // Heads in group order: slot g * (H / G) + c holds the c-th head (in ascending order) of value
   // group g, so a kernel that serves group g reads the heads of slots g * (H / G) ...
-  uint8_t head_of[kMaxH];
+  // (whole-word aligned, so a kernel can read a group's slots as aligned 32-bit words).
+  alignas(4) uint8_t head_of[kMaxH];
 };
 
 hipError_t launch_append(const gva_dims *d, const gva_cache *c, int32_t B, int32_t n_tok,

@@ -313,6 +313,34 @@ constexpr int min_waves_per_simd() {
   return WAVES == 8 ? 2 : !GQA && (KS <= 2 || (KS == 4 && NH > 0)) ? 3 : 2;
 }
 
+// The head in slot h0 + c of a.head_of, for a group of NH slots (1, 2, 4 or 8) starting at h0,
+// a multiple of NH the whole wave agrees on. The slots are read as aligned 32-bit words with a
+// uniform index, which compiles to scalar loads (a byte load from the kernel arguments, or a
+// per-lane index, is a vector memory round trip), and the lane's byte is shifted out.
+template <int NH>
+__device__ __forceinline__ int slot_head(const gva::DecodeArgs &a, int h0, int c) {
+  static_assert(NH == 1 || NH == 2 || NH == 4 || NH == 8, "slot_head: NH");
+  const uint32_t *w = reinterpret_cast<const uint32_t *>(a.head_of) + (h0 >> 2);
+  uint32_t word = w[0];
+  if (NH == 8) word = (c & 4) ? w[1] : word;
+  return static_cast<int>((word >> (8 * ((h0 & 3) + (c & 3)))) & 0xffu);
+}
+
+// The head of this lane's query column in group g: column n of the merged hi/lo layout reads
+// slot g (H / G) + c, c = n mod NH (lanes past the columns read slot c = 0). With NH = 0 (more
+// heads per group than merged columns) column n reads slot g (H / G) + n, a per-lane index.
+template <int NH>
+__device__ __forceinline__ int lane_head(const gva::DecodeArgs &a, int g, int n) {
+  const int nhg = a.H / a.G;
+  const int h0 = g * nhg;
+  if constexpr (NH == 0) {
+    return a.head_of[h0 + (n < nhg ? n : 0)];
+  } else {
+    const int c = n < NH ? n : (n < 2 * NH ? n - NH : 0);
+    return slot_head<NH>(a, h0, c);
+  }
+}
+
 // One chunk of positions [c0, c1) of sequence b for value group g (one wave): scores, online
 // softmax and weighted sum over its tiles, then the partial (m, l, o) of each of the group's heads
 // h at workspace row prow0 + h or, when `direct`, the final output row. len_bad makes the output
@@ -327,11 +355,9 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
   const int n = lane & 15;
   const int q = lane >> 4;
   const int nhg = a.H / a.G;
-  const int h0 = g * nhg;                  // the group's first slot in a.head_of
-  // the query column of this lane: head c (hi or, with merged columns, lo part)
-  const int c = NH > 0 ? (n < NH ? n : n - NH) : n;
   const bool col_ok = NH > 0 ? (n < 2 * NH) : (n < nhg);
   const bool use_lo = NH > 0 && n >= NH;
+  const int head_lane = lane_head<NH>(a, __builtin_amdgcn_readfirstlane(g), n);
   // the lanes that own a head's softmax state and output
   const bool owner = NH > 0 ? (n >= NH && n < 2 * NH) : (n < nhg);
   const int row_len = a.d_h + a.d_r;
@@ -346,18 +372,38 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
 
   if (c0 < c1) {
     // ---- query operands (B layout: column n, K group q) ----
+    // Every lane loads (lanes without a column read their group's first head; d_r is a
+    // multiple of 8, so a lane's eight positional elements are all inside the row or all past
+    // it, and the latter re-read the last eight) and masks with a bitwise and: a select on a
+    // loaded value is compiled as a branch around the load with a wait inside, which would
+    // serialise the query loads.
     bf16x8 QX[KS], QY[KS], RX, RY;
-    const float *qp =
-        a.q_abs + (static_cast<int64_t>(b) * a.H + a.head_of[h0 + (col_ok ? c : 0)]) * row_len;
+    const float *qp = a.q_abs + (static_cast<int64_t>(b) * a.H + head_lane) * row_len;
+    const int col_mask = col_ok ? -1 : 0;
+    float4 qraw[2 * KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      float x[8];
       const float4 *src = reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q);
-      const float4 x0 = src[0], x1 = src[1];
-      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+      qraw[2 * ks] = src[0];
+      qraw[2 * ks + 1] = src[1];
+    }
+    const float4 *rsrc = reinterpret_cast<const float4 *>(qp + a.d_h + 8 * min(q, (a.d_r >> 3) - 1));
+    const float4 r0 = rsrc[0], r1 = rsrc[1];
+    const float rraw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    const int r_mask = 8 * q < a.d_r ? col_mask : 0;
+    // the first two tiles' block-table entries go out behind the query rows: the split below
+    // waits for the query only (loads complete in order), so their round trips overlap
+    const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+    const int lb = a.log2_bs;
+    int32_t PA = load_pages(bt, lb, c0, c1, lane);
+    int32_t PB = load_pages(bt, lb, c0 + kTile, c1, lane);
+    auto masked = [](float v, int m) { return __int_as_float(__float_as_int(v) & m); };
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = col_ok ? x[e] * a.qscale : 0.0f;
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 x0 = qraw[2 * ks], x1 = qraw[2 * ks + 1];
+      float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = masked(x[e], col_mask) * a.qscale;
       u32x4 hi, lo;
       split8(x, hi, lo);
       QX[ks] = as_bf16(use_lo ? lo : hi);
@@ -366,10 +412,7 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
     {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 8 * q + e;
-        x[e] = (col_ok && i < a.d_r) ? qp[a.d_h + i] * a.qscale : 0.0f;
-      }
+      for (int e = 0; e < 8; ++e) x[e] = masked(rraw[e], r_mask) * a.qscale;
       u32x4 hi, lo;
       split8(x, hi, lo);
       RX = as_bf16(use_lo ? lo : hi);
@@ -391,8 +434,6 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
     // the next tile, then the page entries two tiles ahead, then the math of the current tile.
     // (A third buffer, tried for grids of at most two work-groups per CU, gained nothing: the
     // loop runs near the streaming rate already.)
-    const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
-    const int lb = a.log2_bs;
     // SHARE: wave 0 fetches each tile's positional key and stores it in the work-group's key
     // buffer (two tiles, 2 KB each: block tb, lane l at 1024 tb + 16 l); one barrier per tile
     // publishes it. The buffer of tile t + 1 is written after tile t's step and after every
@@ -411,8 +452,6 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
       }
     };
     Tile<KS, GQA> A, Bt;
-    int32_t PA = load_pages(bt, lb, c0, c1, lane);
-    int32_t PB = load_pages(bt, lb, c0 + kTile, c1, lane);
     load_tile<KS, GQA, SHARE>(a, PA, c0, c1, n, vlane, klane, A, bad, fetch_key, kown);
     PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
     publish(kb0, A);
@@ -448,7 +487,7 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
   // empty chunks (past the end of a sequence, or of a sequence with a bad length) are never
   // read by the combine
   if (!direct && c0 >= c1) return;
-  const int h = a.head_of[h0 + c];
+  const int h = head_lane;                 // the owner lane's column is its head's
   if (direct) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h + 4 * q;
@@ -618,7 +657,8 @@ k_decode_mfma(gva::DecodeArgs a) {
     const int len = len_of(b);
     const int c0 = static_cast<int>(t - pb) * kTile;
     const int c1 = min(static_cast<int>(seg_end - pb) * kTile, len);
-    run_chunk<KS, NH, GQA, SHARE>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H, lds, kbuf);
+    run_chunk<KS, NH, GQA, SHARE>(a, b, g, c0, c1, false, false, static_cast<int64_t>(item + b) * a.H,
+                                  lds, kbuf);
     t = seg_end;
     pb += tiles_b;
     ++b;
@@ -741,25 +781,9 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   const int kk = item - b * K;
   if (b >= a.B) return;                                  // uniform per work-group
   if (tid == 0) s_bad = 0;
-  // the group's heads, read once with uniform (scalar) loads; head(c) selects among them (a
-  // per-lane index into the kernel arguments would be a memory round trip at every use)
-  const int gh = g * NH;
-  const int hd0 = a.head_of[gh];
-  const int hd1 = NH > 1 ? a.head_of[gh + 1] : 0;
-  const int hd2 = NH > 2 ? a.head_of[gh + 2] : 0;
-  const int hd3 = NH > 2 ? a.head_of[gh + 3] : 0;
-  const int hd4 = NH > 4 ? a.head_of[gh + 4] : 0;
-  const int hd5 = NH > 4 ? a.head_of[gh + 5] : 0;
-  const int hd6 = NH > 4 ? a.head_of[gh + 6] : 0;
-  const int hd7 = NH > 4 ? a.head_of[gh + 7] : 0;
-  auto head = [&](int c) {
-    const int lo = (c & 1) ? hd1 : hd0;
-    if (NH <= 2) return lo;
-    const int l2 = (c & 2) ? ((c & 1) ? hd3 : hd2) : lo;
-    if (NH <= 4) return l2;
-    const int hi = (c & 2) ? ((c & 1) ? hd7 : hd6) : ((c & 1) ? hd5 : hd4);
-    return (c & 4) ? hi : l2;
-  };
+  // the group's heads: slot_head reads the group's slots with uniform (scalar) loads
+  const int gh = __builtin_amdgcn_readfirstlane(g * NH);
+  auto head = [&](int c) { return slot_head<NH>(a, gh, c); };
   const int d_r = a.d_r;
   const int d_n = s.d_n;
   const int row_len = DH + d_r;
