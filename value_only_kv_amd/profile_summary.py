@@ -48,20 +48,38 @@ def sources_sha256(paths=DECODE_SOURCES) -> str:
 
 
 def _short(name: str) -> str:
-    n = name.split("(gva::")[0].split("(int")[0]
-    n = n.replace("void ", "").replace("(anonymous namespace)::", "")
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):               # drop the parameter list (the first "(" outside <>)
+        depth += (ch == "<") - (ch == ">")
+        if ch == "(" and depth == 0:
+            n = n[:i]
+            break
     if n.startswith(("at::", "__amd")):
         n = "(input generation) " + n.split("<")[0]
     return n
 
 
-def stats(trace_csv: str, cmd: str, note: str = "") -> str:
+def stats(trace_csv: str, cmd: str, note: str = "", splits=(), only=()) -> str:
+    """splits: "NAME:US" entries; the launches of a kernel whose name contains NAME are reported
+    in two rows, below and at or above US microseconds (one grid run on two workload sizes).
+    only: report just the kernels whose names contain one of these strings."""
+    cut = {}
+    for sp in splits:
+        name, us = sp.rsplit(":", 1)
+        cut[name] = float(us) * 1e3
     agg = collections.defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
+        if only and not any(o in r["Kernel_Name"] for o in only):
+            continue
         grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
         wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
         d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        agg[(_short(r["Kernel_Name"]), grid, wg)].append(d)
+        name = _short(r["Kernel_Name"])
+        for sub, ns in cut.items():
+            if sub in r["Kernel_Name"]:
+                name += f" (< {ns / 1e3:g} us)" if d < ns else f" (>= {ns / 1e3:g} us)"
+        agg[(name, grid, wg)].append(d)
     lines = ["# rocprofv3 kernel trace summary", "", "Command:", "", "```", cmd, "```", "",
              "Per kernel and launch grid (grid in threads x, y, z; work-group size); durations "
              "in microseconds.", "", *([note, ""] if note else []),
@@ -136,15 +154,20 @@ def counters(pmc_csv: str, selects, cmd: str, note: str = "") -> str:
         durs[key][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         if r["Counter_Name"] not in names:
             names.append(r["Counter_Name"])
+    sized = ("TCC_EA0_RDREQ_128B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_32B")
+    with_bytes = all(c in names for c in sized)
     lines = ["# rocprofv3 counters per dispatch", "", "Command:", "", "```", cmd, "```", "",
              *([note, ""] if note else []),
              "Means per dispatch. GRBM_GUI_ACTIVE sums the cycles of the 8 XCDs, so the clock is "
              "GRBM_GUI_ACTIVE / 8 / duration. Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / "
              "(1024 SIMDs x GRBM_GUI_ACTIVE / 8): the share of the kernel's cycles an average "
              "SIMD's matrix core was busy.", "",
+             *(["Read bytes = 128 TCC_EA0_RDREQ_128B + 64 TCC_EA0_RDREQ_64B + 32 "
+                "TCC_EA0_RDREQ_32B (HBM read requests by size, summed over the L2 channels; no "
+                "calibration factor).", ""] if with_bytes else []),
              "| kernel | grid | dispatches | avg us | " + " | ".join(names) +
-             " | clock GHz | matrix-core busy |",
-             "|---|---|---|---|" + "---|" * len(names) + "---|---|"]
+             " | clock GHz | matrix-core busy |" + (" read bytes |" if with_bytes else ""),
+             "|---|---|---|---|" + "---|" * len(names) + "---|---|" + ("---|" if with_bytes else "")]
     for sel in selects:
         name, grid = sel.rsplit(":", 1)
         grid = int(grid)
@@ -165,8 +188,11 @@ def counters(pmc_csv: str, selects, cmd: str, note: str = "") -> str:
         if grbm and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
             busy = f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (MI355X_SIMDS * grbm / MI355X_XCDS):.3f}"
         cells = " | ".join(f"{mean[c]:.4g}" if c in mean else "-" for c in names)
+        rb = ""
+        if with_bytes:
+            rb = f" {128 * mean[sized[0]] + 64 * mean[sized[1]] + 32 * mean[sized[2]]:.4g} |"
         lines.append(f"| `{_short(keys[0][0])}` | {grid} | {len(ds)} | {dur_ns / 1e3:.2f} | "
-                     f"{cells} | {clock} | {busy} |")
+                     f"{cells} | {clock} | {busy} |{rb}")
     return "\n".join(lines) + "\n"
 
 
@@ -195,6 +221,8 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--note", default="")
     s.add_argument("-o", "--out", required=True)
+    s.add_argument("--split", action="append", default=[])
+    s.add_argument("--only", action="append", default=[])
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -212,7 +240,7 @@ def main():
     c.add_argument("-o", "--out", required=True)
     a = p.parse_args()
     if a.what == "stats":
-        text = stats(a.trace_csv, a.cmd, a.note)
+        text = stats(a.trace_csv, a.cmd, a.note, a.split, a.only)
     elif a.what == "counters":
         text = counters(a.pmc_csv, a.select, a.cmd, a.note)
     else:
