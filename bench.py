@@ -562,8 +562,8 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
 
 def bench_small(torch, gb, synth, gen, stream, iters=50):
     """Latency of one decode step (append one token per sequence, absorb, decode) at the
-    small-batch shapes, as three calls and as gva_decode_step (append and absorb in one launch).
-    Median of HIP-event times on the launch stream."""
+    small-batch shapes, as three calls and as gva_decode_step (one launch at these shapes; the
+    number is reported). Median of HIP-event times on the launch stream."""
     res = {}
     shapes = (("C2", dict(append_one=True, block_size=8192),
                "B=8, T=4096 (+1 appended), H=16, G=4, d_h=d_n=64, d_r=16, bf16 contiguous"),

@@ -228,11 +228,16 @@ gva_status gva_decode_noalloc(const gva_dims *dims, const gva_cache *cache, int3
  * each append the token (one of them writes it), absorb the group's queries, decode a share
  * of the positions (a wave that reads the new position takes the token it has just rounded,
  * not the cache) and merge their waves' partials; the last of the K to finish merges the K
- * partials (through the workspace and a ticket in its first 1024 bytes). Its outputs equal
- * gva_decode's to rounding (the positions are split differently), not bit for bit. Other arguments take one
- * launch for the append and the absorption, then the decode (and its combine), with outputs
- * bit-identical to the three calls. gva_decode_step_launches tells which. Within one call the
- * block that receives sequence b's token must not be read by another sequence.
+ * partials (through the workspace and a ticket in its first 1024 bytes). Small batches of the
+ * shapes the vector-ALU kernel decodes (float32 caches among them: H / G of 1, 2, 4 or 8,
+ * B G <= 256, max_len <= 1024, the group's rows of M within 72 KiB of LDS, the automatic split
+ * count) also run as ONE launch: one work-group per (sequence, group) appends, absorbs, decodes
+ * all positions over its waves and merges them; no workspace bytes are touched. The one-launch
+ * outputs equal gva_decode's to rounding (the positions are split differently), not bit for
+ * bit. Other arguments take one launch for the append and the absorption, then the decode (and
+ * its combine), with outputs bit-identical to the three calls. gva_decode_step_launches tells
+ * which. Within one call the block that receives sequence b's token must not be read by
+ * another sequence.
  *   pos: device int32 [B], the new token's position (its sequence's length before the step).
  *   v_new: device float32 [B][G][d_h]; kr_raw: device float32 [B][d_r].
  *   q_nope: device float32 [B][H][d_n]; q_rope: device float32 [B][H][d_r];

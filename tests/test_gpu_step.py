@@ -86,6 +86,16 @@ SHAPES = [
                  id="d_h-32-two-heads-per-group"),
     pytest.param("C4", dict(B=2, lengths_uniform=(9000, 12000), H=8, G=8, d_h=64, d_n=64, d_r=8),
                  0, 1, id="one-head-per-group-long"),
+    # the vector-ALU path in one launch: float32 caches and shapes the matrix cores do not take
+    pytest.param("C1", dict(append_one=True, block_size=512), 0, 1, id="C1-fp32-auto"),
+    pytest.param("C4", dict(B=4, lengths_uniform=(0, 600), H=8, G=4, d_h=64, d_n=64, d_r=12), 0, 1,
+                 id="valu-d_r-12-one-launch"),
+    pytest.param("C4", dict(B=3, lengths_uniform=(100, 1000), H=4, G=4, d_h=128, d_n=128,
+                            dtype="f32"), 0, 1, id="valu-fp32-d_h-128-one-launch"),
+    pytest.param("C4", dict(B=5, lengths_uniform=(0, 900), H=16, G=2, d_h=32, d_n=32, d_r=8,
+                            dtype="f32"), 0, 1, id="valu-fp32-eight-heads-per-group"),
+    pytest.param("C4", dict(B=2, lengths_uniform=(1500, 2000), H=8, G=4, d_h=64, d_n=64,
+                            dtype="f32"), 0, 3, id="valu-fp32-long-three-launches"),
 ]
 
 
@@ -177,6 +187,13 @@ def test_step_with_empty_histories():
         assert np.allclose(out[3, h], V[0, c.dims.group_of(h)], rtol=0, atol=1e-6)
 
 
+# the two one-launch kernels: matrix cores (bf16, d_h <= 64) and vector ALU (here d_r = 12, which
+# the matrix-core kernel does not take, and a float32 cache)
+ONE_LAUNCH = [pytest.param({}, "bf16", id="mfma"),
+              pytest.param(dict(d_r=12), "bf16", id="valu-bf16"),
+              pytest.param(dict(dtype="f32"), "f32", id="valu-fp32")]
+
+
 def _one_launch_case(B=6, lo=100, hi=900, **kw):
     kw = dict(dict(d_h=64, d_n=64), **kw)
     c = _case("C4", B=B, lengths_uniform=(lo, hi), **kw)
@@ -184,9 +201,10 @@ def _one_launch_case(B=6, lo=100, hi=900, **kw):
     return c
 
 
-def test_one_launch_step_not_reading_its_token():
+@pytest.mark.parametrize("kw,dtype", ONE_LAUNCH)
+def test_one_launch_step_not_reading_its_token(kw, dtype):
     """seq_len = pos: the token is appended (bit-exact) but the decode reads only the history."""
-    c = _one_launch_case()
+    c = _one_launch_case(**kw)
     w = c.w
     pos, v_new, kr_raw, M, q_nope, q_rope, q_ref = _step_inputs(c, 6)
     sl = pos.copy()
@@ -203,17 +221,18 @@ def test_one_launch_step_not_reading_its_token():
     v_dev, k_dev = c.device_bits()
     assert np.array_equal(v_dev, c.pool.v) and np.array_equal(k_dev, c.pool.kr)
     ref, ref_lse = c.oracle_decode(sl, q_ref)
-    check_output(out.cpu().numpy(), ref, "bf16", "one-launch step, token not read")
-    ok, e = lse_ok(lse.cpu().numpy(), ref_lse, 1e-3)
+    check_output(out.cpu().numpy(), ref, dtype, f"one-launch step, token not read, {kw}")
+    ok, e = lse_ok(lse.cpu().numpy(), ref_lse, 1e-5 if dtype == "f32" else 1e-3)
     assert ok, e
     assert c.err_flag() == 0
 
 
-def test_one_launch_step_device_errors():
+@pytest.mark.parametrize("kw,dtype", ONE_LAUNCH)
+def test_one_launch_step_device_errors(kw, dtype):
     """A bad block-table entry in sequence 1's history and a length above max_len for sequence
     4: their rows are NaN and the BLOCK and LENGTH bits are raised; the token of sequence 4 is
     still appended; the other sequences match the oracle. Every work-group exits normally."""
-    c = _one_launch_case()
+    c = _one_launch_case(**kw)
     w = c.w
     pos, v_new, kr_raw, M, q_nope, q_rope, q_ref = _step_inputs(c, 7)
     c.block_table[1, 2] = c.lay.num_blocks + 11          # positions 32 .. 47 of sequence 1
@@ -238,4 +257,4 @@ def test_one_launch_step_device_errors():
     v_dev, k_dev = c.device_bits()
     assert np.array_equal(v_dev, c.pool.v) and np.array_equal(k_dev, c.pool.kr)
     ref, ref_lse = c.oracle_decode(sl, q_ref, seqs=good)
-    check_output(out[good], ref[good], "bf16", "one-launch step beside device errors")
+    check_output(out[good], ref[good], dtype, f"one-launch step beside device errors, {kw}")

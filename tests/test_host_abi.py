@@ -430,8 +430,10 @@ def test_absorb_requires_aligned_query_rows(L):
 
 
 def test_decode_step_launches_plan(L):
-    """The one-launch step serves small batches of the matrix-core shapes with d_h <= 128, the
-    automatic split count and sequences of at most 4 MiB of values per group."""
+    """The one-launch step serves small batches: on the matrix cores the shapes with d_h of 32
+    or 64, the automatic split count and sequences of at most 4 MiB of values per group; on the
+    vector ALU (float32 caches, or the generic kernel) sequences of at most 1024 positions whose
+    group's rows of M fit the LDS region."""
     d = _dims(H=16, G=4, d_h=64, d_n=64)             # the 350M-class layer
     c = _cache(d=d, max_blocks=4096)
     n = lambda *a: L.gva_decode_step_launches(ctypes.byref(d), ctypes.byref(c), *a)
@@ -446,6 +448,15 @@ def test_decode_step_launches_plan(L):
     assert L.gva_decode_step_launches(ctypes.byref(d128), ctypes.byref(_cache(max_blocks=2048)),
                                       4, 8705, 0, 0) == 3
     c32 = _cache(dtype=gb.GVA_DTYPE_F32, max_blocks=2048)
-    assert L.gva_decode_step_launches(ctypes.byref(d), ctypes.byref(c32), 1, 256, 1, 0) == 2
+    n32 = lambda *a: L.gva_decode_step_launches(ctypes.byref(d), ctypes.byref(c32), *a)
+    assert n32(1, 256, 1, 0) == 2                    # an explicit split count
+    assert n32(1, 257, 0, 0) == 1                    # the vector-ALU step in one launch
+    assert n32(64, 1024, 0, 0) == 1                  # 256 sequence-groups, 1024 positions
+    assert n32(64, 1025, 0, 0) == 3                  # longer: append + absorb, decode, combine
+    assert n32(65, 100, 0, 0) == 3                   # 260 sequence-groups: split and combine
+    assert n(8, 1000, 0, gb.GVA_KERNEL_GENERIC) == 1 # the generic kernel asked for, short
+    d8 = _dims(H=16, G=2, d_h=128, d_n=128)          # 8 heads x 128 x 128 of M: above the region
+    c8 = _cache(d=d8, dtype=gb.GVA_DTYPE_F32, max_blocks=2048)
+    assert L.gva_decode_step_launches(ctypes.byref(d8), ctypes.byref(c8), 2, 300, 0, 0) == 3
     d256 = _dims(H=8, G=2, d_h=256, d_n=256)
     assert L.gva_decode_step_launches(ctypes.byref(d256), ctypes.byref(_cache(d=d256)), 2, 100, 0, 0) == 3

@@ -226,6 +226,31 @@ gva_status gva_decode_step(const gva_dims *dims, const gva_cache *cache, int32_t
     }
     return hip_status(gva::launch_step_fused(sa, stream), "one-launch decode step");
   }
+  if (gva::step_small_supported(dims, cache, B, max_len, num_splits, use_mfma)) {
+    // small batch on the vector-ALU path: the whole step in one launch, one work-group per
+    // (sequence, group), no workspace
+    gva::StepArgs sa{};
+    sa.a = cache_args(dims, cache);
+    sa.a.B = B;
+    sa.a.seq_len = seq_len;
+    sa.a.max_len = max_len;
+    sa.a.qscale = scale * 1.4426950408889634f;
+    sa.a.out = out;
+    sa.a.lse = lse;
+    sa.pos = pos;
+    sa.v_new = v_new;
+    sa.kr_raw = kr_raw;
+    sa.q_nope = q_nope;
+    sa.q_rope = q_rope;
+    sa.M = M;
+    sa.rope = cache->rope;
+    sa.max_pos = cache->max_pos;
+    sa.d_n = dims->d_n;
+    sa.q_abs = q_abs;
+    sa.K = 1;
+    return hip_status(gva::launch_step_small(sa, cache->dtype == GVA_DTYPE_BF16, stream),
+                      "one-launch decode step (vector ALU)");
+  }
   hipError_t e = gva::launch_step_prep(cache_args(dims, cache), cache->dtype == GVA_DTYPE_BF16, B,
                                        pos, v_new, kr_raw, cache->rope, cache->max_pos, dims->d_n,
                                        q_nope, q_rope, M, q_abs, stream);

@@ -291,6 +291,22 @@ bool step_fused_supported(const gva_dims *d, const gva_cache *c, int32_t B, int3
   return true;
 }
 
+bool step_small_supported(const gva_dims *d, const gva_cache *c, int32_t B, int32_t max_len,
+                          int32_t num_splits, bool use_mfma) {
+  // one work-group per (sequence, group) walks the whole sequence with four waves, so the batch
+  // fills at most one work-group per compute unit and the sequences are short
+  (void)c;
+  if (use_mfma || num_splits != 0) return false;
+  const int hpg = d->H / d->G;
+  if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8) return false;
+  if (d->d_n % 4 != 0 || d->d_h > kMaxDh) return false;
+  if (static_cast<int64_t>(B) * d->G > kPlanCUs || max_len > kSmallMaxLen) return false;
+  // the rows of M (padded by 16 bytes) and q_nope of the group's heads are staged in LDS
+  const int64_t m_bytes = static_cast<int64_t>(hpg) * d->d_h * (d->d_n / 4 + 1) * 16 +
+                          static_cast<int64_t>(hpg) * d->d_n * 4;
+  return m_bytes <= kSmallRegionBytes;
+}
+
 bool plan_step(const gva_dims *d, int32_t B, int32_t max_len, StepPlan *plan) {
   if (!d || B < 1 || max_len < 0 || d->G < 1) return false;
   *plan = StepPlan{};
@@ -539,6 +555,7 @@ int32_t gva_decode_step_launches(const gva_dims *dims, const gva_cache *cache, i
   if (kernel == GVA_KERNEL_MFMA && !can) return 0;
   const bool use_mfma = kernel == GVA_KERNEL_MFMA || (kernel == GVA_KERNEL_AUTO && can);
   if (gva::step_fused_supported(dims, cache, B, max_len, num_splits, use_mfma)) return 1;
+  if (gva::step_small_supported(dims, cache, B, max_len, num_splits, use_mfma)) return 1;
   gva::DecodePlan plan;
   if (!gva::plan_decode(dims, B, max_len, num_splits, use_mfma, &plan)) return 0;
   return (plan.num_splits > 1 || plan.num_ranges > 0) ? 3 : 2;

@@ -200,6 +200,15 @@ struct StepArgs {
 // 4 MiB of values per group, and the automatic split count.
 bool step_fused_supported(const gva_dims *d, const gva_cache *c, int32_t B, int32_t max_len,
                           int32_t num_splits, bool use_mfma);
+// Whether the one-launch step of the vector-ALU path serves these arguments: shapes the
+// matrix-core kernel does not take (float32 caches among them) with H / G of 1, 2, 4 or 8, at
+// most kPlanCUs (sequence, group) pairs, sequences of at most kSmallMaxLen positions, the
+// automatic split count, and the group's rows of M (with q_nope) within kSmallRegionBytes.
+constexpr int kSmallMaxLen = 1024;
+constexpr int kSmallRegionBytes = 72 * 1024;
+bool step_small_supported(const gva_dims *d, const gva_cache *c, int32_t B, int32_t max_len,
+                          int32_t num_splits, bool use_mfma);
+hipError_t launch_step_small(const StepArgs &s, bool bf16, hipStream_t stream);
 // Waves per work-group of the one-launch step (two per SIMD, so up to 256 registers each).
 inline int step_waves_of(int d_h) { (void)d_h; return 8; }
 // The first kWsHeader bytes of a decode workspace hold the one-launch step's tickets, one int32

@@ -408,6 +408,399 @@ __global__ __launch_bounds__(256) void k_combine_wave(gva::DecodeArgs a) {
   if (lse && lane == 0) *lse = poison ? qnan : (mx + log2f(L)) * gvad::kLn2;
 }
 
+// ---- the decode step in one launch, vector-ALU path (small batches, short sequences) ---------
+//
+// One work-group of kSmallWaves waves per (sequence b, value group g) does what the append, the
+// absorption and the decode of one step do for that group:
+//   1. absorption: q~ of the group's NH heads, float32 multiply-adds in the order of
+//      gva_absorb_query (so q_abs is bit-identical), the rows of M and q_nope staged through
+//      LDS; the positional slice rotated in float64 at the token's position and rounded once;
+//   2. append: the token's values for group g (and, in group 0's work-group, its rotated
+//      positional key) rounded once and written as gva_cache_append writes them, and kept in
+//      LDS, where the decode takes the token from (this launch is writing it to the cache);
+//   3. decode: wave w takes the w-th of kSmallWaves equal ranges of positions, cut from max_len
+//      so that its first block-table entries are read at the start, and runs the vector-ALU
+//      decode on it: lane-per-position scores, online softmax per head, lanes over the value
+//      dimensions for the weighted sum;
+//   4. merge: the waves' (m, l, o) meet in LDS through their log-sum-exp; the result is the
+//      output row and its lse.
+// Every input that does not depend on another load is requested at the start. No work-group
+// waits on another. The host takes this path when the matrix-core kernel does not serve the
+// shape (float32 caches among them), with at most kPlanCUs (sequence, group) pairs, sequences
+// of at most kSmallMaxLen positions and the group's rows of M within the LDS region.
+constexpr int kSmallWaves = 8;
+using gva::kSmallRegionBytes;
+
+// alt where mask is all ones, else loaded: a bitwise blend, because a select between a loaded
+// value and another one is compiled as a branch around the load with a wait inside, which
+// would serialise the loads of a batch
+__device__ __forceinline__ float blend(float loaded, float alt, int mask) {
+  return __int_as_float((__float_as_int(loaded) & ~mask) | (__float_as_int(alt) & mask));
+}
+
+template <bool BF16, int NH, int DPL>
+__global__ __launch_bounds__(64 * kSmallWaves) void k_step_small(gva::StepArgs s) {
+  constexpr int PV = 64 / DPL;                           // positions per weighted-sum batch
+  __shared__ __align__(16) float region[kSmallRegionBytes / 4];   // M and q_nope, then the merge
+  __shared__ float q_s[NH][gva::kMaxDh + gva::kMaxDr];   // q~ | r, times scale log2(e)
+  __shared__ float tok_v[gva::kMaxDh];                   // the token's values (group g), rounded
+  __shared__ float tok_kr[gva::kMaxDr];                  // its rotated positional key, rounded
+  __shared__ __align__(16) float p_s[kSmallWaves][NH][kTile];
+  __shared__ int64_t vo_s[kSmallWaves][kTile];
+  __shared__ int s_bad;
+  const gva::DecodeArgs &a = s.a;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x / a.G;
+  const int g = blockIdx.x - b * a.G;
+  const int d_h = a.d_h, d_r = a.d_r, d_n = s.d_n, row = d_h + d_r;
+  const int half_r = d_r >> 1;
+  const int lb = a.log2_bs;
+  const int bs_mask = (1 << lb) - 1;
+  const float qnan = __int_as_float(0x7fc00000);
+  if (tid == 0) s_bad = 0;
+  // the group's heads, slots g NH .. g NH + NH - 1 of a.head_of: read as aligned 32-bit words
+  // with uniform indices (scalar loads), the lane's byte shifted out, so that no load has to
+  // wait for a per-lane lookup
+  const int h0 = g * NH;
+  const uint32_t *hw = reinterpret_cast<const uint32_t *>(a.head_of) + (h0 >> 2);
+  const uint32_t hw0 = hw[0];
+  const uint32_t hw1 = NH == 8 ? hw[1] : 0u;
+  auto head = [&](int c) {
+    return static_cast<int>((((c & 4) ? hw1 : hw0) >> (8 * ((h0 & 3) + (c & 3)))) & 0xffu);
+  };
+  const int32_t *__restrict__ bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  // this wave's range [c0, cend) of positions, cut from max_len; the entry of position
+  // min(c0 + lane, cend - 1) for its first tile is requested now
+  const int chunk = (a.max_len + kSmallWaves - 1) / kSmallWaves;
+  const int c0 = wave * chunk;
+  const int cend = min(c0 + chunk, a.max_len);
+  int32_t pe0 = 0;
+  if (c0 < cend) pe0 = bt[min(c0 + lane, cend - 1) >> lb];   // uniform per wave
+  const int p = s.pos[b];
+  const int len = a.seq_len[b];
+  const int cap = a.max_blocks << a.log2_bs;
+  const bool len_bad = len < 0 || len > a.max_len || len > cap;
+  const bool rope_bad = p < 0 || p >= s.max_pos;         // the absorbed query is NaN
+  int32_t aerr = 0;
+  if (p < 0) aerr = GVA_DEVERR_LENGTH;
+  else if (p >= cap) aerr = GVA_DEVERR_CAPACITY;
+  else if (p >= s.max_pos) aerr = GVA_DEVERR_ROPE;
+  // the token's table entry, values and positional key pairs with their (cos, sin), and the
+  // positional query pairs of the group's heads with theirs, all requested now
+  const int32_t pblk = aerr ? 0 : bt[p >> lb];
+  float2 tok_x = {0.f, 0.f}, tok_k = {0.f, 0.f}, rq = {0.f, 0.f};
+  double2 tok_cs = {1.0, 0.0}, rq_cs = {1.0, 0.0};
+  if (!aerr) {
+    if (tid < (d_h >> 1))
+      tok_x = reinterpret_cast<const float2 *>(s.v_new + (static_cast<int64_t>(b) * a.G + g) * d_h)[tid];
+    if (tid < half_r) {
+      tok_k = reinterpret_cast<const float2 *>(s.kr_raw + static_cast<int64_t>(b) * d_r)[tid];
+      tok_cs = reinterpret_cast<const double2 *>(s.rope)[static_cast<int64_t>(p) * half_r + tid];
+    }
+  }
+  if (!rope_bad && tid < NH * half_r) {                  // NH d_r / 2 <= 256 <= 64 kSmallWaves
+    const int c = tid / half_r;
+    const int k = tid - c * half_r;
+    rq = reinterpret_cast<const float2 *>(s.q_rope + (static_cast<int64_t>(b) * a.H + head(c)) * d_r)[k];
+    rq_cs = reinterpret_cast<const double2 *>(s.rope)[static_cast<int64_t>(p) * half_r + k];
+  }
+
+  // ---- 1. absorption ----
+  // the q_abs values this thread forms, written after the barrier that publishes them in LDS
+  // (a barrier waits for the stores before it)
+  float qa_val[4] = {0.f, 0.f, 0.f, 0.f};
+  float2 qr_val = {0.f, 0.f};
+  {
+    const int d4 = d_n >> 2;
+    const int stride4 = d4 + 1;                          // rows padded by 16 bytes
+    const int nrows = NH * d_h;
+    float4 *mst = reinterpret_cast<float4 *>(region);
+    float4 *qst = mst + nrows * stride4;                 // q_nope of the group's heads
+    // Thread t stages element t % d4 of rows t / d4, t / d4 + q, ... of each head's block of M
+    // (q = threads / d4 rows per pass): no division in the loops, and every load and store is
+    // made (row indices are clamped; a duplicate writes the same value to the same place), so
+    // the loads of a head are in flight together.
+    const int q4 = (64 * kSmallWaves) / d4;
+    const int my_r = tid / d4;
+    const int my_j = tid - my_r * d4;
+    const int nk = (d_h + q4 - 1) / q4;
+#pragma unroll
+    for (int c = 0; c < NH; ++c) {
+      const float4 *Mc = reinterpret_cast<const float4 *>(s.M + static_cast<int64_t>(head(c)) * d_h * d_n);
+      float4 *dc = mst + c * d_h * stride4;
+#pragma unroll 4
+      for (int k = 0; k < nk; ++k) {
+        const int i = min(my_r + k * q4, d_h - 1);
+        dc[i * stride4 + my_j] = Mc[i * d4 + my_j];
+      }
+    }
+    for (int e = tid; e < NH * d4; e += 64 * kSmallWaves) {
+      const int c = e / d4;
+      qst[e] = reinterpret_cast<const float4 *>(
+          s.q_nope + (static_cast<int64_t>(b) * a.H + head(c)) * d_n)[e - c * d4];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {                        // nrows <= 8 x 256 = 4 x 512
+      const int o = tid + u * 64 * kSmallWaves;
+      if (o >= nrows) break;
+      const int c = o / d_h;
+      const int i = o - c * d_h;
+      const float4 *mr = mst + o * stride4;
+      const float4 *qr = qst + c * d4;
+      float acc = 0.0f;
+      for (int j4 = 0; j4 < d4; ++j4) {
+        const float4 m4 = mr[j4];
+        const float4 q4v = qr[j4];
+        acc = fmaf(m4.x, q4v.x, acc);
+        acc = fmaf(m4.y, q4v.y, acc);
+        acc = fmaf(m4.z, q4v.z, acc);
+        acc = fmaf(m4.w, q4v.w, acc);
+      }
+      const float v = rope_bad ? qnan : acc;
+      qa_val[u] = v;
+      q_s[c][i] = v * a.qscale;
+    }
+    if (tid < NH * half_r) {
+      const int c = tid / half_r;
+      const int k = tid - c * half_r;
+      float y0f = qnan, y1f = qnan;
+      if (!rope_bad) {
+        double y0, y1;
+        gvad::rotate_pair_f64(static_cast<double>(rq.x), static_cast<double>(rq.y), rq_cs.x,
+                              rq_cs.y, &y0, &y1);
+        y0f = gvad::f64_to_f32(y0);
+        y1f = gvad::f64_to_f32(y1);
+      }
+      qr_val = make_float2(y0f, y1f);
+      q_s[c][d_h + 2 * k] = y0f * a.qscale;
+      q_s[c][d_h + 2 * k + 1] = y1f * a.qscale;
+    }
+  }
+
+  // ---- 2. append (the checks and arithmetic of gva_cache_append) ----
+  int64_t blk = -1;
+  if (!aerr) {
+    if (pblk < 0 || static_cast<int64_t>(pblk) >= a.num_blocks) aerr = GVA_DEVERR_BLOCK;
+    else blk = pblk;
+  }
+  const bool tok_ok = aerr == 0;
+  if (g == 0 && tid == 0) {
+    if (aerr) gvad::raise_err(a.err_flag, aerr);
+    if (rope_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_ROPE);
+    if (len_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_LENGTH);
+  }
+  // the rounded token (cache bits) this thread writes after the barrier
+  uint2 wv = {0u, 0u}, wk = {0u, 0u};
+  if (tok_ok) {
+    if (tid < (d_h >> 1)) {                              // d_h / 2 <= 128 < 64 kSmallWaves
+      if (BF16) {
+        wv.x = gvad::f64_to_bf16_bits(static_cast<double>(tok_x.x));
+        wv.y = gvad::f64_to_bf16_bits(static_cast<double>(tok_x.y));
+        tok_v[2 * tid] = gvad::bf16_bits_to_f32(wv.x);
+        tok_v[2 * tid + 1] = gvad::bf16_bits_to_f32(wv.y);
+      } else {
+        wv.x = gvad::f64_to_f32_bits(static_cast<double>(tok_x.x));
+        wv.y = gvad::f64_to_f32_bits(static_cast<double>(tok_x.y));
+        tok_v[2 * tid] = __uint_as_float(wv.x);
+        tok_v[2 * tid + 1] = __uint_as_float(wv.y);
+      }
+    }
+    if (tid < half_r) {
+      double y0, y1;
+      gvad::rotate_pair_f64(static_cast<double>(tok_k.x), static_cast<double>(tok_k.y), tok_cs.x,
+                            tok_cs.y, &y0, &y1);
+      if (BF16) {
+        wk.x = gvad::f64_to_bf16_bits(y0);
+        wk.y = gvad::f64_to_bf16_bits(y1);
+        tok_kr[2 * tid] = gvad::bf16_bits_to_f32(wk.x);
+        tok_kr[2 * tid + 1] = gvad::bf16_bits_to_f32(wk.y);
+      } else {
+        wk.x = gvad::f64_to_f32_bits(y0);
+        wk.y = gvad::f64_to_f32_bits(y1);
+        tok_kr[2 * tid] = __uint_as_float(wk.x);
+        tok_kr[2 * tid + 1] = __uint_as_float(wk.y);
+      }
+    }
+  }
+  __syncthreads();                                       // q~, r and the token are in LDS
+
+  // ---- 3. decode the wave's range [c0, c1) ----
+  float m[NH], l[NH], o[NH][DPL];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[hh][k] = 0.0f;
+  }
+  bool bad = false;
+  const int c1 = len_bad ? c0 : min(cend, len);
+  for (int t0 = c0; t0 < c1; t0 += kTile) {
+    // ---- scores: one position per lane; the token's position reads it from LDS ----
+    // lane reads position tp = min(t0 + lane, cend - 1) (inside the table; its entry is only
+    // checked, and used, for positions of the sequence)
+    const int t = t0 + lane;
+    const bool valid = t < c1;
+    const int tp = min(t, cend - 1);
+    const int32_t pe = t0 == c0 ? pe0 : bt[tp >> lb];
+    const bool pe_ok = pe >= 0 && static_cast<int64_t>(pe) < a.num_blocks;
+    const bool mine = tok_ok && valid && t == p;
+    if (valid && !pe_ok && !mine) bad = true;
+    const int mmask = mine ? -1 : 0;
+    const int64_t blk_s = pe_ok ? pe : 0;
+    const int64_t voff = blk_s * a.v_sb + static_cast<int64_t>(tp & bs_mask) * a.v_st +
+                         static_cast<int64_t>(g) * a.v_sg;
+    const int64_t koff = blk_s * a.kr_sb + static_cast<int64_t>(tp & bs_mask) * a.kr_st;
+    vo_s[wave][lane] = voff;
+    float sc[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) sc[hh] = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < d_r; i += 2) {
+      const float2 y = load_pair<BF16>(a.kr, koff + i);
+      const float2 x = make_float2(blend(y.x, tok_kr[i], mmask), blend(y.y, tok_kr[i + 1], mmask));
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+        sc[hh] = fmaf(q_s[hh][d_h + i], x.x, fmaf(q_s[hh][d_h + i + 1], x.y, sc[hh]));
+    }
+#pragma unroll 32
+    for (int i = 0; i < d_h; i += 2) {
+      const float2 y = load_pair<BF16>(a.v, voff + i);
+      const float2 x = make_float2(blend(y.x, tok_v[i], mmask), blend(y.y, tok_v[i + 1], mmask));
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) sc[hh] = fmaf(q_s[hh][i], x.x, fmaf(q_s[hh][i + 1], x.y, sc[hh]));
+    }
+    // ---- online softmax over the tile, per head ----
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      const float sv = valid ? sc[hh] : -INFINITY;
+      const float mn = fmaxf(m[hh], gvad::wave_max(sv));
+      const float alpha = exp2f(m[hh] - mn);
+      const float pr = exp2f(sv - mn);
+      l[hh] = l[hh] * alpha + gvad::wave_sum(pr);
+      m[hh] = mn;
+      p_s[wave][hh][lane] = pr;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[hh][k] *= alpha;
+    }
+    // ---- weighted sum: lanes over value dimensions (the wave's own LDS rows: no barrier) ----
+    // every load is issued (positions past the tile's end read a row of the range again, dims
+    // past d_h its last element; neither is used); the token's row comes from LDS
+    const int nt = min(kTile, c1 - t0);
+    const int tokj = tok_ok && p >= t0 && p < t0 + nt ? p - t0 : -1;
+    float tokd[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) tokd[k] = tok_v[min(lane + 64 * k, d_h - 1)];
+    for (int j0 = 0; j0 < nt; j0 += PV) {
+      float x[PV][DPL];
+#pragma unroll
+      for (int u = 0; u < PV; ++u) {
+        const int64_t vo = vo_s[wave][j0 + u];
+        const int tmask = j0 + u == tokj ? -1 : 0;
+        const int vmask = j0 + u < nt ? -1 : 0;         // rows past nt may hold anything
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+          const float xv = blend(load_one<BF16>(a.v, vo + min(lane + 64 * k, d_h - 1)), tokd[k], tmask);
+          x[u][k] = __int_as_float(__float_as_int(xv) & vmask);
+        }
+      }
+      // positions past nt have zero values and zero probabilities (scores of -inf), so every
+      // product is taken; four positions' probabilities per 16-byte LDS read
+#pragma unroll
+      for (int u4 = 0; u4 < PV / 4; ++u4) {
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          const float4 pj = *reinterpret_cast<const float4 *>(&p_s[wave][hh][j0 + 4 * u4]);
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) {
+            o[hh][k] = fmaf(pj.x, x[4 * u4][k], o[hh][k]);
+            o[hh][k] = fmaf(pj.y, x[4 * u4 + 1][k], o[hh][k]);
+            o[hh][k] = fmaf(pj.z, x[4 * u4 + 2][k], o[hh][k]);
+            o[hh][k] = fmaf(pj.w, x[4 * u4 + 3][k], o[hh][k]);
+          }
+        }
+      }
+    }
+  }
+  if (__any(bad) && lane == 0) {
+    atomicOr(&s_bad, 1);
+    gvad::raise_err(a.err_flag, GVA_DEVERR_BLOCK);
+  }
+
+  // ---- 4. merge the waves' (m, l, o) in LDS (the region's M rows are no longer read) ----
+  float *mo = region;                                    // [kSmallWaves][NH][d_h]
+  float *mm = mo + kSmallWaves * NH * d_h;               // [kSmallWaves][NH]
+  float *ml = mm + kSmallWaves * NH;                     // [kSmallWaves][NH]
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int d = lane + 64 * k;
+      if (d < d_h) mo[(wave * NH + hh) * d_h + d] = o[hh][k];
+    }
+    if (lane == 0) {
+      mm[wave * NH + hh] = m[hh];
+      ml[wave * NH + hh] = l[hh];
+    }
+  }
+  __syncthreads();
+  // the global writes of the absorption and the append, which nothing in this launch reads
+  // back (the decode took q~, r and the token from LDS): q_abs, and the token into the cache as
+  // gva_cache_append writes it. They go out last, beside the output rows: before a barrier
+  // they would be waited for there, and before the decode's loads they would be waited for
+  // with them (stores and loads are counted in order).
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int o = tid + u * 64 * kSmallWaves;
+    if (o >= NH * d_h) break;
+    const int c = o / d_h;
+    s.q_abs[(static_cast<int64_t>(b) * a.H + head(c)) * row + (o - c * d_h)] = qa_val[u];
+  }
+  if (tid < NH * half_r) {
+    const int c = tid / half_r;
+    const int k = tid - c * half_r;
+    *reinterpret_cast<float2 *>(s.q_abs + (static_cast<int64_t>(b) * a.H + head(c)) * row + d_h + 2 * k) =
+        qr_val;
+  }
+  if (tok_ok) {
+    const int64_t off = p & bs_mask;
+    if (tid < (d_h >> 1)) {
+      const int64_t o = blk * a.v_sb + off * a.v_st + static_cast<int64_t>(g) * a.v_sg + 2 * tid;
+      if (BF16) reinterpret_cast<uint32_t *>(const_cast<void *>(a.v))[o >> 1] = wv.x | (wv.y << 16);
+      else *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(const_cast<void *>(a.v)) + o) = wv;
+    }
+    if (g == 0 && tid < half_r) {
+      const int64_t o = blk * a.kr_sb + off * a.kr_st + 2 * tid;
+      if (BF16) reinterpret_cast<uint32_t *>(const_cast<void *>(a.kr))[o >> 1] = wk.x | (wk.y << 16);
+      else *reinterpret_cast<uint2 *>(reinterpret_cast<uint32_t *>(const_cast<void *>(a.kr)) + o) = wk;
+    }
+  }
+  const bool poison = len_bad || s_bad != 0;
+  for (int idx = tid; idx < NH * d_h; idx += 64 * kSmallWaves) {
+    const int hh = idx / d_h;
+    const int d = idx - hh * d_h;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) mx = fmaxf(mx, mm[w * NH + hh]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const float mw = mm[w * NH + hh];
+      const float e = mw == -INFINITY ? 0.0f : exp2f(mw - mx);
+      L = fmaf(ml[w * NH + hh], e, L);
+      acc = fmaf(mo[(w * NH + hh) * d_h + d], e, acc);
+    }
+    const int h = head(hh);
+    a.out[(static_cast<int64_t>(b) * a.H + h) * d_h + d] = poison ? qnan : (L > 0.0f ? acc / L : 0.0f);
+    if (a.lse && d == 0)
+      a.lse[static_cast<int64_t>(b) * a.H + h] =
+          poison ? qnan : (L > 0.0f ? (mx + log2f(L)) * gvad::kLn2 : -INFINITY);
+  }
+}
+
 }  // namespace
 
 namespace gva {
@@ -445,6 +838,34 @@ hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t str
   if (bf16) launch_generic_dpl<true>(a, grid, head_passes, nhp, stream);
   else launch_generic_dpl<false>(a, grid, head_passes, nhp, stream);
   return hipGetLastError();
+}
+
+template <bool BF16, int NH>
+hipError_t launch_small_dpl(const StepArgs &sa, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(sa.a.B * sa.a.G));
+  const dim3 block(64 * kSmallWaves);
+  switch ((sa.a.d_h + 63) / 64) {
+    case 1: hipLaunchKernelGGL((k_step_small<BF16, NH, 1>), grid, block, 0, stream, sa); break;
+    case 2: hipLaunchKernelGGL((k_step_small<BF16, NH, 2>), grid, block, 0, stream, sa); break;
+    case 3: hipLaunchKernelGGL((k_step_small<BF16, NH, 3>), grid, block, 0, stream, sa); break;
+    default: hipLaunchKernelGGL((k_step_small<BF16, NH, 4>), grid, block, 0, stream, sa); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_small_nh(const StepArgs &sa, hipStream_t stream) {
+  switch (sa.a.H / sa.a.G) {
+    case 1: return launch_small_dpl<BF16, 1>(sa, stream);
+    case 2: return launch_small_dpl<BF16, 2>(sa, stream);
+    case 4: return launch_small_dpl<BF16, 4>(sa, stream);
+    case 8: return launch_small_dpl<BF16, 8>(sa, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_step_small(const StepArgs &sa, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_small_nh<true>(sa, stream) : launch_small_nh<false>(sa, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
