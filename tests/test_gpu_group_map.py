@@ -54,11 +54,15 @@ def test_decode_with_group_map(shape, num_splits, kernel):
     assert np.max(np.abs(o_plain - out[b])) > 1e-2
 
 
-def test_step_with_group_map():
+@pytest.mark.parametrize("dtype", [pytest.param("bf16", id="matrix-core-one-launch"),
+                                   pytest.param("f32", id="vector-alu-one-launch")])
+def test_step_with_group_map(dtype):
     """gva_decode_step with a map: the append does not depend on it, the absorption and the
-    decode follow it."""
-    w = synth.workload("C4", B=5, lengths_uniform=(50, 500), H=16, G=4, d_h=64, d_n=64, d_r=16)
+    decode follow it (both one-launch kernels)."""
+    w = synth.workload("C4", B=5, lengths_uniform=(50, 500), H=16, G=4, d_h=64, d_n=64, d_r=16,
+                       dtype=dtype)
     c = Case(w, g_of_h=_balanced_map(w.H, w.G, 5))
+    assert gb.gva_decode_step_launches(c.cdims, c.cache, w.B, int(c.lens.max()) + 1, 0) == 1
     c.append_prefix()
     rng = np.random.default_rng(np.random.SeedSequence([4243, 1]))
     v_new = rng.standard_normal((w.B, w.G, w.d_h)).astype(np.float32)
@@ -81,8 +85,8 @@ def test_step_with_group_map():
     v_dev, k_dev = c.device_bits()
     assert np.array_equal(v_dev, c.pool.v) and np.array_equal(k_dev, c.pool.kr)
     ref, ref_lse = c.oracle_decode(sl, q_ref)
-    check_output(out.cpu().numpy(), ref, "bf16", "step with group map")
-    ok, e = lse_ok(lse.cpu().numpy(), ref_lse, 1e-3)
+    check_output(out.cpu().numpy(), ref, dtype, f"step with group map, {dtype}")
+    ok, e = lse_ok(lse.cpu().numpy(), ref_lse, 1e-5 if dtype == "f32" else 1e-3)
     assert ok, e
     assert c.err_flag() == 0
 
