@@ -167,7 +167,12 @@ gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_no
  * through their log-sum-exp. With num_splits == 0 (automatic) the matrix-core kernel instead
  * cuts the 32-position tiles of all sequences, taken in sequence order, into equal ranges (see
  * gva_decode_num_ranges), so every work-group gets the same amount of cache to read whatever
- * the lengths; the chunks of one sequence are merged the same way.
+ * the lengths; the chunks of one sequence are merged the same way. Small batches at d_h of 32
+ * or 64 (B G <= 256 sequence-groups, H / G of 1, 2, 4 or 8; automatic split count, matrix-core
+ * kernel) are decoded in ONE launch instead: K work-groups per (sequence, group) each read a
+ * contiguous share of the positions cut from max_len, and the last of them to finish merges
+ * the K partials (through the workspace, with a ticket per (sequence, group) in its first 1024
+ * bytes); no combine follows.
  * seq_len[b] == 0 gives out = 0 and lse = -inf.
  *   seq_len: device int32 [B]. max_len: host upper bound on every seq_len[b] (it sizes the
  *   split plan; a larger length raises GVA_DEVERR_LENGTH and makes that row NaN).
@@ -180,9 +185,10 @@ gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_no
  *   of 8 elements (returns GVA_ERR_UNSUPPORTED otherwise).
  *   workspace: device, 256-byte aligned, at least gva_decode_workspace_bytes(...) bytes,
  *   zero-filled before its first use (e.g. with hipMemsetAsync once after allocating it). Its
- *   first 1024 bytes hold the tickets of the one-launch decode step (gva_decode_step); no call
- *   writes partials there and every call leaves them at zero, so one fill serves every later
- *   call of any of these entry points. Calls that overlap must not share a workspace. */
+ *   first 1024 bytes hold the tickets of the one-launch plans (small batches of gva_decode and
+ *   gva_decode_step); no call writes partials there and every call leaves them at zero, so one
+ *   fill serves every later call of any of these entry points. Calls that overlap must not
+ *   share a workspace. */
 size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_len,
                                   int32_t num_splits);
 /* The split count gva_decode will use for these arguments with per-sequence chunks (an
@@ -190,7 +196,8 @@ size_t gva_decode_workspace_bytes(const gva_dims *dims, int32_t B, int32_t max_l
 int32_t gva_decode_num_splits(const gva_dims *dims, int32_t B, int32_t max_len,
                               int32_t num_splits);
 /* The number of equal tile ranges of the matrix-core kernel's automatic plan (num_splits == 0);
- * 0 on bad arguments or when that plan falls back to per-sequence chunks. */
+ * 0 on bad arguments, when that plan falls back to per-sequence chunks (one sequence), or when
+ * the batch takes the one-launch plan (small batches at d_h of 32 or 64). */
 int32_t gva_decode_num_ranges(const gva_dims *dims, int32_t B, int32_t max_len);
 gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
                       const int32_t *seq_len, int32_t max_len, const float *q_abs, float scale,
@@ -207,8 +214,10 @@ gva_status gva_decode(const gva_dims *dims, const gva_cache *cache, int32_t B,
  * device current. The call allocates nothing (no hipMalloc, no allocating library routine).
  *   Arguments: as for gva_decode, without workspace and workspace_bytes.
  *   Returns GVA_ERR_WORKSPACE, before any launch, when the plan's partials need more than
- *   GVA_NOALLOC_SCRATCH_BYTES (gva_decode_workspace_bytes gives the need); nothing in the array
- *   has to start at zero, so no call clears it.
+ *   GVA_NOALLOC_SCRATCH_BYTES (gva_decode_workspace_bytes gives the need). The one-launch plan's
+ *   tickets sit in the array's first 1024 bytes: they start at zero (a static array, cleared
+ *   once more by a small kernel on the first call's stream when the array's address is looked
+ *   up) and every call leaves them at zero.
  *   All calls on one device share its array: calls that overlap on one device (other streams,
  *   other threads) race and must be serialised by the caller. */
 #define GVA_NOALLOC_SCRATCH_BYTES (32u << 20)

@@ -204,11 +204,29 @@ def test_balanced_range_planning(L):
     assert gb.gva_decode_num_ranges(d, 2, 0) == 0
     d4 = _dims(H=16, G=4, d_h=64, d_n=64)
     assert gb.gva_decode_num_ranges(d4, 256, 32769) == 768             # 3 x 256 four-wave groups
-    assert gb.gva_decode_num_ranges(d4, 8, 4097) == 256                # 1032 tiles / 32 < 256
+    assert gb.gva_decode_num_ranges(d4, 65, 4097) == 263               # 8385 tiles / 32 > 256
     # the workspace query covers every plan, the GQA comparator's too (two four-wave
     # work-groups per range at G = 8: up to 384 ranges)
     ws = gb.gva_decode_workspace_bytes(d, 256, 32769, 0)
     assert ws >= (384 + 256) * 32 * (128 + 2) * 4 + 257 * 4
+
+
+def test_merged_decode_planning(L):
+    """Small batches at d_h of 32 or 64 (B G <= 256 sequence-groups, automatic split count) take
+    the merged plan: no tile ranges, and a workspace that holds the tickets and K partials per
+    (sequence, group) with K = min(256 / (B G), ceil(tiles / 8), 32). d_h = 128 keeps the
+    ranges."""
+    d64 = _dims(H=16, G=4, d_h=64, d_n=64)
+    assert gb.gva_decode_num_ranges(d64, 8, 4097) == 0
+    assert gb.gva_decode_num_ranges(d64, 64, 100) == 0                 # 256 pairs, K = 1
+    assert gb.gva_decode_num_ranges(d64, 65, 100) > 0                  # 260 pairs: ranges
+    assert gb.gva_decode_num_ranges(_dims(), 8, 32768) == 256          # d_h = 128: ranges
+    assert gb.gva_decode_num_ranges(_dims(H=8, G=4, d_h=32, d_n=32), 3, 5000) == 0
+    # K = min(256 / 32, ceil(129 / 8), 32) = 8 partials of 4 heads per pair, after the tickets
+    ws = gb.gva_decode_workspace_bytes(d64, 8, 4097, 0)
+    assert ws >= 1024 + 8 * 32 * 4 * (64 + 2) * 4 and ws % 256 == 0
+    # an explicit split count keeps the split grid
+    assert gb.gva_decode_num_splits(d64, 8, 4097, 16) == 13      # chunks of 320
 
 
 def test_append_and_absorb_validation(L):
@@ -441,7 +459,8 @@ def test_decode_step_launches_plan(L):
     assert n(64, 4097, 0, 0) == 1                    # 256 sequence-groups
     assert n(65, 4097, 0, 0) == 3                    # 260: the balanced plan and its combine
     assert n(8, 4097, 3, 0) == 3                     # an explicit split count
-    assert n(8, 32769, 0, 0) == 3                    # more than 4 MiB of values per group
+    assert n(8, 32769, 0, 0) == 2                    # more than 4 MiB of values per group:
+    #                                                  append + absorb, then the merged decode
     assert n(8, 4097, 0, gb.GVA_KERNEL_GENERIC) == 3
     assert n(0, 100, 0, 0) == 0 and n(4, 100, 0, 9) == 0
     d128 = _dims()                                   # d_h = 128: two launches

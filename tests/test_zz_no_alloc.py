@@ -61,3 +61,28 @@ def test_noalloc_matches_decode_twice_second_smaller(num_splits, kernel):
     assert lse_ok(l2, ref2_lse, 1e-3)[0]
     assert np.all(o2[0] == 0) and np.all(np.isneginf(l2[0]))
     assert c.err_flag() == 0
+
+
+def test_noalloc_merged_plan_twice_second_smaller():
+    """The merged plan (d_h = 64, a small batch): its tickets live at the head of the static
+    array, start at zero and are left at zero by every call."""
+    w = synth.workload("C4", B=10, lengths_uniform=(300, 3000), H=16, G=4, d_h=64, d_n=64,
+                       d_r=16)
+    c = Case(w)
+    c.append_prefix()
+    assert gb.gva_decode_num_ranges(c.cdims, w.B, int(c.lens.max())) == 0
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((w.B, w.H, w.d_h + w.d_r))
+    (o1, l1), (r1, rl1) = _both(c, c.lens, q)
+    assert o1.tobytes() == r1.tobytes() and l1.tobytes() == rl1.tobytes()
+    ref, ref_lse = c.oracle_decode(c.lens, q)
+    check_output(o1, ref, "bf16", "noalloc merged first call")
+    assert lse_ok(l1, ref_lse, 1e-3)[0]
+    short = np.maximum(c.lens // 4, 1)
+    short[3] = 0
+    (o2, l2), (r2, rl2) = _both(c, short, q)
+    assert o2.tobytes() == r2.tobytes() and l2.tobytes() == rl2.tobytes()
+    ref2, ref2_lse = c.oracle_decode(short, q)
+    check_output(o2, ref2, "bf16", "noalloc merged second call")
+    assert lse_ok(l2, ref2_lse, 1e-3)[0]
+    assert c.err_flag() == 0

@@ -49,8 +49,16 @@ gva_status hip_status(hipError_t e, const char *what) {
   return gva::fail(GVA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Device address of this device's `scratch` (looked up on first use, then cached).
-gva_status device_scratch(void **out) {
+// Zeroes the first n words at p (one work-group).
+__global__ void k_zero_words(uint32_t *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Device address of this device's `scratch` (looked up on first use, then cached). The first
+// lookup on a device also clears the tickets at the head of the array (zero already, as a
+// static array, and left at zero by every call), in order on `stream` before the caller's
+// launches.
+gva_status device_scratch(void **out, hipStream_t stream) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e, "hipGetDevice");
@@ -65,6 +73,10 @@ gva_status device_scratch(void **out) {
       e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
       if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
       if (!p) return gva::fail(GVA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, stream, static_cast<uint32_t *>(p),
+                         static_cast<int>(gva::kWsHeader / 4));
+      e = hipGetLastError();
+      if (e != hipSuccess) return hip_status(e, "scratch ticket clear launch");
       g_scratch_ptr[dev].store(p, std::memory_order_release);
     }
   }
@@ -83,6 +95,23 @@ gva_status launch_decode(const gva_dims *dims, const gva_cache *cache, int32_t B
   a.max_len = max_len;
   a.q_abs = q_abs;
   a.qscale = scale * 1.4426950408889634f;
+  if (plan.merged_K > 0) {
+    // small batch: decode and merge in one launch (tickets and partials in the workspace)
+    gva::StepArgs sa{};
+    sa.a = a;
+    sa.a.out = out;
+    sa.a.lse = lse;
+    sa.K = plan.merged_K;
+    sa.tiles_per_wave = plan.tiles_per_wave;
+    if (plan.merged_K > 1) {
+      char *ws = static_cast<char *>(workspace);
+      sa.ticket = reinterpret_cast<int32_t *>(ws);
+      sa.part_o = reinterpret_cast<float *>(ws + plan.off_o);
+      sa.part_m = reinterpret_cast<float *>(ws + plan.off_m);
+      sa.part_l = reinterpret_cast<float *>(ws + plan.off_l);
+    }
+    return hip_status(gva::launch_decode_merged(sa, stream), "merged decode launch");
+  }
   a.num_splits = plan.num_splits;
   a.chunk = plan.chunk;
   a.num_ranges = plan.num_ranges;
@@ -162,7 +191,7 @@ gva_status gva_decode_noalloc(const gva_dims *dims, const gva_cache *cache, int3
                      plan.ws_bytes, static_cast<size_t>(GVA_NOALLOC_SCRATCH_BYTES));
   void *ws = nullptr;
   if (plan.ws_bytes > 0) {
-    st = device_scratch(&ws);
+    st = device_scratch(&ws, stream);
     if (st != GVA_OK) return st;
   }
   return launch_decode(dims, cache, B, seq_len, max_len, q_abs, scale, plan, use_mfma, ws, out,

@@ -169,6 +169,20 @@ bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_spli
                  bool balanced, DecodePlan *plan, bool share_key) {
   if (!d || B < 1 || max_len < 0 || num_splits < 0 || num_splits > kMaxSplits) return false;
   *plan = DecodePlan{};
+  if (balanced && share_key && num_splits == 0 && decode_merged_shape(d, B)) {
+    // small batch: K work-groups per (sequence, group) merge their partials themselves
+    StepPlan sp;
+    if (!plan_step(d, B, max_len, &sp)) return false;
+    plan->merged_K = sp.K;
+    const int64_t kw = static_cast<int64_t>(sp.K) * step_waves_of(d->d_h);
+    const int64_t tiles = (static_cast<int64_t>(max_len) + kTilePositions - 1) / kTilePositions;
+    plan->tiles_per_wave = static_cast<int32_t>((tiles + kw - 1) / kw);
+    plan->off_o = sp.off_po;
+    plan->off_m = sp.off_pm;
+    plan->off_l = sp.off_pl;
+    plan->ws_bytes = sp.ws_bytes;
+    return true;
+  }
   const int64_t tiles_max = static_cast<int64_t>(B) * ((max_len + kTilePositions - 1) / kTilePositions);
   if (balanced && num_splits == 0 && B > 1 && tiles_max > 0 &&
       tiles_max < (int64_t(1) << 31) && d->G > 0) {
@@ -289,6 +303,13 @@ bool step_fused_supported(const gva_dims *d, const gva_cache *c, int32_t B, int3
   if (static_cast<int64_t>(max_len) * d->d_h * 2 > (int64_t{4} << 20)) return false;
   (void)c;
   return true;
+}
+
+bool decode_merged_shape(const gva_dims *d, int32_t B) {
+  const int hpg = d->H / d->G;
+  if (d->d_h != 32 && d->d_h != 64) return false;
+  if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8) return false;
+  return static_cast<int64_t>(B) * d->G <= kPlanCUs;
 }
 
 bool step_small_supported(const gva_dims *d, const gva_cache *c, int32_t B, int32_t max_len,
@@ -558,7 +579,7 @@ int32_t gva_decode_step_launches(const gva_dims *dims, const gva_cache *cache, i
   if (gva::step_small_supported(dims, cache, B, max_len, num_splits, use_mfma)) return 1;
   gva::DecodePlan plan;
   if (!gva::plan_decode(dims, B, max_len, num_splits, use_mfma, &plan)) return 0;
-  return (plan.num_splits > 1 || plan.num_ranges > 0) ? 3 : 2;
+  return (plan.num_splits > 1 || plan.num_ranges > 0) ? 3 : 2;  // merged: no combine
 }
 
 int32_t gva_decode_num_ranges(const gva_dims *dims, int32_t B, int32_t max_len) {

@@ -82,14 +82,20 @@ struct DecodePlan {
   size_t off_o;
   size_t off_prefix;    // balanced mode: the per-sequence tile prefix, int32 [B + 1]
   size_t off_queue;     // latent comparator: its work queue's counter (256 bytes at the end)
+  // merged mode (small batches): merged_K work-groups per (sequence, group) decode runs of
+  // tiles_per_wave tiles each and merge their partials in the same launch (the one-launch
+  // step's layout: tickets in the header, partials at off_o, off_m, off_l); 0 otherwise
+  int32_t merged_K;
+  int32_t tiles_per_wave;
 };
 // The latent comparator's workspace: the split plan's partials, then one 256-byte word for the
 // counter of its work queue (so it is never empty).
 void add_latent_queue(DecodePlan *plan);
 
-// Plans the split of positions [0, max_len) into chunks (balanced == false), or the cut of all
-// sequences' 32-position tiles into equal ranges (balanced == true, the matrix-core kernel's
-// automatic mode); returns false on bad arguments.
+// Plans the split of positions [0, max_len) into chunks (balanced == false), or, for the
+// matrix-core kernel's automatic mode (balanced == true), the merged plan when the batch is
+// small (B * G <= kPlanCUs, share_key, a shape decode_merged_supported takes) else the cut of
+// all sequences' 32-position tiles into equal ranges; returns false on bad arguments.
 bool plan_decode(const gva_dims *d, int32_t B, int32_t max_len, int32_t num_splits,
                  bool balanced, DecodePlan *plan, bool share_key = true);
 
@@ -225,6 +231,12 @@ struct StepPlan {
 };
 bool plan_step(const gva_dims *d, int32_t B, int32_t max_len, StepPlan *plan);
 hipError_t launch_step_fused(const StepArgs &s, hipStream_t stream);
+// The decode alone with the one-launch step's split and merge (the query rows read from q_abs,
+// no token appended): one launch, no combine. Shapes: d_h of 32 or 64, H / G of 1, 2, 4 or 8,
+// B * G <= kPlanCUs. (At d_h = 128 the two-launch plans measured faster: for one sequence of
+// 131072 positions 69 against 61 us, for 4 of 8705 28 against 26 us.)
+bool decode_merged_shape(const gva_dims *d, int32_t B);
+hipError_t launch_decode_merged(const StepArgs &s, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);

@@ -718,6 +718,9 @@ hipError_t launch_nh(const gva::DecodeArgs &a, dim3 grid, dim3 block, hipStream_
 // No work-group waits on another, and nothing is left for a second launch. (Ordering the merge
 // with release/acquire fences instead writes back and invalidates whole L2 caches: measured
 // 18 to 270 microseconds per launch here, against under 2 for the write-through pattern.)
+// STEP == false is the decode alone with the same split and merge (gva_decode's plan for small
+// batches): steps 1 and 2 are skipped, and each wave loads its query rows from q_abs, as the
+// split decode does, with its first tiles.
 template <int KS>
 constexpr int step_waves() { return 8; }   // gva::step_waves_of(32 KS)
 constexpr int kStepRegionBytes = 144 * 1024;   // staging of M, then tile copies, then the merge
@@ -750,16 +753,16 @@ __device__ __forceinline__ void load_tile_run(const gva::DecodeArgs &a, int32_t 
   }
 }
 
-template <int KS, int NH, int W>
+template <int KS, int NH, int W, bool STEP>
 __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   constexpr int DH = 32 * KS;
   using L = TileLds<KS>;
   static_assert(W * L::kWave <= kStepRegionBytes, "tile copies exceed the region");
   static_assert(W * NH * (DH + 2) * 4 <= kStepRegionBytes, "merge area exceeds the region");
-  static_assert(32 * NH * (DH + 2) * 4 <= kStepRegionBytes, "K <= 32 partials exceed the region");
+  static_assert(32 * NH * (DH + 2) * 4 + 64 <= kStepRegionBytes, "K <= 32 partials exceed the region");
   __shared__ __align__(16) uint8_t region[kStepRegionBytes];
-  __shared__ __align__(16) float q_lds[NH][DH + 32];     // q~ (DH), then r (d_r <= 32)
-  __shared__ __align__(16) uint16_t tok_v[DH];           // the new token's values, group g
+  __shared__ __align__(16) float q_lds[STEP ? NH : 1][DH + 32];  // q~ (DH), then r (d_r <= 32)
+  __shared__ __align__(16) uint16_t tok_v[DH];                   // the new token's values, group g
   __shared__ __align__(16) uint16_t tok_kr[32];          // its rotated positional key (padded)
   __shared__ int s_bad;
   __shared__ int s_last;
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   const int d_n = s.d_n;
   const int row_len = DH + d_r;
   const float qnan = __int_as_float(0x7fc00000);
-  const int p = s.pos[b];
+  const int p = STEP ? s.pos[b] : 0;
   const int len = a.seq_len[b];
   const int cap = a.max_blocks << a.log2_bs;
 
@@ -810,18 +813,20 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   }
   int32_t PA = 0, PB = 0;                                // later tiles' entries (vector loads)
   const bool len_bad = len < 0 || len > a.max_len || len > cap;
-  const bool rope_bad = p < 0 || p >= s.max_pos;         // the absorbed query is NaN
+  const bool rope_bad = STEP && (p < 0 || p >= s.max_pos);  // the absorbed query is NaN
   // the append's inputs go out now too: the token's block-table entry, its values (one pair per
   // lane below d_h / 2) and its positional key pairs with their (cos, sin)
   int32_t aerr = 0;
-  if (p < 0) aerr = GVA_DEVERR_LENGTH;
-  else if (p >= cap) aerr = GVA_DEVERR_CAPACITY;
-  else if (p >= s.max_pos) aerr = GVA_DEVERR_ROPE;
-  const int32_t pblk = aerr ? 0 : bt[p >> lb];
+  if constexpr (STEP) {
+    if (p < 0) aerr = GVA_DEVERR_LENGTH;
+    else if (p >= cap) aerr = GVA_DEVERR_CAPACITY;
+    else if (p >= s.max_pos) aerr = GVA_DEVERR_ROPE;
+  }
+  const int32_t pblk = (!STEP || aerr) ? 0 : bt[p >> lb];
   const int half_r = d_r >> 1;
   float2 tok_x = {0.f, 0.f}, tok_k = {0.f, 0.f};
   double2 tok_cs = {1.0, 0.0};
-  if (!aerr) {
+  if (STEP && !aerr) {
     if (tid < DH / 2)
       tok_x = reinterpret_cast<const float2 *>(s.v_new + (static_cast<int64_t>(b) * a.G + g) * DH)[tid];
     if (tid < half_r) {
@@ -833,7 +838,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   // (lane t < NH d_r / 2 rotates pair t % (d_r / 2) of head t / (d_r / 2))
   float2 rq = {0.f, 0.f};
   double2 rq_cs = {1.0, 0.0};
-  if (!rope_bad && tid < NH * half_r) {
+  if (STEP && !rope_bad && tid < NH * half_r) {
     const int c = tid / half_r;
     const int k = tid - c * half_r;
     rq = reinterpret_cast<const float2 *>(s.q_rope + (static_cast<int64_t>(b) * a.H + head(c)) * d_r)[k];
@@ -855,9 +860,28 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
     }
     tile_a_issued = true;
   };
+  // decode only: the query rows (q~ | r) of this lane's column, as the split decode reads them
+  // (lanes without a column read their group's first head and are masked with a bitwise and)
+  const int cq = n < NH ? n : (n < 2 * NH ? n - NH : 0);
+  const int col_mask = n < 2 * NH ? -1 : 0;
+  float4 qraw[2 * KS], rraw[2];
+  if constexpr (!STEP) {
+    const float *qp = a.q_abs + (static_cast<int64_t>(b) * a.H + head(cq)) * row_len;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 *src = reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q);
+      qraw[2 * ks] = src[0];
+      qraw[2 * ks + 1] = src[1];
+    }
+    const float4 *rsrc = reinterpret_cast<const float4 *>(qp + DH + 8 * min(q, (d_r >> 3) - 1));
+    rraw[0] = rsrc[0];
+    rraw[1] = rsrc[1];
+    issue_tile_a();
+    __syncthreads();                                     // s_bad is cleared
+  }
 
   // ---- 1. absorption (q~ in the order of gva_absorb_query, so q_abs is bit-identical) ----
-  {
+  if constexpr (STEP) {
     float *mst = reinterpret_cast<float *>(region);
     const int d4 = d_n >> 2;
     const int stride4 = d4 + 1;                          // rows padded by 16 bytes
@@ -947,11 +971,14 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
 
   // ---- 2. append (the checks and arithmetic of gva_cache_append) ----
   int64_t blk = -1;
-  if (!aerr) {
-    if (pblk < 0 || static_cast<int64_t>(pblk) >= a.num_blocks) aerr = GVA_DEVERR_BLOCK;
-    else blk = pblk;
+  bool tok_ok = false;                                   // decode only: no token
+  if constexpr (STEP) {
+    if (!aerr) {
+      if (pblk < 0 || static_cast<int64_t>(pblk) >= a.num_blocks) aerr = GVA_DEVERR_BLOCK;
+      else blk = pblk;
+    }
+    tok_ok = aerr == 0;
   }
-  const bool tok_ok = aerr == 0;
   if (g == 0 && kk == 0 && tid == 0) {
     if (aerr) gvad::raise_err(a.err_flag, aerr);
     if (rope_bad) gvad::raise_err(a.err_flag, GVA_DEVERR_ROPE);
@@ -979,7 +1006,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
       reinterpret_cast<uint32_t *>(tok_kr)[tid] = w;
     }
   }
-  __syncthreads();                                       // q~, r and the token are in LDS
+  if constexpr (STEP) __syncthreads();                   // q~, r and the token are in LDS
 
   // ---- 3. decode the wave's run of tiles ----
   constexpr int SH = NH;
@@ -994,32 +1021,59 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   acc.lsum = 0.0f;
   if (c0 < c1) {                                         // uniform per wave
     bf16x8 QX[KS], QY[KS], RX, RY;
-    const float *qp = q_lds[col_ok ? c : 0];
+    if constexpr (STEP) {
+      const float *qp = q_lds[col_ok ? c : 0];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      float x[8];
-      const float4 x0 = *reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q);
-      const float4 x1 = *reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q + 4);
-      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        const float4 x0 = *reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q);
+        const float4 x1 = *reinterpret_cast<const float4 *>(qp + 32 * ks + 8 * q + 4);
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = col_ok ? x[e] * a.qscale : 0.0f;
-      u32x4 hi, lo;
-      split8(x, hi, lo);
-      QX[ks] = as_bf16(use_lo ? lo : hi);
-      QY[ks] = as_bf16(lo);
-    }
-    {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 8 * q + e;
-        x[e] = (col_ok && i < d_r) ? qp[DH + i] * a.qscale : 0.0f;
+        for (int e = 0; e < 8; ++e) x[e] = col_ok ? x[e] * a.qscale : 0.0f;
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        QX[ks] = as_bf16(use_lo ? lo : hi);
+        QY[ks] = as_bf16(lo);
       }
-      u32x4 hi, lo;
-      split8(x, hi, lo);
-      RX = as_bf16(use_lo ? lo : hi);
-      RY = as_bf16(lo);
+      {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * q + e;
+          x[e] = (col_ok && i < d_r) ? qp[DH + i] * a.qscale : 0.0f;
+        }
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        RX = as_bf16(use_lo ? lo : hi);
+        RY = as_bf16(lo);
+      }
+    } else {
+      // the rows loaded at the start, masked (a bitwise and) and scaled as the split decode does
+      auto masked = [](float v, int m) { return __int_as_float(__float_as_int(v) & m); };
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float4 x0 = qraw[2 * ks], x1 = qraw[2 * ks + 1];
+        float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = masked(x[e], col_mask) * a.qscale;
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        QX[ks] = as_bf16(use_lo ? lo : hi);
+        QY[ks] = as_bf16(lo);
+      }
+      {
+        const int r_mask = 8 * q < d_r ? col_mask : 0;
+        const float4 r0 = rraw[0], r1 = rraw[1];
+        float x[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = masked(x[e], r_mask) * a.qscale;
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        RX = as_bf16(use_lo ? lo : hi);
+        RY = as_bf16(lo);
+      }
     }
     uint8_t *lw_wr = region + wave * L::kWave + n * L::kRow + 16 * q;
     const uint8_t *lw_rd = region + wave * L::kWave + (lane >> 2) * L::kRow + 8 * (lane & 3);
@@ -1149,9 +1203,10 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   // the last work-group merges the K partials of (b, g): one round of device-scope loads stages
   // them in LDS (rows prow0 .. prow0 + K NH - 1 are contiguous), then the merge reads LDS
   const int64_t prow0 = static_cast<int64_t>(b * a.G + g) * K * NH;
+  const int kn4 = (K * NH + 3) & ~3;                     // keeps go 16-byte aligned
   float *gm = reinterpret_cast<float *>(region);         // [K][NH]
-  float *gl = gm + K * NH;                               // [K][NH]
-  float *go = gl + K * NH;                               // [K][NH][DH]
+  float *gl = gm + kn4;                                  // [K][NH]
+  float *go = gl + kn4;                                  // [K][NH][DH], then one spare row
   {
     // buffer loads with the device-scope cache policy (sc1): they read past this XCD's L2 like
     // the atomic loads would, but several can be in flight; the ranges end at this pair's rows
@@ -1169,56 +1224,89 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
       mv = __builtin_amdgcn_raw_buffer_load_b32(rm, 4 * tid, 0, kSc1);
       lv = __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * tid, 0, kSc1);
     }
+    // the o rows in batches of 16 loads per lane, all in flight before the first LDS store
+    // (loads past the range return zero; their stores go to a spare slot after the rows, so
+    // every store is made and no load is held back behind a branch)
     const int n4 = K * NH * DH / 4;
-#pragma unroll 4
-    for (int e = tid; e < n4; e += 64 * W)
-      reinterpret_cast<u32x4 *>(go)[e] = __builtin_amdgcn_raw_buffer_load_b128(ro, 16 * e, 0, kSc1);
+    constexpr int kBatchM = 16;
+    for (int e0 = tid; e0 < n4; e0 += kBatchM * 64 * W) {
+      u32x4 v[kBatchM];
+#pragma unroll
+      for (int u = 0; u < kBatchM; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(ro, 16 * (e0 + u * 64 * W), 0, kSc1);
+#pragma unroll
+      for (int u = 0; u < kBatchM; ++u) {
+        const int e = e0 + u * 64 * W;
+        reinterpret_cast<u32x4 *>(go)[e < n4 ? e : n4] = v[u];
+      }
+    }
     if (has_ml) {
       gm[tid] = __uint_as_float(mv);
       gl[tid] = __uint_as_float(lv);
     }
   }
   __syncthreads();
-  for (int o = tid; o < NH * DH; o += 64 * W) {
-    const int ch = o / DH;
-    const int d = o - ch * DH;
+  // a thread per four dims of a head: the K partials' m and l are LDS broadcasts to the head's
+  // threads, and the loops are unrolled so that their LDS reads are in flight together (k in
+  // ascending order, so the sums are those of the one-dim-per-thread form)
+  constexpr int D4 = DH / 4;
+  for (int o4 = tid; o4 < NH * D4; o4 += 64 * W) {
+    const int ch = o4 / D4;
+    const int d4 = o4 - ch * D4;
     float ms = -INFINITY;
     bool nan_in = false;
+#pragma unroll 8
     for (int k = 0; k < K; ++k) {
       const float mk = gm[k * NH + ch];
       nan_in = nan_in || mk != mk;
       ms = fmaxf(ms, mk);
     }
-    float lt = 0.0f, ov = 0.0f;
+    float lt = 0.0f;
+    f32x4 ov = {0.f, 0.f, 0.f, 0.f};
     if (ms != -INFINITY && !nan_in) {
+#pragma unroll 8
       for (int k = 0; k < K; ++k) {
         const float f = __builtin_amdgcn_exp2f(gm[k * NH + ch] - ms);
         lt += gl[k * NH + ch] * f;
-        ov += go[(k * NH + ch) * DH + d] * f;
+        const f32x4 ok = *reinterpret_cast<const f32x4 *>(go + (k * NH + ch) * DH + 4 * d4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] += ok[r] * f;
       }
     }
     const int64_t orow = static_cast<int64_t>(b) * a.H + head(ch);
-    a.out[orow * DH + d] = nan_in ? qnan : (lt > 0.0f ? ov / lt : 0.0f);
-    if (d == 0 && a.lse)
+    f32x4 res;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) res[r] = nan_in ? qnan : (lt > 0.0f ? ov[r] / lt : 0.0f);
+    *reinterpret_cast<f32x4 *>(a.out + orow * DH + 4 * d4) = res;
+    if (d4 == 0 && a.lse)
       a.lse[orow] = nan_in ? qnan : (lt > 0.0f ? (ms + log2f(lt)) * gvad::kLn2 : -INFINITY);
   }
   if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int KS, int NH>
+template <int KS, int NH, bool STEP>
 hipError_t launch_step_ks(const gva::StepArgs &s, hipStream_t stream) {
   constexpr int W = step_waves<KS>();
   const int64_t items = static_cast<int64_t>(s.a.B) * s.K;
   const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8 * s.a.G));
-  hipLaunchKernelGGL((k_step_fused<KS, NH, W>), grid, dim3(64 * W), 0, stream, s);
+  hipLaunchKernelGGL((k_step_fused<KS, NH, W, STEP>), grid, dim3(64 * W), 0, stream, s);
   return hipGetLastError();
 }
 
 template <int NH>
 hipError_t launch_step_nh(const gva::StepArgs &s, hipStream_t stream) {
   switch (s.a.d_h / 32) {
-    case 1: return launch_step_ks<1, NH>(s, stream);
-    case 2: return launch_step_ks<2, NH>(s, stream);
+    case 1: return launch_step_ks<1, NH, true>(s, stream);
+    case 2: return launch_step_ks<2, NH, true>(s, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NH>
+hipError_t launch_merged_nh(const gva::StepArgs &s, hipStream_t stream) {
+  switch (s.a.d_h) {
+    case 32: return launch_step_ks<1, NH, false>(s, stream);
+    case 64: return launch_step_ks<2, NH, false>(s, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1233,6 +1321,16 @@ hipError_t launch_step_fused(const StepArgs &s, hipStream_t stream) {
     case 2: return launch_step_nh<2>(s, stream);
     case 4: return launch_step_nh<4>(s, stream);
     case 8: return launch_step_nh<8>(s, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_merged(const StepArgs &s, hipStream_t stream) {
+  switch (s.a.H / s.a.G) {
+    case 1: return launch_merged_nh<1>(s, stream);
+    case 2: return launch_merged_nh<2>(s, stream);
+    case 4: return launch_merged_nh<4>(s, stream);
+    case 8: return launch_merged_nh<8>(s, stream);
     default: return hipErrorInvalidValue;
   }
 }
