@@ -210,6 +210,8 @@ __global__ __launch_bounds__(64) void k_decode_generic(gva::DecodeArgs a, int he
 constexpr int kCombineMaxWaves = 16;
 // partial rows per sequence up to which the combine takes one wave per (sequence, head)
 constexpr int kCombineWaveRows = 16;
+// o rows per lane of k_combine loaded in the first round
+constexpr int kCombineRows = 16;
 
 __device__ __forceinline__ float block_reduce(float v, float *scratch, int nw, bool is_max) {
   v = is_max ? gvad::wave_max(v) : gvad::wave_sum(v);
@@ -283,9 +285,26 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
     if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
     return;
   }
-  float mx = -INFINITY;
-  float bad = 0.0f;
-  for (int s = tid; s < ns; s += nthr) {
+  // Every partial this thread needs goes out before any is used: split tid's m and l (a thread
+  // past ns re-reads split ns - 1 and stores the same weight as thread ns - 1 does), and
+  // the first kCombineRows of this wave's o rows wave, wave + nw, ... (rows past ns re-read row
+  // ns - 1 and are not used). One round of loads instead of one per step of the reduction; the
+  // arithmetic and its order are unchanged. Split counts above the block's threads, and rows
+  // past the first kCombineRows, are read in further passes.
+  const int64_t step = static_cast<int64_t>(a.H) * a.d_h;
+  const int sm = min(tid, ns - 1);
+  const float m0 = a.part_m[row0 + static_cast<int64_t>(sm) * a.H];
+  const float l0 = a.part_l[row0 + static_cast<int64_t>(sm) * a.H];
+  const float *po = a.part_o + row0 * a.d_h + (dim_ok ? d : 0);
+  float ov[kCombineRows];
+#pragma unroll
+  for (int j = 0; j < kCombineRows; ++j)
+    ov[j] = po[static_cast<int64_t>(min(wave + nw * j, ns - 1)) * step];
+  const int keep = tid < ns ? -1 : 0;                  // a bitwise blend, not a select on a load
+  float mx = fmaxf(-INFINITY, __int_as_float((__float_as_int(m0) & keep) |
+                                             (__float_as_int(-INFINITY) & ~keep)));
+  float bad = (tid < ns && isnan(m0)) ? 1.0f : 0.0f;
+  for (int s = tid + nthr; s < ns; s += nthr) {
     const float ms = a.part_m[row0 + static_cast<int64_t>(s) * a.H];
     bad += isnan(ms) ? 1.0f : 0.0f;
     mx = fmaxf(mx, ms);
@@ -294,7 +313,12 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   mx = block_reduce(mx, scratch, nw, true);
   const bool poison = block_reduce(bad, scratch, nw, false) > 0.0f;
   float L = 0.0f;
-  for (int s = tid; s < ns; s += nthr) {
+  {
+    const float f = exp2f(m0 - mx);
+    w_s[sm] = f;
+    L = __int_as_float(__float_as_int(l0 * f) & keep);
+  }
+  for (int s = tid + nthr; s < ns; s += nthr) {
     const float f = exp2f(w_s[s] - mx);
     w_s[s] = f;
     L += a.part_l[row0 + static_cast<int64_t>(s) * a.H] * f;
@@ -303,10 +327,13 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   if (nw == 1) __syncthreads();  // the w_s writes of other lanes must be visible
   float acc = 0.0f;
   if (dim_ok) {
-    const float *po = a.part_o + row0 * a.d_h + d;
-    const int64_t step = static_cast<int64_t>(a.H) * a.d_h;
+#pragma unroll
+    for (int j = 0; j < kCombineRows; ++j) {
+      const int s = wave + nw * j;
+      if (s < ns) acc = fmaf(ov[j], w_s[s], acc);      // uniform per wave
+    }
 #pragma unroll 8
-    for (int s = wave; s < ns; s += nw) acc = fmaf(po[s * step], w_s[s], acc);
+    for (int s = wave + nw * kCombineRows; s < ns; s += nw) acc = fmaf(po[s * step], w_s[s], acc);
   }
   if (nw > 1) {
     part[wave][lane] = acc;
