@@ -432,7 +432,8 @@ def main():
 
 
 def bench_ceiling(torch, gb, stream, big_bytes, long_bytes, iters=10):
-    """The rate at which plain 16-byte streaming reads leave HBM (gva_diag_stream_read), at the
+    """The rate at which plain 16-byte non-temporal streaming reads leave HBM
+    (gva_diag_stream_read, each load instruction reading 1 KiB of consecutive bytes), at the
     ragged batch's cache size (one buffer, far above the 256 MB last-level cache) and at the
     T = 131072 cache size (three buffers rotated, as the long-context decode is timed), over a
     small sweep of grid sizes and loads in flight; and a plain device copy of 1 GiB (read and

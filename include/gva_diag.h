@@ -4,8 +4,9 @@
  * The decode is bound by HBM reads, so its roofline needs the rate at which this part streams
  * reads in practice, beside the 8 TB/s figure on the data sheet. gva_diag_stream_read is the
  * plainest kernel that moves bytes from HBM to the compute units: every lane issues 16-byte
- * loads, several in flight, over a contiguous buffer, and folds them into one word per
- * work-group so that the loads cannot be dropped.
+ * non-temporal loads (each load instruction reading 1 KiB of consecutive bytes), several in
+ * flight, over a contiguous buffer, and folds them into one word per work-group so that the
+ * loads cannot be dropped.
  */
 #ifndef GVA_DIAG_H_
 #define GVA_DIAG_H_

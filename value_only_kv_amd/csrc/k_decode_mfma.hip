@@ -140,6 +140,29 @@ struct Tile {
   u32x4 x[2][GQA ? KS : 1];        // GVA: positional key rows; GQA: key rows, like v
 };
 
+// A 16-byte load of cache rows that this launch reads once, marked non-temporal. Measured on a
+// plain streaming read of the ragged batch's 9.35 GB: 6.23 TB/s with ordinary loads, 7.10 TB/s
+// with non-temporal ones, but only when every load instruction covers whole 128-byte lines
+// (with the matrix-operand layout, where an instruction reads 64 bytes of each of 16 rows, the
+// non-temporal loads were no faster, and the decode was slower: the second half of each line
+// was fetched again). Hence the line layout below.
+__device__ __forceinline__ u32x4 stream_load(const uint16_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// Line layout of a 16-position block's value loads, for d_h = 32 KS with KS a power of two:
+// a row is 64 KS bytes (4 KS chunks of 16), and load k of lane L reads chunk L mod 4 KS of row
+// k (16 / KS) + L / (4 KS). Each load instruction then reads whole rows (1 KiB of consecutive
+// chunks when the group's rows are adjacent, whole 128-byte lines of each row otherwise, for
+// d_h >= 64). The rows go to the wave's LDS tile as they are, and the score operand is read
+// back from there in the matrix-operand layout.
+template <int KS>
+constexpr bool kLine = (KS & (KS - 1)) == 0;
+template <int KS>
+__device__ __forceinline__ int line_chunk(int lane) { return lane & (4 * KS - 1); }
+template <int KS>
+__device__ __forceinline__ int line_row(int lane, int k) { return k * (16 / KS) + lane / (4 * KS); }
+
 // Block-table entries of the two 16-position blocks of the tile at t0 (clamped to c1 - 1):
 // even lanes hold the first block's entry, odd lanes the second's. The per-lane address makes
 // this a vector load, so it completes in order with the V loads; it is issued a tile ahead and
@@ -155,15 +178,20 @@ __device__ __forceinline__ int32_t load_pages(const int32_t *__restrict__ bt, in
 // waits only for its own data. A block lies inside one cache block (block_size >= 16 and t0 is a
 // multiple of 16), so one table entry serves all of its lanes. Positions >= c1 read position
 // c1 - 1 instead (finite data from a block that is cached already); their scores are masked, so
-// they add exactly zero. vlane/klane are the lane-invariant parts of the element offsets.
+// they add exactly zero. vgrp is the value group's element offset, klane the lane-invariant
+// part of the positional key's. V is loaded in the line layout when kLine<KS> (T.v[tb][k] =
+// load k of block tb), else in the matrix-operand layout (T.v[tb][ks] = dims 32 ks + 8 q ..
+// of row n); the keys of the comparator (GQA) always in the operand layout.
 // SHARE: only the waves with fetch_key read the positional key (the others read a row of their
 // own work-group, kown, which stays in cache, and take the key from LDS instead); every load is
 // still issued, so the loads in flight stay the same on every path.
 template <int KS, bool GQA, bool SHARE>
 __device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, int t0, int c1,
-                                          int n, int64_t vlane, int64_t klane, Tile<KS, GQA> &T,
+                                          int n, int64_t vgrp, int64_t klane, Tile<KS, GQA> &T,
                                           bool &bad, bool fetch_key, int64_t kown) {
   const int mask = (1 << a.log2_bs) - 1;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
   const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
 #pragma unroll
@@ -173,13 +201,22 @@ __device__ __forceinline__ void load_tile(const gva::DecodeArgs &a, int32_t P, i
     bad |= !ok;
     const int64_t blk = ok ? pb : 0;
     const int f = min(t0 + 16 * tb, c1 - 1);          // first position read by this block
-    const int rn = min(n, c1 - 1 - f);                 // row within the block (clamped)
+    const int lim = c1 - 1 - f;                        // rows past it read row lim
+    const int rn = min(n, lim);                        // the operand layout's row (clamped)
     const int64_t row = static_cast<int64_t>((f & mask) + rn);
-    const uint16_t *vp = vbase + blk * a.v_sb + row * a.v_st + vlane;
+    const uint16_t *vblk = vbase + blk * a.v_sb + static_cast<int64_t>(f & mask) * a.v_st + vgrp;
+    if constexpr (kLine<KS>) {
+      const int ch = 8 * line_chunk<KS>(lane);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = *reinterpret_cast<const u32x4 *>(vp + 32 * ks);
+      for (int k = 0; k < KS; ++k)
+        T.v[tb][k] = stream_load(vblk + static_cast<int64_t>(min(line_row<KS>(lane, k), lim)) * a.v_st + ch);
+    } else {
+      const uint16_t *vp = vblk + static_cast<int64_t>(rn) * a.v_st + 8 * q;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = *reinterpret_cast<const u32x4 *>(vp + 32 * ks);
+    }
     if constexpr (GQA) {
-      const uint16_t *kp = static_cast<const uint16_t *>(a.k) + (vp - vbase);
+      const uint16_t *kp = static_cast<const uint16_t *>(a.k) + blk * a.v_sb + row * a.v_st + vgrp + 8 * q;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) T.x[tb][ks] = *reinterpret_cast<const u32x4 *>(kp + 32 * ks);
       (void)kbase;
@@ -209,23 +246,36 @@ template <int KS, int NH, bool GQA, bool SHARE>
 __device__ __forceinline__ void tile_step(const Tile<KS, GQA> &cur, int t0, int c1, int n, int q,
                                           const bf16x8 (&QX)[KS], const bf16x8 (&QY)[KS],
                                           const bf16x8 &RX, const bf16x8 &RY, uint8_t *lw_wr,
-                                          const uint8_t *lw_rd, Acc<KS> &acc,
+                                          uint8_t *lw_line, const uint8_t *lw_rd, Acc<KS> &acc,
                                           const uint8_t *kx) {
   constexpr int SH = NH > 0 ? NH : 1;
   using L = TileLds<KS>;
-  // the tile's V rows go to the wave's LDS copy (row 16 tb + n, columns 32 ks + 8 q ..), to be
-  // read back transposed for the weighted sum
+  // the tile's V rows go to the wave's LDS copy (row-major, rows of L::kRow bytes), to be read
+  // back transposed for the weighted sum: from the line layout (lane's chunk of rows
+  // line_row(k), at lw_line) or from the operand layout (row 16 tb + n, columns 32 ks + 8 q ..)
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      *reinterpret_cast<u32x4 *>(lw_wr + tb * 16 * L::kRow + 64 * ks) = cur.v[tb][ks];
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (kLine<KS>)
+        *reinterpret_cast<u32x4 *>(lw_line + (16 * tb + ks * (16 / KS)) * L::kRow) = cur.v[tb][ks];
+      else
+        *reinterpret_cast<u32x4 *>(lw_wr + tb * 16 * L::kRow + 64 * ks) = cur.v[tb][ks];
+    }
   f32x4 S[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-    // the score operand: the value rows plus the positional key (GVA) or the key rows (GQA)
-    const u32x4 *sx = GQA ? cur.x[tb] : cur.v[tb];
+    // the score operand: the value rows plus the positional key (GVA) or the key rows (GQA);
+    // in the line layout the value rows are read back from LDS in the operand layout (the
+    // wave's own LDS writes above complete first: LDS serves a wave's accesses in order)
+    u32x4 vop[KS];
+    if constexpr (kLine<KS> && !GQA) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        vop[ks] = *reinterpret_cast<const u32x4 *>(lw_wr + tb * 16 * L::kRow + 64 * ks);
+    }
+    const u32x4 *sx = GQA ? cur.x[tb] : (kLine<KS> ? vop : cur.v[tb]);
     // the positional key rows (GVA)
     const u32x4 kx_tb = SHARE ? *reinterpret_cast<const u32x4 *>(kx + 1024 * tb) : cur.x[tb][0];
     if (NH > 0) {
@@ -426,7 +476,8 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
 
     // lane-invariant parts of the element offsets (positional K groups beyond d_r read the
     // row's last 8 elements; they meet zeros in the query operand)
-    const int64_t vlane = static_cast<int64_t>(g) * a.v_sg + 8 * q;
+    const int64_t vgrp = static_cast<int64_t>(g) * a.v_sg;
+    uint8_t *lw_line = lds + wave * L::kWave + (lane / (4 * KS)) * L::kRow + 16 * line_chunk<KS>(lane);
     const int64_t klane = min(8 * q, a.d_r - 8);
 
     // Two tile buffers in ping-pong (A, Bt): while one tile is computed the other one's loads
@@ -452,20 +503,20 @@ __device__ __forceinline__ void run_chunk(const gva::DecodeArgs &a, int b, int g
       }
     };
     Tile<KS, GQA> A, Bt;
-    load_tile<KS, GQA, SHARE>(a, PA, c0, c1, n, vlane, klane, A, bad, fetch_key, kown);
+    load_tile<KS, GQA, SHARE>(a, PA, c0, c1, n, vgrp, klane, A, bad, fetch_key, kown);
     PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
     publish(kb0, A);
     for (int t0 = c0; t0 < c1; t0 += 2 * kTile) {
       const int t1 = t0 + kTile;
-      load_tile<KS, GQA, SHARE>(a, PB, t1, c1, n, vlane, klane, Bt, bad, fetch_key, kown);
+      load_tile<KS, GQA, SHARE>(a, PB, t1, c1, n, vgrp, klane, Bt, bad, fetch_key, kown);
       PB = load_pages(bt, lb, t1 + 2 * kTile, c1, lane);
-      tile_step<KS, NH, GQA, SHARE>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc,
+      tile_step<KS, NH, GQA, SHARE>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_line, lw_rd, acc,
                                     kb0 + 16 * lane);
       publish(kb1, Bt);
-      load_tile<KS, GQA, SHARE>(a, PA, t1 + kTile, c1, n, vlane, klane, A, bad, fetch_key, kown);
+      load_tile<KS, GQA, SHARE>(a, PA, t1 + kTile, c1, n, vgrp, klane, A, bad, fetch_key, kown);
       PA = load_pages(bt, lb, t1 + 3 * kTile, c1, lane);
       if (t1 < c1)                                     // uniform per work-group
-        tile_step<KS, NH, GQA, SHARE>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc,
+        tile_step<KS, NH, GQA, SHARE>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_line, lw_rd, acc,
                                       kb1 + 16 * lane);
       publish(kb0, A);
     }
@@ -732,9 +783,12 @@ constexpr int kStepRegionBytes = 144 * 1024;   // staging of M, then tile copies
 // before use, so only blocks holding positions of the run can raise the bad flag.
 template <int KS>
 __device__ __forceinline__ void load_tile_run(const gva::DecodeArgs &a, int32_t pb0, int32_t pb1,
-                                              int t0, int c1, int n, int64_t vlane, int klane,
+                                              int t0, int c1, int n, int64_t vgrp, int klane,
                                               Tile<KS, false> &T, bool &bad) {
+  static_assert(kLine<KS>, "the one-launch kernels load V in the line layout");
   const int mask = (1 << a.log2_bs) - 1;
+  const int lane = threadIdx.x & 63;
+  const int ch = 8 * line_chunk<KS>(lane);
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v);
   const uint16_t *kbase = static_cast<const uint16_t *>(a.kr);
 #pragma unroll
@@ -744,11 +798,12 @@ __device__ __forceinline__ void load_tile_run(const gva::DecodeArgs &a, int32_t 
     bad |= !ok && t0 + 16 * tb < c1;
     const int64_t blk = ok ? pb : 0;
     const int f = min(t0 + 16 * tb, c1 - 1);
-    const int rn = min(n, c1 - 1 - f);
-    const int64_t row = static_cast<int64_t>((f & mask) + rn);
-    const uint16_t *vp = vbase + blk * a.v_sb + row * a.v_st + vlane;
+    const int lim = c1 - 1 - f;
+    const int64_t row = static_cast<int64_t>((f & mask) + min(n, lim));
+    const uint16_t *vblk = vbase + blk * a.v_sb + static_cast<int64_t>(f & mask) * a.v_st + vgrp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = *reinterpret_cast<const u32x4 *>(vp + 32 * ks);
+    for (int k = 0; k < KS; ++k)
+      T.v[tb][k] = stream_load(vblk + static_cast<int64_t>(min(line_row<KS>(lane, k), lim)) * a.v_st + ch);
     T.x[tb][0] = *reinterpret_cast<const u32x4 *>(kbase + blk * a.kr_sb + row * a.kr_st + klane);
   }
 }
@@ -845,7 +900,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
     rq_cs = reinterpret_cast<const double2 *>(s.rope)[static_cast<int64_t>(p) * half_r + k];
   }
   const int c1 = len_bad ? c0 : min(cend, len);
-  const int64_t vlane = static_cast<int64_t>(g) * a.v_sg + 8 * q;
+  const int64_t vgrp = static_cast<int64_t>(g) * a.v_sg;
   const int klane = min(8 * q, d_r - 8);
   bool bad = false;
   Tile<KS, false> A, Bt;
@@ -853,9 +908,9 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   // the run's first tile, issued between the first staging loads and their LDS stores so that
   // waiting for the staged rows does not wait for it
   auto issue_tile_a = [&]() {
-    if (c0 < c1) load_tile_run<KS>(a, pa0, pa1, c0, c1, n, vlane, klane, A, bad);
+    if (c0 < c1) load_tile_run<KS>(a, pa0, pa1, c0, c1, n, vgrp, klane, A, bad);
     if (c0 + kTile < c1) {
-      load_tile_run<KS>(a, pb0, pb1, c0 + kTile, c1, n, vlane, klane, Bt, bad);
+      load_tile_run<KS>(a, pb0, pb1, c0 + kTile, c1, n, vgrp, klane, Bt, bad);
       if (c0 + 2 * kTile < c1) PA = load_pages(bt, lb, c0 + 2 * kTile, c1, lane);
     }
     tile_a_issued = true;
@@ -1076,8 +1131,10 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
       }
     }
     uint8_t *lw_wr = region + wave * L::kWave + n * L::kRow + 16 * q;
+    uint8_t *lw_line =
+        region + wave * L::kWave + (lane / (4 * KS)) * L::kRow + 16 * line_chunk<KS>(lane);
     const uint8_t *lw_rd = region + wave * L::kWave + (lane >> 2) * L::kRow + 8 * (lane & 3);
-    const u32x4 *tv = reinterpret_cast<const u32x4 *>(tok_v + 8 * q);
+    const u32x4 tvl = *reinterpret_cast<const u32x4 *>(tok_v + 8 * line_chunk<KS>(lane));
     const u32x4 tk = *reinterpret_cast<const u32x4 *>(tok_kr + klane);
     // Before a tile is used: the lanes that read position p take the new token from LDS (this
     // launch is writing it to the cache), and a block lying wholly past c1 is zeroed (it may
@@ -1093,9 +1150,15 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int f = min(t0 + 16 * tb, c1 - 1);
-        const bool at_p = t0 + 16 * tb < c1 && f + min(n, c1 - 1 - f) == p;
+        const bool in_run = t0 + 16 * tb < c1;
+        // V in the line layout: load k of this lane read row line_row(k) (clamped), at this
+        // lane's chunk; the positional key in the operand layout: row n (clamped)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) T.v[tb][ks] = at_p ? tv[4 * ks] : T.v[tb][ks];
+        for (int k = 0; k < KS; ++k) {
+          const bool at_p = in_run && f + min(line_row<KS>(lane, k), c1 - 1 - f) == p;
+          T.v[tb][k] = at_p ? tvl : T.v[tb][k];
+        }
+        const bool at_p = in_run && f + min(n, c1 - 1 - f) == p;
         T.x[tb][0] = at_p ? tk : T.x[tb][0];
       }
     };
@@ -1107,21 +1170,23 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
       const int t1 = t0 + kTile;
       if (!first && t1 < c1) {                           // uniform
         load_tile_run<KS>(a, __builtin_amdgcn_readlane(PB, 0), __builtin_amdgcn_readlane(PB, 1), t1,
-                          c1, n, vlane, klane, Bt, bad);
+                          c1, n, vgrp, klane, Bt, bad);
         if (t1 + kTile < c1) PA = load_pages(bt, lb, t1 + kTile, c1, lane);
       }
       first = false;
       fix_tile(A, t0);
-      tile_step<KS, NH, false, false>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc, nullptr);
+      tile_step<KS, NH, false, false>(A, t0, c1, n, q, QX, QY, RX, RY, lw_wr, lw_line, lw_rd, acc,
+                                      nullptr);
       if (t1 >= c1) break;
       const int t2 = t1 + kTile;
       if (t2 < c1) {
         load_tile_run<KS>(a, __builtin_amdgcn_readlane(PA, 0), __builtin_amdgcn_readlane(PA, 1), t2,
-                          c1, n, vlane, klane, A, bad);
+                          c1, n, vgrp, klane, A, bad);
         if (t2 + kTile < c1) PB = load_pages(bt, lb, t2 + kTile, c1, lane);
       }
       fix_tile(Bt, t1);
-      tile_step<KS, NH, false, false>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_rd, acc, nullptr);
+      tile_step<KS, NH, false, false>(Bt, t1, c1, n, q, QX, QY, RX, RY, lw_wr, lw_line, lw_rd, acc,
+                                      nullptr);
       if (t2 >= c1) break;
       t0 = t2;
     }

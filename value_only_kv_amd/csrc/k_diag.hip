@@ -10,7 +10,11 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // Lane l of work-group w reads 16-byte words w * 256 * F + l + 256 * k (k < F) of each stride
-// of gridDim.x * 256 * F words: F loads in flight per lane, every word read exactly once.
+// of gridDim.x * 256 * F words: F loads in flight per lane, every word read exactly once. The
+// loads are non-temporal (read once, as the decode's cache rows are) and every load
+// instruction covers 1 KiB of consecutive words, whole 128-byte lines. Loads past the end
+// read the last word again (every load is made and every result used, so none is held back
+// behind a branch).
 template <int F>
 __global__ __launch_bounds__(256) void k_stream_read(const u32x4 *__restrict__ src, int64_t words,
                                                      uint32_t *sink) {
@@ -22,7 +26,7 @@ __global__ __launch_bounds__(256) void k_stream_read(const u32x4 *__restrict__ s
 #pragma unroll
     for (int k = 0; k < F; ++k) {
       const int64_t i = base + 256 * k;
-      v[k] = i < words ? src[i] : u32x4{0u, 0u, 0u, 0u};
+      v[k] = __builtin_nontemporal_load(src + (i < words ? i : words - 1));
     }
 #pragma unroll
     for (int k = 0; k < F; ++k) acc ^= v[k];
