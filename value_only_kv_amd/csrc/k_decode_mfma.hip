@@ -814,7 +814,8 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   using L = TileLds<KS>;
   static_assert(W * L::kWave <= kStepRegionBytes, "tile copies exceed the region");
   static_assert(W * NH * (DH + 2) * 4 <= kStepRegionBytes, "merge area exceeds the region");
-  static_assert(32 * NH * (DH + 2) * 4 + 64 <= kStepRegionBytes, "K <= 32 partials exceed the region");
+  static_assert(32 * NH * (DH + 2) * 4 + 64 + 64 * 16 <= kStepRegionBytes,
+                "K <= 32 partials (and the spare slots) exceed the region");
   __shared__ __align__(16) uint8_t region[kStepRegionBytes];
   __shared__ __align__(16) float q_lds[STEP ? NH : 1][DH + 32];  // q~ (DH), then r (d_r <= 32)
   __shared__ __align__(16) uint16_t tok_v[DH];                   // the new token's values, group g
@@ -1271,7 +1272,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
   const int kn4 = (K * NH + 3) & ~3;                     // keeps go 16-byte aligned
   float *gm = reinterpret_cast<float *>(region);         // [K][NH]
   float *gl = gm + kn4;                                  // [K][NH]
-  float *go = gl + kn4;                                  // [K][NH][DH], then one spare row
+  float *go = gl + kn4;                                  // [K][NH][DH], then 64 spare slots
   {
     // buffer loads with the device-scope cache policy (sc1): they read past this XCD's L2 like
     // the atomic loads would, but several can be in flight; the ranges end at this pair's rows
@@ -1289,11 +1290,12 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
       mv = __builtin_amdgcn_raw_buffer_load_b32(rm, 4 * tid, 0, kSc1);
       lv = __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * tid, 0, kSc1);
     }
-    // the o rows in batches of 16 loads per lane, all in flight before the first LDS store
-    // (loads past the range return zero; their stores go to a spare slot after the rows, so
-    // every store is made and no load is held back behind a branch)
+    // the o rows in batches of 8 loads per lane (K NH DH / 4 <= 32 * 8 * 16 = 8 * 512: one
+    // batch), all in flight before the first LDS store (loads past the range return zero; their
+    // stores go to a spare slot per lane after the rows, so every store is made, no load is held
+    // back behind a branch, and no two lanes of a store share an address)
     const int n4 = K * NH * DH / 4;
-    constexpr int kBatchM = 16;
+    constexpr int kBatchM = 8;
     for (int e0 = tid; e0 < n4; e0 += kBatchM * 64 * W) {
       u32x4 v[kBatchM];
 #pragma unroll
@@ -1302,7 +1304,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_step_fused(gva::StepArgs s) {
 #pragma unroll
       for (int u = 0; u < kBatchM; ++u) {
         const int e = e0 + u * 64 * W;
-        reinterpret_cast<u32x4 *>(go)[e < n4 ? e : n4] = v[u];
+        reinterpret_cast<u32x4 *>(go)[e < n4 ? e : n4 + lane] = v[u];
       }
     }
     if (has_ml) {
