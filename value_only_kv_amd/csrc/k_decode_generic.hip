@@ -268,8 +268,31 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   const float qnan = __int_as_float(0x7fc00000);
   float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h;
   const bool write_lse = a.lse && tid == 0 && blockIdx.x == 0;
-  const int len = a.seq_len[b];
   const int cap = a.max_blocks << a.log2_bs;
+  // Every partial this thread needs goes out before any is used: split tid's m and l, and the
+  // first kCombineRows of this wave's o rows wave, wave + nw, ... (loads past the last row
+  // re-read it; what they bring is never used). In the split grid the rows (row0 + s H,
+  // s < num_splits) are known before the length, so these loads go out with it: one round of
+  // loads in all; the balanced plan needs the tile prefix first. The arithmetic and its order
+  // do not depend on this. Split counts above the block's threads, and rows past the first
+  // kCombineRows, are read in further passes.
+  const bool split = a.num_ranges == 0;
+  const int64_t step = static_cast<int64_t>(a.H) * a.d_h;
+  int64_t row0 = split ? static_cast<int64_t>(b) * a.num_splits * a.H + h : 0;
+  float m0 = 0.0f, l0 = 0.0f;
+  float ov[kCombineRows];
+  const float *po = a.part_o;
+  auto issue = [&](int nload) {
+    const int sm = min(tid, nload - 1);
+    m0 = a.part_m[row0 + static_cast<int64_t>(sm) * a.H];
+    l0 = a.part_l[row0 + static_cast<int64_t>(sm) * a.H];
+    po = a.part_o + row0 * a.d_h + (dim_ok ? d : 0);
+#pragma unroll
+    for (int j = 0; j < kCombineRows; ++j)
+      ov[j] = po[static_cast<int64_t>(min(wave + nw * j, nload - 1)) * step];
+  };
+  if (split) issue(a.num_splits);
+  const int len = a.seq_len[b];
   if (len < 0 || len > a.max_len || len > cap) {
     if (wave == 0 && dim_ok) dst[d] = qnan;
     if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = qnan;
@@ -278,28 +301,13 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
     return;
   }
   int ns;
-  int64_t row0;
   partial_rows(a, b, h, len, ns, row0);
   if (ns == 0) {
     if (wave == 0 && dim_ok) dst[d] = 0.0f;
     if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = -INFINITY;
     return;
   }
-  // Every partial this thread needs goes out before any is used: split tid's m and l (a thread
-  // past ns re-reads split ns - 1 and stores the same weight as thread ns - 1 does), and
-  // the first kCombineRows of this wave's o rows wave, wave + nw, ... (rows past ns re-read row
-  // ns - 1 and are not used). One round of loads instead of one per step of the reduction; the
-  // arithmetic and its order are unchanged. Split counts above the block's threads, and rows
-  // past the first kCombineRows, are read in further passes.
-  const int64_t step = static_cast<int64_t>(a.H) * a.d_h;
-  const int sm = min(tid, ns - 1);
-  const float m0 = a.part_m[row0 + static_cast<int64_t>(sm) * a.H];
-  const float l0 = a.part_l[row0 + static_cast<int64_t>(sm) * a.H];
-  const float *po = a.part_o + row0 * a.d_h + (dim_ok ? d : 0);
-  float ov[kCombineRows];
-#pragma unroll
-  for (int j = 0; j < kCombineRows; ++j)
-    ov[j] = po[static_cast<int64_t>(min(wave + nw * j, ns - 1)) * step];
+  if (!split) issue(ns);
   const int keep = tid < ns ? -1 : 0;                  // a bitwise blend, not a select on a load
   float mx = fmaxf(-INFINITY, __int_as_float((__float_as_int(m0) & keep) |
                                              (__float_as_int(-INFINITY) & ~keep)));
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   float L = 0.0f;
   {
     const float f = exp2f(m0 - mx);
-    w_s[sm] = f;
+    if (tid < ns) w_s[tid] = f;
     L = __int_as_float(__float_as_int(l0 * f) & keep);
   }
   for (int s = tid + nthr; s < ns; s += nthr) {
