@@ -122,6 +122,26 @@ def test_d_h_64_and_256(kernel):
         check_output(out, ref, "bf16", f"d_h={d_h}")
 
 
+@pytest.mark.parametrize("d_h,heads", [(96, (6, 3)), (160, (8, 4)), (32, (16, 2)), (256, (4, 2))])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_value_widths_both_load_layouts(d_h, heads, num_splits):
+    """The matrix-core kernel loads value rows whole-line (d_h = 32 KS with KS a power of two,
+    staged through LDS for the score operand) or in the operand layout (other KS): widths of
+    both kinds, token- and group-major, against the oracle."""
+    H, G = heads
+    for group_major in (True, False):
+        c = _ragged_case(B=5, lo=40, hi=900, d_h=d_h, d_n=d_h, H=H, G=G, d_r=16,
+                         group_major=group_major)
+        lens = c.lens.copy()
+        lens[0], lens[1] = 1, 17
+        q = synth.direct_q_abs(c.w, c.w.B)
+        out, lse = c.decode(lens, q, num_splits=num_splits, kernel=MFMA)
+        ref, ref_lse = c.oracle_decode(lens, q.astype(np.float64))
+        check_output(out, ref, "bf16", f"d_h={d_h} H={H} G={G} gm={group_major}")
+        ok, e = lse_ok(lse, ref_lse, 1e-3)
+        assert ok, e
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_peaky_and_flat_scores(kernel):
     c = _ragged_case(B=4, lo=300, hi=900)
