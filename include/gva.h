@@ -176,8 +176,8 @@ gva_status gva_absorb_query(const gva_dims *dims, int32_t n_q, const float *q_no
  * seq_len[b] == 0 gives out = 0 and lse = -inf.
  *   seq_len: device int32 [B]. max_len: host upper bound on every seq_len[b] (it sizes the
  *   split plan; a larger length raises GVA_DEVERR_LENGTH and makes that row NaN).
- *   q_abs: device float32 [B][H][d_h + d_r]. out: device float32 [B][H][d_h].
- *   lse: device float32 [B][H] or NULL.
+ *   q_abs: device float32 [B][H][d_h + d_r], 16-byte aligned. out: device float32
+ *   [B][H][d_h], 16-byte aligned. lse: device float32 [B][H] or NULL.
  *   num_splits: 0 = choose automatically, else 1 .. 1024 (rounded down so no chunk is empty
  *   for a sequence of max_len tokens).
  *   kernel: GVA_KERNEL_* ; the MFMA kernel needs a bf16 cache, d_h % 32 == 0, d_h <= 256,

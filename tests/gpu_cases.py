@@ -110,8 +110,9 @@ class Case:
         return int(self.cache.err_flag.item())
 
     def decode(self, seq_len, q_abs, num_splits=0, kernel=gb.GVA_KERNEL_AUTO, max_len=None,
-               with_lse=True):
-        """Runs gva_decode; returns (out, lse) on the host as float32 arrays."""
+               with_lse=True, ws_fill=None):
+        """Runs gva_decode; returns (out, lse) on the host as float32 arrays. ws_fill: a value
+        the workspace holds past its first 1024 bytes (the tickets stay zero) before the call."""
         d = self.device
         B, H = self.w.B, self.w.H
         seq_len = np.asarray(seq_len, np.int32)
@@ -122,6 +123,8 @@ class Case:
         lse = torch.full((B, H), float("nan"), device=d) if with_lse else None
         wsb = gb.gva_decode_workspace_bytes(self.cdims, B, max_len, num_splits)
         ws = torch.zeros(max(wsb, 256) // 4, dtype=torch.float32, device=d) if wsb else None
+        if ws is not None and ws_fill is not None:
+            ws[256:] = ws_fill
         gb.gva_decode(self.cdims, self.cache, B, sl, max_len, q, self.w.scale, out, lse,
                       num_splits=num_splits, kernel=kernel, workspace=ws)
         torch.cuda.synchronize()

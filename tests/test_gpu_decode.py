@@ -198,6 +198,24 @@ def test_split_counts_one_to_many(kernel):
         check_output(out, ref, "bf16", f"S={S}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("num_splits", [17, 40, 64, 200, 256])
+def test_split_combine_ignores_unwritten_rows(kernel, num_splits):
+    """The split grid's combine loads a (sequence, head)'s partial rows before it knows the
+    sequence's length; rows at or past its chunk count are never written by the decode and
+    here hold NaN: the outputs must not see them."""
+    c = _ragged_case(B=4, lo=4000, hi=4100)
+    lens = np.array([int(c.lens[0]), 900, 33, 0])
+    q = synth.direct_q_abs(c.w, c.w.B)
+    out, lse = c.decode(lens, q, num_splits=num_splits, kernel=kernel, max_len=int(c.lens.max()),
+                        ws_fill=float("nan"))
+    ref, ref_lse = c.oracle_decode(lens, q.astype(np.float64))
+    check_output(out, ref, "bf16", f"S={num_splits}, NaN in unwritten partial rows")
+    ok, e = lse_ok(lse, ref_lse, 1e-3)
+    assert ok, e
+    assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+
+
 def test_combine_many_rows_for_one_sequence():
     """A batch whose plan has few partial rows per sequence on average (so the combine takes one
     wave per (sequence, head)) but one long sequence among short ones, which spans more than 64

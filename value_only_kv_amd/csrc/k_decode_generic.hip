@@ -212,6 +212,8 @@ constexpr int kCombineMaxWaves = 16;
 constexpr int kCombineWaveRows = 16;
 // o rows per lane of k_combine loaded in the first round
 constexpr int kCombineRows = 16;
+// partial rows per lane of k_combine_slice at most (16 lanes share a slice's rows)
+constexpr int kCombineSliceMaxK = 16;
 
 __device__ __forceinline__ float block_reduce(float v, float *scratch, int nw, bool is_max) {
   v = is_max ? gvad::wave_max(v) : gvad::wave_sum(v);
@@ -355,6 +357,95 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
   if (write_lse) a.lse[static_cast<int64_t>(b) * a.H + h] = poison ? qnan : (mx + log2f(L)) * gvad::kLn2;
 }
 
+
+// Split-grid combine for 17 .. 16 K chunks per sequence, one wave per (16-dim slice, head,
+// sequence), with no LDS and no barriers. Lane r + 16 c holds the partial rows s = r + 16 k
+// (k < K) of dims 16 j + 4 c .. + 3, with their m and l. The rows of a (sequence, head) are known
+// before its length, so every load goes out with the length's (rows at or past the sequence's
+// chunk count are loaded but dropped by a bitwise blend: their workspace rows may hold anything).
+// The maximum, the sum of l 2^(m - max) and the weighted rows meet through cross-lane
+// reductions. Same formulas as k_combine (base-2 m and lse, weights 2^(m_s - max)); the order
+// of the sums differs.
+template <int K>
+__global__ __launch_bounds__(64) void k_combine_slice(gva::DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int r = lane & 15;
+  const int c = lane >> 4;
+  const int j = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int S = a.num_splits;
+  const int64_t row0 = static_cast<int64_t>(b) * S * a.H + h;
+  const int d = 16 * j + 4 * c;
+  float4 o[K];
+  float m[K], l[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t row = row0 + static_cast<int64_t>(min(r + 16 * k, S - 1)) * a.H;
+    m[k] = a.part_m[row];
+    l[k] = a.part_l[row];
+    o[k] = *reinterpret_cast<const float4 *>(a.part_o + row * a.d_h + d);
+  }
+  const int len = a.seq_len[b];
+  float *dst = a.out + (static_cast<int64_t>(b) * a.H + h) * a.d_h + d;
+  float *lse = (a.lse && j == 0 && lane == 0) ? a.lse + static_cast<int64_t>(b) * a.H + h : nullptr;
+  const float qnan = __int_as_float(0x7fc00000);
+  const int cap = a.max_blocks << a.log2_bs;
+  if (len < 0 || len > a.max_len || len > cap) {
+    if (r == 0) *reinterpret_cast<float4 *>(dst) = make_float4(qnan, qnan, qnan, qnan);
+    if (lse) *lse = qnan;
+    return;
+  }
+  const int ns = min(S, (len + a.chunk - 1) / a.chunk);
+  if (ns == 0) {
+    if (r == 0) *reinterpret_cast<float4 *>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse) *lse = -INFINITY;
+    return;
+  }
+  float mx = -INFINITY;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int keep = r + 16 * k < ns ? -1 : 0;
+    m[k] = __int_as_float((__float_as_int(m[k]) & keep) | (__float_as_int(-INFINITY) & ~keep));
+    l[k] = __int_as_float(__float_as_int(l[k]) & keep);
+    o[k] = make_float4(__int_as_float(__float_as_int(o[k].x) & keep),
+                       __int_as_float(__float_as_int(o[k].y) & keep),
+                       __int_as_float(__float_as_int(o[k].z) & keep),
+                       __int_as_float(__float_as_int(o[k].w) & keep));
+    bad = bad || isnan(m[k]);
+    mx = fmaxf(mx, m[k]);
+  }
+  mx = gvad::wave_max(mx);
+  const bool poison = __any(bad);
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float f = exp2f(m[k] - mx);               // 0 for dropped rows
+    L = fmaf(l[k], f, L);
+    acc.x = fmaf(o[k].x, f, acc.x);
+    acc.y = fmaf(o[k].y, f, acc.y);
+    acc.z = fmaf(o[k].z, f, acc.z);
+    acc.w = fmaf(o[k].w, f, acc.w);
+  }
+  // sums over r (the lanes of a row of 16 hold the same dims); every row of 16 holds all
+  // partial rows' l once, so L is summed over the lanes of one row
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) {
+    L += __shfl_xor(L, x, 64);
+    acc.x += __shfl_xor(acc.x, x, 64);
+    acc.y += __shfl_xor(acc.y, x, 64);
+    acc.z += __shfl_xor(acc.z, x, 64);
+    acc.w += __shfl_xor(acc.w, x, 64);
+  }
+  if (r == 0) {
+    *reinterpret_cast<float4 *>(dst) =
+        poison ? make_float4(qnan, qnan, qnan, qnan)
+               : make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
+  }
+  if (lse) *lse = poison ? qnan : (mx + log2f(L)) * gvad::kLn2;
+}
 
 // One wave per (sequence, head), four heads per work-group, for sequences with few partial rows
 // (the balanced plan gives about R / B + 1 of them): no LDS and no barriers. The length and the
@@ -915,6 +1006,15 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
       case 3: hipLaunchKernelGGL(k_combine_wave<3>, grid, dim3(256), 0, stream, a); break;
       default: hipLaunchKernelGGL(k_combine_wave<4>, grid, dim3(256), 0, stream, a); break;
     }
+    return hipGetLastError();
+  }
+  if (a.num_ranges == 0 && a.num_splits <= 16 * kCombineSliceMaxK && a.d_h % 16 == 0) {
+    const dim3 grid(a.d_h / 16, a.H, a.B);
+    const int k = (a.num_splits + 15) / 16;
+    if (k <= 2) hipLaunchKernelGGL(k_combine_slice<2>, grid, dim3(64), 0, stream, a);
+    else if (k <= 4) hipLaunchKernelGGL(k_combine_slice<4>, grid, dim3(64), 0, stream, a);
+    else if (k <= 8) hipLaunchKernelGGL(k_combine_slice<8>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(k_combine_slice<16>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
   }
   int nw = per_seq / 16;
