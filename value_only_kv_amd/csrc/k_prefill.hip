@@ -413,8 +413,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
     for (int rt = 0; rt < RT; ++rt) {
       const f32x4 &s0 = S[rt][0], &s1 = S[rt][1];
       mt[rt] = row_max(max2(max3(s0[0], s0[1], s0[2]), max3(s0[3], s1[0], max3(s1[1], s1[2], s1[3]))));
-      raise[rt] = mt[rt] > kLazyRescale || (mref[rt] == -INFINITY && mt[rt] != -INFINITY);
-      any_raise = any_raise || raise[rt];
+      // bitwise, so that the test is one compare chain with no branch per row tile
+      raise[rt] = (mt[rt] > kLazyRescale) | ((mref[rt] == -INFINITY) & (mt[rt] != -INFINITY));
+      any_raise = any_raise | raise[rt];
     }
     if (__any(any_raise)) {   // rare after the first tiles: move the reference to the tile maximum
 #pragma unroll
