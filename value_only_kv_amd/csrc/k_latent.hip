@@ -298,7 +298,8 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
     hook(std::integral_constant<int, 1>{});
     // tile maximum relative to the reference, over the head's 32 keys (4 rows of 16 lanes)
     const float mt = gvad::xor32_max(gvad::xor16_max(fmaxf(max4(Sc[0]), max4(Sc[1]))));
-    const bool raise = mt > kLazyRescale || (mref == -INFINITY && mt != -INFINITY);
+    // bitwise, so that the test compiles to one compare chain with no branch
+    const bool raise = (mt > kLazyRescale) | ((mref == -INFINITY) & (mt != -INFINITY));
     if (__any(raise)) {                                // rare after the first tiles
       const float delta = raise ? mt : 0.0f;
       const float mnew = mref == -INFINITY ? mt : mref + delta;

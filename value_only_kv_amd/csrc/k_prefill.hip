@@ -406,25 +406,28 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   };
   // Online softmax of the scores S into PB (and the rare move of the reference).
   auto softmax = [&]() {
-    float mt[RT];
-    bool raise[RT];
-    bool any_raise = false;
+    // Each lane tests its own eight scores: a row's reference can only move when one of its
+    // lanes holds a score above kLazyRescale (or the row's first unmasked score arrives), so the
+    // exact row maximum, a cross-lane reduction, is formed only on that rare path. The test is
+    // bitwise, one compare chain with no branch per row tile.
+    float lm[RT];
+    bool need = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const f32x4 &s0 = S[rt][0], &s1 = S[rt][1];
-      mt[rt] = row_max(max2(max3(s0[0], s0[1], s0[2]), max3(s0[3], s1[0], max3(s1[1], s1[2], s1[3]))));
-      // bitwise, so that the test is one compare chain with no branch per row tile
-      raise[rt] = (mt[rt] > kLazyRescale) | ((mref[rt] == -INFINITY) & (mt[rt] != -INFINITY));
-      any_raise = any_raise | raise[rt];
+      lm[rt] = max2(max3(s0[0], s0[1], s0[2]), max3(s0[3], s1[0], max3(s1[1], s1[2], s1[3])));
+      need = need | (lm[rt] > kLazyRescale) | ((mref[rt] == -INFINITY) & (lm[rt] != -INFINITY));
     }
-    if (__any(any_raise)) {   // rare after the first tiles: move the reference to the tile maximum
+    if (__any(need)) {   // rare after the first tiles: move the reference to the tile maximum
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const float delta = raise[rt] ? mt[rt] : 0.0f;
-        const float mnew = mref[rt] == -INFINITY ? mt[rt] : mref[rt] + delta;
-        const float alpha = raise[rt] ? __builtin_amdgcn_exp2f(mref[rt] - mnew) : 1.0f;   // 0 from -inf
-        mref[rt] = raise[rt] ? mnew : mref[rt];
-        negm[rt] = raise[rt] ? -mnew : negm[rt];
+        const float mt = row_max(lm[rt]);
+        const bool raise = (mt > kLazyRescale) | ((mref[rt] == -INFINITY) & (mt != -INFINITY));
+        const float delta = raise ? mt : 0.0f;
+        const float mnew = mref[rt] == -INFINITY ? mt : mref[rt] + delta;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(mref[rt] - mnew) : 1.0f;   // 0 from -inf
+        mref[rt] = raise ? mnew : mref[rt];
+        negm[rt] = raise ? -mnew : negm[rt];
         lsum[rt] *= alpha;
 #pragma unroll
         for (int i = 0; i < 2 * KS; ++i) O[rt][i] *= alpha;
