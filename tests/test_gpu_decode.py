@@ -200,20 +200,23 @@ def test_split_counts_one_to_many(kernel):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("num_splits", [17, 40, 64, 200, 256])
-def test_split_combine_ignores_unwritten_rows(kernel, num_splits):
-    """The split grid's combine loads a (sequence, head)'s partial rows before it knows the
-    sequence's length; rows at or past its chunk count are never written by the decode and
-    here hold NaN: the outputs must not see them."""
-    c = _ragged_case(B=4, lo=4000, hi=4100)
-    lens = np.array([int(c.lens[0]), 900, 33, 0])
+@pytest.mark.parametrize("B", [1, 4])
+def test_split_combine_ignores_unwritten_rows(kernel, num_splits, B):
+    """Partial rows at or past a sequence's chunk count are never written by the decode and here
+    hold NaN: the outputs must not see them. Both combines load rows before they know the
+    length: the one-sequence combine every row (the sequence is shorter than max_len here, so
+    some rows are unused), the batch combine its first rows per wave."""
+    c = _ragged_case(B=B, lo=4000, hi=4100)
+    lens = np.array([int(c.lens[0]), 900, 33, 0])[:B] if B > 1 else np.array([900])
     q = synth.direct_q_abs(c.w, c.w.B)
     out, lse = c.decode(lens, q, num_splits=num_splits, kernel=kernel, max_len=int(c.lens.max()),
                         ws_fill=float("nan"))
     ref, ref_lse = c.oracle_decode(lens, q.astype(np.float64))
-    check_output(out, ref, "bf16", f"S={num_splits}, NaN in unwritten partial rows")
+    check_output(out, ref, "bf16", f"B={B} S={num_splits}, NaN in unwritten partial rows")
     ok, e = lse_ok(lse, ref_lse, 1e-3)
     assert ok, e
-    assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+    if B > 1:
+        assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
 
 
 def test_combine_many_rows_for_one_sequence():

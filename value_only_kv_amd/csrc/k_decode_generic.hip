@@ -212,8 +212,8 @@ constexpr int kCombineMaxWaves = 16;
 constexpr int kCombineWaveRows = 16;
 // o rows per lane of k_combine loaded in the first round
 constexpr int kCombineRows = 16;
-// partial rows per lane of k_combine_slice at most (16 lanes share a slice's rows)
-constexpr int kCombineSliceMaxK = 16;
+// partial rows per lane of k_combine_slice at most (8 lanes share a slice's rows)
+constexpr int kCombineSliceMaxK = 32;
 
 __device__ __forceinline__ float block_reduce(float v, float *scratch, int nw, bool is_max) {
   v = is_max ? gvad::wave_max(v) : gvad::wave_sum(v);
@@ -358,30 +358,32 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void k_combine(gva::DecodeAr
 }
 
 
-// Split-grid combine for 17 .. 16 K chunks per sequence, one wave per (16-dim slice, head,
-// sequence), with no LDS and no barriers. Lane r + 16 c holds the partial rows s = r + 16 k
-// (k < K) of dims 16 j + 4 c .. + 3, with their m and l. The rows of a (sequence, head) are known
-// before its length, so every load goes out with the length's (rows at or past the sequence's
-// chunk count are loaded but dropped by a bitwise blend: their workspace rows may hold anything).
-// The maximum, the sum of l 2^(m - max) and the weighted rows meet through cross-lane
-// reductions. Same formulas as k_combine (base-2 m and lse, weights 2^(m_s - max)); the order
-// of the sums differs.
+// Split-grid combine of one sequence over 17 .. 8 K chunks, one wave per (32-dim slice, head),
+// with no LDS and no barriers. Lane r + 8 c holds the partial rows s = r + 8 k (k < K) of dims
+// 32 j + 4 c .. + 3, with their m and l: the 8 lanes of a row read its slice's 128 bytes, one
+// whole line, so each load instruction reads 8 whole lines. The rows are known before the
+// sequence's length and its chunks are usually all in use, so every load goes out with the
+// length's; rows at or past the chunk count are loaded but dropped by a bitwise blend (their
+// workspace rows may hold anything). The maximum, the sum of l 2^(m - max) and the weighted rows
+// meet through cross-lane reductions. Same formulas as k_combine (base-2 m and lse, weights
+// 2^(m_s - max)); the order of the sums differs. Batches keep k_combine: there the chunk counts
+// differ per sequence, and it reads only the rows in use, in whole 256-byte pieces.
 template <int K>
 __global__ __launch_bounds__(64) void k_combine_slice(gva::DecodeArgs a) {
   const int lane = threadIdx.x;
-  const int r = lane & 15;
-  const int c = lane >> 4;
+  const int r = lane & 7;
+  const int c = lane >> 3;
   const int j = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int S = a.num_splits;
   const int64_t row0 = static_cast<int64_t>(b) * S * a.H + h;
-  const int d = 16 * j + 4 * c;
+  const int d = 32 * j + 4 * c;
   float4 o[K];
   float m[K], l[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int64_t row = row0 + static_cast<int64_t>(min(r + 16 * k, S - 1)) * a.H;
+    const int64_t row = row0 + static_cast<int64_t>(min(r + 8 * k, S - 1)) * a.H;
     m[k] = a.part_m[row];
     l[k] = a.part_l[row];
     o[k] = *reinterpret_cast<const float4 *>(a.part_o + row * a.d_h + d);
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(64) void k_combine_slice(gva::DecodeArgs a) {
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int keep = r + 16 * k < ns ? -1 : 0;
+    const int keep = r + 8 * k < ns ? -1 : 0;
     m[k] = __int_as_float((__float_as_int(m[k]) & keep) | (__float_as_int(-INFINITY) & ~keep));
     l[k] = __int_as_float(__float_as_int(l[k]) & keep);
     o[k] = make_float4(__int_as_float(__float_as_int(o[k].x) & keep),
@@ -429,10 +431,10 @@ __global__ __launch_bounds__(64) void k_combine_slice(gva::DecodeArgs a) {
     acc.z = fmaf(o[k].z, f, acc.z);
     acc.w = fmaf(o[k].w, f, acc.w);
   }
-  // sums over r (the lanes of a row of 16 hold the same dims); every row of 16 holds all
-  // partial rows' l once, so L is summed over the lanes of one row
+  // sums over r (the 8 lanes of a group hold the same dims); every group of 8 holds all partial
+  // rows' l once, so L is summed over the lanes of one group
 #pragma unroll
-  for (int x = 1; x < 16; x <<= 1) {
+  for (int x = 1; x < 8; x <<= 1) {
     L += __shfl_xor(L, x, 64);
     acc.x += __shfl_xor(acc.x, x, 64);
     acc.y += __shfl_xor(acc.y, x, 64);
@@ -1008,13 +1010,13 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
     }
     return hipGetLastError();
   }
-  if (a.num_ranges == 0 && a.num_splits <= 16 * kCombineSliceMaxK && a.d_h % 16 == 0) {
-    const dim3 grid(a.d_h / 16, a.H, a.B);
-    const int k = (a.num_splits + 15) / 16;
-    if (k <= 2) hipLaunchKernelGGL(k_combine_slice<2>, grid, dim3(64), 0, stream, a);
-    else if (k <= 4) hipLaunchKernelGGL(k_combine_slice<4>, grid, dim3(64), 0, stream, a);
+  if (a.num_ranges == 0 && a.B == 1 && a.num_splits <= 8 * kCombineSliceMaxK && a.d_h % 32 == 0) {
+    const dim3 grid(a.d_h / 32, a.H, 1);
+    const int k = (a.num_splits + 7) / 8;
+    if (k <= 4) hipLaunchKernelGGL(k_combine_slice<4>, grid, dim3(64), 0, stream, a);
     else if (k <= 8) hipLaunchKernelGGL(k_combine_slice<8>, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(k_combine_slice<16>, grid, dim3(64), 0, stream, a);
+    else if (k <= 16) hipLaunchKernelGGL(k_combine_slice<16>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(k_combine_slice<32>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
   }
   int nw = per_seq / 16;
