@@ -179,6 +179,18 @@ def test_f32_rounding_known_values():
     assert list(got) == [1.0, 1.0 + 2.0 ** -22, 1.0 + 2.0 ** -23]
 
 
+def test_cache_bits_known_patterns():
+    """The cache's storage conversion for both element types, against bit patterns written out
+    by hand: 1 is 0x3f80 / 0x3f800000, pi rounds to 0x4049 (3.140625) in bfloat16, 1 + 2^-8 is
+    a tie that goes to the even pattern 0x3f80, -2 is 0xc000 / 0xc0000000."""
+    xs = np.array([1.0, np.pi, 1.0 + 2.0 ** -8, -2.0])
+    assert list(O.to_cache_bits(xs, "bf16")) == [0x3F80, 0x4049, 0x3F80, 0xC000]
+    assert list(O.to_cache_bits(xs, "f32")) == [0x3F800000, 0x40490FDB, 0x3F808000, 0xC0000000]
+    assert list(O.from_cache_bits(np.array([0x3F80, 0x4049, 0xC000], np.uint16), "bf16")) == \
+        [1.0, 3.140625, -2.0]
+    assert list(O.from_cache_bits(np.array([0x3F808000], np.uint32), "f32")) == [1.0 + 2.0 ** -8]
+
+
 # ----------------------------------------------------------------------------------------
 # Cache accounting against the pages' numbers
 # ----------------------------------------------------------------------------------------
