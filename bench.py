@@ -34,6 +34,25 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# Untimed work issued before each secondary timed series. At the start of a burst of work the
+# GPU's clocks dip and recover over about 10-15 ms (the ragged-batch decode kernel's launches go
+# 1.62 -> 1.32 ms in a kernel trace of this bench), so those series start on a settled GPU.
+SETTLE_S = 0.03
+
+
+def settle(fn, torch):
+    """Issues about SETTLE_S seconds of calls of fn back to back and does not wait for them, so
+    the timed series that follows starts with the GPU still busy. One call, waited for, sizes
+    the burst."""
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    dt = max(time.perf_counter() - t, 1e-6)
+    for _ in range(min(int(SETTLE_S / dt) + 1, 4000)):
+        fn()
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -159,7 +178,12 @@ def main():
     value = read_bytes / t_step / 1e9
     log(f"C4 step: {t_step * 1e3:.3f} ms, {value:.1f} GB/s, {plan}")
 
-    # decode launches alone, timed with HIP events on the launch stream
+    # decode launches alone, timed with HIP events on the launch stream after a settling burst
+    def dec_call():
+        gb.gva_decode(dc.dims, dc.cache, B, seq_len, max_len, q_abs, w.scale, out, lse,
+                      num_splits=args.splits, kernel=args.kernel, workspace=ws, stream=stream)
+
+    settle(dec_call, torch)
     n_ev = max(args.steps, 100)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_ev)]
@@ -191,9 +215,8 @@ def main():
     if not args.no_gqa:
         keys = torch.randn(dc.cache.v.shape, generator=gen, device="cuda").to(torch.bfloat16)
         q_g = torch.randn((B, H, w.d_h), generator=gen, device="cuda")
-        for _ in range(3):
-            gb.gva_gqa_decode(dc.dims, dc.cache, keys, B, seq_len, max_len, q_g, w.scale, out, lse,
-                              workspace=ws, stream=stream)
+        settle(lambda: gb.gva_gqa_decode(dc.dims, dc.cache, keys, B, seq_len, max_len, q_g, w.scale,
+                                         out, lse, workspace=ws, stream=stream), torch)
         evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_ev)]
         for e0, e1 in evg:
@@ -236,8 +259,7 @@ def main():
             gb.gva_recon_decode(dc.dims, dc.cache, B, seq_len, max_len, q_r_t, pos, mt_t, rope_r,
                                 max_pos_r, scale_r, out, lse, workspace=ws_r, stream=stream)
 
-        for _ in range(3):
-            recon_call()
+        settle(recon_call, torch)
         evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(20)]
         for e0, e1 in evr:
@@ -286,8 +308,7 @@ def main():
             gb.gva_mla_decode(mdims, dm.cache, B, seq_len, max_len, q_m, scale_m, out_m, lse_m,
                               workspace=ws_m, stream=stream)
 
-        for _ in range(3):
-            mla_call()
+        settle(mla_call, torch)
         evm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(50)]
         for e0, e1 in evm:
@@ -334,17 +355,20 @@ def main():
             for S_l in (64, 128, 256, 0):
                 wsb_l = gb.gva_decode_workspace_bytes(reps[0].dims, 1, ml, S_l)
                 ws_l = torch.zeros(max(wsb_l, 256) // 4, dtype=torch.float32, device="cuda")
-                for k in range(6):
-                    r = reps[k % 3]
+                rot = [0]
+
+                def long_call():
+                    r = reps[rot[0] % 3]
+                    rot[0] += 1
                     gb.gva_decode(r.dims, r.cache, 1, sl, ml, qa, wl.scale, o1, None,
                                   num_splits=S_l, kernel=args.kernel, workspace=ws_l, stream=stream)
+
+                settle(long_call, torch)
                 evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(30)]
-                for k, (e0, e1) in enumerate(evs):
-                    r = reps[k % 3]
+                for e0, e1 in evs:                       # the rotation goes on from the burst's
                     e0.record(stream)
-                    gb.gva_decode(r.dims, r.cache, 1, sl, ml, qa, wl.scale, o1, None,
-                                  num_splits=S_l, kernel=args.kernel, workspace=ws_l, stream=stream)
+                    long_call()
                     e1.record(stream)
                 torch.cuda.synchronize()
                 ts = sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)
@@ -442,13 +466,19 @@ def bench_ceiling(torch, gb, stream, big_bytes, long_bytes, iters=10):
     sink = torch.empty(65536, dtype=torch.int32, device="cuda")
 
     def timed(fn, n):
-        for _ in range(2):
-            fn(0)
+        ctr = [0]                  # fn(k) reads buffer k mod the buffer count: the rotation goes
+                                   # on from the settling burst into the timed calls
+
+        def nxt():
+            fn(ctr[0])
+            ctr[0] += 1
+
+        settle(nxt, torch)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n)]
-        for k, (e0, e1) in enumerate(evs):
+        for e0, e1 in evs:
             e0.record(stream)
-            fn(k)
+            nxt()
             e1.record(stream)
         torch.cuda.synchronize()
         return sorted(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)[n // 2]
@@ -501,8 +531,7 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
         gb.gva_prefill_chunk(dc.dims, dc.cache, B, start, ms, C, q, v_new, kr_new, w.scale, out,
                              lse, stream=stream)
 
-    for _ in range(3):
-        run()
+    settle(run, torch)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
     for e0, e1 in evs:
@@ -534,8 +563,7 @@ def bench_prefill(torch, gb, synth, gen, stream, iters=20):
         gb.gva_decode_step(dc.dims, dc.cache, B, pos, v1, k1, qn1, qr1, M1, sl, ml, w.scale, q1,
                            o1, None, workspace=ws, stream=stream)
 
-    for _ in range(3):
-        step()
+    settle(step, torch)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
     for e0, e1 in evs:
@@ -614,8 +642,13 @@ def bench_small(torch, gb, synth, gen, stream, iters=50):
                 gb.gva_decode(rc.dims, rc.cache, B, sl, ml, qa, w.scale, out, lse, workspace=ws,
                               stream=stream)
             for label, rot in (("decode_mall_warm_us", False), ("decode_mall_defeated_us", True)):
-                for k in range(5):
-                    dec(k if rot else 0)
+                ctr = [0]
+
+                def dec_next():
+                    dec(ctr[0] if rot else 0)
+                    ctr[0] += 1
+
+                settle(dec_next, torch)
                 evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(iters)]
                 for k, (e0, e1) in enumerate(evs):
@@ -626,8 +659,7 @@ def bench_small(torch, gb, synth, gen, stream, iters=50):
                 r[label] = round(sorted(e0.elapsed_time(e1) for e0, e1 in evs)[iters // 2] * 1e3, 1)
             del reps
         for label, fn in (("three_calls_us", three_calls), ("decode_step_us", fused)):
-            for _ in range(5):
-                fn()
+            settle(fn, torch)
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(iters)]
             for e0, e1 in evs:

@@ -24,8 +24,18 @@ def test_stats_separates_grids(tmp_path):
         ["void (anonymous namespace)::k_decode_mfma<4, 4>(gva::DecodeArgs)", 0, 50000, 512, 64, 1, 512, 1, 1],
     ])
     text = ps.stats(str(p), "cmd")
-    assert "| `k_decode_mfma<4, 4>` | 512x8x1 | 512 | 2 | 2.00 | 1.00 | 3.00 |" in text
-    assert "| `k_decode_mfma<4, 4>` | 512x64x1 | 512 | 1 | 50.00 |" in text
+    assert "| `k_decode_mfma<4, 4>` | 512x8x1 | 512 | 2 | 2.00 | 2.00 | 1.00 | 3.00 |" in text
+    assert "| `k_decode_mfma<4, 4>` | 512x64x1 | 512 | 1 | 50.00 | 50.00 |" in text
+
+
+def test_stats_median_of_odd_and_even_counts(tmp_path):
+    p = tmp_path / "trace.csv"
+    name = "void (anonymous namespace)::k_combine(gva::DecodeArgs)"
+    _write(p, TRACE_COLS, [[name, 0, d, 64, 1, 1, 64, 1, 1] for d in (1000, 9000, 2000)] +
+                          [[name, 0, d, 128, 1, 1, 64, 1, 1] for d in (4000, 1000, 3000, 2000)])
+    text = ps.stats(str(p), "cmd")
+    assert "| `k_combine` | 64x1x1 | 64 | 3 | 4.00 | 2.00 | 1.00 | 9.00 |" in text
+    assert "| `k_combine` | 128x1x1 | 64 | 4 | 2.50 | 2.50 | 1.00 | 4.00 |" in text
 
 
 def test_traffic_calibrates_against_copy(tmp_path):

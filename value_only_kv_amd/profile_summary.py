@@ -83,12 +83,15 @@ def stats(trace_csv: str, cmd: str, note: str = "", splits=(), only=()) -> str:
     lines = ["# rocprofv3 kernel trace summary", "", "Command:", "", "```", cmd, "```", "",
              "Per kernel and launch grid (grid in threads x, y, z; work-group size); durations "
              "in microseconds.", "", *([note, ""] if note else []),
-             "| kernel | grid | wg | calls | avg us | min us | max us | total ms |",
-             "|---|---|---|---|---|---|---|---|"]
+             "| kernel | grid | wg | calls | avg us | median us | min us | max us | total ms |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for (k, g, wg), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{k}` | {g[0]}x{g[1]}x{g[2]} | {wg} | {len(v)} | "
-                     f"{sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} | "
-                     f"{sum(v) / 1e6:.3f} |")
+        srt = sorted(v)
+        n = len(srt)
+        med = srt[n // 2] if n % 2 else (srt[n // 2 - 1] + srt[n // 2]) / 2
+        lines.append(f"| `{k}` | {g[0]}x{g[1]}x{g[2]} | {wg} | {n} | "
+                     f"{sum(v) / n / 1e3:.2f} | {med / 1e3:.2f} | {min(v) / 1e3:.2f} | "
+                     f"{max(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
     return "\n".join(lines) + "\n"
 
 
