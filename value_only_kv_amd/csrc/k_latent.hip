@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_decode(gva::DecodeArgs a) {
         src = static_cast<const uint16_t *>(a.kr) + bb * a.kr_sb + row * a.kr_st + e;
       }
       __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(buf + unit_off(kb, ks, kSteps)),
-                                       16, 0, 0);
+                                       16, 0, 2);   // non-temporal (nt)
     }
   };
   auto stage = [&](uint8_t *buf, int32_t pg0, int32_t pg1, int j0) __attribute__((always_inline)) {
