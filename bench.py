@@ -40,6 +40,28 @@ def log(*a):
 SETTLE_S = 0.03
 
 
+def kernel_medians(fn, n, torch):
+    """Median device time (us) of each kernel that n calls of fn launch, from the PyTorch
+    profiler's device activity records (hardware timestamps of every kernel the process
+    launches, the library's included). None if the profiler cannot record them."""
+    try:
+        from torch.profiler import profile, ProfilerActivity
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+        by = {}
+        for e in prof.events():
+            if e.device_type.name != "CUDA":
+                continue
+            name = e.name.replace("void (anonymous namespace)::", "").split("(gva::")[0]
+            by.setdefault(name, []).append(float(getattr(e, "device_time", None) or e.cuda_time))
+        return {k: round(float(np.median(v)), 2) for k, v in by.items()} or None
+    except Exception as exc:  # a profiler that cannot start leaves the measurement out
+        log(f"kernel durations not recorded: {exc!r}")
+        return None
+
+
 def settle(fn, torch):
     """Issues about SETTLE_S seconds of calls of fn back to back and does not wait for them, so
     the timed series that follows starts with the GPU still busy. One call, waited for, sizes
@@ -378,6 +400,18 @@ def main():
                                    "frac_of_hbm_peak": round(rb / t_med / 1e9 / HBM_PEAK_GBS, 4),
                                    "seq_steps_per_s": round(1.0 / t_med, 1)}
                 log(f"{name} T={ml} S={S_l or 'auto'}: {t_med * 1e6:.1f} us, {rb / t_med / 1e9:.1f} GB/s")
+                if S_l == 0:
+                    # the same calls' kernels one by one: the decode kernel's own rate beside
+                    # the call's (which adds the combine launch)
+                    km = kernel_medians(long_call, 30, torch)
+                    dk = [v for k, v in (km or {}).items() if k.startswith("k_decode_mfma")]
+                    per_s["auto"]["kernel_us"] = km
+                    if dk:
+                        per_s["auto"]["decode_kernel_GB_s"] = round(rb / dk[0] / 1e3, 1)
+                        per_s["auto"]["decode_kernel_frac_of_hbm_peak"] = round(
+                            rb / dk[0] / 1e3 / HBM_PEAK_GBS, 4)
+                        log(f"{name} S=auto kernels: {km}; decode kernel "
+                            f"{rb / dk[0] / 1e3:.1f} GB/s")
             result_extra[name] = {"T": ml, "d_r": d_r, "cache_bytes": rb,
                                   "replicas_rotated": 3, "by_splits": per_s}
             del reps
