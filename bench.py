@@ -41,12 +41,14 @@ SETTLE_S = 0.03
 
 
 def kernel_medians(fn, n, torch):
-    """Median device time (us) of each kernel that n calls of fn launch, from the PyTorch
-    profiler's device activity records (hardware timestamps of every kernel the process
-    launches, the library's included). None if the profiler cannot record them."""
+    """Median device time (us) of each kernel that the last n of a settling burst plus n calls
+    of fn launch, from the PyTorch profiler's device activity records (hardware timestamps of
+    every kernel the process launches, the library's included). None if the profiler cannot
+    record them."""
     try:
         from torch.profiler import profile, ProfilerActivity
         with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            settle(fn, torch)
             for _ in range(n):
                 fn()
             torch.cuda.synchronize()
@@ -55,8 +57,13 @@ def kernel_medians(fn, n, torch):
             if e.device_type.name != "CUDA":
                 continue
             name = e.name.replace("void (anonymous namespace)::", "").split("(gva::")[0]
-            by.setdefault(name, []).append(float(getattr(e, "device_time", None) or e.cuda_time))
-        return {k: round(float(np.median(v)), 2) for k, v in by.items()} or None
+            dur = float(getattr(e, "device_time", None) or e.cuda_time)
+            by.setdefault(name, []).append((e.time_range.start, dur))
+        med = {}
+        for k, v in by.items():
+            last = [d for _, d in sorted(v)[-n:]]          # the n calls after the burst
+            med[k] = round(float(np.median(last)), 2)
+        return med or None
     except Exception as exc:  # a profiler that cannot start leaves the measurement out
         log(f"kernel durations not recorded: {exc!r}")
         return None
@@ -221,6 +228,9 @@ def main():
     dec_gbs = read_bytes / t_dec / 1e9
     log(f"C4 decode (split decode + combine): mean {t_dec * 1e3:.3f} ms (p10 {p10 * 1e3:.3f}, "
         f"median {p50 * 1e3:.3f}, p90 {p90 * 1e3:.3f}), {dec_gbs:.1f} GB/s")
+    # the same calls' kernels one by one (the call above adds the combine's launch)
+    dec_kernels = kernel_medians(dec_call, 20, torch)
+    log(f"C4 decode kernels (median us): {dec_kernels}")
     # HBM bytes per call from the committed counter runs, when they were taken on these sources
     # and this configuration
     traffic = None
@@ -474,7 +484,8 @@ def main():
         "decode_only": {"ms": round(t_dec * 1e3, 4), "GB_s": round(dec_gbs, 1),
                         "seq_steps_per_s": round(B / t_dec, 1), "launches": n_ev,
                         "ms_p10_p50_p90": [round(p10 * 1e3, 4), round(p50 * 1e3, 4),
-                                           round(p90 * 1e3, 4)]},
+                                           round(p90 * 1e3, 4)],
+                        "kernel_us": dec_kernels},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "long_context": result_extra,
