@@ -40,11 +40,16 @@ def log(*a):
 SETTLE_S = 0.03
 
 
-def kernel_medians(fn, n, torch):
+def kernel_medians(fn, n, torch, call_s):
     """Median device time (us) of each kernel that the last n of a settling burst plus n calls
     of fn launch, from the PyTorch profiler's device activity records (hardware timestamps of
-    every kernel the process launches, the library's included). None if the profiler cannot
-    record them."""
+    every kernel the process launches, the library's included). None when another profiler is
+    loaded (rocprofv3's tool takes the same hooks), when the profiler cannot record, or when the
+    kernels' medians do not add up to within 50% of call_s, the event-timed call."""
+    if "rocprofiler" in os.environ.get("LD_PRELOAD", "") or any(
+            k.startswith("ROCPROFILER_") for k in os.environ):
+        log("kernel durations not recorded: another profiler is loaded")
+        return None
     try:
         from torch.profiler import profile, ProfilerActivity
         with profile(activities=[ProfilerActivity.CUDA]) as prof:
@@ -63,7 +68,11 @@ def kernel_medians(fn, n, torch):
         for k, v in by.items():
             last = [d for _, d in sorted(v)[-n:]]          # the n calls after the burst
             med[k] = round(float(np.median(last)), 2)
-        return med or None
+        total = sum(med.values())
+        if not med or not 0.5 * call_s * 1e6 <= total <= 1.5 * call_s * 1e6:
+            log(f"kernel durations not recorded: {med} against a {call_s * 1e6:.1f} us call")
+            return None
+        return med
     except Exception as exc:  # a profiler that cannot start leaves the measurement out
         log(f"kernel durations not recorded: {exc!r}")
         return None
@@ -229,7 +238,7 @@ def main():
     log(f"C4 decode (split decode + combine): mean {t_dec * 1e3:.3f} ms (p10 {p10 * 1e3:.3f}, "
         f"median {p50 * 1e3:.3f}, p90 {p90 * 1e3:.3f}), {dec_gbs:.1f} GB/s")
     # the same calls' kernels one by one (the call above adds the combine's launch)
-    dec_kernels = kernel_medians(dec_call, 20, torch)
+    dec_kernels = kernel_medians(dec_call, 20, torch, t_dec)
     log(f"C4 decode kernels (median us): {dec_kernels}")
     # HBM bytes per call from the committed counter runs, when they were taken on these sources
     # and this configuration
@@ -413,7 +422,7 @@ def main():
                 if S_l == 0:
                     # the same calls' kernels one by one: the decode kernel's own rate beside
                     # the call's (which adds the combine launch)
-                    km = kernel_medians(long_call, 30, torch)
+                    km = kernel_medians(long_call, 30, torch, t_med)
                     dk = [v for k, v in (km or {}).items() if k.startswith("k_decode_mfma")]
                     per_s["auto"]["kernel_us"] = km
                     if dk:
