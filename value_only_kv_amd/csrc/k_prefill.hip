@@ -205,6 +205,13 @@ struct StageSrc {
   int64_t sb[Stage<KS, W>::kPerWave], st[Stage<KS, W>::kPerWave];
 };
 
+// The positional key's k-step holds 32 elements. With d_r <= 16 its upper 16 hold a copy of the
+// lower 16, and the query's operand there holds the lo parts of the positional query, so one
+// product adds both kr . hi and kr . lo (the lo product of that step is left out); above 16 the
+// step holds kr zero-padded to 32 and takes a hi and a lo product like the value steps. Lane
+// (n, q) holds elements 8 rope_lane(q) .. + 7 of the key.
+__device__ __forceinline__ int rope_lane(int q, int d_r) { return d_r <= 16 ? (q & 1) : q; }
+
 template <int KS, int W>
 __device__ __forceinline__ StageSrc<KS, W> stage_src(const gva::DecodeArgs &a, int g, int wave,
                                                      int q) {
@@ -217,8 +224,9 @@ __device__ __forceinline__ StageSrc<KS, W> stage_src(const gva::DecodeArgs &a, i
       src.sb[i] = a.v_sb;
       src.st[i] = a.v_st;
     } else {
-      // lanes with 8 q >= d_r read the last 8 positional-key elements; the store zeroes them
-      src.base[i] = static_cast<const uint16_t *>(a.kr) + min(8 * q, a.d_r - 8);
+      // elements 8 rope_lane(q) ..: lanes past d_r read the last 8 positional-key elements and
+      // the store zeroes them
+      src.base[i] = static_cast<const uint16_t *>(a.kr) + min(8 * rope_lane(q, a.d_r), a.d_r - 8);
       src.sb[i] = a.kr_sb;
       src.st[i] = a.kr_st;
     }
@@ -257,7 +265,7 @@ __device__ __forceinline__ void stage_store(uint16_t *nat, int wave, int n, int 
     const int kb = unit & 1;
     const int ks = unit >> 1;
     u32x4 w = st.u[i];
-    if (ks == KS && 8 * q >= d_r) w = u32x4{0u, 0u, 0u, 0u};   // zero padding up to 32
+    if (ks == KS && 8 * rope_lane(q, d_r) >= d_r) w = u32x4{0u, 0u, 0u, 0u};   // zero padding
     *reinterpret_cast<u32x4 *>(nat + (16 * kb + n) * L::kNatStride + 32 * ks + 8 * q) = w;
   }
 }
@@ -301,6 +309,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
   if (row0 >= nrows) return;                           // uniform per work-group
   const int P0 = p.start[b];
   const int row_len = a.d_h + a.d_r;
+  const bool rope_packed = a.d_r <= 16;                // one product for the positional step
   const float qnan = __int_as_float(0x7fc00000);
   const int cap = a.max_blocks << a.log2_bs;
   // A bad start, or a chunk that does not fit the block table or the RoPE table (the chunk
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
           x0 = qp[32 * ks + 8 * q + 2 * i];
           x1 = qp[32 * ks + 8 * q + 2 * i + 1];
         } else {
-          const int e = 8 * q + 2 * i;
+          const int e = 8 * rope_lane(q, a.d_r) + 2 * i;
           x0 = e < a.d_r ? qp[a.d_h + e] : 0.0f;
           x1 = e + 1 < a.d_r ? qp[a.d_h + e + 1] : 0.0f;
         }
@@ -343,7 +352,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
         hi[i] = w;
         lo[i] = pack2(x0 - low_bf16(w), x1 - high_bf16(w));
       }
-      QH[rt][ks] = as_bf16(hi);
+      // the packed positional step: the upper half of the operand (q >= 2) is the lo part
+      QH[rt][ks] = as_bf16(ks == KS && rope_packed && q >= 2 ? lo : hi);
       QL[rt][ks] = as_bf16(lo);
     }
   }
@@ -389,7 +399,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_prefill(gva::PrefillArgs p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           S[rt][tb] = mfma(as_bf16(ka), QH[rt][ks], S[rt][tb]);
-          S[rt][tb] = mfma(as_bf16(ka), QL[rt][ks], S[rt][tb]);
+          if (ks < KS || !rope_packed)                   // uniform
+            S[rt][tb] = mfma(as_bf16(ka), QL[rt][ks], S[rt][tb]);
         }
       }
     }
