@@ -139,23 +139,36 @@ __device__ __forceinline__ void absorb_tile(const AbsorbArgs &x, int h, int ty, 
   const int i = tid >> 3;                      // row of the tile
   const int tq = tid & 7;                      // tokens tq + 8 k
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // the positions of this thread's tokens, requested before anything waits
+  int32_t tpos[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tpos[k] = tq + 8 * k < nt ? q_pos[k0 + tq + 8 * k] : 0;
   const float4 *Mh = reinterpret_cast<const float4 *>(M + (static_cast<int64_t>(h) * d_h + i0) * d_n);
+  // each thread stages kStage float4 of either operand per chunk; all of its loads go out
+  // before the first LDS store (one round of loads per chunk, not one per float4)
+  constexpr int kStage = kAbsQ * kJ4 / kAbsThreads;
+  static_assert(kAbsQ == kAbsRows && kStage * kAbsThreads == kAbsQ * kJ4, "staging map");
   for (int jc = 0; jc < dn4; jc += kJ4) {
     const int nj = min(kJ4, dn4 - jc);
-    for (int idx = tid; idx < kAbsQ * kJ4; idx += kAbsThreads) {
+    float4 vq[kStage], vm[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int idx = tid + u * kAbsThreads;
+      const int t = idx / kJ4;                  // token (q_nope) or row (M) of the tile
+      const int j4 = idx - t * kJ4;
+      vq[u] = float4{0.f, 0.f, 0.f, 0.f};
+      vm[u] = float4{0.f, 0.f, 0.f, 0.f};
+      if (t < nt && j4 < nj)
+        vq[u] = reinterpret_cast<const float4 *>(q_nope + (static_cast<int64_t>(k0 + t) * H + h) * d_n)[jc + j4];
+      if (t < ni && j4 < nj) vm[u] = Mh[static_cast<int64_t>(t) * dn4 + jc + j4];
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int idx = tid + u * kAbsThreads;
       const int t = idx / kJ4;
       const int j4 = idx - t * kJ4;
-      float4 v = {0.f, 0.f, 0.f, 0.f};
-      if (t < nt && j4 < nj)
-        v = reinterpret_cast<const float4 *>(q_nope + (static_cast<int64_t>(k0 + t) * H + h) * d_n)[jc + j4];
-      qs[t * kStride4 + j4] = v;
-    }
-    for (int idx = tid; idx < kAbsRows * kJ4; idx += kAbsThreads) {
-      const int r = idx / kJ4;
-      const int j4 = idx - r * kJ4;
-      float4 v = {0.f, 0.f, 0.f, 0.f};
-      if (r < ni && j4 < nj) v = Mh[static_cast<int64_t>(r) * dn4 + jc + j4];
-      ms[r * kStride4 + j4] = v;
+      qs[t * kStride4 + j4] = vq[u];
+      ms[t * kStride4 + j4] = vm[u];
     }
     __syncthreads();
     for (int j4 = 0; j4 < nj; ++j4) {
@@ -176,7 +189,7 @@ __device__ __forceinline__ void absorb_tile(const AbsorbArgs &x, int h, int ty, 
     for (int k = 0; k < 4; ++k) {
       const int t = tq + 8 * k;
       if (t >= nt) continue;
-      const int p = q_pos[k0 + t];
+      const int p = tpos[k];
       const bool bad = p < 0 || p >= max_pos;
       q_abs[(static_cast<int64_t>(k0 + t) * H + h) * row + i0 + i] = bad ? __int_as_float(0x7fc00000) : acc[k];
     }
